@@ -1,0 +1,131 @@
+// Device build of the synthetic-input generator (definitions in synth_core.h),
+// plus a plain 16-byte copy kernel used to calibrate HBM byte counters and to
+// give a reachable-bandwidth reference line.  Test and bench infrastructure:
+// the shard-step library does not link against it.
+#include <hip/hip_runtime.h>
+
+#define SYNTH_FN __host__ __device__ static inline
+#include "synth_core.h"
+
+namespace {
+
+constexpr int kBlock = 256;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(kBlock)
+contrib_rows_kernel(uint64_t seed, uint32_t step, int32_t dtype, double sigma, double scale,
+                    uint64_t thresh, double mult, int64_t idx0, int64_t len, int64_t stride,
+                    uint16_t* out) {
+    const uint32_t k = blockIdx.y;
+    const uint64_t kc = synth_stream_key(seed, SYNTH_STREAM_CONTRIB, step, k);
+    const uint64_t ko = synth_stream_key(seed, SYNTH_STREAM_OUTLIER, step, k);
+    uint16_t* row = out + (int64_t)k * stride;
+    const int64_t nvec = stride / 8;  // stride is a multiple of 8 (checked on the host)
+    for (int64_t v = (int64_t)blockIdx.x * kBlock + threadIdx.x; v < nvec;
+         v += (int64_t)gridDim.x * kBlock) {
+        uint16_t h[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t i = v * 8 + j;
+            h[j] = i < len ? synth_contrib_value(kc, ko, thresh, sigma, scale, mult, dtype,
+                                                 (uint64_t)(idx0 + i))
+                           : (uint16_t)0;
+        }
+        uint4 w;
+        w.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+        w.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+        w.z = (uint32_t)h[4] | ((uint32_t)h[5] << 16);
+        w.w = (uint32_t)h[6] | ((uint32_t)h[7] << 16);
+        *reinterpret_cast<uint4*>(row + v * 8) = w;
+    }
+}
+
+__global__ void __launch_bounds__(kBlock)
+master_range_kernel(uint64_t seed, double sigma, int64_t idx0, int64_t len, float* out) {
+    const uint64_t km = synth_stream_key(seed, SYNTH_STREAM_MASTER, 0u, 0u);
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < len;
+         i += (int64_t)gridDim.x * kBlock)
+        out[i] = synth_master_value(km, sigma, (uint64_t)(idx0 + i));
+}
+
+__global__ void __launch_bounds__(kBlock)
+param_range_kernel(uint64_t seed, double sigma, int32_t dtype, int64_t idx0, int64_t len,
+                   uint16_t* out) {
+    const uint64_t km = synth_stream_key(seed, SYNTH_STREAM_MASTER, 0u, 0u);
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < len;
+         i += (int64_t)gridDim.x * kBlock) {
+        const float f = synth_master_value(km, sigma, (uint64_t)(idx0 + i));
+        out[i] = dtype == SYNTH_BF16 ? synth_f32_to_bf16(f) : synth_f32_to_f16(f);
+    }
+}
+
+__global__ void __launch_bounds__(kBlock)
+copy16_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t nvec) {
+    for (int64_t v = (int64_t)blockIdx.x * kBlock + threadIdx.x; v < nvec;
+         v += (int64_t)gridDim.x * kBlock)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + v), dst + v);
+}
+
+unsigned grid_for(int64_t work, int64_t per_block) {
+    int64_t g = (work + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > 65536) g = 65536;
+    return (unsigned)g;
+}
+
+int status(hipError_t e) { return e == hipSuccess ? 0 : -(int)e - 1000; }
+
+}  // namespace
+
+extern "C" {
+
+// Contribution rows k = 0..n-1 of global elements [idx0, idx0+len) into a
+// device buffer laid out [n][stride] (16-bit storage); columns [len, stride)
+// are zero.  stride must be a multiple of 8 and `out` 16-byte aligned.
+int synth_gpu_contrib_rows(uint64_t seed, uint32_t step, int32_t n, int32_t dtype, double sigma,
+                           double scale, uint64_t outlier_thresh, double outlier_mult, int64_t idx0,
+                           int64_t len, int64_t stride, void* out, void* stream) {
+    if (n < 1 || n > 65535 || stride % 8 != 0 || len > stride || len < 0 || out == nullptr ||
+        (reinterpret_cast<uintptr_t>(out) & 15u) != 0)
+        return -1;
+    if (stride == 0) return 0;
+    dim3 grid(grid_for(stride / 8, kBlock), (unsigned)n);
+    hipLaunchKernelGGL(contrib_rows_kernel, grid, dim3(kBlock), 0, (hipStream_t)stream, seed, step,
+                       dtype, sigma, scale, outlier_thresh, outlier_mult, idx0, len, stride,
+                       (uint16_t*)out);
+    return status(hipGetLastError());
+}
+
+int synth_gpu_master_range(uint64_t seed, double sigma, int64_t idx0, int64_t len, float* out,
+                           void* stream) {
+    if (len < 0 || (len > 0 && out == nullptr)) return -1;
+    if (len == 0) return 0;
+    hipLaunchKernelGGL(master_range_kernel, dim3(grid_for(len, kBlock)), dim3(kBlock), 0,
+                       (hipStream_t)stream, seed, sigma, idx0, len, out);
+    return status(hipGetLastError());
+}
+
+// Initial 16-bit parameters: the generator's master values rounded to dtype.
+int synth_gpu_param_range(uint64_t seed, double sigma, int32_t dtype, int64_t idx0, int64_t len,
+                          void* out, void* stream) {
+    if (len < 0 || (len > 0 && out == nullptr)) return -1;
+    if (len == 0) return 0;
+    hipLaunchKernelGGL(param_range_kernel, dim3(grid_for(len, kBlock)), dim3(kBlock), 0,
+                       (hipStream_t)stream, seed, sigma, dtype, idx0, len, (uint16_t*)out);
+    return status(hipGetLastError());
+}
+
+// Plain streaming copy of `bytes` (multiple of 16, both pointers 16-byte aligned).
+int synth_gpu_copy(const void* src, void* dst, int64_t bytes, int32_t grid, void* stream) {
+    if (bytes < 0 || bytes % 16 != 0 || src == nullptr || dst == nullptr ||
+        ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) != 0)
+        return -1;
+    if (bytes == 0) return 0;
+    const int64_t nvec = bytes / 16;
+    unsigned g = grid > 0 ? (unsigned)grid : grid_for(nvec, kBlock * 8);
+    hipLaunchKernelGGL(copy16_kernel, dim3(g), dim3(kBlock), 0, (hipStream_t)stream,
+                       (const u32x4*)src, (u32x4*)dst, nvec);
+    return status(hipGetLastError());
+}
+
+}  // extern "C"
