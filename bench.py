@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the ZeRO per-rank shard step on one MI355X.
+
+A step is one pass of the whole hot path over one rank's shard with its N
+gradient contributions already resident in HBM: reduce + unscale + average,
+overflow check and global norm, Adam(W) on the fp32 master/m/v, cast into the
+rank's slot of the full 16-bit parameter buffer (plus, on the fused path, the
+step decision and the restore check; on the two-pass path, the g buffer).
+
+Prints ONE JSON line.  ``value`` is the effective bandwidth: the step's
+algorithmic bytes (2N + 26 per element fused, 2N + 34 two-pass) divided by
+the measured time per step.  ``roofline`` reports the dominant kernel against
+the 8 TB/s HBM peak with its own HIP-event timing; ``cpu_baseline`` times the
+CPU oracle on a bounded sample of the same workload on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused ZeRO shard step effective GB/s + % of HBM peak (1 MI355X)"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "psi1.3e10_n8_dynscale"
+
+
+def _fmt(x, nd=3):
+    return float(f"{x:.{nd}g}") if x is not None else None
+
+
+def setup(w, torch, synth, Z):
+    """Buffers of the measured rank, inputs generated in HBM."""
+    rank = w.ranks[-1]
+    shard, off, valid = Z.zero_partition(w.psi, w.nranks, rank)
+    stride = w.stride
+    dev = torch.device("cuda", 0)
+    tdt = torch.float16 if w.dtype == Z.F16 else torch.bfloat16
+    contrib = torch.empty((w.nranks, stride), dtype=tdt, device=dev)
+    synth.gpu_contrib_rows(contrib, w.seed, 1, w.dtype, w.contrib_sigma, w.contrib_scale,
+                           w.outlier_p, w.outlier_mult, off, valid)
+    p0 = torch.empty(valid, dtype=torch.float32, device=dev)
+    synth.gpu_master_range(p0, w.seed, w.master_sigma, off)
+    state0 = (p0, torch.zeros_like(p0), torch.zeros_like(p0))
+    fused = w.max_grad_norm <= 0
+    state1 = (torch.empty_like(p0), torch.zeros_like(p0), torch.zeros_like(p0)) if fused else None
+    g = None if fused else torch.empty_like(p0)
+    gather = torch.empty(w.psi, dtype=tdt, device=dev)
+    synth.gpu_param_range(gather, w.seed, w.master_sigma, w.dtype, 0)
+    hp = Z.hparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                   max_grad_norm=w.max_grad_norm, scaler=w.scaler, min_scale=w.min_scale,
+                   growth_interval=w.growth_interval)
+    st = Z.ShardStep(w.nranks, stride, valid, off, w.dtype, w.dtype, hp, state0, state1, g,
+                     w.loss_scale)
+    torch.cuda.synchronize()
+    return dict(rank=rank, shard=shard, off=off, valid=valid, stride=stride, contrib=contrib,
+                gather=gather, step=st, fused=fused)
+
+
+def timed_steps(b, steps, warmup, torch, Z):
+    """Runs warmup + timed steps; events around the whole loop and around each
+    launch of the dominant kernel (the fused pass, or the Adam pass)."""
+    st, contrib, gather = b["step"], b["contrib"], b["gather"]
+    for _ in range(warmup):
+        st.step(contrib, gather)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    ev_red = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hp, n, stride, valid, off = st.hp, st.nranks, st.stride, st.valid_len, st.offset
+    t0.record()
+    for i in range(steps):
+        if b["fused"]:
+            ev[i][0].record()
+            Z.zero_fused_step(contrib, st.dtype, n, stride, st.state0, st.state1, valid, gather,
+                              st.gather_dtype, off, hp, st.ctrl, st.ws)
+            ev[i][1].record()
+            Z.zero_grad_norm_overflow([st.ws], [valid], [st.ctrl], hp, True)
+            Z.zero_fused_restore(st.state0, st.state1, valid, gather, st.gather_dtype, off,
+                                 st.ctrl)
+        else:
+            ev_red[i][0].record()
+            Z.zero_reduce_grads(contrib, st.dtype, n, stride, valid, st.ctrl, st.g, st.ws)
+            ev_red[i][1].record()
+            Z.zero_grad_norm_overflow([st.ws], [valid], [st.ctrl], hp, False)
+            ev[i][0].record()
+            Z.zero_adam_step(st.state0, st.g, valid, hp, st.ctrl, gather, st.gather_dtype, off)
+            ev[i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    kern_ms = [a.elapsed_time(c) for a, c in ev]
+    red_ms = [a.elapsed_time(c) for a, c in ev_red] if not b["fused"] else []
+    ctrl = st.ctrl_dict()
+    return total_ms / steps, kern_ms, red_ms, ctrl
+
+
+def copy_bandwidth(torch, synth, nbytes=8 << 30, reps=10):
+    """Plain device copy: a reachable-bandwidth reference line."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        synth.gpu_copy(src, dst, nbytes)
+    torch.cuda.synchronize()
+    a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        synth.gpu_copy(src, dst, nbytes)
+    c.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(c) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9, ms
+
+
+def cpu_baseline(w, sample_elems):
+    """The CPU oracle, single-threaded, timed on one step of a contiguous sample
+    of the same shard (inputs generated beforehand, not timed)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle as O
+    import synth
+    rank = w.ranks[-1]
+    _, off, valid = O.partition(w.psi, w.nranks, rank)
+    S = min(sample_elems, valid)
+    C = np.empty((w.nranks, S), np.uint16)
+    chunk = 1 << 22
+
+    def gen(i0):
+        n = min(chunk, S - i0)
+        part = synth.contrib_rows(w.seed, 1, w.nranks, w.dtype, w.contrib_sigma, w.contrib_scale,
+                                  w.outlier_p, w.outlier_mult, off + i0, n)
+        C[:, i0:i0 + n] = part
+
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(gen, range(0, S, chunk)))
+    p = synth.master_range(w.seed, w.master_sigma, off, S)
+    m = np.zeros_like(p)
+    v = np.zeros_like(p)
+    hp = O.hparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                   max_grad_norm=w.max_grad_norm, scaler=w.scaler, min_scale=w.min_scale,
+                   growth_interval=w.growth_interval)
+    st = O.new_scalars(w.loss_scale)
+    t0 = time.perf_counter()
+    g, flag = O.reduce(C, w.dtype, S, O.inv_scale(w.nranks, st.scale))
+    rep = O.finalize(hp, st, flag, O.SumSq().add(g))
+    if not rep.skip:
+        O.adam(p, m, v, g, hp, rep.clip, st.pow1, st.pow2)
+        O.cast(p, w.dtype)
+    dt = time.perf_counter() - t0
+    gbps = w.bytes_per_elem * S / dt / 1e9
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": _fmt(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"one step over {S} contiguous elements of the measured shard "
+                      f"({S / valid:.2%} of it), single-threaded C oracle, {dt:.2f} s; "
+                      f"host: {cpu_model}, 1 of {os.cpu_count()} cores",
+            "elements_per_s": _fmt(S / dt, 4)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-sample", type=int, default=96 << 20,
+                    help="elements of the shard the CPU oracle baseline steps over")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy", action="store_true")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="run only the plain copy kernel (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one rank's shard step on ONE GPU; this build has no multi-GPU "
+              "path (collectives are out of its scope). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import zero_partitioned_mixed_amd as Z
+    from synth import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.init()
+    if args.copy_only:
+        gbps, ms = copy_bandwidth(torch, synth)
+        print(json.dumps({"copy_gbps": _fmt(gbps, 4), "copy_ms": _fmt(ms, 4), "bytes": 2 * (8 << 30)}))
+        return
+
+    w = workloads.BY_NAME[args.workload]
+    b = setup(w, torch, synth, Z)
+    ms_step, kern_ms, red_ms, ctrl = timed_steps(b, args.steps, args.warmup, torch, Z)
+    valid = b["valid"]
+    step_bytes = w.bytes_per_elem * valid
+    gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    if b["fused"]:
+        kern_name = "fused_kernel"
+        kern_bytes = step_bytes
+    else:
+        kern_name = "adam_kernel"
+        kern_bytes = (4 + 26) * valid  # g + master/m/v in and out + the 16-bit slot
+    kern_gbps = kern_bytes / (kern_avg * 1e-3) / 1e9
+    del b
+    torch.cuda.empty_cache()
+
+    out = {
+        "metric": METRIC,
+        "value": _fmt(gbps, 5),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": _fmt(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "psi": w.psi, "nranks": w.nranks, "rank": w.ranks[-1],
+                   "shard_elems": valid, "variant": w.variant,
+                   "contrib_dtype": "fp16" if w.dtype == Z.F16 else "bf16",
+                   "bytes_per_elem": w.bytes_per_elem, "step_bytes": step_bytes},
+        "pct_hbm_peak": _fmt(100 * gbps / HBM_PEAK_GBPS, 4),
+        "elements_per_s": _fmt(valid / (ms_step * 1e-3), 5),
+        "roofline": {"bound": "hbm", "kernel": kern_name, "achieved": _fmt(kern_gbps, 5),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": _fmt(kern_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel_ms": _fmt(kern_avg, 5), "bytes_per_launch": kern_bytes},
+        "last_step": {"norm": ctrl["norm"], "skip": ctrl["skip"], "t": ctrl["t"],
+                      "loss_scale": ctrl["loss_scale"]},
+    }
+    if red_ms:
+        red_avg = sum(red_ms) / len(red_ms)
+        out["reduce_kernel"] = {"ms": _fmt(red_avg, 5),
+                                "gbps": _fmt((2 * w.nranks + 4) * valid / (red_avg * 1e-3) / 1e9, 5)}
+    if not args.no_copy:
+        cg, _ = copy_bandwidth(torch, synth)
+        out["copy_gbps"] = _fmt(cg, 5)
+        out["pct_of_copy"] = _fmt(100 * gbps / cg, 4)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,226 @@
+/* zero_shard.h -- C ABI of the ZeRO per-rank shard step on AMD Instinct MI355X (gfx950).
+ *
+ * One data-parallel rank owns a contiguous slice ("shard") of a flat buffer of
+ * Psi parameters.  After the gradient reduce-scatter, the rank holds the N
+ * ranks' 16-bit gradient contributions for its slice.  The shard step
+ *   1. sums them in fp32, removes the loss scale and averages,
+ *   2. checks for inf/NaN and computes the global L2 norm (with optional
+ *      clipping and loss-scale-driven skipping),
+ *   3. runs mixed-precision Adam(W) on the fp32 master weights, momentum and
+ *      variance of the slice,
+ *   4. casts the new master weights to fp16/bf16 into the rank's slot of the
+ *      full parameter buffer that the all-gather fills.
+ * Sources (page titles and sections):
+ *   "CMU 11-868 L18: How ZeRO Cuts Data-Parallel Memory", Mechanism 1, steps 3-6
+ *     (reduce-scatter to fp32, update own slice of variance/momentum/params,
+ *     copy to fp16, all-gather);
+ *   "ZeRO: Memory Optimizations Toward Training Trillion Parameter Models"
+ *     (paper-graph summary), 3.4: model-state analysis (16 Psi bill), Stage 1
+ *     (Pos) and Stage 2 (Pos+g), and the residual-state note on gradient-norm
+ *     buffers;
+ *   "zero-stages-simulation" README: flat partitioning into N near-equal
+ *     contiguous chunks, GPU r owns chunk r;
+ *   "ZeRO: Memory Optimization for Large Models" (lesson), Stage 1 and 2;
+ *   "ZeRO Stage 1/2/3" guide, section 5 (AdamW with weight decay).
+ *
+ * Conventions for every call below.
+ *   - Pointers named *_dev are device pointers (hipMalloc'd or torch tensors);
+ *     all other pointers are host pointers.  Every buffer is owned by the
+ *     caller.  The library never allocates or frees device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls that touch device memory only enqueue work on `stream` and return;
+ *     they never synchronise.  Results are visible after the caller syncs.
+ *   - Arguments are validated before anything is enqueued.  On a nonzero
+ *     return nothing was enqueued and nothing was written; zero_last_error()
+ *     describes the problem.  Faults inside kernels surface at the next sync.
+ *   - 16-bit data is passed as raw storage (uint16 bit patterns); `dtype`
+ *     selects ZERO_F16 (IEEE binary16) or ZERO_BF16 (bfloat16).
+ *   - Element counts and offsets are int64 (Psi reaches 1.3e10 elements).
+ *   - Alignment: contribution buffers, their row stride (a multiple of 8
+ *     elements), g and the fp32 state arrays must be 16-byte aligned.  The
+ *     gather slot needs only 2-byte alignment.
+ *   - valid_len == 0 (an empty tail rank) is legal: nothing is enqueued except
+ *     where the call says otherwise.
+ *   - Calls on different streams are independent as long as they use
+ *     different ctrl blocks and workspaces.
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ZERO_F16 = 1, ZERO_BF16 = 2 };
+
+enum {
+    ZERO_OK = 0,
+    ZERO_EINVAL = -1, /* bad argument (null pointer, count, dtype, ...) */
+    ZERO_EALIGN = -2, /* misaligned pointer or stride */
+    ZERO_ERANGE = -3, /* size or offset out of the supported range */
+    ZERO_ESPACE = -4, /* workspace too small */
+    ZERO_EHIP = -5    /* the HIP runtime refused a launch */
+};
+
+enum { ZERO_SCALER_NONE = 0, ZERO_SCALER_STATIC = 1, ZERO_SCALER_DYNAMIC = 2 };
+
+#define ZERO_MAX_CONTRIB 1024 /* largest N accepted by the reduce */
+#define ZERO_MAX_RANKS 64     /* largest number of ctrl blocks combined in one call */
+
+/* Optimizer, clipping and loss-scale settings, passed by host pointer and
+ * copied into the kernel arguments.  The pages name Adam (Kingma and Ba) and
+ * AdamW with weight_decay but print no update; the library applies
+ * bias-corrected Adam with epsilon outside the square root and decoupled
+ * weight decay:  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g*g;
+ * p = p - lr ((m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps) + wd p),
+ * every operation rounded to fp32, b^t a running fp64 product.
+ * max_grad_norm > 0 turns clipping on: when norm > max_grad_norm, g is
+ * multiplied by max_grad_norm / (norm + 1e-6).
+ * scaler: NONE keeps S = 1; STATIC keeps the initial S; DYNAMIC halves S
+ * (not below min_scale) on a skipped step and doubles it after
+ * growth_interval consecutive applied steps.  A step whose reduced gradient
+ * holds inf or NaN is always skipped. */
+typedef struct zero_hparams {
+    float lr, beta1, beta2, eps, weight_decay, max_grad_norm;
+    int32_t scaler;
+    float min_scale;
+    int32_t growth_interval;
+} zero_hparams;
+
+/* Control block: 64 bytes in DEVICE memory, one per rank, written only by the
+ * library's kernels.  Host code may copy it back to read the decisions.
+ * It carries the step-to-step scalars so that no step needs a host sync. */
+typedef struct zero_ctrl {
+    double sumsq;       /* last step: global sum of g^2 over all ranks (fp64) */
+    double norm;        /* last step: sqrt(sumsq) (inf/NaN when the gradient was) */
+    double beta1_pow;   /* beta1^t */
+    double beta2_pow;   /* beta2^t */
+    float loss_scale;   /* S that the next step's contributions carry */
+    float scale_used;   /* S of the last step */
+    float clip;         /* clip factor applied by the last step (1 when none) */
+    int32_t nonfinite;  /* last step: 1 if any reduced element was inf/NaN */
+    int32_t skip;       /* last step was skipped (state, slot and t unchanged) */
+    int32_t t;          /* applied optimizer steps */
+    int32_t good_steps; /* applied steps since the loss scale last changed */
+    int32_t cur;        /* fused path: which of the two state sets is current */
+} zero_ctrl;
+
+/* One rank's fp32 optimizer state: master weights, Adam m, Adam v, each
+ * valid_len contiguous floats (device). */
+typedef struct zero_state {
+    float *master;
+    float *m;
+    float *v;
+} zero_state;
+
+/* Partition ("zero-stages-simulation" README, flat partitioning paragraph;
+ * lesson "ZeRO: Memory Optimization for Large Models", Stage 1 step 3):
+ * the flat buffer is split into N contiguous shards of ceil(Psi/N) elements,
+ * rank r owns [r*shard, r*shard + valid) with valid = clamp(Psi - r*shard, 0,
+ * shard); tail ranks are short or empty.  Pure host arithmetic.
+ * Returns ZERO_EINVAL for psi < 1, nranks < 1, rank outside [0, nranks) or a
+ * null output pointer. */
+int zero_partition(int64_t psi, int32_t nranks, int32_t rank, int64_t *shard_len,
+                   int64_t *offset, int64_t *valid_len);
+
+/* sizeof(zero_ctrl); allocate that many bytes of device memory per rank. */
+size_t zero_ctrl_bytes(void);
+
+/* Device workspace (bytes) needed by zero_reduce_grads and zero_fused_step
+ * for a shard of valid_len elements: one 16-byte partial (fp64 sum of
+ * squares, non-finite flag) per workgroup.  Never more than 64 KiB. */
+size_t zero_workspace_bytes(int64_t valid_len);
+
+/* Initialise a ctrl block on `stream`: t = 0, beta powers 1, loss scale S
+ * (must be finite and > 0; use 1 without a scaler), cur = 0. */
+int zero_ctrl_init(zero_ctrl *ctrl_dev, float loss_scale, void *stream);
+
+/* Reduce ("CMU 11-868 L18", Mechanism 1 step 3: the reduce-scatter sums and
+ * averages the gradients and each GPU receives its part in FP32; paper
+ * summary 3.4 Stage 2, reduce-scatter of gradients):
+ *   g[i] = fl32( sum_{k=0..N-1} C[k][i] ) * fl32(1 / (N * S)),   i < valid_len,
+ * summed in fp32 in rank order k = 0..N-1; S is ctrl->loss_scale.
+ * contrib_dev: N rows of `stride` elements (16-bit, dtype), row k at
+ * contrib_dev + k*stride; only columns < valid_len are read.
+ * g_dev: valid_len floats, written.
+ * The same pass writes the first level of the norm and overflow reduction,
+ * one partial per workgroup, into ws_dev (ws_bytes >= zero_workspace_bytes).
+ * Errors: EINVAL (null, dtype, nranks outside [1, ZERO_MAX_CONTRIB],
+ * stride < valid_len), EALIGN, ESPACE. */
+int zero_reduce_grads(const void *contrib_dev, int32_t dtype, int32_t nranks, int64_t stride,
+                      int64_t valid_len, const zero_ctrl *ctrl_dev, float *g_dev, void *ws_dev,
+                      size_t ws_bytes, void *stream);
+
+/* Norm, overflow and step decisions (paper summary 3.4, residual states:
+ * gradient-norm computation over all gradients; "CMU 11-868 L18", The memory
+ * bill, same note).  Combines the per-workgroup partials that the previous
+ * zero_reduce_grads or zero_fused_step left in each ws_dev[r] (valid_len[r]
+ * elements), in a fixed order, into the global sum of squares and the global
+ * non-finite flag of the `nranks` ranks given (nranks > 1 stands in for the
+ * scalar all-reduce between data-parallel ranks; with one rank they are its
+ * own).  Then, in every ctrl block: norm = sqrt(sumsq); skip = nonfinite;
+ * loss-scale update; clip factor; if applied: t += 1, beta powers advance and,
+ * when `pingpong` is nonzero, cur flips to the state set the fused step
+ * just wrote.  One workgroup; enqueued even when every valid_len is 0.
+ * ws_dev, valid_len and ctrl_dev are host arrays of nranks entries (ws_dev
+ * and ctrl_dev entries are device pointers).  All ctrl blocks must hold the
+ * same scalars (they do when they are always updated together).
+ * Errors: EINVAL (null, nranks outside [1, ZERO_MAX_RANKS], bad hparams). */
+int zero_grad_norm_overflow(int32_t nranks, void *const *ws_dev, const int64_t *valid_len,
+                            zero_ctrl *const *ctrl_dev, const zero_hparams *hp,
+                            int32_t pingpong, void *stream);
+
+/* Adam on the owned slice ("CMU 11-868 L18", Mechanism 1 step 4: each GPU
+ * updates only its part of the FP32 variance, momentum and parameters;
+ * paper summary 3.4 Stage 1), fused with the cast into the gather slot
+ * (step 5: the updated FP32 parameters are copied to FP16).
+ * Two-pass path: runs after zero_reduce_grads and zero_grad_norm_overflow
+ * (pingpong = 0), reads g_dev and ctrl (skip, clip, t, beta powers), updates
+ * state in place.  When gather_dev is not NULL, writes
+ * RNE_dtype(master[i]) to gather_dev[offset + i].  A skipped step returns
+ * from every workgroup without writing.
+ * Errors: EINVAL, EALIGN, ERANGE (offset < 0). */
+int zero_adam_step(const zero_state *state, const float *g_dev, int64_t valid_len,
+                   const zero_hparams *hp, const zero_ctrl *ctrl_dev, void *gather_dev,
+                   int32_t gather_dtype, int64_t offset, void *stream);
+
+/* Cast ("CMU 11-868 L18", Mechanism 1 steps 5-6; lesson Stage 1 step 4):
+ * gather_dev[offset + i] = RNE_dtype(master_dev[i]) for i < valid_len,
+ * unconditionally (also used to fill the initial parameters). */
+int zero_cast_to_gather(const float *master_dev, int64_t valid_len, void *gather_dev,
+                        int32_t dtype, int64_t offset, void *stream);
+
+/* Fused single pass (clipping off): reduce + norm/overflow partials + Adam +
+ * cast, reading each contribution and each state word once.  Because the
+ * skip decision is only known after every element has been summed, the
+ * state is double-buffered: the kernel reads the set ctrl->cur names
+ * (state0 or state1) and writes the other; zero_grad_norm_overflow with
+ * pingpong = 1 then makes the written set current, or keeps the old one on a
+ * skipped step; zero_fused_restore then rewrites the gather slot from the
+ * kept master on a skipped step.  Bias correction uses t+1.
+ * Requires hp->max_grad_norm <= 0 (EINVAL otherwise).  Other arguments as in
+ * zero_reduce_grads and zero_adam_step; gather_dev must not be NULL. */
+int zero_fused_step(const void *contrib_dev, int32_t contrib_dtype, int32_t nranks,
+                    int64_t stride, const zero_state *state0, const zero_state *state1,
+                    int64_t valid_len, void *gather_dev, int32_t gather_dtype, int64_t offset,
+                    const zero_hparams *hp, const zero_ctrl *ctrl_dev, void *ws_dev,
+                    size_t ws_bytes, void *stream);
+
+/* After a fused step's zero_grad_norm_overflow: if ctrl->skip, rewrite
+ * gather_dev[offset + i] from the current master (state0 or state1 as
+ * ctrl->cur says); otherwise every workgroup returns at once. */
+int zero_fused_restore(const zero_state *state0, const zero_state *state1, int64_t valid_len,
+                       void *gather_dev, int32_t dtype, int64_t offset,
+                       const zero_ctrl *ctrl_dev, void *stream);
+
+/* Message for the last nonzero return on the calling thread ("" if none). */
+const char *zero_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

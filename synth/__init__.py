@@ -68,6 +68,7 @@ def cpu():
         L.synth_master_range.argtypes = [u64, f64, i64, i64, _f32p]
         L.synth_master_at.argtypes = [u64, f64, _i64p, i64, _f32p]
         L.synth_param_range.argtypes = [u64, f64, i32, i64, i64, _u16p]
+        L.synth_param_at.argtypes = [u64, f64, i32, _i64p, i64, _u16p]
         L.synth_bits_range.argtypes = [u64, u32, u32, u32, i64, i64, _u64p]
         L.synth_normal_range.argtypes = [u64, u32, u32, u32, i64, i64, _f64p]
         _cpu = L
@@ -114,6 +115,14 @@ def master_at(seed, sigma, idx: np.ndarray) -> np.ndarray:
 def param_range(seed, sigma, dtype, idx0, length) -> np.ndarray:
     out = np.empty(length, np.uint16)
     cpu().synth_param_range(seed, sigma, dtype, idx0, length, out.ctypes.data_as(_u16p))
+    return out
+
+
+def param_at(seed, sigma, dtype, idx: np.ndarray) -> np.ndarray:
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    out = np.empty(idx.size, np.uint16)
+    cpu().synth_param_at(seed, sigma, dtype, idx.ctypes.data_as(_i64p), idx.size,
+                         out.ctypes.data_as(_u16p))
     return out
 
 

@@ -67,3 +67,12 @@ void synth_param_range(uint64_t seed, double sigma, int32_t dtype, int64_t idx0,
         out[i] = dtype == SYNTH_BF16 ? synth_f32_to_bf16(f) : synth_f32_to_f16(f);
     }
 }
+
+void synth_param_at(uint64_t seed, double sigma, int32_t dtype, const int64_t *idx, int64_t count,
+                    uint16_t *out) {
+    uint64_t km = synth_stream_key(seed, SYNTH_STREAM_MASTER, 0u, 0u);
+    for (int64_t j = 0; j < count; ++j) {
+        float f = synth_master_value(km, sigma, (uint64_t)idx[j]);
+        out[j] = dtype == SYNTH_BF16 ? synth_f32_to_bf16(f) : synth_f32_to_f16(f);
+    }
+}

@@ -1,0 +1,133 @@
+"""The C ABI without a GPU: symbols, the pure-host partition, argument checks.
+
+Every call below either needs no device (zero_partition, the size queries) or
+is rejected by argument validation before anything reaches the HIP runtime.
+Fake non-null device addresses are only ever passed to calls that must fail
+validation.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zero_shard.h")
+
+
+@pytest.fixture(scope="module")
+def Z():
+    import zero_partitioned_mixed_amd as Z
+    return Z
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(zero_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(Z):
+    names = declared_functions()
+    assert len(names) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", Z.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert set(Z.EXPORTS) == set(names)
+
+
+def test_struct_sizes_match_header(Z):
+    assert Z.zero_ctrl_bytes() == 64 == ctypes.sizeof(Z.Ctrl)
+    assert ctypes.sizeof(Z.Hparams) == 36
+    assert ctypes.sizeof(Z.State) == 24
+
+
+def test_partition_matches_oracle(Z, O):
+    for psi in list(range(1, 130)) + [637_824, 637_825, 124_439_808, 13_000_000_000]:
+        for n in (1, 2, 3, 7, 8, 17, 32, 64):
+            for r in range(n):
+                assert Z.zero_partition(psi, n, r) == O.partition(psi, n, r)
+
+
+@pytest.mark.parametrize("args", [(0, 4, 0), (10, 0, 0), (10, 4, 4), (10, 4, -1)])
+def test_partition_rejects(Z, args):
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_partition(*args)
+    assert e.value.code == -1
+
+
+def test_workspace_is_bounded(Z):
+    assert Z.zero_workspace_bytes(0) == 16
+    assert Z.zero_workspace_bytes(1) == 16
+    assert Z.zero_workspace_bytes(8 * 256) == 16
+    assert Z.zero_workspace_bytes(8 * 256 + 1) == 32
+    assert Z.zero_workspace_bytes(13_000_000_000) == 2048 * 16
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address, never dereferenced
+
+
+def _reduce(Z, contrib=FAKE, dtype=1, n=8, stride=64, valid=64, ctrl=FAKE, g=FAKE, ws=FAKE,
+            wsb=64):
+    return Z._lib.zero_reduce_grads(contrib, dtype, n, stride, valid, ctrl, g, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), -1), (dict(n=0), -1), (dict(n=1025), -1), (dict(stride=60), -1),
+    (dict(stride=68, valid=64), -2), (dict(contrib=FAKE + 2), -2), (dict(g=FAKE + 4), -2),
+    (dict(contrib=0), -1), (dict(g=0), -1), (dict(ctrl=0), -1), (dict(ws=0), -1),
+    (dict(wsb=8), -4), (dict(valid=-1), -3),
+])
+def test_reduce_validation(Z, kw, code):
+    assert _reduce(Z, **kw) == code
+    assert Z.zero_last_error() != ""
+
+
+def test_fused_rejects_clipping_and_aliasing(Z):
+    s0 = Z.State(FAKE, FAKE + 256, FAKE + 512)
+    s1 = Z.State(FAKE + 1024, FAKE + 1280, FAKE + 1536)
+    hp = Z.hparams(max_grad_norm=1.0)
+    rc = Z._lib.zero_fused_step(FAKE, 1, 8, 64, ctypes.byref(s0), ctypes.byref(s1), 64, FAKE, 1,
+                                0, ctypes.byref(hp), FAKE, FAKE, 64, None)
+    assert rc == -1 and "two-pass" in Z.zero_last_error()
+    hp = Z.hparams()
+    rc = Z._lib.zero_fused_step(FAKE, 1, 8, 64, ctypes.byref(s0), ctypes.byref(s0), 64, FAKE, 1,
+                                0, ctypes.byref(hp), FAKE, FAKE, 64, None)
+    assert rc == -1 and "distinct" in Z.zero_last_error()
+
+
+def test_hparam_validation(Z):
+    s0 = Z.State(FAKE, FAKE + 256, FAKE + 512)
+    for hp in (Z.hparams(beta1=1.0), Z.hparams(eps=-1.0), Z.hparams(scaler=7),
+               Z.hparams(scaler=2, growth_interval=0)):
+        rc = Z._lib.zero_adam_step(ctypes.byref(s0), FAKE, 64, ctypes.byref(hp), FAKE, None, 1, 0,
+                                   None)
+        assert rc == -1
+
+
+def test_norm_overflow_validation(Z):
+    hp = Z.hparams()
+    arr = (ctypes.c_void_p * 1)(FAKE)
+    lens = (ctypes.c_int64 * 1)(64)
+    assert Z._lib.zero_grad_norm_overflow(0, arr, lens, arr, ctypes.byref(hp), 0, None) == -1
+    assert Z._lib.zero_grad_norm_overflow(65, arr, lens, arr, ctypes.byref(hp), 0, None) == -1
+    nul = (ctypes.c_void_p * 1)(None)
+    assert Z._lib.zero_grad_norm_overflow(1, arr, lens, nul, ctypes.byref(hp), 0, None) == -1
+
+
+def test_slot_and_ctrl_validation(Z):
+    assert Z._lib.zero_cast_to_gather(FAKE, 64, FAKE + 1, 1, 0, None) == -2  # odd gather address
+    assert Z._lib.zero_cast_to_gather(FAKE, 64, FAKE, 1, -5, None) == -3
+    assert Z._lib.zero_cast_to_gather(FAKE, 64, FAKE, 9, 0, None) == -1
+    assert Z._lib.zero_ctrl_init(FAKE, ctypes.c_float(0.0), None) == -1
+    assert Z._lib.zero_ctrl_init(FAKE, ctypes.c_float(float("inf")), None) == -1
+    assert Z._lib.zero_ctrl_init(None, ctypes.c_float(1.0), None) == -1
+
+
+def test_binding_refuses_cpu_tensors(Z):
+    import torch
+    with pytest.raises(ValueError):
+        Z.zero_cast_to_gather(torch.zeros(8), 8, torch.zeros(8, dtype=torch.int16), Z.F16, 0)

@@ -1,0 +1,68 @@
+"""GPU parity at the full 7B and 13B shard sizes, in the launch configuration
+the benchmark times.
+
+The oracle takes every step's global decisions (overflow, skip, norm, clip,
+loss scale) over the whole shard, and the per-element results on a sample of
+shard positions (both ends, the injected-overflow element and its
+neighbours, and 64K random positions).  The 16-bit buffer outside the slot
+is checked on its borders and on random positions.
+"""
+import numpy as np
+import pytest
+
+import harness as H
+from harness import Case
+from synth import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import synth
+    synth.gpu()
+    import zero_partitioned_mixed_amd  # noqa: F401
+    yield
+    torch.cuda.empty_cache()
+
+
+def run_fullsize(w):
+    import synth
+    import torch
+    c = Case(w, w.ranks[0], w.steps)
+    shard, off, valid = c.part
+    H.log(f"{w.name}: shard {shard} at offset {off}, N={w.nranks}, {w.variant}, {w.steps} steps")
+    g = H.GpuRun(c, full_gather=True)
+    g.run()
+    H.log(f"{w.name}: GPU steps done; oracle scalar pass over {valid} x {w.nranks} x {w.steps}")
+    reps = H.oracle_scalars(c)
+    stats = H.assert_reports(g.reports, reps)
+    H.log(f"{w.name}: scalars ok {stats}; skips {[r['skip'] for r in reps]}")
+    extra = [i.col + d for i in c.injections for d in (-1, 0, 1)]
+    cols = H.sample_cols(valid, 65_536, seed=11, extra=extra)
+    p, m, v, slot = g.fetch(cols)
+    rp, rm, rv, rslot = H.oracle_elements(c, reps, cols)
+    stats["master"] = H.assert_f32_close("master", p, rp)
+    stats["m"] = H.assert_f32_close("m", m, rm)
+    stats["v"] = H.assert_f32_close("v", v, rv)
+    stats["slot"] = H.assert_16bit_within_ulp("slot", slot, rslot, w.dtype)
+    rng = np.random.default_rng(5)
+    outside = np.concatenate([np.arange(max(0, off - 4096), off),
+                              np.arange(off + valid, min(w.psi, off + valid + 4096)),
+                              rng.integers(0, off, 8192)]).astype(np.int64)
+    assert np.array_equal(g.gather_bits(outside),
+                          synth.param_at(w.seed, w.master_sigma, w.dtype, outside))
+    H.log(f"{w.name}: ok {stats}")
+    del g
+    torch.cuda.empty_cache()
+
+
+def test_psi7e9_clip_two_pass_fullsize():
+    run_fullsize(workloads.P7B)
+
+
+def test_psi13e9_dynamic_scale_fused_fullsize():
+    run_fullsize(workloads.P13B)

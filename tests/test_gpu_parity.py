@@ -1,0 +1,263 @@
+"""GPU parity: the HIP shard step through the C ABI against the CPU oracle.
+
+Bars: fp32 master/m/v within |d| <= 1e-6 |x| + 1e-9; 16-bit parameters
+within 1 ulp; overflow flags, skip decisions, t and loss scales exact; the
+gradient norm within 1e-5 relative.  Sizes span many workgroup tiles with a
+ragged tail; every slot alignment class, N from 1 to 64, both 16-bit formats,
+both paths (fused single pass, two-pass with clipping), overflow at the first,
+middle and last element, NaN, inf in the padding, empty ranks, and the
+skip-and-halve sequence of the dynamic loss scaler.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import harness as H
+from harness import Case, Inject
+from synth import workloads
+from synth.workloads import BF16, F16, Workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import synth
+    synth.gpu()
+    import zero_partitioned_mixed_amd  # noqa: F401  (fails loudly when the library is missing)
+    torch.cuda.init()
+    yield
+
+
+def run_case(c: Case, label: str, full: bool = True):
+    H.log(f"{label}: psi={c.w.psi} N={c.w.nranks} rank={c.rank} dtype={c.w.dtype} "
+          f"variant={c.w.variant} steps={c.steps} offset={c.part[1]} valid={c.part[2]}")
+    g = H.GpuRun(c, full_gather=full)
+    g.run()
+    ref_reps = H.oracle_scalars(c)
+    stats = H.assert_reports(g.reports, ref_reps)
+    p, m, v, slot = g.fetch()
+    rp, rm, rv, rslot = H.oracle_elements(c, ref_reps)
+    stats["master"] = H.assert_f32_close("master", p, rp)
+    stats["m"] = H.assert_f32_close("m", m, rm)
+    stats["v"] = H.assert_f32_close("v", v, rv)
+    stats["slot"] = H.assert_16bit_within_ulp("slot", slot, rslot, c.w.dtype)
+    if full:  # nothing outside the slot changed
+        import synth
+        w = c.w
+        _, off, valid = c.part
+        outside = np.r_[0:off, off + valid:w.psi]
+        if outside.size:
+            got = g.gather_bits(outside)
+            ref = synth.param_range(w.seed, w.master_sigma, w.dtype, 0, w.psi)[outside]
+            assert np.array_equal(got, ref), "gather buffer changed outside the slot"
+    H.log(f"{label}: ok {stats}")
+    return g, stats
+
+
+def small(psi, n, rank, dtype=F16, steps=3, **kw):
+    w = Workload(name="small", psi=psi, nranks=n, ranks=(rank,), dtype=dtype, steps=steps, **kw)
+    return w
+
+
+# --------------------------------------------------------------------------- generator
+def test_device_generator_matches_host():
+    import torch
+    import synth
+    w = workloads.P13B
+    n, stride, off, ln = 8, 4096, 1_625_000_000 * 7 + 12_345, 4000
+    c = torch.empty((n, stride), dtype=torch.float16, device="cuda")
+    synth.gpu_contrib_rows(c, w.seed, 3, F16, 1e-3, 2.0 ** 15, 1e-3, 100.0, off, ln)
+    ref = synth.contrib_rows(w.seed, 3, n, F16, 1e-3, 2.0 ** 15, 1e-3, 100.0, off, ln, stride=stride)
+    assert np.array_equal(c.view(torch.int16).cpu().numpy().view(np.uint16), ref)
+    for dt, tdt in ((F16, torch.float16), (BF16, torch.bfloat16)):
+        p = torch.empty(5000, dtype=tdt, device="cuda")
+        synth.gpu_param_range(p, 0, 0.02, dt, 10 ** 10)
+        assert np.array_equal(p.view(torch.int16).cpu().numpy().view(np.uint16),
+                              synth.param_range(0, 0.02, dt, 10 ** 10, 5000))
+    mm = torch.empty(5000, dtype=torch.float32, device="cuda")
+    synth.gpu_master_range(mm, 0, 0.02, 999)
+    assert np.array_equal(mm.cpu().numpy(), synth.master_range(0, 0.02, 999, 5000))
+
+
+# --------------------------------------------------------------------------- cast
+CAST_VALUES = np.array(
+    [0.0, -0.0, 1.0, -1.0, 65504.0, 65519.996, 65520.0, 7e4, 2.0 ** -24, 2.0 ** -25,
+     3 * 2.0 ** -25, 2.0 ** -14, 2.0 ** -14 * (1 - 2.0 ** -11), 1e-8, 1e-30, 1e-40, 1.4e-45,
+     3.3895314e38, 3.4e38, np.inf, -np.inf, np.nan, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11,
+     1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 0.1, 0.2, -0.3], np.float32)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("offset", [0, 1, 2, 3, 4, 8, 13])
+def test_cast_to_gather(dtype, offset):
+    import torch
+    import oracle as O
+    import zero_partitioned_mixed_amd as Z
+    rng = np.random.default_rng(offset)
+    vals = np.concatenate([CAST_VALUES, rng.normal(0, 1, 5000).astype(np.float32),
+                           (rng.normal(0, 1, 3000) * 2.0 ** rng.integers(-30, 20, 3000)).astype(np.float32)])
+    n = vals.size
+    master = torch.from_numpy(vals).cuda()
+    tdt = torch.float16 if dtype == F16 else torch.bfloat16
+    gather = torch.full((n + offset + 40,), 7.0, dtype=tdt, device="cuda")
+    Z.zero_cast_to_gather(master, n, gather, dtype, offset)
+    bits = gather.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = O.from_f32(vals, dtype)
+    got = bits[offset:offset + n]
+    nan = np.isnan(vals)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all(np.isnan(O.to_f32(got[nan], dtype)))
+    canary = O.from_f32(np.array([7.0], np.float32), dtype)[0]
+    assert np.all(bits[:offset] == canary) and np.all(bits[offset + n:] == canary)
+
+
+# --------------------------------------------------------------------------- small cases
+SMALL = {
+    "f16_fused_n3_tail_rank": (small(100_003, 3, 2), ()),
+    "f16_twopass_clip_n3": (small(100_003, 3, 1, max_grad_norm=0.01), ()),
+    "bf16_fused_n8_aligned": (small(200_000, 8, 3, dtype=BF16), ()),
+    "bf16_twopass_clip_n8_wd": (small(200_000, 8, 5, dtype=BF16, max_grad_norm=0.05,
+                                      weight_decay=0.01), ()),
+    "f16_fused_n1": (small(50_001, 1, 0, contrib_scale=2.0 ** 8, scaler=1, loss_scale=2.0 ** 8), ()),
+    "f16_fused_n7_offset_odd": (small(69_990, 7, 5), ()),
+    "bf16_fused_n64_ragged": (small(64 * 1_000 + 37, 64, 63, dtype=BF16), ()),
+    "f16_fused_n32_gpt2ish": (small(32 * 4_099, 32, 17, contrib_scale=2.0 ** 16, scaler=1,
+                                    loss_scale=2.0 ** 16, weight_decay=0.01), ()),
+    "f16_fused_inf_first": (small(100_003, 3, 2, steps=4, scaler=2, contrib_scale=2.0 ** 10,
+                                  loss_scale=2.0 ** 10), (Inject(2, 0, 0, np.inf),)),
+    "f16_fused_nan_last": (small(100_003, 3, 2, steps=4, scaler=2, contrib_scale=2.0 ** 10,
+                                 loss_scale=2.0 ** 10), (Inject(3, 2, 33_332, np.nan),)),
+    "f16_fused_inf_and_neg_inf_mid": (small(100_003, 3, 2, steps=3), (
+        Inject(2, 0, 17_001, np.inf), Inject(2, 1, 17_001, -np.inf))),
+    "f16_fused_inf_in_padding": (small(100_003, 3, 2, steps=2), (Inject(1, 1, 33_340, np.inf),)),
+    "bf16_twopass_inf_skip": (small(200_000, 8, 5, dtype=BF16, max_grad_norm=0.05, steps=4),
+                              (Inject(2, 7, 12_345, np.inf),)),
+    "f16_fused_dynamic_growth": (small(60_016, 4, 3, steps=6, scaler=2, growth_interval=2,
+                                       contrib_scale=2.0 ** 12, loss_scale=2.0 ** 12),
+                                 (Inject(4, 1, 5, np.inf),)),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_cases(name):
+    w, extra = SMALL[name]
+    run_case(Case(w, w.ranks[0], w.steps, extra=tuple(extra)), name)
+
+
+def test_empty_tail_rank():
+    import torch
+    import zero_partitioned_mixed_amd as Z
+    # psi = 10 over 7 ranks: shard 2, rank 6 owns nothing
+    w = small(10, 7, 6)
+    c = Case(w, 6, 2)
+    assert c.part == (2, 12, 0)
+    g = H.GpuRun(c)
+    before = g.gather.clone()
+    g.run()
+    assert torch.equal(g.gather.view(torch.int16), before.view(torch.int16))
+    for r in g.reports:
+        assert r["sumsq"] == 0.0 and r["skip"] == 0
+    assert g.reports[-1]["t"] == 2
+
+
+def test_run_to_run_bitwise():
+    w = small(300_007, 8, 6, dtype=BF16, max_grad_norm=0.02)
+    outs = []
+    for _ in range(2):
+        g = H.GpuRun(Case(w, 6, 3))
+        g.run()
+        outs.append((g.fetch(), [r["sumsq"] for r in g.reports]))
+    (a, sa), (b, sb) = outs
+    assert sa == sb
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32) if x.dtype == np.float32 else x,
+                              y.view(np.uint32) if y.dtype == np.float32 else y)
+
+
+# --------------------------------------------------------------------------- toy: all 32 shards
+def _toy(inject=None):
+    import torch
+    import oracle as O
+    import synth
+    import zero_partitioned_mixed_amd as Z
+    w = workloads.TOY
+    n = w.nranks
+    H.log(f"toy: psi={w.psi} N={n} all shards, steps={w.steps}, inject={inject}")
+    gather = torch.empty(w.psi, dtype=torch.float16, device="cuda")
+    synth.gpu_param_range(gather, w.seed, w.master_sigma, F16, 0)
+    hp = Z.hparams(lr=w.lr)
+    steps, contribs, parts = [], [], []
+    for r in range(n):
+        shard, off, valid = Z.zero_partition(w.psi, n, r)
+        stride = (shard + 63) // 64 * 64
+        p0 = torch.empty(valid, dtype=torch.float32, device="cuda")
+        synth.gpu_master_range(p0, w.seed, w.master_sigma, off)
+        s0 = (p0, torch.zeros_like(p0), torch.zeros_like(p0))
+        s1 = (torch.empty_like(p0), torch.zeros_like(p0), torch.zeros_like(p0))
+        steps.append(Z.ShardStep(n, stride, valid, off, F16, F16, hp, s0, s1))
+        contribs.append(torch.empty((n, stride), dtype=torch.float16, device="cuda"))
+        parts.append((off, valid, stride))
+    multi = Z.MultiShardStep(steps)
+    gpu_reps = []
+    for s in range(1, w.steps + 1):
+        for r, (off, valid, stride) in enumerate(parts):
+            synth.gpu_contrib_rows(contribs[r], w.seed, s, F16, w.contrib_sigma, 1.0, 0.0, 100.0,
+                                   off, valid)
+            if inject and inject[0] == s and inject[1] == r:
+                contribs[r][inject[2], inject[3]] = float("inf")
+        multi.step(contribs, gather)
+        gpu_reps.append([Z.read_ctrl(st.ctrl) for st in steps])
+    torch.cuda.synchronize()
+    # oracle: the same step over all 32 ranks with shared scalars
+    ohp = O.hparams(lr=w.lr)
+    sc = O.new_scalars(1.0)
+    states = [O.RankState.fresh(synth.master_range(w.seed, w.master_sigma, off, valid))
+              for off, valid, _ in parts]
+    ogather = synth.param_range(w.seed, w.master_sigma, F16, 0, w.psi)
+    for s in range(1, w.steps + 1):
+        cs = []
+        for r, (off, valid, stride) in enumerate(parts):
+            C = synth.contrib_rows(w.seed, s, n, F16, w.contrib_sigma, 1.0, 0.0, 100.0, off, valid)
+            if inject and inject[0] == s and inject[1] == r:
+                C[inject[2], inject[3]] = 0x7C00
+            cs.append(C)
+        rep = O.shard_step(cs, F16, states, [p[0] for p in parts], sc, ohp, ogather, F16)
+        for rr in gpu_reps[s - 1]:  # every rank agrees on the global decisions
+            assert rr["skip"] == rep.skip and rr["nonfinite"] == rep.nonfinite
+            assert rr["t"] == sc.t
+            if np.isfinite(rep.norm):
+                assert abs(rr["norm"] - rep.norm) <= H.NORM_RTOL * rep.norm
+            else:
+                assert not np.isfinite(rr["norm"]) and np.isnan(rr["norm"]) == np.isnan(rep.norm)
+    for r, st in enumerate(steps):
+        cur = st.current()
+        for name, t, ref in zip(("master", "m", "v"), cur,
+                                (states[r].master, states[r].m, states[r].v)):
+            H.assert_f32_close(f"rank{r}.{name}", t.cpu().numpy(), ref)
+    got = gather.view(torch.int16).cpu().numpy().view(np.uint16)
+    H.assert_16bit_within_ulp("gather", got, ogather, F16)
+    H.log("toy: ok")
+
+
+def test_toy_all_shards():
+    _toy()
+
+
+def test_toy_overflow_on_one_rank_skips_all():
+    _toy(inject=(2, 5, 3, 19_000))
+
+
+# --------------------------------------------------------------------------- full configs
+def test_gpt2_sized_full():
+    w = workloads.GPT2
+    run_case(Case(w, w.ranks[0], w.steps), w.name, full=False)
+
+
+def test_psi1_5b_n64_full():
+    w = workloads.P1_5B
+    run_case(Case(w, w.ranks[0], w.steps), w.name, full=False)

@@ -1,0 +1,278 @@
+"""Python binding of libzero_shard.so, the ZeRO per-rank shard step for MI355X.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Functions carry the C names (include/zero_shard.h) and take torch
+device tensors, passing their data pointers and torch's current HIP stream.
+The library must be built (``__graft_entry__.build()``); importing the package
+without it raises ImportError, and there is no CPU fallback.
+
+``ShardStep`` sequences the calls of one rank's step (two-pass when clipping
+is on, fused single pass otherwise); ``MultiShardStep`` runs several ranks'
+shards held on one GPU with shared global scalars.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libzero_shard.so")
+
+F16 = 1
+BF16 = 2
+SCALER_NONE, SCALER_STATIC, SCALER_DYNAMIC = 0, 1, 2
+MAX_RANKS = 64
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                      "(hipcc --offload-arch=gfx950); there is no fallback path")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+class Hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("max_grad_norm", ctypes.c_float), ("scaler", _i32),
+                ("min_scale", ctypes.c_float), ("growth_interval", _i32)]
+
+
+class Ctrl(ctypes.Structure):
+    _fields_ = [("sumsq", ctypes.c_double), ("norm", ctypes.c_double),
+                ("beta1_pow", ctypes.c_double), ("beta2_pow", ctypes.c_double),
+                ("loss_scale", ctypes.c_float), ("scale_used", ctypes.c_float),
+                ("clip", ctypes.c_float), ("nonfinite", _i32), ("skip", _i32), ("t", _i32),
+                ("good_steps", _i32), ("cur", _i32)]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class State(ctypes.Structure):
+    _fields_ = [("master", _vp), ("m", _vp), ("v", _vp)]
+
+
+_sig = {
+    "zero_partition": (ctypes.c_int, [_i64, _i32, _i32, ctypes.POINTER(_i64),
+                                      ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "zero_ctrl_bytes": (ctypes.c_size_t, []),
+    "zero_workspace_bytes": (ctypes.c_size_t, [_i64]),
+    "zero_ctrl_init": (ctypes.c_int, [_vp, ctypes.c_float, _vp]),
+    "zero_reduce_grads": (ctypes.c_int, [_vp, _i32, _i32, _i64, _i64, _vp, _vp, _vp,
+                                         ctypes.c_size_t, _vp]),
+    "zero_grad_norm_overflow": (ctypes.c_int, [_i32, ctypes.POINTER(_vp), ctypes.POINTER(_i64),
+                                               ctypes.POINTER(_vp), ctypes.POINTER(Hparams),
+                                               _i32, _vp]),
+    "zero_adam_step": (ctypes.c_int, [ctypes.POINTER(State), _vp, _i64, ctypes.POINTER(Hparams),
+                                      _vp, _vp, _i32, _i64, _vp]),
+    "zero_cast_to_gather": (ctypes.c_int, [_vp, _i64, _vp, _i32, _i64, _vp]),
+    "zero_fused_step": (ctypes.c_int, [_vp, _i32, _i32, _i64, ctypes.POINTER(State),
+                                       ctypes.POINTER(State), _i64, _vp, _i32, _i64,
+                                       ctypes.POINTER(Hparams), _vp, _vp, ctypes.c_size_t, _vp]),
+    "zero_fused_restore": (ctypes.c_int, [ctypes.POINTER(State), ctypes.POINTER(State), _i64,
+                                          _vp, _i32, _i64, _vp, _vp]),
+    "zero_last_error": (ctypes.c_char_p, []),
+}
+for _name, (_res, _args) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTS = tuple(_sig)
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, call: str, code: int):
+        msg = _lib.zero_last_error().decode()
+        super().__init__(f"{call} returned {code}: {msg}")
+        self.code = code
+
+
+def _check(call: str, rc: int) -> None:
+    if rc != 0:
+        raise ZeroError(call, rc)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    if t is None:
+        return ctypes.c_void_p(None)
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _state(s) -> State:
+    master, m, v = s
+    return State(_ptr(master), _ptr(m), _ptr(v))
+
+
+def hparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, max_grad_norm=0.0,
+            scaler=SCALER_NONE, min_scale=1.0, growth_interval=1000) -> Hparams:
+    return Hparams(lr, beta1, beta2, eps, weight_decay, max_grad_norm, scaler, min_scale,
+                   growth_interval)
+
+
+# ----------------------------------------------------------------------------- the C calls
+def zero_partition(psi: int, nranks: int, rank: int) -> tuple[int, int, int]:
+    s, o, v = _i64(), _i64(), _i64()
+    _check("zero_partition", _lib.zero_partition(psi, nranks, rank, ctypes.byref(s),
+                                                 ctypes.byref(o), ctypes.byref(v)))
+    return s.value, o.value, v.value
+
+
+def zero_ctrl_bytes() -> int:
+    return _lib.zero_ctrl_bytes()
+
+
+def zero_workspace_bytes(valid_len: int) -> int:
+    return _lib.zero_workspace_bytes(valid_len)
+
+
+def zero_ctrl_init(ctrl, loss_scale: float) -> None:
+    _check("zero_ctrl_init", _lib.zero_ctrl_init(_ptr(ctrl), loss_scale, _stream()))
+
+
+def zero_reduce_grads(contrib, dtype: int, nranks: int, stride: int, valid_len: int, ctrl, g,
+                      ws) -> None:
+    _check("zero_reduce_grads", _lib.zero_reduce_grads(
+        _ptr(contrib), dtype, nranks, stride, valid_len, _ptr(ctrl), _ptr(g), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream()))
+
+
+def zero_grad_norm_overflow(ws_list, valid_lens, ctrls, hp: Hparams, pingpong: bool) -> None:
+    n = len(ctrls)
+    ws_arr = (_vp * n)(*[t.data_ptr() if t is not None else None for t in ws_list])
+    len_arr = (_i64 * n)(*valid_lens)
+    ctrl_arr = (_vp * n)(*[t.data_ptr() for t in ctrls])
+    _check("zero_grad_norm_overflow", _lib.zero_grad_norm_overflow(
+        n, ws_arr, len_arr, ctrl_arr, ctypes.byref(hp), int(bool(pingpong)), _stream()))
+
+
+def zero_adam_step(state, g, valid_len: int, hp: Hparams, ctrl, gather=None,
+                   gather_dtype: int = F16, offset: int = 0) -> None:
+    st = _state(state)
+    _check("zero_adam_step", _lib.zero_adam_step(
+        ctypes.byref(st), _ptr(g), valid_len, ctypes.byref(hp), _ptr(ctrl), _ptr(gather),
+        gather_dtype, offset, _stream()))
+
+
+def zero_cast_to_gather(master, valid_len: int, gather, dtype: int, offset: int) -> None:
+    _check("zero_cast_to_gather", _lib.zero_cast_to_gather(
+        _ptr(master), valid_len, _ptr(gather), dtype, offset, _stream()))
+
+
+def zero_fused_step(contrib, contrib_dtype: int, nranks: int, stride: int, state0, state1,
+                    valid_len: int, gather, gather_dtype: int, offset: int, hp: Hparams, ctrl,
+                    ws) -> None:
+    s0, s1 = _state(state0), _state(state1)
+    _check("zero_fused_step", _lib.zero_fused_step(
+        _ptr(contrib), contrib_dtype, nranks, stride, ctypes.byref(s0), ctypes.byref(s1),
+        valid_len, _ptr(gather), gather_dtype, offset, ctypes.byref(hp), _ptr(ctrl), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream()))
+
+
+def zero_fused_restore(state0, state1, valid_len: int, gather, dtype: int, offset: int,
+                       ctrl) -> None:
+    s0, s1 = _state(state0), _state(state1)
+    _check("zero_fused_restore", _lib.zero_fused_restore(
+        ctypes.byref(s0), ctypes.byref(s1), valid_len, _ptr(gather), dtype, offset, _ptr(ctrl),
+        _stream()))
+
+
+def zero_last_error() -> str:
+    return _lib.zero_last_error().decode()
+
+
+def read_ctrl(ctrl) -> dict:
+    """Copies a ctrl block back to the host (synchronises) and decodes it."""
+    raw = bytes(ctrl.detach().cpu().numpy().tobytes())
+    return Ctrl.from_buffer_copy(raw).as_dict()
+
+
+# ----------------------------------------------------------------------------- sequencing helpers
+class ShardStep:
+    """One rank's shard step over caller-provided device buffers.
+
+    contrib: [N, stride] 16-bit tensor; state0 (and state1 for the fused
+    path): (master, m, v) fp32 tensors of valid_len; gather: the full 16-bit
+    parameter buffer, this rank's slot at ``offset``.
+    """
+
+    def __init__(self, nranks, stride, valid_len, offset, dtype, gather_dtype, hp: Hparams,
+                 state0, state1=None, g=None, loss_scale=1.0):
+        import torch
+        self.nranks, self.stride, self.valid_len, self.offset = nranks, stride, valid_len, offset
+        self.dtype, self.gather_dtype, self.hp = dtype, gather_dtype, hp
+        self.state0, self.state1, self.g = state0, state1, g
+        self.fused = hp.max_grad_norm <= 0
+        if self.fused and state1 is None:
+            raise ValueError("the fused path needs a second state set")
+        if not self.fused and g is None:
+            raise ValueError("the two-pass path needs a g buffer")
+        dev = state0[0].device
+        self.ctrl = torch.empty(zero_ctrl_bytes(), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(zero_workspace_bytes(valid_len), dtype=torch.uint8, device=dev)
+        zero_ctrl_init(self.ctrl, loss_scale)
+
+    def step(self, contrib, gather) -> None:
+        if self.fused:
+            zero_fused_step(contrib, self.dtype, self.nranks, self.stride, self.state0,
+                            self.state1, self.valid_len, gather, self.gather_dtype, self.offset,
+                            self.hp, self.ctrl, self.ws)
+            zero_grad_norm_overflow([self.ws], [self.valid_len], [self.ctrl], self.hp, True)
+            zero_fused_restore(self.state0, self.state1, self.valid_len, gather,
+                               self.gather_dtype, self.offset, self.ctrl)
+        else:
+            zero_reduce_grads(contrib, self.dtype, self.nranks, self.stride, self.valid_len,
+                              self.ctrl, self.g, self.ws)
+            zero_grad_norm_overflow([self.ws], [self.valid_len], [self.ctrl], self.hp, False)
+            zero_adam_step(self.state0, self.g, self.valid_len, self.hp, self.ctrl, gather,
+                           self.gather_dtype, self.offset)
+
+    def current(self):
+        """(master, m, v) holding the current state (reads ctrl: synchronises)."""
+        if not self.fused:
+            return self.state0
+        return self.state1 if read_ctrl(self.ctrl)["cur"] else self.state0
+
+    def ctrl_dict(self) -> dict:
+        return read_ctrl(self.ctrl)
+
+
+class MultiShardStep:
+    """Several ranks' shard steps on one GPU whose norm and overflow decisions
+    are combined across the ranks (the scalar all-reduce between ranks)."""
+
+    def __init__(self, steps: list):
+        if not 1 <= len(steps) <= MAX_RANKS:
+            raise ValueError("between 1 and 64 ranks")
+        self.steps = steps
+        self.fused = steps[0].fused
+
+    def step(self, contribs, gather) -> None:
+        ss = self.steps
+        if self.fused:
+            for s, c in zip(ss, contribs):
+                zero_fused_step(c, s.dtype, s.nranks, s.stride, s.state0, s.state1, s.valid_len,
+                                gather, s.gather_dtype, s.offset, s.hp, s.ctrl, s.ws)
+        else:
+            for s, c in zip(ss, contribs):
+                zero_reduce_grads(c, s.dtype, s.nranks, s.stride, s.valid_len, s.ctrl, s.g, s.ws)
+        zero_grad_norm_overflow([s.ws for s in ss], [s.valid_len for s in ss],
+                                [s.ctrl for s in ss], ss[0].hp, self.fused)
+        for s in ss:
+            if self.fused:
+                zero_fused_restore(s.state0, s.state1, s.valid_len, gather, s.gather_dtype,
+                                   s.offset, s.ctrl)
+            else:
+                zero_adam_step(s.state0, s.g, s.valid_len, s.hp, s.ctrl, gather, s.gather_dtype,
+                               s.offset)
