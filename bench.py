@@ -48,15 +48,17 @@ def setup(w, torch, synth, Z):
     synth.gpu_master_range(p0, w.seed, w.master_sigma, off)
     state0 = (p0, torch.zeros_like(p0), torch.zeros_like(p0))
     fused = w.max_grad_norm <= 0
-    state1 = (torch.empty_like(p0), torch.zeros_like(p0), torch.zeros_like(p0)) if fused else None
     g = None if fused else torch.empty_like(p0)
     gather = torch.empty(w.psi, dtype=tdt, device=dev)
     synth.gpu_param_range(gather, w.seed, w.master_sigma, w.dtype, 0)
     hp = Z.hparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
                    max_grad_norm=w.max_grad_norm, scaler=w.scaler, min_scale=w.min_scale,
                    growth_interval=w.growth_interval)
-    st = Z.ShardStep(w.nranks, stride, valid, off, w.dtype, w.dtype, hp, state0, state1, g,
+    st = Z.ShardStep(w.nranks, stride, valid, off, w.dtype, w.dtype, hp, state0, g,
                      w.loss_scale)
+    if fused:  # the flat state is only needed to load the paired copy
+        del state0, p0
+        st.state = None
     torch.cuda.synchronize()
     return dict(rank=rank, shard=shard, off=off, valid=valid, stride=stride, contrib=contrib,
                 gather=gather, step=st, fused=fused)
@@ -79,19 +81,18 @@ def timed_steps(b, steps, warmup, torch, Z):
     for i in range(steps):
         if b["fused"]:
             ev[i][0].record()
-            Z.zero_fused_step(contrib, st.dtype, n, stride, st.state0, st.state1, valid, gather,
+            Z.zero_fused_step(contrib, st.dtype, n, stride, st.pair, valid, gather,
                               st.gather_dtype, off, hp, st.ctrl, st.ws)
             ev[i][1].record()
             Z.zero_grad_norm_overflow([st.ws], [valid], [st.ctrl], hp, True)
-            Z.zero_fused_restore(st.state0, st.state1, valid, gather, st.gather_dtype, off,
-                                 st.ctrl)
+            Z.zero_fused_restore(st.pair, valid, gather, st.gather_dtype, off, st.ctrl)
         else:
             ev_red[i][0].record()
             Z.zero_reduce_grads(contrib, st.dtype, n, stride, valid, st.ctrl, st.g, st.ws)
             ev_red[i][1].record()
             Z.zero_grad_norm_overflow([st.ws], [valid], [st.ctrl], hp, False)
             ev[i][0].record()
-            Z.zero_adam_step(st.state0, st.g, valid, hp, st.ctrl, gather, st.gather_dtype, off)
+            Z.zero_adam_step(st.state, st.g, valid, hp, st.ctrl, gather, st.gather_dtype, off)
             ev[i][1].record()
     t1.record()
     torch.cuda.synchronize()

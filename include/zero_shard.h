@@ -90,7 +90,7 @@ typedef struct zero_hparams {
     int32_t growth_interval;
 } zero_hparams;
 
-/* Control block: 64 bytes in DEVICE memory, one per rank, written only by the
+/* Control block: 128 bytes in DEVICE memory, one per rank, written only by the
  * library's kernels.  Host code may copy it back to read the decisions.
  * It carries the step-to-step scalars so that no step needs a host sync. */
 typedef struct zero_ctrl {
@@ -105,11 +105,23 @@ typedef struct zero_ctrl {
     int32_t skip;       /* last step was skipped (state, slot and t unchanged) */
     int32_t t;          /* applied optimizer steps */
     int32_t good_steps; /* applied steps since the loss scale last changed */
-    int32_t cur;        /* fused path: which of the two state sets is current */
+    int32_t cur;        /* fused path: which set of the paired state is current */
+    uint32_t arrive;    /* internal: arrival counter of the norm reduction, 0 between calls */
+    uint32_t reserved[15];
 } zero_ctrl;
 
-/* One rank's fp32 optimizer state: master weights, Adam m, Adam v, each
- * valid_len contiguous floats (device). */
+/* Elements per workgroup tile of every streaming pass.  The fused path's
+ * double-buffered state interleaves its two sets tile by tile. */
+#define ZERO_TILE 2048
+
+/* One rank's fp32 optimizer state: master weights, Adam m, Adam v.
+ * Flat form (two-pass path, pack/unpack): valid_len contiguous floats each.
+ * Paired form (fused path): zero_pair_elems(valid_len) floats each, holding
+ * two copies of the state interleaved per tile of ZERO_TILE elements:
+ * element i of set s lives at [(i / ZERO_TILE) * 2 * ZERO_TILE + s * ZERO_TILE
+ * + i % ZERO_TILE].  Keeping both copies of a tile adjacent lets the fused
+ * pass read one set and write the other with the access locality of an
+ * in-place update. */
 typedef struct zero_state {
     float *master;
     float *m;
@@ -131,11 +143,17 @@ size_t zero_ctrl_bytes(void);
 
 /* Device workspace (bytes) needed by zero_reduce_grads and zero_fused_step
  * for a shard of valid_len elements: one 16-byte partial (fp64 sum of
- * squares, non-finite flag) per workgroup.  Never more than 64 KiB. */
+ * squares, non-finite flag) per tile of ZERO_TILE elements, plus 256 slots
+ * for the second level of the reduction (about 0.8% of the shard's fp16
+ * size). */
 size_t zero_workspace_bytes(int64_t valid_len);
 
+/* Floats in each array of a paired (fused-path) state for valid_len
+ * elements: 2 * ceil(valid_len / ZERO_TILE) * ZERO_TILE. */
+size_t zero_pair_elems(int64_t valid_len);
+
 /* Initialise a ctrl block on `stream`: t = 0, beta powers 1, loss scale S
- * (must be finite and > 0; use 1 without a scaler), cur = 0. */
+ * (must be finite and > 0; use 1 without a scaler), cur = 0, arrive = 0. */
 int zero_ctrl_init(zero_ctrl *ctrl_dev, float loss_scale, void *stream);
 
 /* Reduce ("CMU 11-868 L18", Mechanism 1 step 3: the reduce-scatter sums and
@@ -196,25 +214,34 @@ int zero_cast_to_gather(const float *master_dev, int64_t valid_len, void *gather
 /* Fused single pass (clipping off): reduce + norm/overflow partials + Adam +
  * cast, reading each contribution and each state word once.  Because the
  * skip decision is only known after every element has been summed, the
- * state is double-buffered: the kernel reads the set ctrl->cur names
- * (state0 or state1) and writes the other; zero_grad_norm_overflow with
- * pingpong = 1 then makes the written set current, or keeps the old one on a
- * skipped step; zero_fused_restore then rewrites the gather slot from the
- * kept master on a skipped step.  Bias correction uses t+1.
- * Requires hp->max_grad_norm <= 0 (EINVAL otherwise).  Other arguments as in
- * zero_reduce_grads and zero_adam_step; gather_dev must not be NULL. */
+ * state is double-buffered in the paired layout (zero_state above): the
+ * kernel reads the set ctrl->cur names and writes the other one;
+ * zero_grad_norm_overflow with pingpong = 1 then makes the written set
+ * current, or keeps the old one on a skipped step, and zero_fused_restore
+ * rewrites the gather slot from the kept master on a skipped step.  Bias
+ * correction uses t+1.  pair: paired state, zero_pair_elems(valid_len)
+ * floats per array, 16-byte aligned.  Requires hp->max_grad_norm <= 0
+ * (EINVAL otherwise).  Other arguments as in zero_reduce_grads and
+ * zero_adam_step; gather_dev must not be NULL. */
 int zero_fused_step(const void *contrib_dev, int32_t contrib_dtype, int32_t nranks,
-                    int64_t stride, const zero_state *state0, const zero_state *state1,
-                    int64_t valid_len, void *gather_dev, int32_t gather_dtype, int64_t offset,
-                    const zero_hparams *hp, const zero_ctrl *ctrl_dev, void *ws_dev,
-                    size_t ws_bytes, void *stream);
+                    int64_t stride, const zero_state *pair, int64_t valid_len, void *gather_dev,
+                    int32_t gather_dtype, int64_t offset, const zero_hparams *hp,
+                    const zero_ctrl *ctrl_dev, void *ws_dev, size_t ws_bytes, void *stream);
 
 /* After a fused step's zero_grad_norm_overflow: if ctrl->skip, rewrite
- * gather_dev[offset + i] from the current master (state0 or state1 as
- * ctrl->cur says); otherwise every workgroup returns at once. */
-int zero_fused_restore(const zero_state *state0, const zero_state *state1, int64_t valid_len,
-                       void *gather_dev, int32_t dtype, int64_t offset,
-                       const zero_ctrl *ctrl_dev, void *stream);
+ * gather_dev[offset + i] from the current master of the paired state;
+ * otherwise every workgroup returns at once. */
+int zero_fused_restore(const zero_state *pair, int64_t valid_len, void *gather_dev,
+                       int32_t dtype, int64_t offset, const zero_ctrl *ctrl_dev, void *stream);
+
+/* Copies a flat state (valid_len floats per array) into the current set of a
+ * paired state (set ctrl->cur), e.g. to load initial or checkpointed weights. */
+int zero_pair_store(const zero_state *flat, const zero_state *pair, int64_t valid_len,
+                    const zero_ctrl *ctrl_dev, void *stream);
+
+/* Copies the current set of a paired state out to a flat state. */
+int zero_pair_load(const zero_state *pair, const zero_state *flat, int64_t valid_len,
+                   const zero_ctrl *ctrl_dev, void *stream);
 
 /* Message for the last nonzero return on the calling thread ("" if none). */
 const char *zero_last_error(void);

@@ -192,7 +192,6 @@ class GpuRun:
         z = lambda: torch.zeros(n_state, dtype=torch.float32, device=dev)
         self.state0 = (p0, z(), z())
         fused = w.max_grad_norm <= 0
-        self.state1 = (torch.empty_like(p0), z(), z()) if fused else None
         self.g = None if fused else torch.empty(n_state, dtype=torch.float32, device=dev)
         self.gather_len = w.psi if full_gather else valid
         self.gather_off = off if full_gather else 0
@@ -203,7 +202,7 @@ class GpuRun:
                        weight_decay=w.weight_decay, max_grad_norm=w.max_grad_norm,
                        scaler=w.scaler, min_scale=w.min_scale, growth_interval=w.growth_interval)
         self.step_obj = Z.ShardStep(w.nranks, c.stride, valid, self.gather_off, w.dtype, w.dtype,
-                                    hp, self.state0, self.state1, self.g, w.loss_scale)
+                                    hp, self.state0, self.g, w.loss_scale)
         self.reports = []
 
     def fill(self, step: int) -> None:

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(Z):
 
 
 def test_struct_sizes_match_header(Z):
-    assert Z.zero_ctrl_bytes() == 64 == ctypes.sizeof(Z.Ctrl)
+    assert Z.zero_ctrl_bytes() == 128 == ctypes.sizeof(Z.Ctrl)
     assert ctypes.sizeof(Z.Hparams) == 36
     assert ctypes.sizeof(Z.State) == 24
 
@@ -59,19 +59,24 @@ def test_partition_rejects(Z, args):
     assert e.value.code == -1
 
 
-def test_workspace_is_bounded(Z):
-    assert Z.zero_workspace_bytes(0) == 16
-    assert Z.zero_workspace_bytes(1) == 16
-    assert Z.zero_workspace_bytes(8 * 256) == 16
-    assert Z.zero_workspace_bytes(8 * 256 + 1) == 32
-    assert Z.zero_workspace_bytes(13_000_000_000) == 2048 * 16
+def test_workspace_and_pair_sizes(Z):
+    # one 16-byte partial per 2048-element tile plus 256 second-level slots
+    assert Z.zero_workspace_bytes(0) == 256 * 16
+    assert Z.zero_workspace_bytes(1) == 257 * 16
+    assert Z.zero_workspace_bytes(2048) == 257 * 16
+    assert Z.zero_workspace_bytes(2049) == 258 * 16
+    assert Z.zero_workspace_bytes(1_625_000_000) == (793_458 + 256) * 16
+    assert Z.zero_pair_elems(0) == 0
+    assert Z.zero_pair_elems(1) == 2 * 2048
+    assert Z.zero_pair_elems(4096) == 4 * 2048
+    assert Z.zero_pair_elems(4097) == 6 * 2048
 
 
 FAKE = 1 << 20  # a 16-byte aligned non-null address, never dereferenced
 
 
 def _reduce(Z, contrib=FAKE, dtype=1, n=8, stride=64, valid=64, ctrl=FAKE, g=FAKE, ws=FAKE,
-            wsb=64):
+            wsb=1 << 16):
     return Z._lib.zero_reduce_grads(contrib, dtype, n, stride, valid, ctrl, g, ws, wsb, None)
 
 
@@ -79,7 +84,7 @@ def _reduce(Z, contrib=FAKE, dtype=1, n=8, stride=64, valid=64, ctrl=FAKE, g=FAK
     (dict(dtype=3), -1), (dict(n=0), -1), (dict(n=1025), -1), (dict(stride=60), -1),
     (dict(stride=68, valid=64), -2), (dict(contrib=FAKE + 2), -2), (dict(g=FAKE + 4), -2),
     (dict(contrib=0), -1), (dict(g=0), -1), (dict(ctrl=0), -1), (dict(ws=0), -1),
-    (dict(wsb=8), -4), (dict(valid=-1), -3),
+    (dict(wsb=4096), -4), (dict(valid=-1), -3), (dict(ctrl=FAKE + 4), -2),
 ])
 def test_reduce_validation(Z, kw, code):
     assert _reduce(Z, **kw) == code
@@ -87,16 +92,19 @@ def test_reduce_validation(Z, kw, code):
 
 
 def test_fused_rejects_clipping_and_aliasing(Z):
-    s0 = Z.State(FAKE, FAKE + 256, FAKE + 512)
-    s1 = Z.State(FAKE + 1024, FAKE + 1280, FAKE + 1536)
+    pair = Z.State(FAKE, FAKE + 65536, FAKE + 131072)
     hp = Z.hparams(max_grad_norm=1.0)
-    rc = Z._lib.zero_fused_step(FAKE, 1, 8, 64, ctypes.byref(s0), ctypes.byref(s1), 64, FAKE, 1,
-                                0, ctypes.byref(hp), FAKE, FAKE, 64, None)
+    rc = Z._lib.zero_fused_step(FAKE, 1, 8, 64, ctypes.byref(pair), 64, FAKE, 1, 0,
+                                ctypes.byref(hp), FAKE, FAKE, 1 << 20, None)
     assert rc == -1 and "two-pass" in Z.zero_last_error()
     hp = Z.hparams()
-    rc = Z._lib.zero_fused_step(FAKE, 1, 8, 64, ctypes.byref(s0), ctypes.byref(s0), 64, FAKE, 1,
-                                0, ctypes.byref(hp), FAKE, FAKE, 64, None)
+    alias = Z.State(FAKE, FAKE, FAKE + 131072)
+    rc = Z._lib.zero_fused_step(FAKE, 1, 8, 64, ctypes.byref(alias), 64, FAKE, 1, 0,
+                                ctypes.byref(hp), FAKE, FAKE, 1 << 20, None)
     assert rc == -1 and "distinct" in Z.zero_last_error()
+    rc = Z._lib.zero_fused_step(FAKE, 1, 8, 64, ctypes.byref(pair), 64, FAKE, 1, 0,
+                                ctypes.byref(hp), FAKE, FAKE, 16, None)
+    assert rc == -4  # workspace too small
 
 
 def test_hparam_validation(Z):

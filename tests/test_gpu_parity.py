@@ -198,8 +198,7 @@ def _toy(inject=None):
         p0 = torch.empty(valid, dtype=torch.float32, device="cuda")
         synth.gpu_master_range(p0, w.seed, w.master_sigma, off)
         s0 = (p0, torch.zeros_like(p0), torch.zeros_like(p0))
-        s1 = (torch.empty_like(p0), torch.zeros_like(p0), torch.zeros_like(p0))
-        steps.append(Z.ShardStep(n, stride, valid, off, F16, F16, hp, s0, s1))
+        steps.append(Z.ShardStep(n, stride, valid, off, F16, F16, hp, s0))
         contribs.append(torch.empty((n, stride), dtype=torch.float16, device="cuda"))
         parts.append((off, valid, stride))
     multi = Z.MultiShardStep(steps)

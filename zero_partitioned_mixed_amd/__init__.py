@@ -46,10 +46,14 @@ class Ctrl(ctypes.Structure):
                 ("beta1_pow", ctypes.c_double), ("beta2_pow", ctypes.c_double),
                 ("loss_scale", ctypes.c_float), ("scale_used", ctypes.c_float),
                 ("clip", ctypes.c_float), ("nonfinite", _i32), ("skip", _i32), ("t", _i32),
-                ("good_steps", _i32), ("cur", _i32)]
+                ("good_steps", _i32), ("cur", _i32), ("arrive", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32 * 15)]
 
     def as_dict(self) -> dict:
-        return {f: getattr(self, f) for f, _ in self._fields_}
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+
+
+TILE = 2048  # ZERO_TILE
 
 
 class State(ctypes.Structure):
@@ -61,6 +65,7 @@ _sig = {
                                       ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "zero_ctrl_bytes": (ctypes.c_size_t, []),
     "zero_workspace_bytes": (ctypes.c_size_t, [_i64]),
+    "zero_pair_elems": (ctypes.c_size_t, [_i64]),
     "zero_ctrl_init": (ctypes.c_int, [_vp, ctypes.c_float, _vp]),
     "zero_reduce_grads": (ctypes.c_int, [_vp, _i32, _i32, _i64, _i64, _vp, _vp, _vp,
                                          ctypes.c_size_t, _vp]),
@@ -70,11 +75,15 @@ _sig = {
     "zero_adam_step": (ctypes.c_int, [ctypes.POINTER(State), _vp, _i64, ctypes.POINTER(Hparams),
                                       _vp, _vp, _i32, _i64, _vp]),
     "zero_cast_to_gather": (ctypes.c_int, [_vp, _i64, _vp, _i32, _i64, _vp]),
-    "zero_fused_step": (ctypes.c_int, [_vp, _i32, _i32, _i64, ctypes.POINTER(State),
-                                       ctypes.POINTER(State), _i64, _vp, _i32, _i64,
-                                       ctypes.POINTER(Hparams), _vp, _vp, ctypes.c_size_t, _vp]),
-    "zero_fused_restore": (ctypes.c_int, [ctypes.POINTER(State), ctypes.POINTER(State), _i64,
-                                          _vp, _i32, _i64, _vp, _vp]),
+    "zero_fused_step": (ctypes.c_int, [_vp, _i32, _i32, _i64, ctypes.POINTER(State), _i64, _vp,
+                                       _i32, _i64, ctypes.POINTER(Hparams), _vp, _vp,
+                                       ctypes.c_size_t, _vp]),
+    "zero_fused_restore": (ctypes.c_int, [ctypes.POINTER(State), _i64, _vp, _i32, _i64, _vp,
+                                          _vp]),
+    "zero_pair_store": (ctypes.c_int, [ctypes.POINTER(State), ctypes.POINTER(State), _i64, _vp,
+                                       _vp]),
+    "zero_pair_load": (ctypes.c_int, [ctypes.POINTER(State), ctypes.POINTER(State), _i64, _vp,
+                                      _vp]),
     "zero_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _sig.items():
@@ -137,6 +146,10 @@ def zero_workspace_bytes(valid_len: int) -> int:
     return _lib.zero_workspace_bytes(valid_len)
 
 
+def zero_pair_elems(valid_len: int) -> int:
+    return _lib.zero_pair_elems(valid_len)
+
+
 def zero_ctrl_init(ctrl, loss_scale: float) -> None:
     _check("zero_ctrl_init", _lib.zero_ctrl_init(_ptr(ctrl), loss_scale, _stream()))
 
@@ -170,22 +183,32 @@ def zero_cast_to_gather(master, valid_len: int, gather, dtype: int, offset: int)
         _ptr(master), valid_len, _ptr(gather), dtype, offset, _stream()))
 
 
-def zero_fused_step(contrib, contrib_dtype: int, nranks: int, stride: int, state0, state1,
+def zero_fused_step(contrib, contrib_dtype: int, nranks: int, stride: int, pair,
                     valid_len: int, gather, gather_dtype: int, offset: int, hp: Hparams, ctrl,
                     ws) -> None:
-    s0, s1 = _state(state0), _state(state1)
+    st = _state(pair)
     _check("zero_fused_step", _lib.zero_fused_step(
-        _ptr(contrib), contrib_dtype, nranks, stride, ctypes.byref(s0), ctypes.byref(s1),
-        valid_len, _ptr(gather), gather_dtype, offset, ctypes.byref(hp), _ptr(ctrl), _ptr(ws),
+        _ptr(contrib), contrib_dtype, nranks, stride, ctypes.byref(st), valid_len, _ptr(gather),
+        gather_dtype, offset, ctypes.byref(hp), _ptr(ctrl), _ptr(ws),
         ws.numel() * ws.element_size(), _stream()))
 
 
-def zero_fused_restore(state0, state1, valid_len: int, gather, dtype: int, offset: int,
-                       ctrl) -> None:
-    s0, s1 = _state(state0), _state(state1)
+def zero_fused_restore(pair, valid_len: int, gather, dtype: int, offset: int, ctrl) -> None:
+    st = _state(pair)
     _check("zero_fused_restore", _lib.zero_fused_restore(
-        ctypes.byref(s0), ctypes.byref(s1), valid_len, _ptr(gather), dtype, offset, _ptr(ctrl),
-        _stream()))
+        ctypes.byref(st), valid_len, _ptr(gather), dtype, offset, _ptr(ctrl), _stream()))
+
+
+def zero_pair_store(flat, pair, valid_len: int, ctrl) -> None:
+    f, p = _state(flat), _state(pair)
+    _check("zero_pair_store", _lib.zero_pair_store(ctypes.byref(f), ctypes.byref(p), valid_len,
+                                                   _ptr(ctrl), _stream()))
+
+
+def zero_pair_load(pair, flat, valid_len: int, ctrl) -> None:
+    p, f = _state(pair), _state(flat)
+    _check("zero_pair_load", _lib.zero_pair_load(ctypes.byref(p), ctypes.byref(f), valid_len,
+                                                 _ptr(ctrl), _stream()))
 
 
 def zero_last_error() -> str:
@@ -202,47 +225,54 @@ def read_ctrl(ctrl) -> dict:
 class ShardStep:
     """One rank's shard step over caller-provided device buffers.
 
-    contrib: [N, stride] 16-bit tensor; state0 (and state1 for the fused
-    path): (master, m, v) fp32 tensors of valid_len; gather: the full 16-bit
-    parameter buffer, this rank's slot at ``offset``.
+    contrib: [N, stride] 16-bit tensor; gather: the full 16-bit parameter
+    buffer, this rank's slot at ``offset``.  ``state`` is the flat
+    (master, m, v) fp32 state of valid_len elements.  The two-pass path
+    (clipping on) updates it in place through ``g``; the fused path keeps
+    its double-buffered copy in ``pair`` (allocated here, loaded from
+    ``state``) and ``current()`` copies the current set back out.
     """
 
     def __init__(self, nranks, stride, valid_len, offset, dtype, gather_dtype, hp: Hparams,
-                 state0, state1=None, g=None, loss_scale=1.0):
+                 state, g=None, loss_scale=1.0):
         import torch
         self.nranks, self.stride, self.valid_len, self.offset = nranks, stride, valid_len, offset
         self.dtype, self.gather_dtype, self.hp = dtype, gather_dtype, hp
-        self.state0, self.state1, self.g = state0, state1, g
+        self.state, self.g = state, g
         self.fused = hp.max_grad_norm <= 0
-        if self.fused and state1 is None:
-            raise ValueError("the fused path needs a second state set")
         if not self.fused and g is None:
             raise ValueError("the two-pass path needs a g buffer")
-        dev = state0[0].device
+        dev = state[0].device
         self.ctrl = torch.empty(zero_ctrl_bytes(), dtype=torch.uint8, device=dev)
         self.ws = torch.empty(zero_workspace_bytes(valid_len), dtype=torch.uint8, device=dev)
         zero_ctrl_init(self.ctrl, loss_scale)
+        self.pair = None
+        if self.fused:
+            n = max(zero_pair_elems(valid_len), 4)
+            self.pair = tuple(torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3))
+            zero_pair_store(state, self.pair, valid_len, self.ctrl)
 
     def step(self, contrib, gather) -> None:
         if self.fused:
-            zero_fused_step(contrib, self.dtype, self.nranks, self.stride, self.state0,
-                            self.state1, self.valid_len, gather, self.gather_dtype, self.offset,
-                            self.hp, self.ctrl, self.ws)
+            zero_fused_step(contrib, self.dtype, self.nranks, self.stride, self.pair,
+                            self.valid_len, gather, self.gather_dtype, self.offset, self.hp,
+                            self.ctrl, self.ws)
             zero_grad_norm_overflow([self.ws], [self.valid_len], [self.ctrl], self.hp, True)
-            zero_fused_restore(self.state0, self.state1, self.valid_len, gather,
-                               self.gather_dtype, self.offset, self.ctrl)
+            zero_fused_restore(self.pair, self.valid_len, gather, self.gather_dtype, self.offset,
+                               self.ctrl)
         else:
             zero_reduce_grads(contrib, self.dtype, self.nranks, self.stride, self.valid_len,
                               self.ctrl, self.g, self.ws)
             zero_grad_norm_overflow([self.ws], [self.valid_len], [self.ctrl], self.hp, False)
-            zero_adam_step(self.state0, self.g, self.valid_len, self.hp, self.ctrl, gather,
+            zero_adam_step(self.state, self.g, self.valid_len, self.hp, self.ctrl, gather,
                            self.gather_dtype, self.offset)
 
     def current(self):
-        """(master, m, v) holding the current state (reads ctrl: synchronises)."""
-        if not self.fused:
-            return self.state0
-        return self.state1 if read_ctrl(self.ctrl)["cur"] else self.state0
+        """(master, m, v): the current state, flat (the fused path copies it
+        out of the paired buffers into ``state``)."""
+        if self.fused:
+            zero_pair_load(self.pair, self.state, self.valid_len, self.ctrl)
+        return self.state
 
     def ctrl_dict(self) -> dict:
         return read_ctrl(self.ctrl)
@@ -262,8 +292,8 @@ class MultiShardStep:
         ss = self.steps
         if self.fused:
             for s, c in zip(ss, contribs):
-                zero_fused_step(c, s.dtype, s.nranks, s.stride, s.state0, s.state1, s.valid_len,
-                                gather, s.gather_dtype, s.offset, s.hp, s.ctrl, s.ws)
+                zero_fused_step(c, s.dtype, s.nranks, s.stride, s.pair, s.valid_len, gather,
+                                s.gather_dtype, s.offset, s.hp, s.ctrl, s.ws)
         else:
             for s, c in zip(ss, contribs):
                 zero_reduce_grads(c, s.dtype, s.nranks, s.stride, s.valid_len, s.ctrl, s.g, s.ws)
@@ -271,8 +301,7 @@ class MultiShardStep:
                                 [s.ctrl for s in ss], ss[0].hp, self.fused)
         for s in ss:
             if self.fused:
-                zero_fused_restore(s.state0, s.state1, s.valid_len, gather, s.gather_dtype,
-                                   s.offset, s.ctrl)
+                zero_fused_restore(s.pair, s.valid_len, gather, s.gather_dtype, s.offset, s.ctrl)
             else:
-                zero_adam_step(s.state0, s.g, s.valid_len, s.hp, s.ctrl, gather, s.gather_dtype,
+                zero_adam_step(s.state, s.g, s.valid_len, s.hp, s.ctrl, gather, s.gather_dtype,
                                s.offset)

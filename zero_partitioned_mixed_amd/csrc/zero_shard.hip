@@ -3,20 +3,24 @@
 // Every kernel here streams HBM: the work per element is a handful of fp32
 // operations against 26 + 2N bytes, so nothing is a contraction and nothing
 // uses the matrix cores.  The design points are
-//   * 16-byte vector loads/stores (8 sixteen-bit or 4 fp32 values per access)
-//     with non-temporal hints: every byte is touched once per step, so it
-//     should not displace anything in L2 or the Infinity Cache;
-//   * a grid of at most kMaxParts workgroups of 4 waves looping over the
-//     shard (grid-stride), so each workgroup leaves exactly one 16-byte
-//     partial of the norm reduction and the second level is a single small
-//     workgroup;
+//   * one workgroup per tile of ZERO_TILE = 2048 elements (256 threads x 8
+//     elements), launched as one grid over the whole shard: a block moves
+//     16-byte vectors (8 sixteen-bit or 4 fp32 values per access, 4 KiB per
+//     instruction per workgroup) for every stream it touches and retires, so
+//     the dispatcher keeps the active window of the shard compact, which is
+//     what lets HBM pages be reused across the streams;
+//   * non-temporal hints on every access: each byte is touched once per step;
+//   * the fused path double-buffers the optimizer state with the two sets of
+//     a tile adjacent in memory, so reading one set and writing the other
+//     keeps the locality of an in-place update;
 //   * fp32 reduction in rank order k = 0..N-1 and each Adam operation rounded
 //     once in the written order (compiled with -ffp-contract=off, correctly
 //     rounded division and square root), so results are reproducible and
 //     agree with a scalar reference operation for operation;
-//   * the squared norm accumulated in fp64 per lane, reduced per wave with
-//     cross-lane shuffles, per workgroup through LDS, then across workgroups
-//     in a fixed order: deterministic and far inside the clip tolerance;
+//   * the squared norm accumulated in fp64: per lane, per wave with
+//     cross-lane shuffles, per workgroup through LDS (one 16-byte partial per
+//     tile), then over contiguous ranges of partials and finally over those
+//     ranges in index order: deterministic and far inside the clip tolerance;
 //   * all step-to-step scalars (loss scale, t, beta powers, skip, clip, the
 //     current state set) live in a device control block, so a step never
 //     waits for the host.
@@ -31,10 +35,14 @@
 
 namespace {
 
-constexpr int kBlock = 256;           // threads per workgroup: 4 wave64s
-constexpr int kWaves = kBlock / 64;
-constexpr int kVec = 8;               // elements per thread per iteration
-constexpr int64_t kMaxParts = 2048;   // workgroups of a streaming pass (8 per CU)
+constexpr int kBlock = 256;                 // threads per streaming workgroup: 4 wave64s
+constexpr int kVec = 8;                     // elements per thread
+constexpr int64_t kTile = ZERO_TILE;        // elements per workgroup
+static_assert(kTile == (int64_t)kBlock * kVec, "tile = threads x elements per thread");
+constexpr int kFinBlock = 1024;             // threads per finalize workgroup
+constexpr int kFinGroups = 256;             // most first-level groups of the finalize
+constexpr int64_t kFinPer = 4096;           // partials per first-level finalize group
+constexpr int kRestoreGrid = 1024;          // workgroups of the (usually idle) restore pass
 constexpr int64_t kMaxLen = int64_t(1) << 40;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -47,14 +55,9 @@ struct Partial {
     uint32_t pad;
 };
 static_assert(sizeof(Partial) == 16, "partial layout");
-static_assert(sizeof(zero_ctrl) == 64, "ctrl layout");
+static_assert(sizeof(zero_ctrl) == 128, "ctrl layout");
 
-int64_t parts_for(int64_t len) {
-    if (len <= 0) return 0;
-    int64_t nvec = (len + kVec - 1) / kVec;
-    int64_t g = (nvec + kBlock - 1) / kBlock;
-    return g > kMaxParts ? kMaxParts : g;
-}
+int64_t tiles_for(int64_t len) { return len <= 0 ? 0 : (len + kTile - 1) / kTile; }
 
 // ---------------------------------------------------------------- conversions
 template <int DT>
@@ -212,17 +215,24 @@ __device__ __forceinline__ void store_h8(uint16_t* __restrict__ dst, const uint3
     }
 }
 
+// Offset of this thread's 8 elements of set `s` in a paired state array.
+__device__ __forceinline__ int64_t pair_off(int64_t tile, int s) {
+    return tile * 2 * kTile + (int64_t)s * kTile + threadIdx.x * kVec;
+}
+
 // ---------------------------------------------------------------- norm partials
-// Reduces (sumsq, nonfinite) over the workgroup: cross-lane within each wave,
-// then the kWaves wave results in wave order.  Thread 0 gets the result.
+// Reduces (sumsq, nonfinite) over a workgroup of NT threads: cross-lane within
+// each wave, then the wave results in wave order.  Thread 0 gets the result.
+template <int NT>
 __device__ __forceinline__ void block_reduce(double& ss, uint32_t& bad) {
+    constexpr int kW = NT / 64;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         ss += __shfl_xor(ss, off, 64);
         bad |= __shfl_xor(bad, off, 64);
     }
-    __shared__ double s_ss[kWaves];
-    __shared__ uint32_t s_bad[kWaves];
+    __shared__ double s_ss[kW];
+    __shared__ uint32_t s_bad[kW];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     if (lane == 0) {
@@ -234,7 +244,7 @@ __device__ __forceinline__ void block_reduce(double& ss, uint32_t& bad) {
         double t = 0.0;
         uint32_t b = 0;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < kW; ++w) {
             t += s_ss[w];
             b |= s_bad[w];
         }
@@ -244,7 +254,7 @@ __device__ __forceinline__ void block_reduce(double& ss, uint32_t& bad) {
 }
 
 __device__ __forceinline__ void write_partial(Partial* __restrict__ ws, double ss, uint32_t bad) {
-    block_reduce(ss, bad);
+    block_reduce<kBlock>(ss, bad);
     if (threadIdx.x == 0) {
         Partial p;
         p.sumsq = ss;
@@ -255,22 +265,20 @@ __device__ __forceinline__ void write_partial(Partial* __restrict__ ws, double s
 }
 
 // ---------------------------------------------------------------- kernels
-__global__ void ctrl_init_kernel(zero_ctrl* __restrict__ c, float loss_scale) {
+struct InitArgs {
+    zero_ctrl* ctrl;
+    float loss_scale;
+};
+
+__global__ void ctrl_init_kernel(InitArgs a) {
     if (blockIdx.x == 0 && threadIdx.x == 0) {
-        zero_ctrl z;
-        z.sumsq = 0.0;
-        z.norm = 0.0;
+        zero_ctrl z = {};
         z.beta1_pow = 1.0;
         z.beta2_pow = 1.0;
-        z.loss_scale = loss_scale;
-        z.scale_used = loss_scale;
+        z.loss_scale = a.loss_scale;
+        z.scale_used = a.loss_scale;
         z.clip = 1.0f;
-        z.nonfinite = 0;
-        z.skip = 0;
-        z.t = 0;
-        z.good_steps = 0;
-        z.cur = 0;
-        *c = z;
+        *a.ctrl = z;
     }
 }
 
@@ -284,18 +292,17 @@ struct ReduceArgs {
     int32_t n;
 };
 
-// Pass 1 of the two-pass step: g = fl32(sum_k C[k]) * inv, plus partials.
+// Pass 1 of the two-pass step: g = fl32(sum_k C[k]) * inv, plus one partial
+// per tile.
 template <int DT>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
     const float inv = (float)(1.0 / ((double)a.n * (double)a.ctrl->loss_scale));
     double ss = 0.0;
     uint32_t bad = 0;
-    const int64_t nvec = a.len / kVec;
-    const int64_t gstride = (int64_t)gridDim.x * kBlock;
-    const int64_t tid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    for (int64_t vi = tid; vi < nvec; vi += gstride) {
+    const int64_t e = (int64_t)blockIdx.x * kTile + threadIdx.x * kVec;
+    if (e + kVec <= a.len) {
         float acc[kVec], out[kVec];
-        sum_rows<DT>(a.contrib + vi * kVec, a.n, a.stride, acc);
+        sum_rows<DT>(a.contrib + e, a.n, a.stride, acc);
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             bad |= __builtin_isfinite(acc[j]) ? 0u : 1u;
@@ -303,15 +310,15 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
             ss += (double)gj * (double)gj;
             out[j] = gj;
         }
-        store8(a.g + vi * kVec, out);
-    }
-    const int64_t e = nvec * kVec + tid;  // the < 8 tail elements: threads 0.. of workgroup 0
-    if (e < a.len) {
-        const float acc = sum_rows1<DT>(a.contrib + e, a.n, a.stride);
-        bad |= __builtin_isfinite(acc) ? 0u : 1u;
-        const float gj = acc * inv;
-        ss += (double)gj * (double)gj;
-        a.g[e] = gj;
+        store8(a.g + e, out);
+    } else {
+        for (int64_t i = e; i < a.len; ++i) {
+            const float acc = sum_rows1<DT>(a.contrib + i, a.n, a.stride);
+            bad |= __builtin_isfinite(acc) ? 0u : 1u;
+            const float gj = acc * inv;
+            ss += (double)gj * (double)gj;
+            a.g[i] = gj;
+        }
     }
     write_partial(a.ws, ss, bad);
 }
@@ -319,27 +326,60 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
 struct CombineArgs {
     const Partial* ws[ZERO_MAX_RANKS];
     zero_ctrl* ctrl[ZERO_MAX_RANKS];
-    int32_t nparts[ZERO_MAX_RANKS];
+    int64_t first[ZERO_MAX_RANKS + 1];  // prefix offsets of each rank's partials
+    Partial* level1;                    // kFinGroups slots (behind rank 0's partials)
+    int64_t per;                        // partials per first-level group
     int32_t nranks;
     int32_t pingpong;
     zero_hparams hp;
 };
 
-// Second level of the norm/overflow reduction and the step decisions.
-__global__ void __launch_bounds__(kBlock) finalize_kernel(CombineArgs a) {
+// Second level of the norm/overflow reduction and the step decisions.  Group
+// g sums partials [g*per, (g+1)*per) of the ranks' concatenated lists in
+// order; with several groups, the last group to arrive sums the group results
+// in group order.  Which group finishes last changes nothing in the result.
+__global__ void __launch_bounds__(kFinBlock) finalize_kernel(CombineArgs a) {
+    const int64_t total = a.first[a.nranks];
+    const int64_t lo = (int64_t)blockIdx.x * a.per;
+    const int64_t hi = lo + a.per < total ? lo + a.per : total;
     double ss = 0.0;
     uint32_t bad = 0;
-    for (int r = 0; r < a.nranks; ++r) {
-        const Partial* __restrict__ w = a.ws[r];
-        for (int i = threadIdx.x; i < a.nparts[r]; i += kBlock) {
-            ss += w[i].sumsq;
-            bad |= w[i].nonfinite;
-        }
+    int r = 0;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += kFinBlock) {
+        while (i >= a.first[r + 1]) ++r;
+        const Partial p = a.ws[r][i - a.first[r]];
+        ss += p.sumsq;
+        bad |= p.nonfinite;
     }
-    block_reduce(ss, bad);
+    block_reduce<kFinBlock>(ss, bad);
+    if (gridDim.x > 1) {
+        __shared__ uint32_t s_last;
+        if (threadIdx.x == 0) {
+            Partial p;
+            p.sumsq = ss;
+            p.nonfinite = bad;
+            p.pad = 0u;
+            a.level1[blockIdx.x] = p;
+            __threadfence();
+            const uint32_t prev = atomicAdd(&a.ctrl[0]->arrive, 1u);
+            s_last = prev == gridDim.x - 1 ? 1u : 0u;
+        }
+        __syncthreads();
+        if (!s_last) return;
+        __threadfence();
+        ss = 0.0;
+        bad = 0;
+        for (int g = threadIdx.x; g < (int)gridDim.x; g += kFinBlock) {
+            const Partial p = a.level1[g];
+            ss += p.sumsq;
+            bad |= p.nonfinite;
+        }
+        block_reduce<kFinBlock>(ss, bad);
+    }
     if (threadIdx.x != 0) return;
     const zero_hparams& hp = a.hp;
     zero_ctrl c = *a.ctrl[0];
+    c.arrive = 0u;
     c.sumsq = ss;
     c.norm = sqrt(ss);
     c.nonfinite = bad ? 1 : 0;
@@ -367,7 +407,7 @@ __global__ void __launch_bounds__(kBlock) finalize_kernel(CombineArgs a) {
         c.beta2_pow = c.beta2_pow * (double)hp.beta2;
         if (a.pingpong) c.cur ^= 1;
     }
-    for (int r = 0; r < a.nranks; ++r) *a.ctrl[r] = c;
+    for (int q = 0; q < a.nranks; ++q) *a.ctrl[q] = c;
 }
 
 struct AdamArgs {
@@ -388,75 +428,103 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(AdamArgs a) {
     if (c->skip) return;
     const float clip = c->clip;
     const AdamK k = make_adam(a.hp, c->beta1_pow, c->beta2_pow);
-    const int64_t nvec = a.len / kVec;
-    const int64_t gstride = (int64_t)gridDim.x * kBlock;
-    const int64_t tid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    for (int64_t vi = tid; vi < nvec; vi += gstride) {
-        const int64_t o = vi * kVec;
+    const int64_t e = (int64_t)blockIdx.x * kTile + threadIdx.x * kVec;
+    if (e + kVec <= a.len) {
         float g[kVec], p[kVec], m[kVec], v[kVec];
         uint32_t h[kVec];
-        load8(a.g + o, g);
-        load8(a.master + o, p);
-        load8(a.m + o, m);
-        load8(a.v + o, v);
+        load8(a.g + e, g);
+        load8(a.master + e, p);
+        load8(a.m + e, m);
+        load8(a.v + e, v);
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             adam_elem(k, g[j] * clip, p[j], m[j], v[j]);
             h[j] = narrow<DT>(p[j]);
         }
-        store8(a.master + o, p);
-        store8(a.m + o, m);
-        store8(a.v + o, v);
-        if (GW > 0) store_h8<(GW > 0 ? GW : 1)>(a.slot + o, h);
-    }
-    const int64_t e = nvec * kVec + tid;
-    if (e < a.len) {
-        float p = a.master[e], m = a.m[e], v = a.v[e];
-        adam_elem(k, a.g[e] * clip, p, m, v);
-        a.master[e] = p;
-        a.m[e] = m;
-        a.v[e] = v;
-        if (GW > 0) a.slot[e] = (uint16_t)narrow<DT>(p);
+        store8(a.master + e, p);
+        store8(a.m + e, m);
+        store8(a.v + e, v);
+        if constexpr (GW > 0) store_h8<GW>(a.slot + e, h);
+    } else {
+        for (int64_t i = e; i < a.len; ++i) {
+            float p = a.master[i], m = a.m[i], v = a.v[i];
+            adam_elem(k, a.g[i] * clip, p, m, v);
+            a.master[i] = p;
+            a.m[i] = m;
+            a.v[i] = v;
+            if constexpr (GW > 0) a.slot[i] = (uint16_t)narrow<DT>(p);
+        }
     }
 }
 
 struct CastArgs {
-    const float* master0;
-    const float* master1;
+    const float* master;  // flat master, or the paired master (RESTORE)
     uint16_t* slot;
     int64_t len;
-    const zero_ctrl* ctrl;  // restore only
+    const zero_ctrl* ctrl;  // RESTORE only
 };
 
-// gather slot <- RNE(master).  RESTORE: only when ctrl->skip, from the
-// current set (master0 or master1 as ctrl->cur says).
-template <int DT, int GW, bool RESTORE>
+// gather slot <- RNE(master), one tile per workgroup.
+template <int DT, int GW>
 __global__ void __launch_bounds__(kBlock) cast_kernel(CastArgs a) {
-    const float* __restrict__ src = a.master0;
-    if (RESTORE) {
-        if (!a.ctrl->skip) return;
-        src = a.ctrl->cur ? a.master1 : a.master0;
-    }
-    const int64_t nvec = a.len / kVec;
-    const int64_t gstride = (int64_t)gridDim.x * kBlock;
-    const int64_t tid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    for (int64_t vi = tid; vi < nvec; vi += gstride) {
+    const int64_t e = (int64_t)blockIdx.x * kTile + threadIdx.x * kVec;
+    if (e + kVec <= a.len) {
         float p[kVec];
         uint32_t h[kVec];
-        load8(src + vi * kVec, p);
+        load8(a.master + e, p);
 #pragma unroll
         for (int j = 0; j < kVec; ++j) h[j] = narrow<DT>(p[j]);
-        store_h8<GW>(a.slot + vi * kVec, h);
+        store_h8<GW>(a.slot + e, h);
+    } else {
+        for (int64_t i = e; i < a.len; ++i) a.slot[i] = (uint16_t)narrow<DT>(a.master[i]);
     }
-    const int64_t e = nvec * kVec + tid;
-    if (e < a.len) a.slot[e] = (uint16_t)narrow<DT>(src[e]);
+}
+
+// After a skipped fused step: gather slot <- RNE(current set of the paired
+// master).  A fixed small grid walks the tiles; with no skip every
+// workgroup returns after reading the flag.
+template <int DT>
+__global__ void __launch_bounds__(kBlock) restore_kernel(CastArgs a) {
+    if (!a.ctrl->skip) return;
+    const int cur = a.ctrl->cur;
+    const int64_t ntile = (a.len + kTile - 1) / kTile;
+    for (int64_t tile = blockIdx.x; tile < ntile; tile += gridDim.x) {
+        const int64_t e = tile * kTile + threadIdx.x * kVec;
+        const float* src = a.master + pair_off(tile, cur);
+        for (int j = 0; j < kVec && e + j < a.len; ++j)
+            a.slot[e + j] = (uint16_t)narrow<DT>(src[j]);
+    }
+}
+
+struct PackArgs {
+    float* flat[3];
+    float* pair[3];
+    int64_t len;
+    const zero_ctrl* ctrl;
+};
+
+// TO_PAIR: flat -> current set of the pair; otherwise current set -> flat.
+template <bool TO_PAIR>
+__global__ void __launch_bounds__(kBlock) pack_kernel(PackArgs a) {
+    const int cur = a.ctrl->cur;
+    const int64_t tile = blockIdx.x;
+    const int64_t e = tile * kTile + threadIdx.x * kVec;
+    const int64_t po = pair_off(tile, cur);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        for (int j = 0; j < kVec && e + j < a.len; ++j) {
+            if (TO_PAIR)
+                a.pair[q][po + j] = a.flat[q][e + j];
+            else
+                a.flat[q][e + j] = a.pair[q][po + j];
+        }
+    }
 }
 
 struct FusedArgs {
     const uint16_t* contrib;
     int64_t stride;
-    float* set0[3];  // master, m, v
-    float* set1[3];
+    float* pair[3];  // master, m, v in the paired layout
     uint16_t* slot;
     int64_t len;
     const zero_ctrl* ctrl;
@@ -465,33 +533,28 @@ struct FusedArgs {
     int32_t n;
 };
 
-// Single pass: reduce + partials + Adam (read set cur, write set 1-cur) + cast.
+// Single pass: reduce + partial + Adam (read set cur, write set 1-cur of the
+// tile) + cast, one tile per workgroup.
 template <int DTI, int DTO, int GW>
 __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
     const zero_ctrl* __restrict__ c = a.ctrl;
     const int cur = c->cur;
-    const float* __restrict__ ps = cur ? a.set1[0] : a.set0[0];
-    const float* __restrict__ ms = cur ? a.set1[1] : a.set0[1];
-    const float* __restrict__ vs = cur ? a.set1[2] : a.set0[2];
-    float* __restrict__ pd = cur ? a.set0[0] : a.set1[0];
-    float* __restrict__ md = cur ? a.set0[1] : a.set1[1];
-    float* __restrict__ vd = cur ? a.set0[2] : a.set1[2];
     const float inv = (float)(1.0 / ((double)a.n * (double)c->loss_scale));
     const AdamK k = make_adam(a.hp, c->beta1_pow * (double)a.hp.beta1,
                               c->beta2_pow * (double)a.hp.beta2);
+    const int64_t tile = blockIdx.x;
+    const int64_t e = tile * kTile + threadIdx.x * kVec;
+    const int64_t so = pair_off(tile, cur);
+    const int64_t dof = pair_off(tile, cur ^ 1);
     double ss = 0.0;
     uint32_t bad = 0;
-    const int64_t nvec = a.len / kVec;
-    const int64_t gstride = (int64_t)gridDim.x * kBlock;
-    const int64_t tid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    for (int64_t vi = tid; vi < nvec; vi += gstride) {
-        const int64_t o = vi * kVec;
+    if (e + kVec <= a.len) {
         float acc[kVec], p[kVec], m[kVec], v[kVec];
         uint32_t h[kVec];
-        load8(ps + o, p);
-        load8(ms + o, m);
-        load8(vs + o, v);
-        sum_rows<DTI>(a.contrib + o, a.n, a.stride, acc);
+        sum_rows<DTI>(a.contrib + e, a.n, a.stride, acc);
+        load8(a.pair[0] + so, p);
+        load8(a.pair[1] + so, m);
+        load8(a.pair[2] + so, v);
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             bad |= __builtin_isfinite(acc[j]) ? 0u : 1u;
@@ -500,23 +563,23 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
             adam_elem(k, gj, p[j], m[j], v[j]);
             h[j] = narrow<DTO>(p[j]);
         }
-        store8(pd + o, p);
-        store8(md + o, m);
-        store8(vd + o, v);
-        store_h8<GW>(a.slot + o, h);
-    }
-    const int64_t e = nvec * kVec + tid;
-    if (e < a.len) {
-        const float acc = sum_rows1<DTI>(a.contrib + e, a.n, a.stride);
-        bad |= __builtin_isfinite(acc) ? 0u : 1u;
-        const float gj = acc * inv;
-        ss += (double)gj * (double)gj;
-        float p = ps[e], m = ms[e], v = vs[e];
-        adam_elem(k, gj, p, m, v);
-        pd[e] = p;
-        md[e] = m;
-        vd[e] = v;
-        a.slot[e] = (uint16_t)narrow<DTO>(p);
+        store8(a.pair[0] + dof, p);
+        store8(a.pair[1] + dof, m);
+        store8(a.pair[2] + dof, v);
+        store_h8<GW>(a.slot + e, h);
+    } else {
+        for (int j = 0; e + j < a.len; ++j) {
+            const float acc = sum_rows1<DTI>(a.contrib + e + j, a.n, a.stride);
+            bad |= __builtin_isfinite(acc) ? 0u : 1u;
+            const float gj = acc * inv;
+            ss += (double)gj * (double)gj;
+            float p = a.pair[0][so + j], m = a.pair[1][so + j], v = a.pair[2][so + j];
+            adam_elem(k, gj, p, m, v);
+            a.pair[0][dof + j] = p;
+            a.pair[1][dof + j] = m;
+            a.pair[2][dof + j] = v;
+            a.slot[e + j] = (uint16_t)narrow<DTO>(p);
+        }
     }
     write_partial(a.ws, ss, bad);
 }
@@ -537,12 +600,6 @@ int ok() {
     return ZERO_OK;
 }
 
-int launched(const char* what) {
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
-    return ok();
-}
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool valid_dtype(int32_t dt) { return dt == ZERO_F16 || dt == ZERO_BF16; }
@@ -554,6 +611,12 @@ int store_width(const void* p) {
     if ((a & 7u) == 0) return 4;
     if ((a & 3u) == 0) return 2;
     return 1;
+}
+
+int check_len(int64_t len, const char* what) {
+    if (len < 0 || len > kMaxLen)
+        return fail(ZERO_ERANGE, "%s: valid_len %lld out of range", what, (long long)len);
+    return ZERO_OK;
 }
 
 int check_hp(const zero_hparams* hp) {
@@ -570,7 +633,8 @@ int check_hp(const zero_hparams* hp) {
 }
 
 int check_contrib(const void* contrib, int32_t dtype, int32_t n, int64_t stride, int64_t len) {
-    if (len < 0 || len > kMaxLen) return fail(ZERO_ERANGE, "valid_len %lld out of range", (long long)len);
+    int rc;
+    if ((rc = check_len(len, "contributions")) != ZERO_OK) return rc;
     if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, "unknown contribution dtype %d", dtype);
     if (n < 1 || n > ZERO_MAX_CONTRIB)
         return fail(ZERO_EINVAL, "nranks %d outside [1, %d]", n, ZERO_MAX_CONTRIB);
@@ -589,6 +653,8 @@ int check_state(const zero_state* s, const char* what) {
         return fail(ZERO_EINVAL, "%s: null state pointer", what);
     if (!aligned16(s->master) || !aligned16(s->m) || !aligned16(s->v))
         return fail(ZERO_EALIGN, "%s: state arrays must be 16-byte aligned", what);
+    if (s->master == s->m || s->master == s->v || s->m == s->v)
+        return fail(ZERO_EINVAL, "%s: master, m and v must be distinct arrays", what);
     return ZERO_OK;
 }
 
@@ -597,55 +663,72 @@ int check_ws(const void* ws, size_t ws_bytes, int64_t len) {
     if (ws == nullptr) return fail(ZERO_EINVAL, "workspace pointer is null");
     if (ws_bytes < need)
         return fail(ZERO_ESPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
-    if ((reinterpret_cast<uintptr_t>(ws) & 15u) != 0)
-        return fail(ZERO_EALIGN, "workspace not 16-byte aligned");
+    if (!aligned16(ws)) return fail(ZERO_EALIGN, "workspace not 16-byte aligned");
     return ZERO_OK;
 }
 
 int check_slot(const void* gather, int32_t dtype, int64_t offset) {
     if (gather == nullptr) return fail(ZERO_EINVAL, "gather pointer is null");
     if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, "unknown gather dtype %d", dtype);
-    if (offset < 0 || offset > kMaxLen * 64) return fail(ZERO_ERANGE, "offset %lld out of range", (long long)offset);
+    if (offset < 0 || offset > kMaxLen * 64)
+        return fail(ZERO_ERANGE, "offset %lld out of range", (long long)offset);
     if ((reinterpret_cast<uintptr_t>(gather) & 1u) != 0)
         return fail(ZERO_EALIGN, "gather buffer not 2-byte aligned");
     return ZERO_OK;
 }
 
-template <int GW>
-void* select_fused_gw(int dti, int dto) {
-    if (dti == ZERO_F16 && dto == ZERO_F16) return (void*)fused_kernel<ZERO_F16, ZERO_F16, GW>;
-    if (dti == ZERO_F16 && dto == ZERO_BF16) return (void*)fused_kernel<ZERO_F16, ZERO_BF16, GW>;
-    if (dti == ZERO_BF16 && dto == ZERO_F16) return (void*)fused_kernel<ZERO_BF16, ZERO_F16, GW>;
-    return (void*)fused_kernel<ZERO_BF16, ZERO_BF16, GW>;
-}
-
-template <int DT>
-void* select_adam_gw(int gw) {
-    switch (gw) {
-        case 8: return (void*)adam_kernel<DT, 8>;
-        case 4: return (void*)adam_kernel<DT, 4>;
-        case 2: return (void*)adam_kernel<DT, 2>;
-        case 1: return (void*)adam_kernel<DT, 1>;
-        default: return (void*)adam_kernel<DT, 0>;
-    }
-}
-
-template <bool RESTORE, int DT>
-void* select_cast_gw(int gw) {
-    switch (gw) {
-        case 8: return (void*)cast_kernel<DT, 8, RESTORE>;
-        case 4: return (void*)cast_kernel<DT, 4, RESTORE>;
-        case 2: return (void*)cast_kernel<DT, 2, RESTORE>;
-        default: return (void*)cast_kernel<DT, 1, RESTORE>;
-    }
+int check_ctrl(const zero_ctrl* c, const char* what) {
+    if (c == nullptr) return fail(ZERO_EINVAL, "%s: null ctrl", what);
+    if ((reinterpret_cast<uintptr_t>(c) & 7u) != 0)
+        return fail(ZERO_EALIGN, "%s: ctrl not 8-byte aligned", what);
+    return ZERO_OK;
 }
 
 template <class Args>
-int launch(void* kernel, unsigned grid, hipStream_t s, const Args& args, const char* what) {
+using Kernel = void (*)(Args);
+
+template <int GW>
+Kernel<FusedArgs> fused_for(int dti, int dto) {
+    if (dti == ZERO_F16 && dto == ZERO_F16) return fused_kernel<ZERO_F16, ZERO_F16, GW>;
+    if (dti == ZERO_F16 && dto == ZERO_BF16) return fused_kernel<ZERO_F16, ZERO_BF16, GW>;
+    if (dti == ZERO_BF16 && dto == ZERO_F16) return fused_kernel<ZERO_BF16, ZERO_F16, GW>;
+    return fused_kernel<ZERO_BF16, ZERO_BF16, GW>;
+}
+
+template <int DT>
+Kernel<AdamArgs> adam_for(int gw) {
+    switch (gw) {
+        case 8: return adam_kernel<DT, 8>;
+        case 4: return adam_kernel<DT, 4>;
+        case 2: return adam_kernel<DT, 2>;
+        case 1: return adam_kernel<DT, 1>;
+        default: return adam_kernel<DT, 0>;
+    }
+}
+
+template <int DT>
+Kernel<CastArgs> cast_for(int gw) {
+    switch (gw) {
+        case 8: return cast_kernel<DT, 8>;
+        case 4: return cast_kernel<DT, 4>;
+        case 2: return cast_kernel<DT, 2>;
+        default: return cast_kernel<DT, 1>;
+    }
+}
+
+// Launches a kernel whose only parameter is its argument struct (the type
+// check below keeps the two in step).
+template <class Args>
+int launch(Kernel<Args> kernel, int64_t grid, int block, hipStream_t s, const Args& args,
+           const char* what) {
+    if (grid < 1 || grid > 0x7FFFFFFF) return fail(ZERO_ERANGE, "%s: grid of %lld workgroups", what, (long long)grid);
     void* params[] = {const_cast<Args*>(&args)};
-    const hipError_t e = hipLaunchKernel(kernel, dim3(grid), dim3(kBlock), params, 0, s);
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)grid),
+                                         dim3(block), params, 0, s);
     if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
-    return launched(what);
+    const hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e2));
+    return ok();
 }
 
 }  // namespace
@@ -672,19 +755,20 @@ int zero_partition(int64_t psi, int32_t nranks, int32_t rank, int64_t* shard_len
 size_t zero_ctrl_bytes(void) { return sizeof(zero_ctrl); }
 
 size_t zero_workspace_bytes(int64_t valid_len) {
-    const int64_t p = parts_for(valid_len);
-    return (size_t)(p > 0 ? p : 1) * sizeof(Partial);
+    return (size_t)(tiles_for(valid_len) + kFinGroups) * sizeof(Partial);
+}
+
+size_t zero_pair_elems(int64_t valid_len) {
+    return (size_t)(2 * tiles_for(valid_len) * kTile);
 }
 
 int zero_ctrl_init(zero_ctrl* ctrl, float loss_scale, void* stream) {
-    if (ctrl == nullptr) return fail(ZERO_EINVAL, "zero_ctrl_init: null ctrl");
+    int rc;
+    if ((rc = check_ctrl(ctrl, "zero_ctrl_init")) != ZERO_OK) return rc;
     if (!(loss_scale > 0.0f) || loss_scale > 3.0e38f)
         return fail(ZERO_EINVAL, "zero_ctrl_init: loss scale must be finite and > 0");
-    if ((reinterpret_cast<uintptr_t>(ctrl) & 7u) != 0)
-        return fail(ZERO_EALIGN, "zero_ctrl_init: ctrl not 8-byte aligned");
-    hipLaunchKernelGGL(ctrl_init_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, ctrl,
-                       loss_scale);
-    return launched("zero_ctrl_init");
+    const InitArgs a{ctrl, loss_scale};
+    return launch<InitArgs>(ctrl_init_kernel, 1, 64, (hipStream_t)stream, a, "zero_ctrl_init");
 }
 
 int zero_reduce_grads(const void* contrib, int32_t dtype, int32_t nranks, int64_t stride,
@@ -692,13 +776,14 @@ int zero_reduce_grads(const void* contrib, int32_t dtype, int32_t nranks, int64_
                       size_t ws_bytes, void* stream) {
     int rc;
     if ((rc = check_contrib(contrib, dtype, nranks, stride, valid_len)) != ZERO_OK) return rc;
-    if (ctrl == nullptr || g == nullptr) return fail(ZERO_EINVAL, "zero_reduce_grads: null ctrl or g");
+    if ((rc = check_ctrl(ctrl, "zero_reduce_grads")) != ZERO_OK) return rc;
+    if (g == nullptr) return fail(ZERO_EINVAL, "zero_reduce_grads: null g");
     if (!aligned16(g)) return fail(ZERO_EALIGN, "zero_reduce_grads: g not 16-byte aligned");
     if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
     if (valid_len == 0) return ok();
     ReduceArgs a{(const uint16_t*)contrib, stride, valid_len, ctrl, g, (Partial*)ws, nranks};
-    void* k = dtype == ZERO_F16 ? (void*)reduce_kernel<ZERO_F16> : (void*)reduce_kernel<ZERO_BF16>;
-    return launch(k, (unsigned)parts_for(valid_len), (hipStream_t)stream, a, "zero_reduce_grads");
+    Kernel<ReduceArgs> k = dtype == ZERO_F16 ? reduce_kernel<ZERO_F16> : reduce_kernel<ZERO_BF16>;
+    return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, "zero_reduce_grads");
 }
 
 int zero_grad_norm_overflow(int32_t nranks, void* const* ws, const int64_t* valid_len,
@@ -712,31 +797,37 @@ int zero_grad_norm_overflow(int32_t nranks, void* const* ws, const int64_t* vali
         return fail(ZERO_EINVAL, "zero_grad_norm_overflow: null array");
     if ((rc = check_hp(hp)) != ZERO_OK) return rc;
     CombineArgs a{};
+    a.first[0] = 0;
     for (int r = 0; r < nranks; ++r) {
-        if (ctrl[r] == nullptr) return fail(ZERO_EINVAL, "zero_grad_norm_overflow: null ctrl[%d]", r);
-        if (valid_len[r] < 0 || valid_len[r] > kMaxLen)
-            return fail(ZERO_ERANGE, "zero_grad_norm_overflow: valid_len[%d] out of range", r);
-        const int64_t np = parts_for(valid_len[r]);
-        if (np > 0 && ws[r] == nullptr)
-            return fail(ZERO_EINVAL, "zero_grad_norm_overflow: null ws[%d]", r);
+        if ((rc = check_ctrl(ctrl[r], "zero_grad_norm_overflow")) != ZERO_OK) return rc;
+        if ((rc = check_len(valid_len[r], "zero_grad_norm_overflow")) != ZERO_OK) return rc;
+        if (ws[r] == nullptr || !aligned16(ws[r]))
+            return fail(ZERO_EINVAL, "zero_grad_norm_overflow: ws[%d] null or misaligned", r);
         a.ws[r] = (const Partial*)ws[r];
         a.ctrl[r] = ctrl[r];
-        a.nparts[r] = (int32_t)np;
+        a.first[r + 1] = a.first[r] + tiles_for(valid_len[r]);
     }
+    const int64_t total = a.first[nranks];
+    int64_t groups = (total + kFinPer - 1) / kFinPer;
+    groups = groups < 1 ? 1 : (groups > kFinGroups ? kFinGroups : groups);
+    a.per = groups == 1 ? (total > 0 ? total : 1) : (total + groups - 1) / groups;
+    a.level1 = (Partial*)ws[0] + tiles_for(valid_len[0]);
     a.nranks = nranks;
     a.pingpong = pingpong ? 1 : 0;
     a.hp = *hp;
-    return launch((void*)finalize_kernel, 1u, (hipStream_t)stream, a, "zero_grad_norm_overflow");
+    return launch<CombineArgs>(finalize_kernel, groups, kFinBlock, (hipStream_t)stream, a,
+                  "zero_grad_norm_overflow");
 }
 
 int zero_adam_step(const zero_state* state, const float* g, int64_t valid_len,
                    const zero_hparams* hp, const zero_ctrl* ctrl, void* gather,
                    int32_t gather_dtype, int64_t offset, void* stream) {
     int rc;
-    if (valid_len < 0 || valid_len > kMaxLen) return fail(ZERO_ERANGE, "zero_adam_step: valid_len out of range");
+    if ((rc = check_len(valid_len, "zero_adam_step")) != ZERO_OK) return rc;
     if ((rc = check_state(state, "zero_adam_step")) != ZERO_OK) return rc;
     if ((rc = check_hp(hp)) != ZERO_OK) return rc;
-    if (g == nullptr || ctrl == nullptr) return fail(ZERO_EINVAL, "zero_adam_step: null g or ctrl");
+    if ((rc = check_ctrl(ctrl, "zero_adam_step")) != ZERO_OK) return rc;
+    if (g == nullptr) return fail(ZERO_EINVAL, "zero_adam_step: null g");
     if (!aligned16(g)) return fail(ZERO_EALIGN, "zero_adam_step: g not 16-byte aligned");
     uint16_t* slot = nullptr;
     int gw = 0;
@@ -747,72 +838,89 @@ int zero_adam_step(const zero_state* state, const float* g, int64_t valid_len,
     }
     if (valid_len == 0) return ok();
     AdamArgs a{state->master, state->m, state->v, g, slot, valid_len, ctrl, *hp};
-    void* k = gather_dtype == ZERO_BF16 && gather != nullptr ? select_adam_gw<ZERO_BF16>(gw)
-                                                              : select_adam_gw<ZERO_F16>(gw);
-    return launch(k, (unsigned)parts_for(valid_len), (hipStream_t)stream, a, "zero_adam_step");
+    Kernel<AdamArgs> k = gather != nullptr && gather_dtype == ZERO_BF16 ? adam_for<ZERO_BF16>(gw)
+                                                              : adam_for<ZERO_F16>(gw);
+    return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, "zero_adam_step");
 }
 
 int zero_cast_to_gather(const float* master, int64_t valid_len, void* gather, int32_t dtype,
                         int64_t offset, void* stream) {
     int rc;
-    if (valid_len < 0 || valid_len > kMaxLen) return fail(ZERO_ERANGE, "zero_cast_to_gather: valid_len out of range");
+    if ((rc = check_len(valid_len, "zero_cast_to_gather")) != ZERO_OK) return rc;
     if (master == nullptr) return fail(ZERO_EINVAL, "zero_cast_to_gather: null master");
     if (!aligned16(master)) return fail(ZERO_EALIGN, "zero_cast_to_gather: master not 16-byte aligned");
     if ((rc = check_slot(gather, dtype, offset)) != ZERO_OK) return rc;
     if (valid_len == 0) return ok();
     uint16_t* slot = (uint16_t*)gather + offset;
-    CastArgs a{master, master, slot, valid_len, nullptr};
+    CastArgs a{master, slot, valid_len, nullptr};
     const int gw = store_width(slot);
-    void* k = dtype == ZERO_F16 ? select_cast_gw<false, ZERO_F16>(gw) : select_cast_gw<false, ZERO_BF16>(gw);
-    return launch(k, (unsigned)parts_for(valid_len), (hipStream_t)stream, a, "zero_cast_to_gather");
+    Kernel<CastArgs> k = dtype == ZERO_F16 ? cast_for<ZERO_F16>(gw) : cast_for<ZERO_BF16>(gw);
+    return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, "zero_cast_to_gather");
 }
 
 int zero_fused_step(const void* contrib, int32_t contrib_dtype, int32_t nranks, int64_t stride,
-                    const zero_state* state0, const zero_state* state1, int64_t valid_len,
-                    void* gather, int32_t gather_dtype, int64_t offset, const zero_hparams* hp,
-                    const zero_ctrl* ctrl, void* ws, size_t ws_bytes, void* stream) {
+                    const zero_state* pair, int64_t valid_len, void* gather, int32_t gather_dtype,
+                    int64_t offset, const zero_hparams* hp, const zero_ctrl* ctrl, void* ws,
+                    size_t ws_bytes, void* stream) {
     int rc;
     if ((rc = check_contrib(contrib, contrib_dtype, nranks, stride, valid_len)) != ZERO_OK) return rc;
-    if ((rc = check_state(state0, "zero_fused_step state0")) != ZERO_OK) return rc;
-    if ((rc = check_state(state1, "zero_fused_step state1")) != ZERO_OK) return rc;
-    if (state0->master == state1->master || state0->m == state1->m || state0->v == state1->v)
-        return fail(ZERO_EINVAL, "zero_fused_step: the two state sets must be distinct buffers");
+    if ((rc = check_state(pair, "zero_fused_step")) != ZERO_OK) return rc;
     if ((rc = check_hp(hp)) != ZERO_OK) return rc;
     if (hp->max_grad_norm > 0.0f)
         return fail(ZERO_EINVAL, "zero_fused_step: clipping needs the two-pass path");
-    if (ctrl == nullptr) return fail(ZERO_EINVAL, "zero_fused_step: null ctrl");
+    if ((rc = check_ctrl(ctrl, "zero_fused_step")) != ZERO_OK) return rc;
     if ((rc = check_slot(gather, gather_dtype, offset)) != ZERO_OK) return rc;
     if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
     if (valid_len == 0) return ok();
     uint16_t* slot = (uint16_t*)gather + offset;
-    FusedArgs a{(const uint16_t*)contrib, stride,
-                {state0->master, state0->m, state0->v}, {state1->master, state1->m, state1->v},
-                slot, valid_len, ctrl, (Partial*)ws, *hp, nranks};
-    void* k;
+    FusedArgs a{(const uint16_t*)contrib, stride, {pair->master, pair->m, pair->v}, slot,
+                valid_len, ctrl, (Partial*)ws, *hp, nranks};
+    Kernel<FusedArgs> k;
     switch (store_width(slot)) {
-        case 8: k = select_fused_gw<8>(contrib_dtype, gather_dtype); break;
-        case 4: k = select_fused_gw<4>(contrib_dtype, gather_dtype); break;
-        case 2: k = select_fused_gw<2>(contrib_dtype, gather_dtype); break;
-        default: k = select_fused_gw<1>(contrib_dtype, gather_dtype); break;
+        case 8: k = fused_for<8>(contrib_dtype, gather_dtype); break;
+        case 4: k = fused_for<4>(contrib_dtype, gather_dtype); break;
+        case 2: k = fused_for<2>(contrib_dtype, gather_dtype); break;
+        default: k = fused_for<1>(contrib_dtype, gather_dtype); break;
     }
-    return launch(k, (unsigned)parts_for(valid_len), (hipStream_t)stream, a, "zero_fused_step");
+    return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, "zero_fused_step");
 }
 
-int zero_fused_restore(const zero_state* state0, const zero_state* state1, int64_t valid_len,
-                       void* gather, int32_t dtype, int64_t offset, const zero_ctrl* ctrl,
-                       void* stream) {
+int zero_fused_restore(const zero_state* pair, int64_t valid_len, void* gather, int32_t dtype,
+                       int64_t offset, const zero_ctrl* ctrl, void* stream) {
     int rc;
-    if (valid_len < 0 || valid_len > kMaxLen) return fail(ZERO_ERANGE, "zero_fused_restore: valid_len out of range");
-    if ((rc = check_state(state0, "zero_fused_restore state0")) != ZERO_OK) return rc;
-    if ((rc = check_state(state1, "zero_fused_restore state1")) != ZERO_OK) return rc;
-    if (ctrl == nullptr) return fail(ZERO_EINVAL, "zero_fused_restore: null ctrl");
+    if ((rc = check_len(valid_len, "zero_fused_restore")) != ZERO_OK) return rc;
+    if ((rc = check_state(pair, "zero_fused_restore")) != ZERO_OK) return rc;
+    if ((rc = check_ctrl(ctrl, "zero_fused_restore")) != ZERO_OK) return rc;
     if ((rc = check_slot(gather, dtype, offset)) != ZERO_OK) return rc;
     if (valid_len == 0) return ok();
-    uint16_t* slot = (uint16_t*)gather + offset;
-    CastArgs a{state0->master, state1->master, slot, valid_len, ctrl};
-    const int gw = store_width(slot);
-    void* k = dtype == ZERO_F16 ? select_cast_gw<true, ZERO_F16>(gw) : select_cast_gw<true, ZERO_BF16>(gw);
-    return launch(k, (unsigned)parts_for(valid_len), (hipStream_t)stream, a, "zero_fused_restore");
+    CastArgs a{pair->master, (uint16_t*)gather + offset, valid_len, ctrl};
+    const int64_t nt = tiles_for(valid_len);
+    Kernel<CastArgs> k = dtype == ZERO_F16 ? restore_kernel<ZERO_F16> : restore_kernel<ZERO_BF16>;
+    return launch(k, nt < kRestoreGrid ? nt : kRestoreGrid, kBlock, (hipStream_t)stream, a,
+                  "zero_fused_restore");
+}
+
+static int pair_copy(const zero_state* flat, const zero_state* pair, int64_t valid_len,
+                     const zero_ctrl* ctrl, void* stream, bool to_pair, const char* what) {
+    int rc;
+    if ((rc = check_len(valid_len, what)) != ZERO_OK) return rc;
+    if ((rc = check_state(flat, what)) != ZERO_OK) return rc;
+    if ((rc = check_state(pair, what)) != ZERO_OK) return rc;
+    if ((rc = check_ctrl(ctrl, what)) != ZERO_OK) return rc;
+    if (valid_len == 0) return ok();
+    PackArgs a{{flat->master, flat->m, flat->v}, {pair->master, pair->m, pair->v}, valid_len, ctrl};
+    Kernel<PackArgs> k = to_pair ? pack_kernel<true> : pack_kernel<false>;
+    return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, what);
+}
+
+int zero_pair_store(const zero_state* flat, const zero_state* pair, int64_t valid_len,
+                    const zero_ctrl* ctrl, void* stream) {
+    return pair_copy(flat, pair, valid_len, ctrl, stream, true, "zero_pair_store");
+}
+
+int zero_pair_load(const zero_state* pair, const zero_state* flat, int64_t valid_len,
+                   const zero_ctrl* ctrl, void* stream) {
+    return pair_copy(flat, pair, valid_len, ctrl, stream, false, "zero_pair_load");
 }
 
 const char* zero_last_error(void) { return g_err; }
