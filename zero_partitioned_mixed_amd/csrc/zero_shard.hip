@@ -109,22 +109,60 @@ __device__ __forceinline__ void add8(float acc[kVec], u32x4 w) {
     }
 }
 
-// acc[j] = sum over rows k = 0..n-1, in that order, of element j of the
-// 8-element group at p + k*stride.  Loads are issued eight rows at a time.
+// Loads rows k0 .. k0+7 of the 8-element group at p (row k at p + k*stride).
+__device__ __forceinline__ void load_rows8(const uint16_t* __restrict__ p, int64_t stride, int k0,
+                                           u32x4 w[8]) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        w[r] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(p + (int64_t)(k0 + r) * stride));
+}
+
 template <int DT>
-__device__ __forceinline__ void sum_rows(const uint16_t* __restrict__ p, int n, int64_t stride,
-                                         float acc[kVec]) {
+__device__ __forceinline__ void add_rows8(float acc[kVec], const u32x4 w[8]) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) add8<DT>(acc, w[r]);
+}
+
+// Row sums of the 8-element group at p over rows k = 0..n-1, added in that
+// order, in two phases so that callers can issue all of an element group's
+// loads before its first use.  sum_rows_issue loads the first eight rows
+// (n >= 8); sum_rows_finish adds them and streams the remaining rows, with
+// the loads of the next eight rows in flight while the current eight are
+// added.
+// NR = 8 compiles the common case of exactly eight rows without the
+// streaming loop (and its second set of load registers); NR = 0 takes any n.
+struct RowLoads {
+    u32x4 w[8];
+};
+
+template <int NR>
+__device__ __forceinline__ void sum_rows_issue(const uint16_t* __restrict__ p, int n,
+                                               int64_t stride, RowLoads& L) {
+    if (NR == 8 || n >= 8) load_rows8(p, stride, 0, L.w);
+}
+
+template <int DT, int NR>
+__device__ __forceinline__ void sum_rows_finish(const uint16_t* __restrict__ p, int n,
+                                                int64_t stride, RowLoads& L, float acc[kVec]) {
 #pragma unroll
     for (int j = 0; j < kVec; ++j) acc[j] = 0.0f;
+    if constexpr (NR == 8) {
+        add_rows8<DT>(acc, L.w);
+        return;
+    }
     int k = 0;
-    for (; k + 8 <= n; k += 8) {
-        u32x4 w[8];
+    if (n >= 8) {
+        for (; k + 16 <= n; k += 8) {
+            u32x4 nxt[8];
+            load_rows8(p, stride, k + 8, nxt);
+            __builtin_amdgcn_sched_barrier(0);
+            add_rows8<DT>(acc, L.w);
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            w[r] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4*>(p + (int64_t)(k + r) * stride));
-#pragma unroll
-        for (int r = 0; r < 8; ++r) add8<DT>(acc, w[r]);
+            for (int r = 0; r < 8; ++r) L.w[r] = nxt[r];
+        }
+        add_rows8<DT>(acc, L.w);
+        k += 8;
     }
     for (; k < n; ++k)
         add8<DT>(acc, __builtin_nontemporal_load(
@@ -294,7 +332,7 @@ struct ReduceArgs {
 
 // Pass 1 of the two-pass step: g = fl32(sum_k C[k]) * inv, plus one partial
 // per tile.
-template <int DT>
+template <int DT, int NR>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
     const float inv = (float)(1.0 / ((double)a.n * (double)a.ctrl->loss_scale));
     double ss = 0.0;
@@ -302,7 +340,10 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
     const int64_t e = (int64_t)blockIdx.x * kTile + threadIdx.x * kVec;
     if (e + kVec <= a.len) {
         float acc[kVec], out[kVec];
-        sum_rows<DT>(a.contrib + e, a.n, a.stride, acc);
+        RowLoads L;
+        sum_rows_issue<NR>(a.contrib + e, a.n, a.stride, L);
+        __builtin_amdgcn_sched_barrier(0);
+        sum_rows_finish<DT, NR>(a.contrib + e, a.n, a.stride, L, acc);
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             bad |= __builtin_isfinite(acc[j]) ? 0u : 1u;
@@ -436,6 +477,7 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(AdamArgs a) {
         load8(a.master + e, p);
         load8(a.m + e, m);
         load8(a.v + e, v);
+        __builtin_amdgcn_sched_barrier(0);  // every load of the group is in flight first
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             adam_elem(k, g[j] * clip, p[j], m[j], v[j]);
@@ -535,7 +577,7 @@ struct FusedArgs {
 
 // Single pass: reduce + partial + Adam (read set cur, write set 1-cur of the
 // tile) + cast, one tile per workgroup.
-template <int DTI, int DTO, int GW>
+template <int DTI, int DTO, int GW, int NR>
 __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
     const zero_ctrl* __restrict__ c = a.ctrl;
     const int cur = c->cur;
@@ -551,10 +593,13 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
     if (e + kVec <= a.len) {
         float acc[kVec], p[kVec], m[kVec], v[kVec];
         uint32_t h[kVec];
-        sum_rows<DTI>(a.contrib + e, a.n, a.stride, acc);
+        RowLoads L;
+        sum_rows_issue<NR>(a.contrib + e, a.n, a.stride, L);
         load8(a.pair[0] + so, p);
         load8(a.pair[1] + so, m);
         load8(a.pair[2] + so, v);
+        __builtin_amdgcn_sched_barrier(0);  // every load of the group is in flight first
+        sum_rows_finish<DTI, NR>(a.contrib + e, a.n, a.stride, L, acc);
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             bad |= __builtin_isfinite(acc[j]) ? 0u : 1u;
@@ -687,12 +732,17 @@ int check_ctrl(const zero_ctrl* c, const char* what) {
 template <class Args>
 using Kernel = void (*)(Args);
 
+template <int GW, int NR>
+Kernel<FusedArgs> fused_for_nr(int dti, int dto) {
+    if (dti == ZERO_F16 && dto == ZERO_F16) return fused_kernel<ZERO_F16, ZERO_F16, GW, NR>;
+    if (dti == ZERO_F16 && dto == ZERO_BF16) return fused_kernel<ZERO_F16, ZERO_BF16, GW, NR>;
+    if (dti == ZERO_BF16 && dto == ZERO_F16) return fused_kernel<ZERO_BF16, ZERO_F16, GW, NR>;
+    return fused_kernel<ZERO_BF16, ZERO_BF16, GW, NR>;
+}
+
 template <int GW>
-Kernel<FusedArgs> fused_for(int dti, int dto) {
-    if (dti == ZERO_F16 && dto == ZERO_F16) return fused_kernel<ZERO_F16, ZERO_F16, GW>;
-    if (dti == ZERO_F16 && dto == ZERO_BF16) return fused_kernel<ZERO_F16, ZERO_BF16, GW>;
-    if (dti == ZERO_BF16 && dto == ZERO_F16) return fused_kernel<ZERO_BF16, ZERO_F16, GW>;
-    return fused_kernel<ZERO_BF16, ZERO_BF16, GW>;
+Kernel<FusedArgs> fused_for(int dti, int dto, int n) {
+    return n == 8 ? fused_for_nr<GW, 8>(dti, dto) : fused_for_nr<GW, 0>(dti, dto);
 }
 
 template <int DT>
@@ -782,7 +832,11 @@ int zero_reduce_grads(const void* contrib, int32_t dtype, int32_t nranks, int64_
     if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
     if (valid_len == 0) return ok();
     ReduceArgs a{(const uint16_t*)contrib, stride, valid_len, ctrl, g, (Partial*)ws, nranks};
-    Kernel<ReduceArgs> k = dtype == ZERO_F16 ? reduce_kernel<ZERO_F16> : reduce_kernel<ZERO_BF16>;
+    Kernel<ReduceArgs> k;
+    if (nranks == 8)
+        k = dtype == ZERO_F16 ? reduce_kernel<ZERO_F16, 8> : reduce_kernel<ZERO_BF16, 8>;
+    else
+        k = dtype == ZERO_F16 ? reduce_kernel<ZERO_F16, 0> : reduce_kernel<ZERO_BF16, 0>;
     return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, "zero_reduce_grads");
 }
 
@@ -877,10 +931,10 @@ int zero_fused_step(const void* contrib, int32_t contrib_dtype, int32_t nranks, 
                 valid_len, ctrl, (Partial*)ws, *hp, nranks};
     Kernel<FusedArgs> k;
     switch (store_width(slot)) {
-        case 8: k = fused_for<8>(contrib_dtype, gather_dtype); break;
-        case 4: k = fused_for<4>(contrib_dtype, gather_dtype); break;
-        case 2: k = fused_for<2>(contrib_dtype, gather_dtype); break;
-        default: k = fused_for<1>(contrib_dtype, gather_dtype); break;
+        case 8: k = fused_for<8>(contrib_dtype, gather_dtype, nranks); break;
+        case 4: k = fused_for<4>(contrib_dtype, gather_dtype, nranks); break;
+        case 2: k = fused_for<2>(contrib_dtype, gather_dtype, nranks); break;
+        default: k = fused_for<1>(contrib_dtype, gather_dtype, nranks); break;
     }
     return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, "zero_fused_step");
 }
