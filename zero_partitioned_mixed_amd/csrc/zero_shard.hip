@@ -36,7 +36,7 @@
 namespace {
 
 constexpr int kBlock = 256;                 // threads per streaming workgroup: 4 wave64s
-constexpr int kVec = 8;                     // elements per thread
+constexpr int kVec = 8;                     // elements per thread (two runs of four)
 constexpr int64_t kTile = ZERO_TILE;        // elements per workgroup
 static_assert(kTile == (int64_t)kBlock * kVec, "tile = threads x elements per thread");
 constexpr int kFinBlock = 1024;             // threads per finalize workgroup
@@ -58,6 +58,35 @@ static_assert(sizeof(Partial) == 16, "partial layout");
 static_assert(sizeof(zero_ctrl) == 128, "ctrl layout");
 
 int64_t tiles_for(int64_t len) { return len <= 0 ? 0 : (len + kTile - 1) / kTile; }
+
+// ---------------------------------------------------------------- element mapping
+// A tile of 2048 elements belongs to one workgroup of 4 waves; wave w covers
+// elements [512w, 512w + 512) of the tile.  Lane l owns two runs of four:
+// [512w + 4l, +4) ("run a") and the same 256 elements later ("run b").  Each
+// memory instruction of a wave therefore covers one contiguous span (1 KiB
+// of fp32, 512 B of 16-bit data), and every cache line is filled by a single
+// instruction: no line is ever written back half-filled.
+constexpr int kRun = 4;
+
+struct Runs {
+    int64_t a, b;  // first element of run a and of run b
+};
+
+__device__ __forceinline__ Runs runs_of(int64_t tile) {
+    const int64_t a = tile * kTile + (threadIdx.x >> 6) * 512 + (threadIdx.x & 63) * kRun;
+    return Runs{a, a + 256};
+}
+
+// Index of shard element i of set s in a paired state array (ZERO_TILE interleave).
+__device__ __forceinline__ int64_t pair_index(int64_t i, int s) {
+    const int64_t tile = i / kTile;
+    return tile * 2 * kTile + (int64_t)s * kTile + (i - tile * kTile);
+}
+
+// Element j (0..7) of the thread's group: run a for j < 4, run b otherwise.
+__device__ __forceinline__ int64_t elem(const Runs& r, int j) {
+    return j < kRun ? r.a + j : r.b + (j - kRun);
+}
 
 // ---------------------------------------------------------------- conversions
 template <int DT>
@@ -99,52 +128,64 @@ __device__ __forceinline__ uint32_t narrow<ZERO_BF16>(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-// Adds contribution word vector w (8 sixteen-bit values) into acc[0..7].
-template <int DT>
-__device__ __forceinline__ void add8(float acc[kVec], u32x4 w) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        acc[2 * j] = acc[2 * j] + widen_lo<DT>(w[j]);
-        acc[2 * j + 1] = acc[2 * j + 1] + widen_hi<DT>(w[j]);
-    }
-}
+// ---------------------------------------------------------------- contribution rows
+// One row's 8 values of the thread's group: 4 at run a, 4 at run b.
+struct Row {
+    u32x2 a, b;
+};
 
-// Loads rows k0 .. k0+7 of the 8-element group at p (row k at p + k*stride).
-__device__ __forceinline__ void load_rows8(const uint16_t* __restrict__ p, int64_t stride, int k0,
-                                           u32x4 w[8]) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-        w[r] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(p + (int64_t)(k0 + r) * stride));
+__device__ __forceinline__ Row load_row(const uint16_t* __restrict__ base, const Runs& r) {
+    Row w;
+    w.a = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + r.a));
+    w.b = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + r.b));
+    return w;
 }
 
 template <int DT>
-__device__ __forceinline__ void add_rows8(float acc[kVec], const u32x4 w[8]) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) add8<DT>(acc, w[r]);
+__device__ __forceinline__ void add_row(float acc[kVec], const Row& w) {
+    acc[0] = acc[0] + widen_lo<DT>(w.a.x);
+    acc[1] = acc[1] + widen_hi<DT>(w.a.x);
+    acc[2] = acc[2] + widen_lo<DT>(w.a.y);
+    acc[3] = acc[3] + widen_hi<DT>(w.a.y);
+    acc[4] = acc[4] + widen_lo<DT>(w.b.x);
+    acc[5] = acc[5] + widen_hi<DT>(w.b.x);
+    acc[6] = acc[6] + widen_lo<DT>(w.b.y);
+    acc[7] = acc[7] + widen_hi<DT>(w.b.y);
 }
 
-// Row sums of the 8-element group at p over rows k = 0..n-1, added in that
+__device__ __forceinline__ void load_rows8(const uint16_t* __restrict__ C, int64_t stride, int k0,
+                                           const Runs& r, Row w[8]) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q] = load_row(C + (int64_t)(k0 + q) * stride, r);
+}
+
+template <int DT>
+__device__ __forceinline__ void add_rows8(float acc[kVec], const Row w[8]) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) add_row<DT>(acc, w[q]);
+}
+
+// Row sums of the thread's 8 elements over rows k = 0..n-1, added in that
 // order, in two phases so that callers can issue all of an element group's
 // loads before its first use.  sum_rows_issue loads the first eight rows
-// (n >= 8); sum_rows_finish adds them and streams the remaining rows, with
-// the loads of the next eight rows in flight while the current eight are
-// added.
+// (n >= 8); sum_rows_finish adds them and streams the remaining rows with
+// the next eight rows' loads in flight while the current eight are added.
 // NR = 8 compiles the common case of exactly eight rows without the
 // streaming loop (and its second set of load registers); NR = 0 takes any n.
 struct RowLoads {
-    u32x4 w[8];
+    Row w[8];
 };
 
 template <int NR>
-__device__ __forceinline__ void sum_rows_issue(const uint16_t* __restrict__ p, int n,
-                                               int64_t stride, RowLoads& L) {
-    if (NR == 8 || n >= 8) load_rows8(p, stride, 0, L.w);
+__device__ __forceinline__ void sum_rows_issue(const uint16_t* __restrict__ C, int n,
+                                               int64_t stride, const Runs& r, RowLoads& L) {
+    if (NR == 8 || n >= 8) load_rows8(C, stride, 0, r, L.w);
 }
 
 template <int DT, int NR>
-__device__ __forceinline__ void sum_rows_finish(const uint16_t* __restrict__ p, int n,
-                                                int64_t stride, RowLoads& L, float acc[kVec]) {
+__device__ __forceinline__ void sum_rows_finish(const uint16_t* __restrict__ C, int n,
+                                                int64_t stride, const Runs& r, RowLoads& L,
+                                                float acc[kVec]) {
 #pragma unroll
     for (int j = 0; j < kVec; ++j) acc[j] = 0.0f;
     if constexpr (NR == 8) {
@@ -154,21 +195,20 @@ __device__ __forceinline__ void sum_rows_finish(const uint16_t* __restrict__ p, 
     int k = 0;
     if (n >= 8) {
         for (; k + 16 <= n; k += 8) {
-            u32x4 nxt[8];
-            load_rows8(p, stride, k + 8, nxt);
+            Row nxt[8];
+            load_rows8(C, stride, k + 8, r, nxt);
             __builtin_amdgcn_sched_barrier(0);
             add_rows8<DT>(acc, L.w);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) L.w[r] = nxt[r];
+            for (int q = 0; q < 8; ++q) L.w[q] = nxt[q];
         }
         add_rows8<DT>(acc, L.w);
         k += 8;
     }
-    for (; k < n; ++k)
-        add8<DT>(acc, __builtin_nontemporal_load(
-                          reinterpret_cast<const u32x4*>(p + (int64_t)k * stride)));
+    for (; k < n; ++k) add_row<DT>(acc, load_row(C + (int64_t)k * stride, r));
 }
 
+// Scalar row sum of one element (partial tiles).
 template <int DT>
 __device__ __forceinline__ float sum_rows1(const uint16_t* __restrict__ p, int n, int64_t stride) {
     float acc = 0.0f;
@@ -208,54 +248,47 @@ __device__ __forceinline__ void adam_elem(const AdamK& k, float g, float& p, flo
 }
 
 // ---------------------------------------------------------------- vector I/O
-__device__ __forceinline__ void load8(const float* __restrict__ p, float x[kVec]) {
-    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+// fp32 values of the thread's group: x[0..3] at pa, x[4..7] at pb.
+__device__ __forceinline__ void load8(const float* __restrict__ pa, const float* __restrict__ pb,
+                                      float x[kVec]) {
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(pa));
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(pb));
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
-__device__ __forceinline__ void store8(float* __restrict__ p, const float x[kVec]) {
+__device__ __forceinline__ void store8(float* __restrict__ pa, float* __restrict__ pb,
+                                       const float x[kVec]) {
     f32x4 a, b;
     a.x = x[0]; a.y = x[1]; a.z = x[2]; a.w = x[3];
     b.x = x[4]; b.y = x[5]; b.z = x[6]; b.w = x[7];
-    __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(p));
-    __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(p + 4));
+    __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(pa));
+    __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(pb));
 }
 
-// Stores 8 sixteen-bit values h[0..7] at dst with accesses of GW elements
-// (GW = 8, 4, 2, 1 for 16-, 8-, 4-, 2-byte aligned dst).
+// Stores 4 sixteen-bit values at dst with accesses of GW elements (GW = 4,
+// 2, 1 for an 8-, 4-, 2-byte aligned dst).
 template <int GW>
-__device__ __forceinline__ void store_h8(uint16_t* __restrict__ dst, const uint32_t h[kVec]) {
-    if constexpr (GW == 8) {
-        u32x4 w;
+__device__ __forceinline__ void store_h4(uint16_t* __restrict__ dst, const uint32_t* h) {
+    if constexpr (GW == 4) {
+        u32x2 w;
         w.x = h[0] | (h[1] << 16);
         w.y = h[2] | (h[3] << 16);
-        w.z = h[4] | (h[5] << 16);
-        w.w = h[6] | (h[7] << 16);
-        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst));
-    } else if constexpr (GW == 4) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            u32x2 w;
-            w.x = h[4 * q] | (h[4 * q + 1] << 16);
-            w.y = h[4 * q + 2] | (h[4 * q + 3] << 16);
-            __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(dst + 4 * q));
-        }
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(dst));
     } else if constexpr (GW == 2) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            __builtin_nontemporal_store(h[2 * q] | (h[2 * q + 1] << 16),
-                                        reinterpret_cast<uint32_t*>(dst + 2 * q));
+        __builtin_nontemporal_store(h[0] | (h[1] << 16), reinterpret_cast<uint32_t*>(dst));
+        __builtin_nontemporal_store(h[2] | (h[3] << 16), reinterpret_cast<uint32_t*>(dst + 2));
     } else {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) __builtin_nontemporal_store((uint16_t)h[q], dst + q);
+        for (int q = 0; q < 4; ++q) __builtin_nontemporal_store((uint16_t)h[q], dst + q);
     }
 }
 
-// Offset of this thread's 8 elements of set `s` in a paired state array.
-__device__ __forceinline__ int64_t pair_off(int64_t tile, int s) {
-    return tile * 2 * kTile + (int64_t)s * kTile + threadIdx.x * kVec;
+template <int GW>
+__device__ __forceinline__ void store_slot(uint16_t* __restrict__ slot, const Runs& r,
+                                           const uint32_t h[kVec]) {
+    store_h4<GW>(slot + r.a, h);
+    store_h4<GW>(slot + r.b, h + kRun);
 }
 
 // ---------------------------------------------------------------- norm partials
@@ -337,13 +370,13 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
     const float inv = (float)(1.0 / ((double)a.n * (double)a.ctrl->loss_scale));
     double ss = 0.0;
     uint32_t bad = 0;
-    const int64_t e = (int64_t)blockIdx.x * kTile + threadIdx.x * kVec;
-    if (e + kVec <= a.len) {
+    const Runs r = runs_of(blockIdx.x);
+    if (r.b + kRun <= a.len) {
         float acc[kVec], out[kVec];
         RowLoads L;
-        sum_rows_issue<NR>(a.contrib + e, a.n, a.stride, L);
+        sum_rows_issue<NR>(a.contrib, a.n, a.stride, r, L);
         __builtin_amdgcn_sched_barrier(0);
-        sum_rows_finish<DT, NR>(a.contrib + e, a.n, a.stride, L, acc);
+        sum_rows_finish<DT, NR>(a.contrib, a.n, a.stride, r, L, acc);
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             bad |= __builtin_isfinite(acc[j]) ? 0u : 1u;
@@ -351,9 +384,11 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
             ss += (double)gj * (double)gj;
             out[j] = gj;
         }
-        store8(a.g + e, out);
+        store8(a.g + r.a, a.g + r.b, out);
     } else {
-        for (int64_t i = e; i < a.len; ++i) {
+        for (int j = 0; j < kVec; ++j) {
+            const int64_t i = elem(r, j);
+            if (i >= a.len) continue;
             const float acc = sum_rows1<DT>(a.contrib + i, a.n, a.stride);
             bad |= __builtin_isfinite(acc) ? 0u : 1u;
             const float gj = acc * inv;
@@ -469,26 +504,28 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(AdamArgs a) {
     if (c->skip) return;
     const float clip = c->clip;
     const AdamK k = make_adam(a.hp, c->beta1_pow, c->beta2_pow);
-    const int64_t e = (int64_t)blockIdx.x * kTile + threadIdx.x * kVec;
-    if (e + kVec <= a.len) {
+    const Runs r = runs_of(blockIdx.x);
+    if (r.b + kRun <= a.len) {
         float g[kVec], p[kVec], m[kVec], v[kVec];
         uint32_t h[kVec];
-        load8(a.g + e, g);
-        load8(a.master + e, p);
-        load8(a.m + e, m);
-        load8(a.v + e, v);
+        load8(a.g + r.a, a.g + r.b, g);
+        load8(a.master + r.a, a.master + r.b, p);
+        load8(a.m + r.a, a.m + r.b, m);
+        load8(a.v + r.a, a.v + r.b, v);
         __builtin_amdgcn_sched_barrier(0);  // every load of the group is in flight first
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             adam_elem(k, g[j] * clip, p[j], m[j], v[j]);
             h[j] = narrow<DT>(p[j]);
         }
-        store8(a.master + e, p);
-        store8(a.m + e, m);
-        store8(a.v + e, v);
-        if constexpr (GW > 0) store_h8<GW>(a.slot + e, h);
+        store8(a.master + r.a, a.master + r.b, p);
+        store8(a.m + r.a, a.m + r.b, m);
+        store8(a.v + r.a, a.v + r.b, v);
+        if constexpr (GW > 0) store_slot<GW>(a.slot, r, h);
     } else {
-        for (int64_t i = e; i < a.len; ++i) {
+        for (int j = 0; j < kVec; ++j) {
+            const int64_t i = elem(r, j);
+            if (i >= a.len) continue;
             float p = a.master[i], m = a.m[i], v = a.v[i];
             adam_elem(k, a.g[i] * clip, p, m, v);
             a.master[i] = p;
@@ -500,25 +537,28 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(AdamArgs a) {
 }
 
 struct CastArgs {
-    const float* master;  // flat master, or the paired master (RESTORE)
+    const float* master;  // flat master, or the paired master (restore)
     uint16_t* slot;
     int64_t len;
-    const zero_ctrl* ctrl;  // RESTORE only
+    const zero_ctrl* ctrl;  // restore only
 };
 
 // gather slot <- RNE(master), one tile per workgroup.
 template <int DT, int GW>
 __global__ void __launch_bounds__(kBlock) cast_kernel(CastArgs a) {
-    const int64_t e = (int64_t)blockIdx.x * kTile + threadIdx.x * kVec;
-    if (e + kVec <= a.len) {
+    const Runs r = runs_of(blockIdx.x);
+    if (r.b + kRun <= a.len) {
         float p[kVec];
         uint32_t h[kVec];
-        load8(a.master + e, p);
+        load8(a.master + r.a, a.master + r.b, p);
 #pragma unroll
         for (int j = 0; j < kVec; ++j) h[j] = narrow<DT>(p[j]);
-        store_h8<GW>(a.slot + e, h);
+        store_slot<GW>(a.slot, r, h);
     } else {
-        for (int64_t i = e; i < a.len; ++i) a.slot[i] = (uint16_t)narrow<DT>(a.master[i]);
+        for (int j = 0; j < kVec; ++j) {
+            const int64_t i = elem(r, j);
+            if (i < a.len) a.slot[i] = (uint16_t)narrow<DT>(a.master[i]);
+        }
     }
 }
 
@@ -531,10 +571,11 @@ __global__ void __launch_bounds__(kBlock) restore_kernel(CastArgs a) {
     const int cur = a.ctrl->cur;
     const int64_t ntile = (a.len + kTile - 1) / kTile;
     for (int64_t tile = blockIdx.x; tile < ntile; tile += gridDim.x) {
-        const int64_t e = tile * kTile + threadIdx.x * kVec;
-        const float* src = a.master + pair_off(tile, cur);
-        for (int j = 0; j < kVec && e + j < a.len; ++j)
-            a.slot[e + j] = (uint16_t)narrow<DT>(src[j]);
+        const Runs r = runs_of(tile);
+        for (int j = 0; j < kVec; ++j) {
+            const int64_t i = elem(r, j);
+            if (i < a.len) a.slot[i] = (uint16_t)narrow<DT>(a.master[pair_index(i, cur)]);
+        }
     }
 }
 
@@ -549,16 +590,16 @@ struct PackArgs {
 template <bool TO_PAIR>
 __global__ void __launch_bounds__(kBlock) pack_kernel(PackArgs a) {
     const int cur = a.ctrl->cur;
-    const int64_t tile = blockIdx.x;
-    const int64_t e = tile * kTile + threadIdx.x * kVec;
-    const int64_t po = pair_off(tile, cur);
+    const Runs r = runs_of(blockIdx.x);
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
-        for (int j = 0; j < kVec && e + j < a.len; ++j) {
+        for (int j = 0; j < kVec; ++j) {
+            const int64_t i = elem(r, j);
+            if (i >= a.len) continue;
             if (TO_PAIR)
-                a.pair[q][po + j] = a.flat[q][e + j];
+                a.pair[q][pair_index(i, cur)] = a.flat[q][i];
             else
-                a.flat[q][e + j] = a.pair[q][po + j];
+                a.flat[q][i] = a.pair[q][pair_index(i, cur)];
         }
     }
 }
@@ -584,22 +625,23 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
     const float inv = (float)(1.0 / ((double)a.n * (double)c->loss_scale));
     const AdamK k = make_adam(a.hp, c->beta1_pow * (double)a.hp.beta1,
                               c->beta2_pow * (double)a.hp.beta2);
-    const int64_t tile = blockIdx.x;
-    const int64_t e = tile * kTile + threadIdx.x * kVec;
-    const int64_t so = pair_off(tile, cur);
-    const int64_t dof = pair_off(tile, cur ^ 1);
+    const Runs r = runs_of(blockIdx.x);
     double ss = 0.0;
     uint32_t bad = 0;
-    if (e + kVec <= a.len) {
+    if (r.b + kRun <= a.len) {
+        // run a and run b of one tile sit at the same distance from their
+        // set's start in the paired layout
+        const int64_t sa = pair_index(r.a, cur), sb = sa + 256;
+        const int64_t da = pair_index(r.a, cur ^ 1), db = da + 256;
         float acc[kVec], p[kVec], m[kVec], v[kVec];
         uint32_t h[kVec];
         RowLoads L;
-        sum_rows_issue<NR>(a.contrib + e, a.n, a.stride, L);
-        load8(a.pair[0] + so, p);
-        load8(a.pair[1] + so, m);
-        load8(a.pair[2] + so, v);
+        sum_rows_issue<NR>(a.contrib, a.n, a.stride, r, L);
+        load8(a.pair[0] + sa, a.pair[0] + sb, p);
+        load8(a.pair[1] + sa, a.pair[1] + sb, m);
+        load8(a.pair[2] + sa, a.pair[2] + sb, v);
         __builtin_amdgcn_sched_barrier(0);  // every load of the group is in flight first
-        sum_rows_finish<DTI, NR>(a.contrib + e, a.n, a.stride, L, acc);
+        sum_rows_finish<DTI, NR>(a.contrib, a.n, a.stride, r, L, acc);
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             bad |= __builtin_isfinite(acc[j]) ? 0u : 1u;
@@ -608,22 +650,25 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
             adam_elem(k, gj, p[j], m[j], v[j]);
             h[j] = narrow<DTO>(p[j]);
         }
-        store8(a.pair[0] + dof, p);
-        store8(a.pair[1] + dof, m);
-        store8(a.pair[2] + dof, v);
-        store_h8<GW>(a.slot + e, h);
+        store8(a.pair[0] + da, a.pair[0] + db, p);
+        store8(a.pair[1] + da, a.pair[1] + db, m);
+        store8(a.pair[2] + da, a.pair[2] + db, v);
+        store_slot<GW>(a.slot, r, h);
     } else {
-        for (int j = 0; e + j < a.len; ++j) {
-            const float acc = sum_rows1<DTI>(a.contrib + e + j, a.n, a.stride);
+        for (int j = 0; j < kVec; ++j) {
+            const int64_t i = elem(r, j);
+            if (i >= a.len) continue;
+            const float acc = sum_rows1<DTI>(a.contrib + i, a.n, a.stride);
             bad |= __builtin_isfinite(acc) ? 0u : 1u;
             const float gj = acc * inv;
             ss += (double)gj * (double)gj;
-            float p = a.pair[0][so + j], m = a.pair[1][so + j], v = a.pair[2][so + j];
+            const int64_t si = pair_index(i, cur), di = pair_index(i, cur ^ 1);
+            float p = a.pair[0][si], m = a.pair[1][si], v = a.pair[2][si];
             adam_elem(k, gj, p, m, v);
-            a.pair[0][dof + j] = p;
-            a.pair[1][dof + j] = m;
-            a.pair[2][dof + j] = v;
-            a.slot[e + j] = (uint16_t)narrow<DTO>(p);
+            a.pair[0][di] = p;
+            a.pair[1][di] = m;
+            a.pair[2][di] = v;
+            a.slot[i] = (uint16_t)narrow<DTO>(p);
         }
     }
     write_partial(a.ws, ss, bad);
@@ -649,10 +694,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool valid_dtype(int32_t dt) { return dt == ZERO_F16 || dt == ZERO_BF16; }
 
-// Store width (elements) for a 16-bit destination: 8, 4, 2 or 1.
+// Store width (elements) for 16-bit runs of four at dst: 4, 2 or 1.
 int store_width(const void* p) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-    if ((a & 15u) == 0) return 8;
     if ((a & 7u) == 0) return 4;
     if ((a & 3u) == 0) return 2;
     return 1;
@@ -748,7 +792,6 @@ Kernel<FusedArgs> fused_for(int dti, int dto, int n) {
 template <int DT>
 Kernel<AdamArgs> adam_for(int gw) {
     switch (gw) {
-        case 8: return adam_kernel<DT, 8>;
         case 4: return adam_kernel<DT, 4>;
         case 2: return adam_kernel<DT, 2>;
         case 1: return adam_kernel<DT, 1>;
@@ -759,7 +802,6 @@ Kernel<AdamArgs> adam_for(int gw) {
 template <int DT>
 Kernel<CastArgs> cast_for(int gw) {
     switch (gw) {
-        case 8: return cast_kernel<DT, 8>;
         case 4: return cast_kernel<DT, 4>;
         case 2: return cast_kernel<DT, 2>;
         default: return cast_kernel<DT, 1>;
@@ -931,7 +973,6 @@ int zero_fused_step(const void* contrib, int32_t contrib_dtype, int32_t nranks, 
                 valid_len, ctrl, (Partial*)ws, *hp, nranks};
     Kernel<FusedArgs> k;
     switch (store_width(slot)) {
-        case 8: k = fused_for<8>(contrib_dtype, gather_dtype, nranks); break;
         case 4: k = fused_for<4>(contrib_dtype, gather_dtype, nranks); break;
         case 2: k = fused_for<2>(contrib_dtype, gather_dtype, nranks); break;
         default: k = fused_for<1>(contrib_dtype, gather_dtype, nranks); break;
