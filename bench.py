@@ -26,12 +26,49 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "fused ZeRO shard step effective GB/s + % of HBM peak (1 MI355X)"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ("zero_partitioned_mixed_amd/csrc/zero_shard.hip", "include/zero_shard.h")
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "psi1.3e10_n8_dynscale"
 
 
 def _fmt(x, nd=3):
     return float(f"{x:.{nd}g}") if x is not None else None
+
+
+def kernel_source_sha256() -> str:
+    """Digest of the library's kernel sources (comments and layout stripped,
+    so documentation edits do not count as kernel changes) and hipcc flags."""
+    import hashlib
+    import re
+
+    from zero_partitioned_mixed_amd import build as zbuild
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        text = open(os.path.join(ROOT, rel)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    h.update(" ".join(zbuild.HIPCC_FLAGS[:-1]).encode())  # the include path varies by machine
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed PMC summary of this kernel and
+    workload, or None when there is none or the kernel source has changed
+    since the counters were taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.md")
+    try:
+        fields = {}
+        for line in open(path):
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+        if fields.get("source_sha256") != kernel_source_sha256():
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def setup(w, torch, synth, Z):
@@ -181,7 +218,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--cpu-sample", type=int, default=96 << 20,
+    ap.add_argument("--cpu-sample", type=int, default=160 << 20,
                     help="elements of the shard the CPU oracle baseline steps over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true")
@@ -248,7 +285,8 @@ def main():
         "elements_per_s": _fmt(valid / (ms_step * 1e-3), 5),
         "roofline": {"bound": "hbm", "kernel": kern_name, "achieved": _fmt(kern_gbps, 5),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": _fmt(kern_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": _fmt(kern_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(kern_name, w.name),
                      "kernel_ms": _fmt(kern_avg, 5), "bytes_per_launch": kern_bytes},
         "last_step": {"norm": ctrl["norm"], "skip": ctrl["skip"], "t": ctrl["t"],
                       "loss_scale": ctrl["loss_scale"]},

@@ -174,19 +174,25 @@ int zero_reduce_grads(const void *contrib_dev, int32_t dtype, int32_t nranks, in
 
 /* Norm, overflow and step decisions (paper summary 3.4, residual states:
  * gradient-norm computation over all gradients; "CMU 11-868 L18", The memory
- * bill, same note).  Combines the per-workgroup partials that the previous
+ * bill, same note).  Combines the per-tile partials that the previous
  * zero_reduce_grads or zero_fused_step left in each ws_dev[r] (valid_len[r]
- * elements), in a fixed order, into the global sum of squares and the global
- * non-finite flag of the `nranks` ranks given (nranks > 1 stands in for the
- * scalar all-reduce between data-parallel ranks; with one rank they are its
- * own).  Then, in every ctrl block: norm = sqrt(sumsq); skip = nonfinite;
- * loss-scale update; clip factor; if applied: t += 1, beta powers advance and,
- * when `pingpong` is nonzero, cur flips to the state set the fused step
- * just wrote.  One workgroup; enqueued even when every valid_len is 0.
- * ws_dev, valid_len and ctrl_dev are host arrays of nranks entries (ws_dev
- * and ctrl_dev entries are device pointers).  All ctrl blocks must hold the
- * same scalars (they do when they are always updated together).
- * Errors: EINVAL (null, nranks outside [1, ZERO_MAX_RANKS], bad hparams). */
+ * elements) into the global sum of squares and the global non-finite flag of
+ * the `nranks` ranks given (nranks > 1 stands in for the scalar all-reduce
+ * between data-parallel ranks; with one rank they are its own).  The
+ * reduction is deterministic: contiguous ranges of the concatenated partials
+ * are summed in order, then the ranges in index order.  Then, in every ctrl
+ * block: norm = sqrt(sumsq); skip = nonfinite; loss-scale update; clip
+ * factor; if applied: t += 1, beta powers advance and, when `pingpong` is
+ * nonzero, cur flips to the state set the fused step just wrote.  Enqueued
+ * even when every valid_len is 0.
+ * ws_dev, valid_len and ctrl_dev are host arrays of nranks entries (ws_dev and
+ * ctrl_dev entries are device pointers).  Each ws_dev[r] must be the whole
+ * workspace of zero_workspace_bytes(valid_len[r]) bytes that the step used
+ * (the reduction keeps its second level behind rank 0's partials).  All ctrl
+ * blocks must hold the same scalars (they do when they are always updated
+ * together), and calls sharing ctrl_dev[0] must not overlap.
+ * Errors: EINVAL (null, nranks outside [1, ZERO_MAX_RANKS], bad hparams),
+ * EALIGN, ERANGE. */
 int zero_grad_norm_overflow(int32_t nranks, void *const *ws_dev, const int64_t *valid_len,
                             zero_ctrl *const *ctrl_dev, const zero_hparams *hp,
                             int32_t pingpong, void *stream);
