@@ -102,19 +102,28 @@ def setup(w, torch, synth, Z):
 
 
 def timed_steps(b, steps, warmup, torch, Z):
-    """Runs warmup + timed steps; events around the whole loop and around each
-    launch of the dominant kernel (the fused pass, or the Adam pass)."""
+    """Warmup, then two timed passes of `steps` steps each on the same stream:
+    the first with events only around the whole loop (the step time), the
+    second with events also around each launch of the dominant kernel (the
+    fused pass, or the Adam pass; plus the reduce pass on the two-pass path).
+    Event records between kernels cost a few microseconds each, so they are
+    kept out of the loop that gives the step time."""
     st, contrib, gather = b["step"], b["contrib"], b["gather"]
     for _ in range(warmup):
         st.step(contrib, gather)
     torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        st.step(contrib, gather)
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     ev_red = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     hp, n, stride, valid, off = st.hp, st.nranks, st.stride, st.valid_len, st.offset
-    t0.record()
     for i in range(steps):
         if b["fused"]:
             ev[i][0].record()
@@ -131,13 +140,11 @@ def timed_steps(b, steps, warmup, torch, Z):
             ev[i][0].record()
             Z.zero_adam_step(st.state, st.g, valid, hp, st.ctrl, gather, st.gather_dtype, off)
             ev[i][1].record()
-    t1.record()
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
     kern_ms = [a.elapsed_time(c) for a, c in ev]
     red_ms = [a.elapsed_time(c) for a, c in ev_red] if not b["fused"] else []
     ctrl = st.ctrl_dict()
-    return total_ms / steps, kern_ms, red_ms, ctrl
+    return step_ms, kern_ms, red_ms, ctrl
 
 
 def copy_bandwidth(torch, synth, nbytes=8 << 30, reps=10):

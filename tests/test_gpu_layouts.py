@@ -1,0 +1,195 @@
+"""ZeRO-0/1/2/3 layouts and a bucketed reduce on the GPU, through the C ABI.
+
+The simulation README reports that the four stages train identically: they
+change where bytes live, not the arithmetic ("zero-stages-simulation"
+README, opening summary and the equality table; its "during backward /
+gradient sync / optimizer step" table gives each stage's data flow).  On the
+toy workload (Psi = 637,824, N = 32, 3 steps):
+
+  ZeRO-0  one replica steps all of Psi after the all-reduce mean (N = 32
+          contributions over the whole buffer, fused path);
+  ZeRO-1  the full averaged gradient is reduced once, then every rank's Adam
+          runs on its slice of it (two-pass calls with clipping off);
+  ZeRO-2  every rank reduces only its slice (fused path, shared decisions);
+  ZeRO-3  as ZeRO-2, but each rank's 16-bit output is a shard-local buffer.
+
+All four must agree bit for bit, and with the oracle.  The bucketed reduce
+(the reduce-scatter arriving in tile-aligned buckets during backward, paper
+summary 3.4 Stage 2, bucketization) must equal the one-shot reduce bit for
+bit, norm included.
+"""
+import numpy as np
+import pytest
+
+import harness as H
+from synth import workloads
+from synth.workloads import F16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import synth
+    synth.gpu()
+    import zero_partitioned_mixed_amd  # noqa: F401
+    yield
+
+
+def _toy_layout(stage):
+    import torch
+    import synth
+    import zero_partitioned_mixed_amd as Z
+    w = workloads.TOY
+    n, psi = w.nranks, w.psi
+    dev = torch.device("cuda", 0)
+    hp = Z.hparams(lr=w.lr)
+    p_full = torch.empty(psi, dtype=torch.float32, device=dev)
+    synth.gpu_master_range(p_full, w.seed, w.master_sigma, 0)
+    parts = [Z.zero_partition(psi, n, r) for r in range(n)]
+
+    def fill(buf, step, off, valid):
+        synth.gpu_contrib_rows(buf, w.seed, step, F16, w.contrib_sigma, 1.0, 0.0, 100.0, off, valid)
+
+    if stage == 0:
+        stride = (psi + 63) // 64 * 64
+        C = torch.empty((n, stride), dtype=torch.float16, device=dev)
+        gather = torch.empty(psi, dtype=torch.float16, device=dev)
+        synth.gpu_param_range(gather, w.seed, w.master_sigma, F16, 0)
+        st = Z.ShardStep(n, stride, psi, 0, F16, F16, hp,
+                         (p_full, torch.zeros_like(p_full), torch.zeros_like(p_full)))
+        for s in range(1, w.steps + 1):
+            fill(C, s, 0, psi)
+            st.step(C, gather)
+        master, m, v = [t.cpu().numpy() for t in st.current()]
+        params = gather.view(torch.int16).cpu().numpy().view(np.uint16)
+        return master, m, v, params, st.ctrl_dict()
+
+    if stage == 1:
+        stride = (psi + 63) // 64 * 64
+        C = torch.empty((n, stride), dtype=torch.float16, device=dev)
+        g = torch.empty(psi, dtype=torch.float32, device=dev)
+        gather = torch.empty(psi, dtype=torch.float16, device=dev)
+        synth.gpu_param_range(gather, w.seed, w.master_sigma, F16, 0)
+        ctrl = torch.empty(Z.zero_ctrl_bytes(), dtype=torch.uint8, device=dev)
+        ws = torch.empty(Z.zero_workspace_bytes(psi), dtype=torch.uint8, device=dev)
+        Z.zero_ctrl_init(ctrl, 1.0)
+        states = [(p_full[off:off + valid].clone(), torch.zeros(valid, device=dev),
+                   torch.zeros(valid, device=dev)) for _, off, valid in parts]
+        for s in range(1, w.steps + 1):
+            fill(C, s, 0, psi)
+            Z.zero_reduce_grads(C, F16, n, stride, psi, ctrl, g, ws)  # all-reduce mean
+            Z.zero_grad_norm_overflow([ws], [psi], [ctrl], hp, False)
+            for (_, off, valid), st in zip(parts, states):  # each rank: its slice
+                Z.zero_adam_step(st, g[off:off + valid], valid, hp, ctrl, gather, F16, off)
+        master = np.concatenate([st[0].cpu().numpy() for st in states])
+        m = np.concatenate([st[1].cpu().numpy() for st in states])
+        v = np.concatenate([st[2].cpu().numpy() for st in states])
+        params = gather.view(torch.int16).cpu().numpy().view(np.uint16)
+        return master, m, v, params, Z.read_ctrl(ctrl)
+
+    # stages 2 and 3: one fused shard step per rank with shared decisions
+    local = stage == 3
+    gather = torch.empty(psi, dtype=torch.float16, device=dev)
+    synth.gpu_param_range(gather, w.seed, w.master_sigma, F16, 0)
+    steps, contribs, outs = [], [], []
+    for _, off, valid in parts:
+        stride = (valid + 63) // 64 * 64
+        st = Z.ShardStep(n, stride, valid, 0 if local else off, F16, F16, hp,
+                         (p_full[off:off + valid].clone(), torch.zeros(valid, device=dev),
+                          torch.zeros(valid, device=dev)))
+        steps.append(st)
+        contribs.append(torch.empty((n, stride), dtype=torch.float16, device=dev))
+        if local:
+            o = torch.empty(valid, dtype=torch.float16, device=dev)
+            synth.gpu_param_range(o, w.seed, w.master_sigma, F16, off)
+            outs.append(o)
+    multi = Z.MultiShardStep(steps)
+    for s in range(1, w.steps + 1):
+        for (_, off, valid), c in zip(parts, contribs):
+            fill(c, s, off, valid)
+        if local:  # each rank writes its own shard-local buffer
+            for st, c, o in zip(steps, contribs, outs):
+                Z.zero_fused_step(c, F16, n, st.stride, st.pair, st.valid_len, o, F16, 0, hp,
+                                  st.ctrl, st.ws)
+            Z.zero_grad_norm_overflow([st.ws for st in steps], [st.valid_len for st in steps],
+                                      [st.ctrl for st in steps], hp, True)
+            for st, o in zip(steps, outs):
+                Z.zero_fused_restore(st.pair, st.valid_len, o, F16, 0, st.ctrl)
+        else:
+            multi.step(contribs, gather)
+    cur = [st.current() for st in steps]
+    master = np.concatenate([c[0].cpu().numpy() for c in cur])
+    m = np.concatenate([c[1].cpu().numpy() for c in cur])
+    v = np.concatenate([c[2].cpu().numpy() for c in cur])
+    if local:
+        params = np.concatenate([o.view(torch.int16).cpu().numpy().view(np.uint16) for o in outs])
+    else:
+        params = gather.view(torch.int16).cpu().numpy().view(np.uint16)
+    return master, m, v, params, steps[0].ctrl_dict()
+
+
+def test_zero_stage_layouts_bitwise_equal_on_gpu():
+    import oracle as O
+    from oracle import layouts
+    import synth
+    res = {}
+    for stage in (0, 1, 2, 3):
+        res[stage] = _toy_layout(stage)
+        H.log(f"layout ZeRO-{stage}: t={res[stage][4]['t']} norm={res[stage][4]['norm']:.12g}")
+    for stage in (1, 2, 3):
+        for name, a, b in zip(("master", "m", "v"), res[0][:3], res[stage][:3]):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), (stage, name)
+        assert np.array_equal(res[0][3], res[stage][3]), (stage, "params")
+        assert res[stage][4]["sumsq"] == res[0][4]["sumsq"] or stage in (2, 3)
+    # and the oracle's ZeRO-2 layout
+    w = workloads.TOY
+    contrib = lambda s: synth.contrib_rows(w.seed, s, w.nranks, F16, w.contrib_sigma, 1.0, 0.0,
+                                           100.0, 0, w.psi)
+    om, omm, ov, op, _ = layouts.run(2, w.psi, w.nranks, w.steps, contrib,
+                                     synth.master_range(w.seed, w.master_sigma, 0, w.psi),
+                                     O.hparams(lr=w.lr))
+    H.assert_f32_close("master", res[0][0], om)
+    H.assert_f32_close("m", res[0][1], omm)
+    H.assert_f32_close("v", res[0][2], ov)
+    H.assert_16bit_within_ulp("params", res[0][3], op, F16)
+
+
+def test_bucketed_reduce_equals_one_shot():
+    import torch
+    import synth
+    import zero_partitioned_mixed_amd as Z
+    w = workloads.GPT2
+    shard, off, valid = Z.zero_partition(w.psi, w.nranks, 7)
+    stride = w.stride
+    dev = torch.device("cuda", 0)
+    C = torch.empty((w.nranks, stride), dtype=torch.float16, device=dev)
+    synth.gpu_contrib_rows(C, w.seed, 1, F16, w.contrib_sigma, w.contrib_scale, 0.0, 100.0, off,
+                           valid)
+    hp = Z.hparams(max_grad_norm=1.0, scaler=Z.SCALER_STATIC)
+    outs = []
+    for bucket in (None, 2048 * 1024, 2048 * 37):
+        g = torch.empty(valid, dtype=torch.float32, device=dev)
+        ctrl = torch.empty(Z.zero_ctrl_bytes(), dtype=torch.uint8, device=dev)
+        ws = torch.empty(Z.zero_workspace_bytes(valid), dtype=torch.uint8, device=dev)
+        Z.zero_ctrl_init(ctrl, w.loss_scale)
+        if bucket is None:
+            Z.zero_reduce_grads(C, F16, w.nranks, stride, valid, ctrl, g, ws)
+        else:
+            for b0 in range(0, valid, bucket):  # buckets arrive one by one
+                ln = min(bucket, valid - b0)
+                wsb = ws[(b0 // 2048) * 16:]
+                Z._check("zero_reduce_grads", Z._lib.zero_reduce_grads(
+                    Z._ptr(C) .value + 2 * b0, F16, w.nranks, stride, ln, Z._ptr(ctrl),
+                    Z._ptr(g).value + 4 * b0, Z._ptr(wsb), wsb.numel(), Z._stream()))
+        Z.zero_grad_norm_overflow([ws], [valid], [ctrl], hp, False)
+        torch.cuda.synchronize()
+        outs.append((g.cpu().numpy(), Z.read_ctrl(ctrl)))
+    g0, c0 = outs[0]
+    for g1, c1 in outs[1:]:
+        assert np.array_equal(g0.view(np.uint32), g1.view(np.uint32))
+        assert c1["sumsq"] == c0["sumsq"] and c1["clip"] == c0["clip"] and c1["t"] == c0["t"]
+    H.log(f"bucketed reduce: norm {c0['norm']:.12g}, clip {c0['clip']}")

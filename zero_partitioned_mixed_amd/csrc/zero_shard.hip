@@ -41,8 +41,8 @@ constexpr int64_t kTile = ZERO_TILE;        // elements per workgroup
 static_assert(kTile == (int64_t)kBlock * kVec, "tile = threads x elements per thread");
 constexpr int kFinBlock = 1024;             // threads per finalize workgroup
 constexpr int kFinGroups = 256;             // most first-level groups of the finalize
-constexpr int64_t kFinPer = 4096;           // partials per first-level finalize group
-constexpr int kRestoreGrid = 1024;          // workgroups of the (usually idle) restore pass
+constexpr int64_t kFinPer = 16384;          // partials per first-level finalize group
+constexpr int kRestoreGrid = 256;           // workgroups of the (usually idle) restore pass
 constexpr int64_t kMaxLen = int64_t(1) << 40;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -168,10 +168,10 @@ __device__ __forceinline__ void add_rows8(float acc[kVec], const Row w[8]) {
 // Row sums of the thread's 8 elements over rows k = 0..n-1, added in that
 // order, in two phases so that callers can issue all of an element group's
 // loads before its first use.  sum_rows_issue loads the first eight rows
-// (n >= 8); sum_rows_finish adds them and streams the remaining rows with
-// the next eight rows' loads in flight while the current eight are added.
-// NR = 8 compiles the common case of exactly eight rows without the
-// streaming loop (and its second set of load registers); NR = 0 takes any n.
+// (n >= 8); sum_rows_finish adds them and streams the remaining rows eight
+// at a time (all eight loads in flight before the first add).  NR = 8
+// compiles the common case of exactly eight rows without the loop; NR = 0
+// takes any n.
 struct RowLoads {
     Row w[8];
 };
@@ -194,16 +194,12 @@ __device__ __forceinline__ void sum_rows_finish(const uint16_t* __restrict__ C, 
     }
     int k = 0;
     if (n >= 8) {
-        for (; k + 16 <= n; k += 8) {
-            Row nxt[8];
-            load_rows8(C, stride, k + 8, r, nxt);
+        add_rows8<DT>(acc, L.w);
+        for (k = 8; k + 8 <= n; k += 8) {
+            load_rows8(C, stride, k, r, L.w);
             __builtin_amdgcn_sched_barrier(0);
             add_rows8<DT>(acc, L.w);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) L.w[q] = nxt[q];
         }
-        add_rows8<DT>(acc, L.w);
-        k += 8;
     }
     for (; k < n; ++k) add_row<DT>(acc, load_row(C + (int64_t)k * stride, r));
 }
@@ -420,12 +416,32 @@ __global__ void __launch_bounds__(kFinBlock) finalize_kernel(CombineArgs a) {
     const int64_t hi = lo + a.per < total ? lo + a.per : total;
     double ss = 0.0;
     uint32_t bad = 0;
-    int r = 0;
-    for (int64_t i = lo + threadIdx.x; i < hi; i += kFinBlock) {
-        while (i >= a.first[r + 1]) ++r;
-        const Partial p = a.ws[r][i - a.first[r]];
-        ss += p.sumsq;
-        bad |= p.nonfinite;
+    if (a.nranks == 1) {
+        // one rank: four independent loads in flight per thread, added in index order
+        const Partial* __restrict__ w = a.ws[0];
+        int64_t i = lo + threadIdx.x;
+        for (; i + 3 * kFinBlock < hi; i += 4 * kFinBlock) {
+            Partial p[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) p[q] = w[i + q * kFinBlock];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                ss += p[q].sumsq;
+                bad |= p[q].nonfinite;
+            }
+        }
+        for (; i < hi; i += kFinBlock) {
+            ss += w[i].sumsq;
+            bad |= w[i].nonfinite;
+        }
+    } else {
+        int r = 0;
+        for (int64_t i = lo + threadIdx.x; i < hi; i += kFinBlock) {
+            while (i >= a.first[r + 1]) ++r;
+            const Partial p = a.ws[r][i - a.first[r]];
+            ss += p.sumsq;
+            bad |= p.nonfinite;
+        }
     }
     block_reduce<kFinBlock>(ss, bad);
     if (gridDim.x > 1) {
