@@ -80,11 +80,14 @@ _lib = None
 
 
 def lib():
+    """The oracle library (``ORACLE_LIB`` may name another build of oracle.c:
+    the mutation tests use it to run the pins against planted mistakes)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        path = os.environ.get("ORACLE_LIB", _LIB)
+        if path == _LIB and not os.path.exists(_LIB):
             build(force=False)
-        L = ctypes.CDLL(_LIB)
+        L = ctypes.CDLL(path)
         L.oracle_to_f32.restype = ctypes.c_float
         L.oracle_to_f32.argtypes = [ctypes.c_uint16, ctypes.c_int32]
         L.oracle_from_f32.restype = ctypes.c_uint16
