@@ -260,3 +260,32 @@ def test_gpt2_sized_full():
 def test_psi1_5b_n64_full():
     w = workloads.P1_5B
     run_case(Case(w, w.ranks[0], w.steps), w.name, full=False)
+
+
+# --------------------------------------------------------------------------- paired state, finalize groups
+def test_pair_store_load_round_trip():
+    import torch
+    import zero_partitioned_mixed_amd as Z
+    dev = torch.device("cuda", 0)
+    for n in (1, 7, 2048, 2049, 100_003):
+        flat = tuple(torch.randn(n, device=dev) for _ in range(3))
+        pair = tuple(torch.full((Z.zero_pair_elems(n),), float("nan"), device=dev) for _ in range(3))
+        ctrl = torch.empty(Z.zero_ctrl_bytes(), dtype=torch.uint8, device=dev)
+        Z.zero_ctrl_init(ctrl, 1.0)
+        Z.zero_pair_store(flat, pair, n, ctrl)
+        back = tuple(torch.empty(n, device=dev) for _ in range(3))
+        Z.zero_pair_load(pair, back, n, ctrl)
+        for a, b in zip(flat, back):
+            assert torch.equal(a, b)
+        # set 0 of each tile holds the data, set 1 is untouched
+        p = pair[0].view(-1, 2, 2048)
+        assert torch.isnan(p[:, 1, :]).all()
+        assert torch.equal(p[:, 0, :].reshape(-1)[:n], flat[0])
+
+
+@pytest.mark.parametrize("tiles", [16384, 16385])
+def test_finalize_single_and_grouped(tiles):
+    """One finalize workgroup takes up to 16384 per-tile partials; beyond that
+    the grouped path (ranges, then the last group to arrive) runs."""
+    w = small(tiles * 2048 - 1000, 1, 0, dtype=BF16, steps=2, max_grad_norm=0.5)
+    run_case(Case(w, 0, 2), f"finalize_{tiles}_tiles", full=False)
