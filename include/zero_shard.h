@@ -156,8 +156,8 @@ size_t zero_pair_elems(int64_t valid_len);
  * (must be finite and > 0; use 1 without a scaler), cur = 0, arrive = 0. */
 int zero_ctrl_init(zero_ctrl *ctrl_dev, float loss_scale, void *stream);
 
-/* Reduce ("CMU 11-868 L18", Mechanism 1 step 3: the reduce-scatter sums and
- * averages the gradients and each GPU receives its part in FP32; paper
+/* Reduce ("CMU 11-868 L18", Mechanism 1 step 3: the reduce-scatter leaves each
+ * rank the fp32 mean of all ranks' gradients over its own slice only; paper
  * summary 3.4 Stage 2, reduce-scatter of gradients):
  *   g[i] = fl32( sum_{k=0..N-1} C[k][i] ) * fl32(1 / (N * S)),   i < valid_len,
  * summed in fp32 in rank order k = 0..N-1; S is ctrl->loss_scale.

@@ -19,7 +19,7 @@
  *
  * Precision: the pages fix fp16/bf16 gradients and parameters and fp32 master,
  * momentum, variance and reduced gradient ([pg] 3.4 "16 Psi baseline"; [cmu]
- * Mechanism 1 step 3 "in FP32").  The oracle computes exactly those types,
+ * Mechanism 1 step 3, fp32 reduced gradient).  The oracle computes exactly those types,
  * every operation rounded once in the order written (compiled with
  * -ffp-contract=off, SSE scalar arithmetic).  The squared-norm is exact.
  *
@@ -139,7 +139,7 @@ void oracle_from_f32_bits_range(uint32_t b0, int64_t n, int32_t dtype, uint16_t 
 /* ------------------------------------------------------------------------ */
 /* Partition.  Every flattened tensor is split into N near-equal contiguous   */
 /* chunks and rank r owns chunk r ([sim] partitioning paragraph; [pg] 3.4     */
-/* Stage 1 "the i-th process ... the i-th partition"; [grasp] Stage 1 step 3). */
+/* Stage 1, process r updates only partition r; [grasp] Stage 1 step 3).     */
 /* Equal ceil(Psi/N) chunks, so the tail ranks are short or empty.            */
 /* ------------------------------------------------------------------------ */
 int oracle_partition(int64_t psi, int32_t nranks, int32_t rank, int64_t *shard, int64_t *offset,
@@ -156,8 +156,8 @@ int oracle_partition(int64_t psi, int32_t nranks, int32_t rank, int64_t *shard, 
 
 /* ------------------------------------------------------------------------ */
 /* Reduce.  The reduce-scatter sums the N ranks' gradients for the owned slice */
-/* and averages them, delivering fp32 ([cmu] Mechanism 1 step 3; [sim] table   */
-/* "all-reduce mean"; [pg] 3.4 Stage 2 reduce-scatter).  Sum in fp32 in rank   */
+/* and averages them, delivering fp32 ([cmu] Mechanism 1 step 3; [sim] data-  */
+/* flow table, gradient-sync column; [pg] 3.4 Stage 2).  Sum in fp32 in rank  */
 /* order k = 0..N-1; overflow is tested on the sum; then multiply by           */
 /* inv = fl32(1 / (N * S)), which removes the loss scale S and averages.       */
 /* C is laid out [n][stride] (16-bit patterns); only columns < len are read.   */
@@ -180,8 +180,8 @@ void oracle_reduce(const uint16_t *C, int32_t dtype, int32_t n, int64_t stride, 
 
 /* ------------------------------------------------------------------------ */
 /* Squared L2 norm of the reduced gradient, exactly.  Gradient-norm           */
-/* computation over all gradients ([pg] 3.4 residual states, "Temporary       */
-/* buffers"; [cmu] "The memory bill").  Each g is M 2^(e-24) with M < 2^24,   */
+/* computation over all gradients ([pg] 3.4 residual states, temporary       */
+/* buffers; [cmu] "The memory bill").  Each g is M 2^(e-24) with M < 2^24,    */
 /* so g^2 = M^2 2^(2e-48) is an integer below 2^48 placed at bit 2e+296 of a   */
 /* 640-bit fixed-point accumulator (least significant bit 2^-344, enough for   */
 /* every binary32 square and 2^34 terms).  The sum is therefore independent of */

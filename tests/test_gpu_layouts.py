@@ -2,8 +2,8 @@
 
 The simulation README reports that the four stages train identically: they
 change where bytes live, not the arithmetic ("zero-stages-simulation"
-README, opening summary and the equality table; its "during backward /
-gradient sync / optimizer step" table gives each stage's data flow).  On the
+README, opening summary and the equality table; its per-stage data-flow
+table gives where gradients and optimizer state live at each phase).  On the
 toy workload (Psi = 637,824, N = 32, 3 steps):
 
   ZeRO-0  one replica steps all of Psi after the all-reduce mean (N = 32
