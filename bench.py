@@ -71,8 +71,10 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
-def setup(w, torch, synth, Z):
-    """Buffers of the measured rank, inputs generated in HBM."""
+def setup(w, torch, synth, Z, rows=False):
+    """Buffers of the measured rank, inputs generated in HBM.  With `rows`, the
+    N contribution rows live in N separate allocations and the step goes
+    through the row-table calls."""
     rank = w.ranks[-1]
     shard, off, valid = Z.zero_partition(w.psi, w.nranks, rank)
     stride = w.stride
@@ -96,6 +98,14 @@ def setup(w, torch, synth, Z):
     if fused:  # the flat state is only needed to load the paired copy
         del state0, p0
         st.state = None
+    if rows:
+        table = [torch.empty(valid, dtype=tdt, device=dev) for _ in range(w.nranks)]
+        for k, r in enumerate(table):
+            r.copy_(contrib[k, :valid])
+        torch.cuda.synchronize()
+        del contrib
+        torch.cuda.empty_cache()
+        contrib = table
     torch.cuda.synchronize()
     return dict(rank=rank, shard=shard, off=off, valid=valid, stride=stride, contrib=contrib,
                 gather=gather, step=st, fused=fused)
@@ -109,6 +119,7 @@ def timed_steps(b, steps, warmup, torch, Z):
     Event records between kernels cost a few microseconds each, so they are
     kept out of the loop that gives the step time."""
     st, contrib, gather = b["step"], b["contrib"], b["gather"]
+    table = isinstance(contrib, list)
     for _ in range(warmup):
         st.step(contrib, gather)
     torch.cuda.synchronize()
@@ -119,6 +130,14 @@ def timed_steps(b, steps, warmup, torch, Z):
     t1.record()
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
+    # per-step spread: one event at each step boundary
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    bounds[0].record()
+    for i in range(steps):
+        st.step(contrib, gather)
+        bounds[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(steps))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     ev_red = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -127,14 +146,21 @@ def timed_steps(b, steps, warmup, torch, Z):
     for i in range(steps):
         if b["fused"]:
             ev[i][0].record()
-            Z.zero_fused_step(contrib, st.dtype, n, stride, st.pair, valid, gather,
-                              st.gather_dtype, off, hp, st.ctrl, st.ws)
+            if table:
+                Z.zero_fused_step_rows(contrib, st.dtype, st.pair, valid, gather,
+                                       st.gather_dtype, off, hp, st.ctrl, st.ws)
+            else:
+                Z.zero_fused_step(contrib, st.dtype, n, stride, st.pair, valid, gather,
+                                  st.gather_dtype, off, hp, st.ctrl, st.ws)
             ev[i][1].record()
             Z.zero_grad_norm_overflow([st.ws], [valid], [st.ctrl], hp, True)
             Z.zero_fused_restore(st.pair, valid, gather, st.gather_dtype, off, st.ctrl)
         else:
             ev_red[i][0].record()
-            Z.zero_reduce_grads(contrib, st.dtype, n, stride, valid, st.ctrl, st.g, st.ws)
+            if table:
+                Z.zero_reduce_grads_rows(contrib, st.dtype, valid, st.ctrl, st.g, st.ws)
+            else:
+                Z.zero_reduce_grads(contrib, st.dtype, n, stride, valid, st.ctrl, st.g, st.ws)
             ev_red[i][1].record()
             Z.zero_grad_norm_overflow([st.ws], [valid], [st.ctrl], hp, False)
             ev[i][0].record()
@@ -144,7 +170,7 @@ def timed_steps(b, steps, warmup, torch, Z):
     kern_ms = [a.elapsed_time(c) for a, c in ev]
     red_ms = [a.elapsed_time(c) for a, c in ev_red] if not b["fused"] else []
     ctrl = st.ctrl_dict()
-    return step_ms, kern_ms, red_ms, ctrl
+    return step_ms, per_step, kern_ms, red_ms, ctrl
 
 
 def copy_bandwidth(torch, synth, nbytes=8 << 30, reps=10):
@@ -225,6 +251,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--rows", action="store_true",
+                    help="contribution rows in N separate allocations, through the row-table "
+                         "calls (one pointer per row) instead of one [N, stride] buffer")
     ap.add_argument("--cpu-sample", type=int, default=160 << 20,
                     help="elements of the shard the CPU oracle baseline steps over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -255,14 +284,14 @@ def main():
         return
 
     w = workloads.BY_NAME[args.workload]
-    b = setup(w, torch, synth, Z)
-    ms_step, kern_ms, red_ms, ctrl = timed_steps(b, args.steps, args.warmup, torch, Z)
+    b = setup(w, torch, synth, Z, rows=args.rows)
+    ms_step, per_step, kern_ms, red_ms, ctrl = timed_steps(b, args.steps, args.warmup, torch, Z)
     valid = b["valid"]
     step_bytes = w.bytes_per_elem * valid
     gbps = step_bytes / (ms_step * 1e-3) / 1e9
     kern_avg = sum(kern_ms) / len(kern_ms)
     if b["fused"]:
-        kern_name = "fused_kernel"
+        kern_name = "fused_kernel_rows" if args.rows else "fused_kernel"
         kern_bytes = step_bytes
     else:
         kern_name = "adam_kernel"
@@ -287,7 +316,10 @@ def main():
         "config": {"workload": w.name, "psi": w.psi, "nranks": w.nranks, "rank": w.ranks[-1],
                    "shard_elems": valid, "variant": w.variant,
                    "contrib_dtype": "fp16" if w.dtype == Z.F16 else "bf16",
-                   "bytes_per_elem": w.bytes_per_elem, "step_bytes": step_bytes},
+                   "bytes_per_elem": w.bytes_per_elem, "step_bytes": step_bytes,
+                   "contrib_layout": "row_table" if args.rows else "strided"},
+        "step_ms_median": _fmt(per_step[len(per_step) // 2], 5),
+        "step_ms_min": _fmt(per_step[0], 5),
         "pct_hbm_peak": _fmt(100 * gbps / HBM_PEAK_GBPS, 4),
         "elements_per_s": _fmt(valid / (ms_step * 1e-3), 5),
         "roofline": {"bound": "hbm", "kernel": kern_name, "achieved": _fmt(kern_gbps, 5),

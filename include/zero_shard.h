@@ -37,8 +37,8 @@
  *     selects ZERO_F16 (IEEE binary16) or ZERO_BF16 (bfloat16).
  *   - Element counts and offsets are int64 (Psi reaches 1.3e10 elements).
  *   - Alignment: contribution buffers, their row stride (a multiple of 8
- *     elements), g and the fp32 state arrays must be 16-byte aligned.  The
- *     gather slot needs only 2-byte alignment.
+ *     elements), g and the fp32 state arrays must be 16-byte aligned; rows of
+ *     a row table need 8 bytes.  The gather slot needs only 2-byte alignment.
  *   - valid_len == 0 (an empty tail rank) is legal: nothing is enqueued except
  *     where the call says otherwise.
  *   - Calls on different streams are independent as long as they use
@@ -68,7 +68,7 @@ enum {
 enum { ZERO_SCALER_NONE = 0, ZERO_SCALER_STATIC = 1, ZERO_SCALER_DYNAMIC = 2 };
 
 #define ZERO_MAX_CONTRIB 1024 /* largest N accepted by the reduce */
-#define ZERO_MAX_RANKS 64     /* largest number of ctrl blocks combined in one call */
+#define ZERO_MAX_RANKS 64     /* most ctrl blocks combined in one call; most rows in a row table */
 
 /* Optimizer, clipping and loss-scale settings, passed by host pointer and
  * copied into the kernel arguments.  The pages name Adam (Kingma and Ba) and
@@ -172,6 +172,22 @@ int zero_reduce_grads(const void *contrib_dev, int32_t dtype, int32_t nranks, in
                       int64_t valid_len, const zero_ctrl *ctrl_dev, float *g_dev, void *ws_dev,
                       size_t ws_bytes, void *stream);
 
+/* zero_reduce_grads with the N contribution rows in separate places: row k
+ * starts at rows_dev[k] (valid_len 16-bit values; element i of the shard at
+ * rows_dev[k][i]).  This is the form a reduce-scatter takes when every rank
+ * reads its slice of the N ranks' gradient buffers directly, each slice
+ * mapped into this process from its owner's memory ("CMU 11-868 L18",
+ * Mechanism 1 step 3; paper summary 3.4 Stage 2): no staging copy into one
+ * [N, stride] buffer.  The result is bit-identical to zero_reduce_grads on
+ * the same rows (same order k = 0..N-1).  rows_dev is a host array of nranks
+ * device pointers, copied into the launch (reusable on return); each pointer
+ * must be non-NULL and 8-byte aligned, rows may alias (they are only read).
+ * Errors: EINVAL (null table or row, dtype, nranks outside
+ * [1, ZERO_MAX_RANKS]), EALIGN (a row not 8-byte aligned, g), ESPACE. */
+int zero_reduce_grads_rows(const void *const *rows_dev, int32_t dtype, int32_t nranks,
+                           int64_t valid_len, const zero_ctrl *ctrl_dev, float *g_dev,
+                           void *ws_dev, size_t ws_bytes, void *stream);
+
 /* Norm, overflow and step decisions (paper summary 3.4, residual states:
  * gradient-norm computation over all gradients; "CMU 11-868 L18", The memory
  * bill, same note).  Combines the per-tile partials that the previous
@@ -233,6 +249,16 @@ int zero_fused_step(const void *contrib_dev, int32_t contrib_dtype, int32_t nran
                     int64_t stride, const zero_state *pair, int64_t valid_len, void *gather_dev,
                     int32_t gather_dtype, int64_t offset, const zero_hparams *hp,
                     const zero_ctrl *ctrl_dev, void *ws_dev, size_t ws_bytes, void *stream);
+
+/* zero_fused_step with the contribution rows given as a table of row
+ * pointers, as in zero_reduce_grads_rows (same requirements on rows_dev and
+ * nranks <= ZERO_MAX_RANKS): the one-pass reduce-scatter + Adam + cast of a
+ * rank that reads the N ranks' slices where they lie.  Bit-identical to
+ * zero_fused_step on the same rows. */
+int zero_fused_step_rows(const void *const *rows_dev, int32_t contrib_dtype, int32_t nranks,
+                         const zero_state *pair, int64_t valid_len, void *gather_dev,
+                         int32_t gather_dtype, int64_t offset, const zero_hparams *hp,
+                         const zero_ctrl *ctrl_dev, void *ws_dev, size_t ws_bytes, void *stream);
 
 /* After a fused step's zero_grad_norm_overflow: if ctrl->skip, rewrite
  * gather_dev[offset + i] from the current master of the paired state;

@@ -172,10 +172,22 @@ def oracle_elements(c: Case, reps: list[dict], cols: np.ndarray | None = None):
 
 
 # ----------------------------------------------------------------------------- GPU side
-class GpuRun:
-    """One rank's buffers in HBM and its steps through the C ABI."""
+ROW_LAYOUTS = ("strided", "rows", "rows_shifted")
 
-    def __init__(self, c: Case, full_gather: bool = True):
+
+class GpuRun:
+    """One rank's buffers in HBM and its steps through the C ABI.
+
+    layout: how the contribution rows are handed to the library.
+      strided       one [N, stride] buffer (zero_fused_step / zero_reduce_grads);
+      rows          N separate allocations, one pointer per row (the *_rows calls);
+      rows_shifted  N rows packed in one buffer at 8-byte but not 16-byte
+                    aligned starts (as a peer's slice at an odd multiple of
+                    four elements would be), through the *_rows calls.
+    The row copies are filled from the strided buffer, so all three hand the
+    library the same values."""
+
+    def __init__(self, c: Case, full_gather: bool = True, layout: str = "strided"):
         import torch
         import zero_partitioned_mixed_amd as Z
         self.c, self.Z, self.torch = c, Z, torch
@@ -204,6 +216,19 @@ class GpuRun:
         self.step_obj = Z.ShardStep(w.nranks, c.stride, valid, self.gather_off, w.dtype, w.dtype,
                                     hp, self.state0, self.g, w.loss_scale)
         self.reports = []
+        if layout not in ROW_LAYOUTS:
+            raise ValueError(layout)
+        self.layout = layout
+        self.rows = None
+        n = w.nranks
+        if layout == "rows":
+            self.rows = [torch.empty(max(valid, 1), dtype=tdt, device=dev) for _ in range(n)]
+        elif layout == "rows_shifted":
+            span = (valid + 7) // 8 * 8 + 8          # a multiple of 8 elements
+            self.row_buf = torch.empty(4 + n * span, dtype=tdt, device=dev)
+            self.rows = [self.row_buf[4 + k * span:4 + k * span + max(valid, 1)] for k in range(n)]
+            for r in self.rows:
+                assert r.data_ptr() % 8 == 0 and r.data_ptr() % 16 == 8
 
     def fill(self, step: int) -> None:
         w, c = self.c.w, self.c
@@ -212,12 +237,15 @@ class GpuRun:
         for inj in c.injections:
             if inj.step == step:
                 self.contrib[inj.k, inj.col] = inj.value
+        if self.rows is not None and self.valid:
+            for k, r in enumerate(self.rows):
+                r[:self.valid].copy_(self.contrib[k, :self.valid])
 
     def run(self, steps: int | None = None, record: bool = True) -> None:
         steps = self.c.steps if steps is None else steps
         for s in range(1, steps + 1):
             self.fill(s)
-            self.step_obj.step(self.contrib, self.gather)
+            self.step_obj.step(self.contrib if self.rows is None else self.rows, self.gather)
             if record:
                 self.reports.append(self.step_obj.ctrl_dict())
         self.torch.cuda.synchronize()
@@ -244,6 +272,35 @@ class GpuRun:
         torch = self.torch
         ix = torch.from_numpy(idx.astype(np.int64)).to(self.gather.device)
         return self.gather.index_select(0, ix).view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_and_compare(c: Case, label: str, full: bool = True, layout: str = "strided"):
+    """Runs case `c` on the GPU and checks every step's decisions and the final
+    master/m/v/slot of the whole shard against the oracle; with `full`, also
+    that the gather buffer is unchanged outside the slot."""
+    log(f"{label}: psi={c.w.psi} N={c.w.nranks} rank={c.rank} dtype={c.w.dtype} "
+        f"variant={c.w.variant} steps={c.steps} offset={c.part[1]} valid={c.part[2]} "
+        f"layout={layout}")
+    g = GpuRun(c, full_gather=full, layout=layout)
+    g.run()
+    ref_reps = oracle_scalars(c)
+    stats = assert_reports(g.reports, ref_reps)
+    p, m, v, slot = g.fetch()
+    rp, rm, rv, rslot = oracle_elements(c, ref_reps)
+    stats["master"] = assert_f32_close("master", p, rp)
+    stats["m"] = assert_f32_close("m", m, rm)
+    stats["v"] = assert_f32_close("v", v, rv)
+    stats["slot"] = assert_16bit_within_ulp("slot", slot, rslot, c.w.dtype)
+    if full:  # nothing outside the slot changed
+        w = c.w
+        _, off, valid = c.part
+        outside = np.r_[0:off, off + valid:w.psi]
+        if outside.size:
+            got = g.gather_bits(outside)
+            ref = synth.param_range(w.seed, w.master_sigma, w.dtype, 0, w.psi)[outside]
+            assert np.array_equal(got, ref), "gather buffer changed outside the slot"
+    log(f"{label}: ok {stats}")
+    return g, stats
 
 
 # ----------------------------------------------------------------------------- comparisons

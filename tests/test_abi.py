@@ -139,3 +139,38 @@ def test_binding_refuses_cpu_tensors(Z):
     import torch
     with pytest.raises(ValueError):
         Z.zero_cast_to_gather(torch.zeros(8), 8, torch.zeros(8, dtype=torch.int16), Z.F16, 0)
+
+
+def _rows_call(Z, fused, rows, n=None, dtype=1, valid=64, ctrl=FAKE, g=FAKE, wsb=1 << 16):
+    n = len(rows) if n is None else n
+    arr = (ctypes.c_void_p * max(len(rows), 1))(*rows) if rows is not None else None
+    if not fused:
+        return Z._lib.zero_reduce_grads_rows(arr, dtype, n, valid, ctrl, g, FAKE, wsb, None)
+    pair = Z.State(FAKE, FAKE + 65536, FAKE + 131072)
+    hp = Z.hparams()
+    return Z._lib.zero_fused_step_rows(arr, dtype, n, ctypes.byref(pair), valid, FAKE, 1, 0,
+                                       ctypes.byref(hp), ctrl, FAKE, wsb, None)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("rows,kw,code,msg", [
+    (None, dict(n=8), -1, "null row table"),
+    ([FAKE] * 8, dict(n=0), -1, "outside"),
+    ([FAKE] * 65, dict(), -1, "outside"),                   # more rows than a table holds
+    ([FAKE, FAKE, 0, FAKE], dict(), -1, "row 2 is null"),
+    ([FAKE, FAKE + 4], dict(), -2, "row 1 not 8-byte"),      # 4-byte aligned only
+    ([FAKE] * 4, dict(dtype=5), -1, "dtype"),
+    ([FAKE] * 4, dict(valid=-3), -3, "out of range"),
+    ([FAKE] * 4, dict(wsb=16), -4, "workspace"),
+    ([FAKE] * 4, dict(ctrl=0), -1, "ctrl"),
+])
+def test_row_table_validation(Z, fused, rows, kw, code, msg):
+    assert _rows_call(Z, fused, rows, **kw) == code
+    assert msg in Z.zero_last_error()
+
+
+def test_row_table_accepts_8_byte_aligned_rows(Z):
+    # 8-byte aligned rows (a peer slice at an odd multiple of 4 elements) pass
+    # every check; only a misaligned g then stops the call before any launch.
+    assert _rows_call(Z, False, [FAKE + 8, FAKE + 24, FAKE], g=FAKE + 4) == -2
+    assert "g not 16-byte" in Z.zero_last_error()

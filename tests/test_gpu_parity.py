@@ -34,29 +34,7 @@ def gpu():
 
 
 def run_case(c: Case, label: str, full: bool = True):
-    H.log(f"{label}: psi={c.w.psi} N={c.w.nranks} rank={c.rank} dtype={c.w.dtype} "
-          f"variant={c.w.variant} steps={c.steps} offset={c.part[1]} valid={c.part[2]}")
-    g = H.GpuRun(c, full_gather=full)
-    g.run()
-    ref_reps = H.oracle_scalars(c)
-    stats = H.assert_reports(g.reports, ref_reps)
-    p, m, v, slot = g.fetch()
-    rp, rm, rv, rslot = H.oracle_elements(c, ref_reps)
-    stats["master"] = H.assert_f32_close("master", p, rp)
-    stats["m"] = H.assert_f32_close("m", m, rm)
-    stats["v"] = H.assert_f32_close("v", v, rv)
-    stats["slot"] = H.assert_16bit_within_ulp("slot", slot, rslot, c.w.dtype)
-    if full:  # nothing outside the slot changed
-        import synth
-        w = c.w
-        _, off, valid = c.part
-        outside = np.r_[0:off, off + valid:w.psi]
-        if outside.size:
-            got = g.gather_bits(outside)
-            ref = synth.param_range(w.seed, w.master_sigma, w.dtype, 0, w.psi)[outside]
-            assert np.array_equal(got, ref), "gather buffer changed outside the slot"
-    H.log(f"{label}: ok {stats}")
-    return g, stats
+    return H.run_and_compare(c, label, full)
 
 
 def small(psi, n, rank, dtype=F16, steps=3, **kw):

@@ -69,6 +69,8 @@ _sig = {
     "zero_ctrl_init": (ctypes.c_int, [_vp, ctypes.c_float, _vp]),
     "zero_reduce_grads": (ctypes.c_int, [_vp, _i32, _i32, _i64, _i64, _vp, _vp, _vp,
                                          ctypes.c_size_t, _vp]),
+    "zero_reduce_grads_rows": (ctypes.c_int, [ctypes.POINTER(_vp), _i32, _i32, _i64, _vp, _vp,
+                                              _vp, ctypes.c_size_t, _vp]),
     "zero_grad_norm_overflow": (ctypes.c_int, [_i32, ctypes.POINTER(_vp), ctypes.POINTER(_i64),
                                                ctypes.POINTER(_vp), ctypes.POINTER(Hparams),
                                                _i32, _vp]),
@@ -78,6 +80,10 @@ _sig = {
     "zero_fused_step": (ctypes.c_int, [_vp, _i32, _i32, _i64, ctypes.POINTER(State), _i64, _vp,
                                        _i32, _i64, ctypes.POINTER(Hparams), _vp, _vp,
                                        ctypes.c_size_t, _vp]),
+    "zero_fused_step_rows": (ctypes.c_int, [ctypes.POINTER(_vp), _i32, _i32,
+                                            ctypes.POINTER(State), _i64, _vp, _i32, _i64,
+                                            ctypes.POINTER(Hparams), _vp, _vp, ctypes.c_size_t,
+                                            _vp]),
     "zero_fused_restore": (ctypes.c_int, [ctypes.POINTER(State), _i64, _vp, _i32, _i64, _vp,
                                           _vp]),
     "zero_pair_store": (ctypes.c_int, [ctypes.POINTER(State), ctypes.POINTER(State), _i64, _vp,
@@ -117,6 +123,18 @@ def _ptr(t) -> ctypes.c_void_p:
 def _stream():
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _rows(rows):
+    """Host array of row pointers: each entry a GPU tensor (its data pointer)
+    or an integer device address."""
+    ptrs = []
+    for r in rows:
+        if isinstance(r, int):
+            ptrs.append(r)
+        else:
+            ptrs.append(_ptr(r).value)
+    return (_vp * max(len(ptrs), 1))(*ptrs), len(ptrs)
 
 
 def _state(s) -> State:
@@ -161,6 +179,13 @@ def zero_reduce_grads(contrib, dtype: int, nranks: int, stride: int, valid_len: 
         ws.numel() * ws.element_size(), _stream()))
 
 
+def zero_reduce_grads_rows(rows, dtype: int, valid_len: int, ctrl, g, ws) -> None:
+    arr, n = _rows(rows)
+    _check("zero_reduce_grads_rows", _lib.zero_reduce_grads_rows(
+        arr, dtype, n, valid_len, _ptr(ctrl), _ptr(g), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream()))
+
+
 def zero_grad_norm_overflow(ws_list, valid_lens, ctrls, hp: Hparams, pingpong: bool) -> None:
     n = len(ctrls)
     ws_arr = (_vp * n)(*[t.data_ptr() if t is not None else None for t in ws_list])
@@ -191,6 +216,15 @@ def zero_fused_step(contrib, contrib_dtype: int, nranks: int, stride: int, pair,
         _ptr(contrib), contrib_dtype, nranks, stride, ctypes.byref(st), valid_len, _ptr(gather),
         gather_dtype, offset, ctypes.byref(hp), _ptr(ctrl), _ptr(ws),
         ws.numel() * ws.element_size(), _stream()))
+
+
+def zero_fused_step_rows(rows, contrib_dtype: int, pair, valid_len: int, gather,
+                         gather_dtype: int, offset: int, hp: Hparams, ctrl, ws) -> None:
+    arr, n = _rows(rows)
+    st = _state(pair)
+    _check("zero_fused_step_rows", _lib.zero_fused_step_rows(
+        arr, contrib_dtype, n, ctypes.byref(st), valid_len, _ptr(gather), gather_dtype, offset,
+        ctypes.byref(hp), _ptr(ctrl), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
 
 
 def zero_fused_restore(pair, valid_len: int, gather, dtype: int, offset: int, ctrl) -> None:
@@ -225,7 +259,8 @@ def read_ctrl(ctrl) -> dict:
 class ShardStep:
     """One rank's shard step over caller-provided device buffers.
 
-    contrib: [N, stride] 16-bit tensor; gather: the full 16-bit parameter
+    contrib: [N, stride] 16-bit tensor, or a list of N row tensors (or device
+    addresses) taken by the row-table calls; gather: the full 16-bit parameter
     buffer, this rank's slot at ``offset``.  ``state`` is the flat
     (master, m, v) fp32 state of valid_len elements.  The two-pass path
     (clipping on) updates it in place through ``g``; the fused path keeps
@@ -253,16 +288,27 @@ class ShardStep:
             zero_pair_store(state, self.pair, valid_len, self.ctrl)
 
     def step(self, contrib, gather) -> None:
+        table = isinstance(contrib, (list, tuple))
+        if table and len(contrib) != self.nranks:
+            raise ValueError(f"{len(contrib)} rows for {self.nranks} ranks")
         if self.fused:
-            zero_fused_step(contrib, self.dtype, self.nranks, self.stride, self.pair,
-                            self.valid_len, gather, self.gather_dtype, self.offset, self.hp,
-                            self.ctrl, self.ws)
+            if table:
+                zero_fused_step_rows(contrib, self.dtype, self.pair, self.valid_len, gather,
+                                     self.gather_dtype, self.offset, self.hp, self.ctrl, self.ws)
+            else:
+                zero_fused_step(contrib, self.dtype, self.nranks, self.stride, self.pair,
+                                self.valid_len, gather, self.gather_dtype, self.offset, self.hp,
+                                self.ctrl, self.ws)
             zero_grad_norm_overflow([self.ws], [self.valid_len], [self.ctrl], self.hp, True)
             zero_fused_restore(self.pair, self.valid_len, gather, self.gather_dtype, self.offset,
                                self.ctrl)
         else:
-            zero_reduce_grads(contrib, self.dtype, self.nranks, self.stride, self.valid_len,
-                              self.ctrl, self.g, self.ws)
+            if table:
+                zero_reduce_grads_rows(contrib, self.dtype, self.valid_len, self.ctrl, self.g,
+                                       self.ws)
+            else:
+                zero_reduce_grads(contrib, self.dtype, self.nranks, self.stride, self.valid_len,
+                                  self.ctrl, self.g, self.ws)
             zero_grad_norm_overflow([self.ws], [self.valid_len], [self.ctrl], self.hp, False)
             zero_adam_step(self.state, self.g, self.valid_len, self.hp, self.ctrl, gather,
                            self.gather_dtype, self.offset)

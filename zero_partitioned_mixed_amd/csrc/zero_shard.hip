@@ -129,6 +129,24 @@ __device__ __forceinline__ uint32_t narrow<ZERO_BF16>(float x) {
 }
 
 // ---------------------------------------------------------------- contribution rows
+// Where the N contribution rows of the shard live.  StridedRows: one
+// allocation, row k at base + k * stride.  TableRows: row k anywhere in
+// device-accessible memory (a local buffer, or a peer GPU's slice mapped into
+// this process), one pointer per row carried in the kernel arguments.  Both
+// are read-only and index elements of the shard from 0.
+struct StridedRows {
+    const uint16_t* base;
+    int64_t stride;
+    __device__ __forceinline__ const uint16_t* row(int k) const {
+        return base + (int64_t)k * stride;
+    }
+};
+
+struct TableRows {
+    const uint16_t* p[ZERO_MAX_RANKS];
+    __device__ __forceinline__ const uint16_t* row(int k) const { return p[k]; }
+};
+
 // One row's 8 values of the thread's group: 4 at run a, 4 at run b.
 struct Row {
     u32x2 a, b;
@@ -153,10 +171,10 @@ __device__ __forceinline__ void add_row(float acc[kVec], const Row& w) {
     acc[7] = acc[7] + widen_hi<DT>(w.b.y);
 }
 
-__device__ __forceinline__ void load_rows8(const uint16_t* __restrict__ C, int64_t stride, int k0,
-                                           const Runs& r, Row w[8]) {
+template <class RS>
+__device__ __forceinline__ void load_rows8(const RS& R, int k0, const Runs& r, Row w[8]) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) w[q] = load_row(C + (int64_t)(k0 + q) * stride, r);
+    for (int q = 0; q < 8; ++q) w[q] = load_row(R.row(k0 + q), r);
 }
 
 template <int DT>
@@ -176,15 +194,13 @@ struct RowLoads {
     Row w[8];
 };
 
-template <int NR>
-__device__ __forceinline__ void sum_rows_issue(const uint16_t* __restrict__ C, int n,
-                                               int64_t stride, const Runs& r, RowLoads& L) {
-    if (NR == 8 || n >= 8) load_rows8(C, stride, 0, r, L.w);
+template <int NR, class RS>
+__device__ __forceinline__ void sum_rows_issue(const RS& R, int n, const Runs& r, RowLoads& L) {
+    if (NR == 8 || n >= 8) load_rows8(R, 0, r, L.w);
 }
 
-template <int DT, int NR>
-__device__ __forceinline__ void sum_rows_finish(const uint16_t* __restrict__ C, int n,
-                                                int64_t stride, const Runs& r, RowLoads& L,
+template <int DT, int NR, class RS>
+__device__ __forceinline__ void sum_rows_finish(const RS& R, int n, const Runs& r, RowLoads& L,
                                                 float acc[kVec]) {
 #pragma unroll
     for (int j = 0; j < kVec; ++j) acc[j] = 0.0f;
@@ -196,19 +212,19 @@ __device__ __forceinline__ void sum_rows_finish(const uint16_t* __restrict__ C, 
     if (n >= 8) {
         add_rows8<DT>(acc, L.w);
         for (k = 8; k + 8 <= n; k += 8) {
-            load_rows8(C, stride, k, r, L.w);
+            load_rows8(R, k, r, L.w);
             __builtin_amdgcn_sched_barrier(0);
             add_rows8<DT>(acc, L.w);
         }
     }
-    for (; k < n; ++k) add_row<DT>(acc, load_row(C + (int64_t)k * stride, r));
+    for (; k < n; ++k) add_row<DT>(acc, load_row(R.row(k), r));
 }
 
-// Scalar row sum of one element (partial tiles).
-template <int DT>
-__device__ __forceinline__ float sum_rows1(const uint16_t* __restrict__ p, int n, int64_t stride) {
+// Scalar row sum of element i (partial tiles).
+template <int DT, class RS>
+__device__ __forceinline__ float sum_rows1(const RS& R, int n, int64_t i) {
     float acc = 0.0f;
-    for (int k = 0; k < n; ++k) acc = acc + widen1<DT>(p[(int64_t)k * stride]);
+    for (int k = 0; k < n; ++k) acc = acc + widen1<DT>(R.row(k)[i]);
     return acc;
 }
 
@@ -349,9 +365,9 @@ __global__ void ctrl_init_kernel(InitArgs a) {
     }
 }
 
+template <class RS>
 struct ReduceArgs {
-    const uint16_t* contrib;
-    int64_t stride;
+    RS rows;
     int64_t len;
     const zero_ctrl* ctrl;
     float* g;
@@ -361,8 +377,8 @@ struct ReduceArgs {
 
 // Pass 1 of the two-pass step: g = fl32(sum_k C[k]) * inv, plus one partial
 // per tile.
-template <int DT, int NR>
-__global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
+template <int DT, int NR, class RS>
+__global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs<RS> a) {
     const float inv = (float)(1.0 / ((double)a.n * (double)a.ctrl->loss_scale));
     double ss = 0.0;
     uint32_t bad = 0;
@@ -370,9 +386,9 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
     if (r.b + kRun <= a.len) {
         float acc[kVec], out[kVec];
         RowLoads L;
-        sum_rows_issue<NR>(a.contrib, a.n, a.stride, r, L);
+        sum_rows_issue<NR>(a.rows, a.n, r, L);
         __builtin_amdgcn_sched_barrier(0);
-        sum_rows_finish<DT, NR>(a.contrib, a.n, a.stride, r, L, acc);
+        sum_rows_finish<DT, NR>(a.rows, a.n, r, L, acc);
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             bad |= __builtin_isfinite(acc[j]) ? 0u : 1u;
@@ -385,7 +401,7 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
         for (int j = 0; j < kVec; ++j) {
             const int64_t i = elem(r, j);
             if (i >= a.len) continue;
-            const float acc = sum_rows1<DT>(a.contrib + i, a.n, a.stride);
+            const float acc = sum_rows1<DT>(a.rows, a.n, i);
             bad |= __builtin_isfinite(acc) ? 0u : 1u;
             const float gj = acc * inv;
             ss += (double)gj * (double)gj;
@@ -620,9 +636,9 @@ __global__ void __launch_bounds__(kBlock) pack_kernel(PackArgs a) {
     }
 }
 
+template <class RS>
 struct FusedArgs {
-    const uint16_t* contrib;
-    int64_t stride;
+    RS rows;
     float* pair[3];  // master, m, v in the paired layout
     uint16_t* slot;
     int64_t len;
@@ -634,8 +650,8 @@ struct FusedArgs {
 
 // Single pass: reduce + partial + Adam (read set cur, write set 1-cur of the
 // tile) + cast, one tile per workgroup.
-template <int DTI, int DTO, int GW, int NR>
-__global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
+template <int DTI, int DTO, int GW, int NR, class RS>
+__global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs<RS> a) {
     const zero_ctrl* __restrict__ c = a.ctrl;
     const int cur = c->cur;
     const float inv = (float)(1.0 / ((double)a.n * (double)c->loss_scale));
@@ -652,12 +668,12 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
         float acc[kVec], p[kVec], m[kVec], v[kVec];
         uint32_t h[kVec];
         RowLoads L;
-        sum_rows_issue<NR>(a.contrib, a.n, a.stride, r, L);
+        sum_rows_issue<NR>(a.rows, a.n, r, L);
         load8(a.pair[0] + sa, a.pair[0] + sb, p);
         load8(a.pair[1] + sa, a.pair[1] + sb, m);
         load8(a.pair[2] + sa, a.pair[2] + sb, v);
         __builtin_amdgcn_sched_barrier(0);  // every load of the group is in flight first
-        sum_rows_finish<DTI, NR>(a.contrib, a.n, a.stride, r, L, acc);
+        sum_rows_finish<DTI, NR>(a.rows, a.n, r, L, acc);
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             bad |= __builtin_isfinite(acc[j]) ? 0u : 1u;
@@ -674,7 +690,7 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
         for (int j = 0; j < kVec; ++j) {
             const int64_t i = elem(r, j);
             if (i >= a.len) continue;
-            const float acc = sum_rows1<DTI>(a.contrib + i, a.n, a.stride);
+            const float acc = sum_rows1<DTI>(a.rows, a.n, i);
             bad |= __builtin_isfinite(acc) ? 0u : 1u;
             const float gj = acc * inv;
             ss += (double)gj * (double)gj;
@@ -753,6 +769,26 @@ int check_contrib(const void* contrib, int32_t dtype, int32_t n, int64_t stride,
     return ZERO_OK;
 }
 
+// Row table: nranks in [1, ZERO_MAX_RANKS] pointers, each non-null and
+// 8-byte aligned (the widest contribution access is four 16-bit values).
+int check_rows(const void* const* rows, int32_t dtype, int32_t n, int64_t len, TableRows* out,
+               const char* what) {
+    int rc;
+    if ((rc = check_len(len, what)) != ZERO_OK) return rc;
+    if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, "%s: unknown contribution dtype %d", what, dtype);
+    if (n < 1 || n > ZERO_MAX_RANKS)
+        return fail(ZERO_EINVAL, "%s: nranks %d outside [1, %d]", what, n, ZERO_MAX_RANKS);
+    if (rows == nullptr) return fail(ZERO_EINVAL, "%s: null row table", what);
+    for (int k = 0; k < ZERO_MAX_RANKS; ++k) out->p[k] = nullptr;
+    for (int k = 0; k < n; ++k) {
+        if (rows[k] == nullptr) return fail(ZERO_EINVAL, "%s: row %d is null", what, k);
+        if ((reinterpret_cast<uintptr_t>(rows[k]) & 7u) != 0)
+            return fail(ZERO_EALIGN, "%s: row %d not 8-byte aligned", what, k);
+        out->p[k] = (const uint16_t*)rows[k];
+    }
+    return ZERO_OK;
+}
+
 int check_state(const zero_state* s, const char* what) {
     if (s == nullptr || s->master == nullptr || s->m == nullptr || s->v == nullptr)
         return fail(ZERO_EINVAL, "%s: null state pointer", what);
@@ -792,17 +828,23 @@ int check_ctrl(const zero_ctrl* c, const char* what) {
 template <class Args>
 using Kernel = void (*)(Args);
 
-template <int GW, int NR>
-Kernel<FusedArgs> fused_for_nr(int dti, int dto) {
-    if (dti == ZERO_F16 && dto == ZERO_F16) return fused_kernel<ZERO_F16, ZERO_F16, GW, NR>;
-    if (dti == ZERO_F16 && dto == ZERO_BF16) return fused_kernel<ZERO_F16, ZERO_BF16, GW, NR>;
-    if (dti == ZERO_BF16 && dto == ZERO_F16) return fused_kernel<ZERO_BF16, ZERO_F16, GW, NR>;
-    return fused_kernel<ZERO_BF16, ZERO_BF16, GW, NR>;
+template <int GW, int NR, class RS>
+Kernel<FusedArgs<RS>> fused_for_nr(int dti, int dto) {
+    if (dti == ZERO_F16 && dto == ZERO_F16) return fused_kernel<ZERO_F16, ZERO_F16, GW, NR, RS>;
+    if (dti == ZERO_F16 && dto == ZERO_BF16) return fused_kernel<ZERO_F16, ZERO_BF16, GW, NR, RS>;
+    if (dti == ZERO_BF16 && dto == ZERO_F16) return fused_kernel<ZERO_BF16, ZERO_F16, GW, NR, RS>;
+    return fused_kernel<ZERO_BF16, ZERO_BF16, GW, NR, RS>;
 }
 
-template <int GW>
-Kernel<FusedArgs> fused_for(int dti, int dto, int n) {
-    return n == 8 ? fused_for_nr<GW, 8>(dti, dto) : fused_for_nr<GW, 0>(dti, dto);
+template <int GW, class RS>
+Kernel<FusedArgs<RS>> fused_for(int dti, int dto, int n) {
+    return n == 8 ? fused_for_nr<GW, 8, RS>(dti, dto) : fused_for_nr<GW, 0, RS>(dti, dto);
+}
+
+template <class RS>
+Kernel<ReduceArgs<RS>> reduce_for(int dt, int n) {
+    if (n == 8) return dt == ZERO_F16 ? reduce_kernel<ZERO_F16, 8, RS> : reduce_kernel<ZERO_BF16, 8, RS>;
+    return dt == ZERO_F16 ? reduce_kernel<ZERO_F16, 0, RS> : reduce_kernel<ZERO_BF16, 0, RS>;
 }
 
 template <int DT>
@@ -837,6 +879,33 @@ int launch(Kernel<Args> kernel, int64_t grid, int block, hipStream_t s, const Ar
     const hipError_t e2 = hipGetLastError();
     if (e2 != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e2));
     return ok();
+}
+
+// Checks and launches shared by the two fused entry points (the rows are
+// already checked).
+template <class RS>
+int fused_launch(const RS& rows, int32_t contrib_dtype, int32_t nranks, const zero_state* pair,
+                 int64_t valid_len, void* gather, int32_t gather_dtype, int64_t offset,
+                 const zero_hparams* hp, const zero_ctrl* ctrl, void* ws, size_t ws_bytes,
+                 void* stream, const char* what) {
+    int rc;
+    if ((rc = check_state(pair, what)) != ZERO_OK) return rc;
+    if ((rc = check_hp(hp)) != ZERO_OK) return rc;
+    if (hp->max_grad_norm > 0.0f) return fail(ZERO_EINVAL, "%s: clipping needs the two-pass path", what);
+    if ((rc = check_ctrl(ctrl, what)) != ZERO_OK) return rc;
+    if ((rc = check_slot(gather, gather_dtype, offset)) != ZERO_OK) return rc;
+    if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
+    if (valid_len == 0) return ok();
+    uint16_t* slot = (uint16_t*)gather + offset;
+    const FusedArgs<RS> a{rows, {pair->master, pair->m, pair->v}, slot, valid_len, ctrl,
+                          (Partial*)ws, *hp, nranks};
+    Kernel<FusedArgs<RS>> k;
+    switch (store_width(slot)) {
+        case 4: k = fused_for<4, RS>(contrib_dtype, gather_dtype, nranks); break;
+        case 2: k = fused_for<2, RS>(contrib_dtype, gather_dtype, nranks); break;
+        default: k = fused_for<1, RS>(contrib_dtype, gather_dtype, nranks); break;
+    }
+    return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, what);
 }
 
 }  // namespace
@@ -889,13 +958,31 @@ int zero_reduce_grads(const void* contrib, int32_t dtype, int32_t nranks, int64_
     if (!aligned16(g)) return fail(ZERO_EALIGN, "zero_reduce_grads: g not 16-byte aligned");
     if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
     if (valid_len == 0) return ok();
-    ReduceArgs a{(const uint16_t*)contrib, stride, valid_len, ctrl, g, (Partial*)ws, nranks};
-    Kernel<ReduceArgs> k;
-    if (nranks == 8)
-        k = dtype == ZERO_F16 ? reduce_kernel<ZERO_F16, 8> : reduce_kernel<ZERO_BF16, 8>;
-    else
-        k = dtype == ZERO_F16 ? reduce_kernel<ZERO_F16, 0> : reduce_kernel<ZERO_BF16, 0>;
-    return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, "zero_reduce_grads");
+    const ReduceArgs<StridedRows> a{{(const uint16_t*)contrib, stride}, valid_len, ctrl, g,
+                                    (Partial*)ws, nranks};
+    return launch(reduce_for<StridedRows>(dtype, nranks), tiles_for(valid_len), kBlock,
+                  (hipStream_t)stream, a, "zero_reduce_grads");
+}
+
+int zero_reduce_grads_rows(const void* const* rows, int32_t dtype, int32_t nranks,
+                           int64_t valid_len, const zero_ctrl* ctrl, float* g, void* ws,
+                           size_t ws_bytes, void* stream) {
+    int rc;
+    ReduceArgs<TableRows> a{};
+    if ((rc = check_rows(rows, dtype, nranks, valid_len, &a.rows, "zero_reduce_grads_rows")) != ZERO_OK)
+        return rc;
+    if ((rc = check_ctrl(ctrl, "zero_reduce_grads_rows")) != ZERO_OK) return rc;
+    if (g == nullptr) return fail(ZERO_EINVAL, "zero_reduce_grads_rows: null g");
+    if (!aligned16(g)) return fail(ZERO_EALIGN, "zero_reduce_grads_rows: g not 16-byte aligned");
+    if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
+    if (valid_len == 0) return ok();
+    a.len = valid_len;
+    a.ctrl = ctrl;
+    a.g = g;
+    a.ws = (Partial*)ws;
+    a.n = nranks;
+    return launch(reduce_for<TableRows>(dtype, nranks), tiles_for(valid_len), kBlock,
+                  (hipStream_t)stream, a, "zero_reduce_grads_rows");
 }
 
 int zero_grad_norm_overflow(int32_t nranks, void* const* ws, const int64_t* valid_len,
@@ -976,24 +1063,21 @@ int zero_fused_step(const void* contrib, int32_t contrib_dtype, int32_t nranks, 
                     size_t ws_bytes, void* stream) {
     int rc;
     if ((rc = check_contrib(contrib, contrib_dtype, nranks, stride, valid_len)) != ZERO_OK) return rc;
-    if ((rc = check_state(pair, "zero_fused_step")) != ZERO_OK) return rc;
-    if ((rc = check_hp(hp)) != ZERO_OK) return rc;
-    if (hp->max_grad_norm > 0.0f)
-        return fail(ZERO_EINVAL, "zero_fused_step: clipping needs the two-pass path");
-    if ((rc = check_ctrl(ctrl, "zero_fused_step")) != ZERO_OK) return rc;
-    if ((rc = check_slot(gather, gather_dtype, offset)) != ZERO_OK) return rc;
-    if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
-    if (valid_len == 0) return ok();
-    uint16_t* slot = (uint16_t*)gather + offset;
-    FusedArgs a{(const uint16_t*)contrib, stride, {pair->master, pair->m, pair->v}, slot,
-                valid_len, ctrl, (Partial*)ws, *hp, nranks};
-    Kernel<FusedArgs> k;
-    switch (store_width(slot)) {
-        case 4: k = fused_for<4>(contrib_dtype, gather_dtype, nranks); break;
-        case 2: k = fused_for<2>(contrib_dtype, gather_dtype, nranks); break;
-        default: k = fused_for<1>(contrib_dtype, gather_dtype, nranks); break;
-    }
-    return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, "zero_fused_step");
+    return fused_launch(StridedRows{(const uint16_t*)contrib, stride}, contrib_dtype, nranks, pair,
+                        valid_len, gather, gather_dtype, offset, hp, ctrl, ws, ws_bytes, stream,
+                        "zero_fused_step");
+}
+
+int zero_fused_step_rows(const void* const* rows, int32_t contrib_dtype, int32_t nranks,
+                         const zero_state* pair, int64_t valid_len, void* gather,
+                         int32_t gather_dtype, int64_t offset, const zero_hparams* hp,
+                         const zero_ctrl* ctrl, void* ws, size_t ws_bytes, void* stream) {
+    int rc;
+    TableRows t;
+    if ((rc = check_rows(rows, contrib_dtype, nranks, valid_len, &t, "zero_fused_step_rows")) != ZERO_OK)
+        return rc;
+    return fused_launch(t, contrib_dtype, nranks, pair, valid_len, gather, gather_dtype, offset,
+                        hp, ctrl, ws, ws_bytes, stream, "zero_fused_step_rows");
 }
 
 int zero_fused_restore(const zero_state* pair, int64_t valid_len, void* gather, int32_t dtype,
