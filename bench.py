@@ -334,6 +334,10 @@ def main():
         red_avg = sum(red_ms) / len(red_ms)
         out["reduce_kernel"] = {"ms": _fmt(red_avg, 5),
                                 "gbps": _fmt((2 * w.nranks + 4) * valid / (red_avg * 1e-3) / 1e9, 5)}
+    try:
+        out["device"] = synth.gpu_device_info(0)
+    except (RuntimeError, OSError, AttributeError) as e:  # informational only
+        out["device"] = {"error": str(e)}
     if not args.no_copy:
         cg, _ = copy_bandwidth(torch, synth)
         out["copy_gbps"] = _fmt(cg, 5)

@@ -116,6 +116,15 @@ def lib():
                                   ctypes.POINTER(Hparams), ctypes.c_float, ctypes.c_double,
                                   ctypes.c_double]
         L.oracle_cast.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int32, _u16p]
+        _u8p = ctypes.POINTER(ctypes.c_uint8)
+        L.oracle_qblock.restype = ctypes.c_int64
+        L.oracle_qblock.argtypes = []
+        L.oracle_quantize.argtypes = [_u16p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _u8p,
+                                      _f32p, _i32p]
+        L.oracle_dequantize.argtypes = [_u8p, _f32p, _i32p, ctypes.c_int32, ctypes.c_int64, _f32p]
+        L.oracle_reduce_q.argtypes = [ctypes.POINTER(_u8p), ctypes.POINTER(_f32p),
+                                      ctypes.POINTER(_i32p), ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int64, ctypes.c_float, _f32p, _i32p]
         _lib = L
     return _lib
 
@@ -236,6 +245,69 @@ def cast(p: np.ndarray, dtype: int) -> np.ndarray:
     out = np.empty(p.size, np.uint16)
     lib().oracle_cast(_p(p, _f32p), p.size, dtype, _p(out, _u16p))
     return out
+
+
+# --------------------------------------------------------------------------- block quantisation
+QBLOCK = 2048  # the reading's block size; the library reports its own in qblock()
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+
+
+def qblock() -> int:
+    """Elements per quantisation block, as the oracle library defines it."""
+    return int(lib().oracle_qblock())
+
+
+@dataclass
+class QBuffer:
+    """A block-quantised buffer: packed codes, one (scale, zero) per block."""
+    codes: np.ndarray   # uint8: len bytes (8 bits) or ceil(len/2) (4 bits)
+    scale: np.ndarray   # float32, one per 2048-element block
+    zero: np.ndarray    # int32, one per block
+    bits: int
+    length: int
+
+
+def qcode_bytes(length: int, bits: int) -> int:
+    return length if bits == 8 else (length + 1) // 2
+
+
+def quantize(src: np.ndarray, dtype: int, bits: int) -> QBuffer:
+    """Block-quantise 16-bit patterns ``src`` to INT8 or INT4 codes."""
+    assert bits in (4, 8)
+    src = _need(np.ascontiguousarray(src), np.uint16)
+    n = src.size
+    nblk = (n + qblock() - 1) // qblock()
+    codes = np.zeros(max(qcode_bytes(n, bits), 1), np.uint8)
+    scale = np.zeros(max(nblk, 1), np.float32)
+    zero = np.zeros(max(nblk, 1), np.int32)
+    lib().oracle_quantize(_p(src, _u16p), dtype, n, bits, _p(codes, _u8p), _p(scale, _f32p),
+                          _p(zero, _i32p))
+    return QBuffer(codes[:qcode_bytes(n, bits)], scale[:nblk], zero[:nblk], bits, n)
+
+
+def dequantize(q: QBuffer) -> np.ndarray:
+    """fp32 values S_b * (q_i - Z_b) of a quantised buffer."""
+    out = np.empty(q.length, np.float32)
+    codes = np.ascontiguousarray(q.codes) if q.codes.size else np.zeros(1, np.uint8)
+    lib().oracle_dequantize(_p(codes, _u8p), _p(q.scale, _f32p), _p(q.zero, _i32p), q.bits,
+                            q.length, _p(out, _f32p))
+    return out
+
+
+def reduce_q(rows: list, valid: int, inv: float) -> tuple[np.ndarray, int]:
+    """The reduce over N quantised contribution rows (each a QBuffer of at
+    least ``valid`` elements, same bits)."""
+    n = len(rows)
+    bits = rows[0].bits
+    keep = [(np.ascontiguousarray(r.codes), np.ascontiguousarray(r.scale),
+             np.ascontiguousarray(r.zero)) for r in rows]
+    cp = (_u8p * n)(*[_p(c, _u8p) for c, _, _ in keep])
+    sp = (_f32p * n)(*[_p(sc, _f32p) for _, sc, _ in keep])
+    zp = (_i32p * n)(*[_p(z, _i32p) for _, _, z in keep])
+    g = np.empty(valid, np.float32)
+    flag = ctypes.c_int32()
+    lib().oracle_reduce_q(cp, sp, zp, bits, n, valid, inv, _p(g, _f32p), ctypes.byref(flag))
+    return g, int(flag.value)
 
 
 # --------------------------------------------------------------------------- one full step

@@ -347,3 +347,105 @@ void oracle_adam(float *p, float *m, float *v, const float *g, int64_t len,
 void oracle_cast(const float *p, int64_t len, int32_t dtype, uint16_t *out) {
     for (int64_t i = 0; i < len; ++i) out[i] = oracle_from_f32(p[i], dtype);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Block quantisation (ZeRO++).  [cmu] "Other memory optimizations" names     */
+/* ZeRO++'s quantised communication: parameters block-wise from 16 bits to    */
+/* INT8 with a zero point for the forward all-gather, and the gradient         */
+/* reduce-scatter in INT8 or INT4.  The page fixes neither block size nor      */
+/* rounding; the reading taken here:                                          */
+/*   blocks of ORACLE_QBLOCK = 2048 consecutive elements from the start of    */
+/*   the buffer (the last one may be short); Q = 2^bits - 1;                   */
+/*   a block holding a non-finite value gets scale NaN, zero 0, codes 0, so   */
+/*   every element of it dequantises to NaN and an overflow check downstream  */
+/*   still fires;                                                             */
+/*   otherwise, the affine (zero-point) mapping whose range contains 0:       */
+/*     lo = min(0, min x), hi = max(0, max x)           (exact)               */
+/*     S  = (hi - lo) / Q, replaced by 1 when it is 0   (fp32, rounded)       */
+/*     Z  = clamp(rint(-lo / S), 0, Q)                  (integer)             */
+/*     q  = clamp(rint(x / S) + Z, 0, Q)                (integer)             */
+/*     x' = S * (q - Z)                                 (fp32, rounded once)  */
+/*   a block whose S overflows counts as non-finite;                           */
+/*   rint rounds half to even; INT4 codes are packed two to a byte, the       */
+/*   element with the even index in the low nibble.                            */
+/* Real zero maps to Z and back to exactly 0; |x - x'| <= S/2 up to the two   */
+/* fp32 roundings.                                                            */
+/* ------------------------------------------------------------------------ */
+#define ORACLE_QBLOCK 2048
+
+int64_t oracle_qblock(void) { return ORACLE_QBLOCK; }
+
+static float q_clamp_code(float r, float qmax) { return r < 0.0f ? 0.0f : (r > qmax ? qmax : r); }
+
+void oracle_quantize(const uint16_t *src, int32_t dtype, int64_t len, int32_t bits, uint8_t *codes,
+                     float *scale, int32_t *zero) {
+    const float qmax = (float)((1 << bits) - 1);
+    const int64_t nblk = (len + ORACLE_QBLOCK - 1) / ORACLE_QBLOCK;
+    const int64_t ncode_bytes = bits == 8 ? len : (len + 1) / 2;
+    for (int64_t i = 0; i < ncode_bytes; ++i) codes[i] = 0;
+    for (int64_t b = 0; b < nblk; ++b) {
+        const int64_t i0 = b * ORACLE_QBLOCK;
+        const int64_t i1 = i0 + ORACLE_QBLOCK < len ? i0 + ORACLE_QBLOCK : len;
+        float lo = 0.0f, hi = 0.0f;
+        int finite = 1;
+        for (int64_t i = i0; i < i1; ++i) {
+            const float x = oracle_to_f32(src[i], dtype);
+            if (!isfinite(x)) finite = 0;
+            else {
+                if (x < lo) lo = x;
+                if (x > hi) hi = x;
+            }
+        }
+        float s = (hi - lo) / qmax;
+        if (finite && !isfinite(s)) finite = 0;
+        if (!finite) {
+            scale[b] = NAN;
+            zero[b] = 0;
+            continue;  /* codes stay 0 */
+        }
+        if (s == 0.0f) s = 1.0f;
+        const float z = q_clamp_code(rintf(-lo / s), qmax);
+        scale[b] = s;
+        zero[b] = (int32_t)z;
+        for (int64_t i = i0; i < i1; ++i) {
+            const float x = oracle_to_f32(src[i], dtype);
+            const uint8_t q = (uint8_t)q_clamp_code(rintf(x / s) + z, qmax);
+            if (bits == 8) codes[i] = q;
+            else codes[i / 2] = (uint8_t)(codes[i / 2] | (q << (4 * (i % 2))));
+        }
+    }
+}
+
+/* Code of element i of a quantised buffer. */
+static int32_t q_code(const uint8_t *codes, int32_t bits, int64_t i) {
+    if (bits == 8) return codes[i];
+    return (codes[i / 2] >> (4 * (i % 2))) & 15;
+}
+
+/* x'_i = S_b * (q_i - Z_b), b = i / 2048, in fp32. */
+void oracle_dequantize(const uint8_t *codes, const float *scale, const int32_t *zero, int32_t bits,
+                       int64_t len, float *out) {
+    for (int64_t i = 0; i < len; ++i) {
+        const int64_t b = i / ORACLE_QBLOCK;
+        out[i] = scale[b] * (float)(q_code(codes, bits, i) - zero[b]);
+    }
+}
+
+/* The reduce of Reduce above over quantised contributions: row k is given as */
+/* codes[k] with per-block scale[k] and zero[k]; each value is dequantised    */
+/* as in oracle_dequantize, then summed in fp32 in rank order; the overflow   */
+/* test and the multiplication by inv are unchanged.                          */
+void oracle_reduce_q(const uint8_t *const *codes, const float *const *scale,
+                     const int32_t *const *zero, int32_t bits, int32_t n, int64_t len, float inv,
+                     float *g, int32_t *nonfinite) {
+    int32_t flag = 0;
+    for (int64_t i = 0; i < len; ++i) {
+        const int64_t b = i / ORACLE_QBLOCK;
+        float acc = 0.0f;
+        for (int32_t k = 0; k < n; ++k)
+            acc = acc + scale[k][b] * (float)(q_code(codes[k], bits, i) - zero[k][b]);
+        if (!isfinite(acc)) flag = 1;
+        g[i] = acc * inv;
+    }
+    *nonfinite = flag;
+}

@@ -152,8 +152,10 @@ def gpu():
         L.synth_gpu_master_range.argtypes = [u64, f64, i64, i64, vp, vp]
         L.synth_gpu_param_range.argtypes = [u64, f64, i32, i64, i64, vp, vp]
         L.synth_gpu_copy.argtypes = [vp, vp, i64, i32, vp]
+        pi = ctypes.POINTER(i32)
+        L.synth_gpu_device_info.argtypes = [i32, pi, pi, pi, pi]
         for f in (L.synth_gpu_contrib_rows, L.synth_gpu_master_range, L.synth_gpu_param_range,
-                  L.synth_gpu_copy):
+                  L.synth_gpu_copy, L.synth_gpu_device_info):
             f.restype = ctypes.c_int
         _gpu = L
     return _gpu
@@ -197,3 +199,13 @@ def gpu_param_range(out, seed, sigma, dtype, idx0) -> None:
 def gpu_copy(src, dst, nbytes: int, grid: int = 0) -> None:
     _check(gpu().synth_gpu_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
                                 nbytes, grid, _stream()), "synth_gpu_copy")
+
+
+def gpu_device_info(device: int = 0) -> dict:
+    """Peak memory clock, bus width, CU count and shader clock of a device, and
+    the HBM peak they imply (double data rate: 2 transfers per clock)."""
+    v = [ctypes.c_int32() for _ in range(4)]
+    _check(gpu().synth_gpu_device_info(device, *[ctypes.byref(x) for x in v]), "device_info")
+    mem_khz, bus, cus, clk = (x.value for x in v)
+    return {"mem_clock_mhz": mem_khz / 1e3, "bus_bits": bus, "cus": cus, "clock_mhz": clk / 1e3,
+            "hbm_peak_gbps_from_props": round(2 * mem_khz * 1e3 * bus / 8 / 1e9, 1)}

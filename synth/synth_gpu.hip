@@ -132,4 +132,19 @@ int synth_gpu_copy(const void* src, void* dst, int64_t bytes, int32_t grid, void
     return status(hipGetLastError());
 }
 
+// Device facts for the benchmark's peak figures: peak memory clock (kHz),
+// memory bus width (bits), compute units and peak shader clock (kHz).
+int synth_gpu_device_info(int32_t device, int32_t* mem_clock_khz, int32_t* bus_bits, int32_t* cus,
+                          int32_t* clock_khz) {
+    if (!mem_clock_khz || !bus_bits || !cus || !clock_khz) return -1;
+    hipError_t e;
+    if ((e = hipDeviceGetAttribute(mem_clock_khz, hipDeviceAttributeMemoryClockRate, device)) != hipSuccess)
+        return status(e);
+    if ((e = hipDeviceGetAttribute(bus_bits, hipDeviceAttributeMemoryBusWidth, device)) != hipSuccess)
+        return status(e);
+    if ((e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, device)) != hipSuccess)
+        return status(e);
+    return status(hipDeviceGetAttribute(clock_khz, hipDeviceAttributeClockRate, device));
+}
+
 }  // extern "C"

@@ -19,6 +19,7 @@ PART = "tests/test_oracle_partition_bytes.py"
 INV = "tests/test_oracle_invariant.py"
 FMT = "tests/test_oracle_formats.py::test_round_trip_and_boundaries"
 FMT_ALL = "tests/test_oracle_formats.py::test_f16_to_f32_all_patterns"
+QUANT = "tests/test_oracle_quant.py"
 
 # (original text, planted mistake, pin files that must catch it)
 MUTANTS = {
@@ -58,6 +59,25 @@ MUTANTS = {
     "skip_ignores_overflow": ("rep->skip = rep->nonfinite;", "rep->skip = 0;", [ADAM]),
     "growth_without_reset": ("st->scale = st->scale * 2.0f;\n                st->good = 0;",
                              "st->scale = st->scale * 2.0f;", [ADAM]),
+    "quant_no_zero_point": ("const float z = q_clamp_code(rintf(-lo / s), qmax);",
+                            "const float z = 0.0f;", [QUANT]),
+    "quant_truncates": ("q_clamp_code(rintf(x / s) + z, qmax)", "q_clamp_code(truncf(x / s) + z, qmax)",
+                        [QUANT]),
+    "quant_round_half_away": ("q_clamp_code(rintf(x / s) + z, qmax)",
+                              "q_clamp_code(roundf(x / s) + z, qmax)", [QUANT]),
+    "quant_levels_off_by_one": ("const float qmax = (float)((1 << bits) - 1);",
+                                "const float qmax = (float)(1 << bits);", [QUANT]),
+    "quant_range_without_zero": ("float lo = 0.0f, hi = 0.0f;",
+                                 "float lo = 3.0e38f, hi = -3.0e38f;", [QUANT]),
+    "quant_nibble_order": ("(q << (4 * (i % 2)))", "(q << (4 * (1 - i % 2)))", [QUANT]),
+    "quant_nan_ignored": ("if (!isfinite(x)) finite = 0;", "if (isinf(x)) finite = 0;", [QUANT]),
+    "quant_block_size": ("#define ORACLE_QBLOCK 2048", "#define ORACLE_QBLOCK 1024", [QUANT]),
+    "dequant_sign_of_zero_point": ("out[i] = scale[b] * (float)(q_code(codes, bits, i) - zero[b]);",
+                                   "out[i] = scale[b] * (float)(q_code(codes, bits, i) + zero[b]);",
+                                   [QUANT]),
+    "reduce_q_reverse_order": ("for (int32_t k = 0; k < n; ++k)\n            acc = acc + scale[k][b]",
+                               "for (int32_t k = n - 1; k >= 0; --k)\n            acc = acc + scale[k][b]",
+                               [QUANT]),
 }
 
 

@@ -1,0 +1,196 @@
+"""Pins of the oracle's block quantisation (ZeRO++ quantised communication,
+"CMU 11-868 L18", Other memory optimizations: parameters quantised block-wise
+from 16 bits to INT8 with a zero point, gradients to INT8 or INT4).
+
+The page gives neither block size nor rounding; the oracle's reading is the
+affine zero-point map over 2048-element blocks whose range contains 0, with
+round-half-even.  What is pinned here is fixed by that definition and by
+arithmetic, not by retyping it: hand-worked examples, the error bound of
+rounding to a grid, exact zero, the end points of the range, monotonicity,
+exactness on grid values, block independence and size, non-finite blocks,
+and the quantised reduce against the plain reduce on exactly representable
+rows (including an order-sensitive case).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+
+F16, BF16 = 1, 2
+
+
+def bits16(x, dtype):
+    return O.from_f32(np.asarray(x, np.float32), dtype)
+
+
+def values(src, dtype):
+    return O.to_f32(src, dtype)
+
+
+def test_int4_worked_example():
+    # 0, 0.5, ..., 7.5: lo = 0, hi = 7.5, S = 7.5 / 15 = 0.5 exactly, Z = 0,
+    # codes 0..15; element 2j in the low nibble of byte j.
+    x = np.arange(16, dtype=np.float32) * 0.5
+    q = O.quantize(bits16(x, F16), F16, 4)
+    assert q.codes.tolist() == [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]
+    assert q.scale.tolist() == [0.5] and q.zero.tolist() == [0]
+    assert np.array_equal(O.dequantize(q), x)
+
+
+def test_int8_worked_example():
+    # -1, 0, 0.5, 2: S = fl(3/255); -lo/S = 85.000... -> Z = 85; 0.5/S = 42.5 (to
+    # within rounding) -> 42 (half to even) + 85 = 127; 2/S = 170 -> 255.
+    q = O.quantize(bits16([-1.0, 0.0, 0.5, 2.0], F16), F16, 8)
+    assert q.scale[0] == np.float32(3.0) / np.float32(255.0)
+    assert q.zero.tolist() == [85]
+    assert q.codes.tolist() == [0, 85, 127, 255]
+    d = O.dequantize(q)
+    assert d[1] == 0.0                                    # zero is exact
+    assert np.all(np.abs(d - np.array([-1, 0, 0.5, 2])) <= q.scale[0] / 2 * (1 + 2 ** -20))
+
+
+def _random_blocks(rng, dtype, n):
+    kinds = [rng.normal(0, 1e-3, n), rng.normal(5, 1, n), -np.abs(rng.normal(0, 30, n)),
+             rng.uniform(-1e4, 1e4, n), rng.normal(0, 1e-6, n),
+             np.where(rng.random(n) < 0.01, rng.normal(0, 100, n), rng.normal(0, 0.01, n))]
+    return [bits16(k.astype(np.float32), dtype) for k in kinds]
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_error_bound_and_code_range(bits, dtype):
+    rng = np.random.default_rng(bits * 10 + dtype)
+    Q = (1 << bits) - 1
+    for src in _random_blocks(rng, dtype, 3 * O.QBLOCK + 77):
+        q = O.quantize(src, dtype, bits)
+        x = values(src, dtype).astype(np.float64)
+        d = O.dequantize(q).astype(np.float64)
+        assert np.all((q.zero >= 0) & (q.zero <= Q))
+        for b in range(q.scale.size):
+            sl = slice(b * O.QBLOCK, min((b + 1) * O.QBLOCK, src.size))
+            S = float(q.scale[b])
+            lo, hi = min(0.0, x[sl].min()), max(0.0, x[sl].max())
+            assert S >= (hi - lo) / Q * (1 - 2 ** -22)
+            err = np.abs(x[sl] - d[sl])
+            assert np.all(err <= S * (0.5 + 2 ** -16) + 2 ** -23 * np.abs(x[sl])), (b, err.max(), S)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_zero_exact_endpoints_monotone(bits):
+    Q = (1 << bits) - 1
+    rng = np.random.default_rng(7 + bits)
+    x = np.sort(rng.normal(0.3, 2.0, O.QBLOCK).astype(np.float32))
+    x[100] = 0.0
+    x = np.sort(x)
+    src = bits16(x, BF16)
+    q = O.quantize(src, BF16, bits)
+    codes = _unpack(q)
+    xv = values(src, BF16)
+    z = int(q.zero[0])
+    assert np.all(codes[xv == 0.0] == z)                 # real zero -> the zero point
+    assert np.all(O.dequantize(q)[xv == 0.0] == 0.0)     # ... and back to exactly 0
+    assert codes[0] == 0 and codes[-1] >= Q - 1           # lo -> 0, hi -> Q (or Q - 1)
+    assert np.all(np.diff(codes.astype(int)) >= 0)        # monotone in x
+    assert codes.max() <= Q
+
+
+def _unpack(q):
+    if q.bits == 8:
+        return q.codes.astype(np.int64)[:q.length]
+    lo, hi = q.codes & 15, q.codes >> 4
+    return np.stack([lo, hi], 1).reshape(-1)[:q.length].astype(np.int64)
+
+
+@pytest.mark.parametrize("bits,S0,Z0", [(8, 2.0 ** -10, 100), (4, 2.0 ** -3, 6)])
+def test_grid_values_are_exact(bits, S0, Z0):
+    Q = (1 << bits) - 1
+    j = np.concatenate([np.arange(Q + 1), np.random.default_rng(1).integers(0, Q + 1, 500)])
+    x = (S0 * (j - Z0)).astype(np.float32)
+    q = O.quantize(bits16(x, F16), F16, bits)
+    assert q.scale[0] == S0 and q.zero[0] == Z0
+    assert np.array_equal(_unpack(q), j)
+    assert np.array_equal(O.dequantize(q), x)
+
+
+def test_one_sided_and_zero_blocks():
+    Q = 255
+    pos = O.quantize(bits16(np.linspace(1, 2, 300), F16), F16, 8)
+    assert pos.zero[0] == 0 and _unpack(pos)[-1] == Q
+    neg = O.quantize(bits16(-np.linspace(1, 2, 300), F16), F16, 8)
+    assert neg.zero[0] == Q and _unpack(neg)[-1] == 0      # -2 is lo: code 0
+    zer = O.quantize(np.zeros(70, np.uint16), F16, 8)
+    assert zer.scale[0] == 1.0 and zer.zero[0] == 0
+    assert not zer.codes.any() and not O.dequantize(zer).any()
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_blocks_are_independent_and_2048_long(bits):
+    rng = np.random.default_rng(3)
+    n = 2 * O.QBLOCK + 5
+    x = rng.normal(0, 1, n).astype(np.float32)
+    x[O.QBLOCK:2 * O.QBLOCK] *= 50          # a different range in block 1
+    src = bits16(x, F16)
+    whole = O.quantize(src, F16, bits)
+    assert O.qblock() == 2048 and whole.scale.size == 3
+    for b in range(3):
+        part = O.quantize(src[b * O.QBLOCK:(b + 1) * O.QBLOCK], F16, bits)
+        assert part.scale[0] == whole.scale[b] and part.zero[0] == whole.zero[b]
+        assert np.array_equal(_unpack(part), _unpack(whole)[b * O.QBLOCK:(b + 1) * O.QBLOCK])
+    # a block boundary one element off would mix the ranges of blocks 0 and 1
+    shifted = O.quantize(src[1:O.QBLOCK + 1], F16, bits)
+    assert shifted.scale[0] != whole.scale[0]
+
+
+@pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_non_finite_block(bad, bits):
+    rng = np.random.default_rng(5)
+    x = rng.normal(0, 1, 3 * O.QBLOCK).astype(np.float32)
+    x[O.QBLOCK + 17] = bad
+    src = bits16(x, F16)
+    q = O.quantize(src, F16, bits)
+    assert np.isnan(q.scale[1]) and q.zero[1] == 0
+    assert not _unpack(q)[O.QBLOCK:2 * O.QBLOCK].any()
+    d = O.dequantize(q)
+    assert np.all(np.isnan(d[O.QBLOCK:2 * O.QBLOCK]))
+    assert np.all(np.isfinite(d[:O.QBLOCK])) and np.all(np.isfinite(d[2 * O.QBLOCK:]))
+    alone = O.quantize(src[:O.QBLOCK], F16, bits)
+    assert alone.scale[0] == q.scale[0]
+
+
+def test_reduce_q_equals_reduce_on_grid_rows():
+    """Rows whose values lie on their blocks' grids (each block holds both
+    ends of its grid, so S and Z come out exact) dequantise exactly, so the
+    quantised reduce must equal the plain reduce of the 16-bit rows.  Element 0
+    is order-sensitive: 255*2^-10, +255*2^16, -255*2^16 sums to 0 in rank
+    order (the small value is absorbed) and to 255*2^-10 last-to-first."""
+    length = O.QBLOCK + 9
+    rng = np.random.default_rng(9)
+    grids = [(2.0 ** -10, 0), (2.0 ** 16, 0), (2.0 ** 16, 255)]   # (S, Z) per row
+    rows = []
+    for S0, Z0 in grids:
+        j = rng.integers(0, 256, length)
+        for b0 in (0, O.QBLOCK):
+            j[b0 + 1], j[b0 + 2] = 0, 255
+        j[0] = 255 if Z0 == 0 else 0
+        rows.append((S0 * (j - Z0)).astype(np.float32))
+    assert rows[0][0] == 255 * 2.0 ** -10 and rows[1][0] == -rows[2][0] == 255 * 2.0 ** 16
+    C = np.stack([bits16(r, BF16) for r in rows])
+    n = len(rows)
+    qs = [O.quantize(C[k], BF16, 8) for k in range(n)]
+    for k in range(n):
+        assert np.array_equal(O.dequantize(qs[k]), values(C[k], BF16)), k
+    inv = O.inv_scale(n, 1.0)
+    g_ref, f_ref = O.reduce(C, BF16, length, inv)
+    g, f = O.reduce_q(qs, length, inv)
+    assert np.array_equal(g.view(np.uint32), g_ref.view(np.uint32)) and f == f_ref == 0
+    assert g[0] == 0.0   # the small value is absorbed by the large one in rank order
+
+
+def test_reduce_q_flags_non_finite_block():
+    x = np.random.default_rng(2).normal(0, 1, O.QBLOCK + 3).astype(np.float32)
+    clean = O.quantize(bits16(x, F16), F16, 4)
+    x[O.QBLOCK + 1] = np.inf
+    dirty = O.quantize(bits16(x, F16), F16, 4)
+    g, f = O.reduce_q([clean, dirty], x.size, O.inv_scale(2, 1.0))
+    assert f == 1 and np.all(np.isnan(g[O.QBLOCK:])) and np.all(np.isfinite(g[:O.QBLOCK]))
