@@ -71,10 +71,19 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
-def setup(w, torch, synth, Z, rows=False):
+def quant_bytes_per_elem(w, bits: int) -> float:
+    """Algorithmic bytes per element with block-quantised contributions: N
+    rows of bits/8-byte codes plus one 8-byte block record per 2048 elements
+    per row, instead of N 16-bit values."""
+    return w.bytes_per_elem - 2 * w.nranks + w.nranks * (bits / 8 + 8 / 2048)
+
+
+def setup(w, torch, synth, Z, rows=False, qbits=0):
     """Buffers of the measured rank, inputs generated in HBM.  With `rows`, the
     N contribution rows live in N separate allocations and the step goes
-    through the row-table calls."""
+    through the row-table calls; with `qbits`, the rows are block-quantised
+    (INT8 or INT4, quantised on the GPU from the 16-bit rows) and the step
+    goes through the quantised calls."""
     rank = w.ranks[-1]
     shard, off, valid = Z.zero_partition(w.psi, w.nranks, rank)
     stride = w.stride
@@ -98,7 +107,15 @@ def setup(w, torch, synth, Z, rows=False):
     if fused:  # the flat state is only needed to load the paired copy
         del state0, p0
         st.state = None
-    if rows:
+    if qbits:
+        q = Z.QuantRows.alloc(w.nranks, valid, qbits, dev)
+        for k, (codes, blocks) in enumerate(q.rows):
+            Z.zero_quantize_blocks(contrib[k], w.dtype, valid, qbits, codes, blocks)
+        torch.cuda.synchronize()
+        del contrib
+        torch.cuda.empty_cache()
+        contrib = q
+    elif rows:
         table = [torch.empty(valid, dtype=tdt, device=dev) for _ in range(w.nranks)]
         for k, r in enumerate(table):
             r.copy_(contrib[k, :valid])
@@ -120,6 +137,7 @@ def timed_steps(b, steps, warmup, torch, Z):
     kept out of the loop that gives the step time."""
     st, contrib, gather = b["step"], b["contrib"], b["gather"]
     table = isinstance(contrib, list)
+    quant = isinstance(contrib, Z.QuantRows)
     for _ in range(warmup):
         st.step(contrib, gather)
     torch.cuda.synchronize()
@@ -146,7 +164,10 @@ def timed_steps(b, steps, warmup, torch, Z):
     for i in range(steps):
         if b["fused"]:
             ev[i][0].record()
-            if table:
+            if quant:
+                Z.zero_fused_step_q(contrib, st.pair, valid, gather, st.gather_dtype, off, hp,
+                                    st.ctrl, st.ws)
+            elif table:
                 Z.zero_fused_step_rows(contrib, st.dtype, st.pair, valid, gather,
                                        st.gather_dtype, off, hp, st.ctrl, st.ws)
             else:
@@ -157,7 +178,9 @@ def timed_steps(b, steps, warmup, torch, Z):
             Z.zero_fused_restore(st.pair, valid, gather, st.gather_dtype, off, st.ctrl)
         else:
             ev_red[i][0].record()
-            if table:
+            if quant:
+                Z.zero_reduce_grads_q(contrib, valid, st.ctrl, st.g, st.ws)
+            elif table:
                 Z.zero_reduce_grads_rows(contrib, st.dtype, valid, st.ctrl, st.g, st.ws)
             else:
                 Z.zero_reduce_grads(contrib, st.dtype, n, stride, valid, st.ctrl, st.g, st.ws)
@@ -251,6 +274,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--quant", type=int, choices=(0, 4, 8), default=0,
+                    help="block-quantised (ZeRO++) INT8 or INT4 contributions through the "
+                         "quantised calls")
     ap.add_argument("--rows", action="store_true",
                     help="contribution rows in N separate allocations, through the row-table "
                          "calls (one pointer per row) instead of one [N, stride] buffer")
@@ -284,14 +310,16 @@ def main():
         return
 
     w = workloads.BY_NAME[args.workload]
-    b = setup(w, torch, synth, Z, rows=args.rows)
+    b = setup(w, torch, synth, Z, rows=args.rows, qbits=args.quant)
     ms_step, per_step, kern_ms, red_ms, ctrl = timed_steps(b, args.steps, args.warmup, torch, Z)
     valid = b["valid"]
-    step_bytes = w.bytes_per_elem * valid
+    bpe = quant_bytes_per_elem(w, args.quant) if args.quant else w.bytes_per_elem
+    step_bytes = int(round(bpe * valid))
     gbps = step_bytes / (ms_step * 1e-3) / 1e9
     kern_avg = sum(kern_ms) / len(kern_ms)
     if b["fused"]:
-        kern_name = "fused_kernel_rows" if args.rows else "fused_kernel"
+        kern_name = ("fused_kernel_q%d" % args.quant if args.quant else
+                     "fused_kernel_rows" if args.rows else "fused_kernel")
         kern_bytes = step_bytes
     else:
         kern_name = "adam_kernel"
@@ -316,8 +344,9 @@ def main():
         "config": {"workload": w.name, "psi": w.psi, "nranks": w.nranks, "rank": w.ranks[-1],
                    "shard_elems": valid, "variant": w.variant,
                    "contrib_dtype": "fp16" if w.dtype == Z.F16 else "bf16",
-                   "bytes_per_elem": w.bytes_per_elem, "step_bytes": step_bytes,
-                   "contrib_layout": "row_table" if args.rows else "strided"},
+                   "bytes_per_elem": _fmt(bpe, 6), "step_bytes": step_bytes,
+                   "contrib_layout": ("int%d_blocks" % args.quant if args.quant else
+                                      "row_table" if args.rows else "strided")},
         "step_ms_median": _fmt(per_step[len(per_step) // 2], 5),
         "step_ms_min": _fmt(per_step[0], 5),
         "pct_hbm_peak": _fmt(100 * gbps / HBM_PEAK_GBPS, 4),
@@ -332,8 +361,9 @@ def main():
     }
     if red_ms:
         red_avg = sum(red_ms) / len(red_ms)
+        red_bpe = 4 + (w.nranks * (args.quant / 8 + 8 / 2048) if args.quant else 2 * w.nranks)
         out["reduce_kernel"] = {"ms": _fmt(red_avg, 5),
-                                "gbps": _fmt((2 * w.nranks + 4) * valid / (red_avg * 1e-3) / 1e9, 5)}
+                                "gbps": _fmt(red_bpe * valid / (red_avg * 1e-3) / 1e9, 5)}
     try:
         out["device"] = synth.gpu_device_info(0)
     except (RuntimeError, OSError, AttributeError) as e:  # informational only

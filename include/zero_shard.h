@@ -69,6 +69,14 @@ enum { ZERO_SCALER_NONE = 0, ZERO_SCALER_STATIC = 1, ZERO_SCALER_DYNAMIC = 2 };
 
 #define ZERO_MAX_CONTRIB 1024 /* largest N accepted by the reduce */
 #define ZERO_MAX_RANKS 64     /* most ctrl blocks combined in one call; most rows in a row table */
+#define ZERO_QBLOCK 2048      /* elements per quantisation block (one tile) */
+
+/* Parameters of one quantisation block: value = scale * (code - zero).  A
+ * block that held a non-finite value has scale NaN and zero 0. */
+typedef struct {
+    float scale;
+    int32_t zero;
+} zero_qblock;
 
 /* Optimizer, clipping and loss-scale settings, passed by host pointer and
  * copied into the kernel arguments.  The pages name Adam (Kingma and Ba) and
@@ -274,6 +282,68 @@ int zero_pair_store(const zero_state *flat, const zero_state *pair, int64_t vali
 /* Copies the current set of a paired state out to a flat state. */
 int zero_pair_load(const zero_state *pair, const zero_state *flat, int64_t valid_len,
                    const zero_ctrl *ctrl_dev, void *stream);
+
+/* ---- Block-quantised payloads (ZeRO++) --------------------------------------
+ * "CMU 11-868 L18", Other memory optimizations: ZeRO++ quantises the
+ * parameters of the forward all-gather block-wise from 16 bits to INT8 with a
+ * zero point, and the gradient reduce-scatter to INT8 or INT4.  The page
+ * gives neither block size nor rounding; this library's reading:
+ *   blocks of ZERO_QBLOCK consecutive elements from the start of the buffer
+ *   (the last may be short), Q = 2^bits - 1, and per block
+ *     lo = min(0, min x), hi = max(0, max x),
+ *     scale = (hi - lo) / Q (1 when that is 0),
+ *     zero  = clamp(rint(-lo / scale), 0, Q),
+ *     code  = clamp(rint(x / scale) + zero, 0, Q),
+ *   each operation one fp32 rounding, rint half to even.  Real 0 is exact;
+ *   |x - value| <= scale / 2 up to the roundings.  A block holding inf or
+ *   NaN, or whose scale overflows, gets scale NaN, zero 0 and codes 0, so it
+ *   dequantises to NaN and a downstream overflow check still fires.
+ *   Codes: bits = 8, one byte per element; bits = 4, two per byte, the
+ *   even-indexed element in the low nibble.
+ * Pointers (codes, blocks, 16-bit src/dst) must be 8-byte aligned. */
+
+/* Blocks of a quantised buffer of len elements: ceil(len / ZERO_QBLOCK). */
+size_t zero_qblock_count(int64_t len);
+
+/* Code bytes of a quantised buffer of len elements: len (8 bits) or
+ * ceil(len / 2) (4 bits); 0 for len <= 0. */
+size_t zero_qcode_bytes(int64_t len, int32_t bits);
+
+/* Quantises len 16-bit values (dtype) at src_dev into codes_dev
+ * (zero_qcode_bytes) and blocks_dev (zero_qblock_count entries): a sender's
+ * gradient slice for a quantised reduce-scatter, or a rank's parameter slot
+ * for a quantised all-gather.  Deterministic (no atomics).
+ * Errors: EINVAL (null, dtype, bits not 8 or 4), EALIGN, ERANGE. */
+int zero_quantize_blocks(const void *src_dev, int32_t dtype, int64_t len, int32_t bits,
+                         void *codes_dev, zero_qblock *blocks_dev, void *stream);
+
+/* dst_dev[i] = RNE_dtype(scale_b * (code_i - zero_b)), b = i / ZERO_QBLOCK:
+ * the receiving side of a quantised all-gather. */
+int zero_dequantize_blocks(const void *codes_dev, const zero_qblock *blocks_dev, int32_t bits,
+                           int64_t len, void *dst_dev, int32_t dtype, void *stream);
+
+/* zero_reduce_grads over quantised contributions: row k is codes_dev[k] with
+ * blocks_dev[k], each quantised from the start of this rank's slice (the
+ * sender quantises every destination's slice on its own), so block b covers
+ * shard elements [b * ZERO_QBLOCK, ...).  Each value is dequantised as above
+ * (one fp32 rounding) and the N values are summed in fp32 in rank order;
+ * overflow flag, 1/(N*S) and the norm partials are as in zero_reduce_grads.
+ * codes_dev and blocks_dev are host arrays of nranks device pointers
+ * (nranks <= ZERO_MAX_RANKS), copied into the launch.
+ * Errors: EINVAL (null table or row, bits, nranks), EALIGN, ESPACE, ERANGE. */
+int zero_reduce_grads_q(const void *const *codes_dev, const zero_qblock *const *blocks_dev,
+                        int32_t bits, int32_t nranks, int64_t valid_len,
+                        const zero_ctrl *ctrl_dev, float *g_dev, void *ws_dev, size_t ws_bytes,
+                        void *stream);
+
+/* zero_fused_step over quantised contributions (rows as in
+ * zero_reduce_grads_q): the one-pass step of a rank whose gradient
+ * reduce-scatter arrives as INT8 or INT4 blocks. */
+int zero_fused_step_q(const void *const *codes_dev, const zero_qblock *const *blocks_dev,
+                      int32_t bits, int32_t nranks, const zero_state *pair, int64_t valid_len,
+                      void *gather_dev, int32_t gather_dtype, int64_t offset,
+                      const zero_hparams *hp, const zero_ctrl *ctrl_dev, void *ws_dev,
+                      size_t ws_bytes, void *stream);
 
 /* Message for the last nonzero return on the calling thread ("" if none). */
 const char *zero_last_error(void);

@@ -203,9 +203,11 @@ def gpu_copy(src, dst, nbytes: int, grid: int = 0) -> None:
 
 def gpu_device_info(device: int = 0) -> dict:
     """Peak memory clock, bus width, CU count and shader clock of a device, and
-    the HBM peak they imply (double data rate: 2 transfers per clock)."""
+    the HBM peak they imply.  HBM3E moves four bits per pin per clock that the
+    device reports (MI355X: 2000 MHz, 8 Gb/s per pin), so the peak is
+    bus_bits / 8 * 4 * clock."""
     v = [ctypes.c_int32() for _ in range(4)]
     _check(gpu().synth_gpu_device_info(device, *[ctypes.byref(x) for x in v]), "device_info")
     mem_khz, bus, cus, clk = (x.value for x in v)
     return {"mem_clock_mhz": mem_khz / 1e3, "bus_bits": bus, "cus": cus, "clock_mhz": clk / 1e3,
-            "hbm_peak_gbps_from_props": round(2 * mem_khz * 1e3 * bus / 8 / 1e9, 1)}
+            "hbm_peak_gbps_from_props": round(4 * mem_khz * 1e3 * bus / 8 / 1e9, 1)}

@@ -31,6 +31,7 @@ F32_ATOL = 1e-9
 NORM_RTOL = 1e-5
 THREADS = max(1, min(16, os.cpu_count() or 1))
 CHUNK = 1 << 20
+assert CHUNK % O.QBLOCK == 0  # oracle chunks start quantisation blocks
 
 
 def log(msg: str) -> None:
@@ -53,6 +54,7 @@ class Case:
     steps: int
     extra: tuple = ()          # Inject entries on top of the workload's own
     stride_pad: int = 0        # extra padding columns beyond the workload stride
+    qbits: int = 0             # 8 or 4: contributions arrive block-quantised (ZeRO++)
 
     @property
     def part(self):
@@ -91,6 +93,15 @@ def _contrib_chunk(c: Case, step: int, col0: int, ncol: int) -> np.ndarray:
     return C
 
 
+def _reduce(c: Case, C: np.ndarray, ncol: int, inv: float):
+    """The oracle's reduce of a contribution chunk whose first column starts a
+    quantisation block: plain, or over the rows block-quantised by the oracle."""
+    if not c.qbits:
+        return O.reduce(C, c.w.dtype, ncol, inv)
+    rows = [O.quantize(C[k, :ncol], c.w.dtype, c.qbits) for k in range(C.shape[0])]
+    return O.reduce_q(rows, ncol, inv)
+
+
 def oracle_scalars(c: Case) -> list[dict]:
     """Per-step decisions of the oracle over the whole shard."""
     w = c.w
@@ -105,7 +116,7 @@ def oracle_scalars(c: Case) -> list[dict]:
 
             def work(ch, s=s, inv=inv):
                 C = _contrib_chunk(c, s, ch[0], ch[1])
-                g, flag = O.reduce(C, w.dtype, ch[1], inv)
+                g, flag = _reduce(c, C, ch[1], inv)
                 return O.SumSq().add(g), flag
 
             acc, flag = O.SumSq(), 0
@@ -136,13 +147,23 @@ def _elements(c: Case, reps: list[dict], cols: np.ndarray | None, col0: int = 0,
             continue
         if cols is None:
             C = _contrib_chunk(c, s, col0, ncol)
+        elif c.qbits:  # whole quantisation blocks around the sampled columns
+            g = np.empty(cols.size, np.float32)
+            blk = cols // O.QBLOCK
+            for b in np.unique(blk):
+                b0 = int(b) * O.QBLOCK
+                nb = min(O.QBLOCK, c.part[2] - b0)
+                gb, _ = _reduce(c, _contrib_chunk(c, s, b0, nb), nb, rep["inv"])
+                g[blk == b] = gb[cols[blk == b] - b0]
+            O.adam(p, m, v, g, hp, rep["clip"], rep["pow1"], rep["pow2"])
+            continue
         else:
             C = synth.contrib_at(w.seed, s, w.nranks, w.dtype, w.contrib_sigma, w.contrib_scale,
                                  w.outlier_p, w.outlier_mult, off + cols)
             for inj in c.injections:
                 if inj.step == s:
                     C[inj.k, cols == inj.col] = bits16(inj.value, w.dtype)
-        g, _ = O.reduce(np.ascontiguousarray(C), w.dtype, p.size, rep["inv"])
+        g, _ = _reduce(c, np.ascontiguousarray(C), p.size, rep["inv"])
         O.adam(p, m, v, g, hp, rep["clip"], rep["pow1"], rep["pow2"])
     return p, m, v
 
@@ -220,7 +241,10 @@ class GpuRun:
             raise ValueError(layout)
         self.layout = layout
         self.rows = None
+        self.qrows = None
         n = w.nranks
+        if c.qbits:
+            self.qrows = Z.QuantRows.alloc(n, valid, c.qbits, dev)
         if layout == "rows":
             self.rows = [torch.empty(max(valid, 1), dtype=tdt, device=dev) for _ in range(n)]
         elif layout == "rows_shifted":
@@ -240,12 +264,18 @@ class GpuRun:
         if self.rows is not None and self.valid:
             for k, r in enumerate(self.rows):
                 r[:self.valid].copy_(self.contrib[k, :self.valid])
+        if self.qrows is not None and self.valid:
+            for k, (codes, blocks) in enumerate(self.qrows.rows):
+                self.Z.zero_quantize_blocks(self.contrib[k], w.dtype, self.valid, c.qbits, codes,
+                                            blocks)
 
     def run(self, steps: int | None = None, record: bool = True) -> None:
         steps = self.c.steps if steps is None else steps
         for s in range(1, steps + 1):
             self.fill(s)
-            self.step_obj.step(self.contrib if self.rows is None else self.rows, self.gather)
+            src = self.qrows if self.qrows is not None else (
+                self.contrib if self.rows is None else self.rows)
+            self.step_obj.step(src, self.gather)
             if record:
                 self.reports.append(self.step_obj.ctrl_dict())
         self.torch.cuda.synchronize()
@@ -280,7 +310,7 @@ def run_and_compare(c: Case, label: str, full: bool = True, layout: str = "strid
     that the gather buffer is unchanged outside the slot."""
     log(f"{label}: psi={c.w.psi} N={c.w.nranks} rank={c.rank} dtype={c.w.dtype} "
         f"variant={c.w.variant} steps={c.steps} offset={c.part[1]} valid={c.part[2]} "
-        f"layout={layout}")
+        f"layout={layout} qbits={c.qbits}")
     g = GpuRun(c, full_gather=full, layout=layout)
     g.run()
     ref_reps = oracle_scalars(c)

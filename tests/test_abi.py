@@ -174,3 +174,54 @@ def test_row_table_accepts_8_byte_aligned_rows(Z):
     # every check; only a misaligned g then stops the call before any launch.
     assert _rows_call(Z, False, [FAKE + 8, FAKE + 24, FAKE], g=FAKE + 4) == -2
     assert "g not 16-byte" in Z.zero_last_error()
+
+
+def test_quant_sizes(Z):
+    assert Z.zero_qblock_count(0) == 0 and Z.zero_qblock_count(1) == 1
+    assert Z.zero_qblock_count(2048) == 1 and Z.zero_qblock_count(2049) == 2
+    assert Z.zero_qcode_bytes(5, 8) == 5 and Z.zero_qcode_bytes(5, 4) == 3
+    assert Z.zero_qcode_bytes(4, 4) == 2 and Z.zero_qcode_bytes(-1, 8) == 0
+    assert ctypes.sizeof(ctypes.c_float) + ctypes.sizeof(ctypes.c_int32) == 8  # zero_qblock
+
+
+def test_quantize_validation(Z):
+    L = Z._lib
+    assert L.zero_quantize_blocks(FAKE, 1, 64, 3, FAKE, FAKE, None) == -1          # bits
+    assert L.zero_quantize_blocks(FAKE, 7, 64, 8, FAKE, FAKE, None) == -1          # dtype
+    assert L.zero_quantize_blocks(0, 1, 64, 8, FAKE, FAKE, None) == -1
+    assert L.zero_quantize_blocks(FAKE + 2, 1, 64, 8, FAKE, FAKE, None) == -2
+    assert L.zero_quantize_blocks(FAKE, 1, 64, 4, FAKE + 4, FAKE, None) == -2
+    assert L.zero_quantize_blocks(FAKE, 1, -5, 8, FAKE, FAKE, None) == -3
+    assert L.zero_dequantize_blocks(FAKE, FAKE, 4, 64, FAKE + 6, 1, None) == -2
+    assert L.zero_dequantize_blocks(FAKE, FAKE, 2, 64, FAKE, 1, None) == -1
+    assert L.zero_dequantize_blocks(FAKE, None, 8, 64, FAKE, 2, None) == -1
+
+
+def _q_call(Z, fused, codes, blocks, bits=8, n=None, valid=64, g=FAKE, wsb=1 << 16):
+    n = len(codes) if n is None else n
+    ca = (ctypes.c_void_p * max(len(codes), 1))(*codes) if codes is not None else None
+    ba = (ctypes.c_void_p * max(len(blocks), 1))(*blocks) if blocks is not None else None
+    if not fused:
+        return Z._lib.zero_reduce_grads_q(ca, ba, bits, n, valid, FAKE, g, FAKE, wsb, None)
+    pair = Z.State(FAKE, FAKE + 65536, FAKE + 131072)
+    hp = Z.hparams()
+    return Z._lib.zero_fused_step_q(ca, ba, bits, n, ctypes.byref(pair), valid, FAKE, 1, 0,
+                                    ctypes.byref(hp), FAKE, FAKE, wsb, None)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("codes,blocks,kw,code,msg", [
+    ([FAKE] * 2, [FAKE] * 2, dict(bits=2), -1, "bits"),
+    (None, [FAKE], dict(n=1), -1, "null row table"),
+    ([FAKE] * 2, None, dict(n=2), -1, "null row table"),
+    ([FAKE] * 65, [FAKE] * 65, dict(), -1, "outside"),
+    ([FAKE, 0], [FAKE, FAKE], dict(), -1, "row 1 is null"),
+    ([FAKE, FAKE], [FAKE, 0], dict(), -1, "row 1 is null"),
+    ([FAKE, FAKE + 4], [FAKE, FAKE], dict(), -2, "row 1 not 8-byte"),
+    ([FAKE, FAKE], [FAKE + 4, FAKE], dict(), -2, "row 0 not 8-byte"),
+    ([FAKE] * 2, [FAKE] * 2, dict(valid=-1), -3, "out of range"),
+    ([FAKE] * 2, [FAKE] * 2, dict(wsb=16), -4, "workspace"),
+])
+def test_quant_rows_validation(Z, fused, codes, blocks, kw, code, msg):
+    assert _q_call(Z, fused, codes, blocks, **kw) == code
+    assert msg in Z.zero_last_error()

@@ -44,7 +44,13 @@ MUTANTS = {
         [REDUCE]),
     "reduce_no_average": ("return (float)(1.0 / ((double)nranks * (double)loss_scale));",
                           "return (float)(1.0 / (double)loss_scale);", [REDUCE]),
-    "overflow_not_flagged": ("if (!isfinite(acc)) flag = 1;", "if (isnan(acc)) flag = 1;", [REDUCE]),
+    "overflow_not_flagged": (
+        "oracle_to_f32(C[(int64_t)k * stride + i], dtype);\n        if (!isfinite(acc)) flag = 1;",
+        "oracle_to_f32(C[(int64_t)k * stride + i], dtype);\n        if (isnan(acc)) flag = 1;",
+        [REDUCE]),
+    "reduce_q_overflow_not_flagged": (
+        "zero[k][b]);\n        if (!isfinite(acc)) flag = 1;",
+        "zero[k][b]);\n        if (acc != acc) flag = acc != acc;", [QUANT]),
     "norm_ignores_inf": ("if (isinf(x)) { a->has_inf = 1; continue; }", "if (isinf(x)) { continue; }",
                          [REDUCE]),
     "partition_floor": ("int64_t s = psi / nranks + (psi % nranks != 0 ? 1 : 0);",

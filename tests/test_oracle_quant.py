@@ -194,3 +194,16 @@ def test_reduce_q_flags_non_finite_block():
     dirty = O.quantize(bits16(x, F16), F16, 4)
     g, f = O.reduce_q([clean, dirty], x.size, O.inv_scale(2, 1.0))
     assert f == 1 and np.all(np.isnan(g[O.QBLOCK:])) and np.all(np.isfinite(g[:O.QBLOCK]))
+
+
+def test_reduce_q_flags_fp32_overflow_of_finite_rows():
+    """Two finite bf16 rows of 1.5 * 2^127 each dequantise to finite values
+    whose fp32 sum exceeds the largest binary32 (about 3.4e38): the sum is
+    +inf and must raise the overflow flag."""
+    x = np.zeros(64, np.float32)
+    x[3] = np.float32(1.5 * 2.0 ** 127)
+    q = O.quantize(bits16(x, BF16), BF16, 8)
+    d = O.dequantize(q)
+    assert np.all(np.isfinite(d)) and d[3] > 2.0 ** 127
+    g, f = O.reduce_q([q, q], x.size, 1.0)
+    assert f == 1 and np.isinf(g[3]) and np.all(np.isfinite(np.delete(g, 3)))

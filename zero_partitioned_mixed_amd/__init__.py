@@ -54,6 +54,7 @@ class Ctrl(ctypes.Structure):
 
 
 TILE = 2048  # ZERO_TILE
+QBLOCK = 2048  # ZERO_QBLOCK
 
 
 class State(ctypes.Structure):
@@ -90,6 +91,15 @@ _sig = {
                                        _vp]),
     "zero_pair_load": (ctypes.c_int, [ctypes.POINTER(State), ctypes.POINTER(State), _i64, _vp,
                                       _vp]),
+    "zero_qblock_count": (ctypes.c_size_t, [_i64]),
+    "zero_qcode_bytes": (ctypes.c_size_t, [_i64, _i32]),
+    "zero_quantize_blocks": (ctypes.c_int, [_vp, _i32, _i64, _i32, _vp, _vp, _vp]),
+    "zero_dequantize_blocks": (ctypes.c_int, [_vp, _vp, _i32, _i64, _vp, _i32, _vp]),
+    "zero_reduce_grads_q": (ctypes.c_int, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _i32,
+                                           _i64, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "zero_fused_step_q": (ctypes.c_int, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _i32,
+                                         ctypes.POINTER(State), _i64, _vp, _i32, _i64,
+                                         ctypes.POINTER(Hparams), _vp, _vp, ctypes.c_size_t, _vp]),
     "zero_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _sig.items():
@@ -245,6 +255,63 @@ def zero_pair_load(pair, flat, valid_len: int, ctrl) -> None:
                                                  _ptr(ctrl), _stream()))
 
 
+def zero_qblock_count(length: int) -> int:
+    return _lib.zero_qblock_count(length)
+
+
+def zero_qcode_bytes(length: int, bits: int) -> int:
+    return _lib.zero_qcode_bytes(length, bits)
+
+
+def zero_quantize_blocks(src, dtype: int, length: int, bits: int, codes, blocks) -> None:
+    _check("zero_quantize_blocks", _lib.zero_quantize_blocks(
+        _ptr(src), dtype, length, bits, _ptr(codes), _ptr(blocks), _stream()))
+
+
+def zero_dequantize_blocks(codes, blocks, bits: int, length: int, dst, dtype: int) -> None:
+    _check("zero_dequantize_blocks", _lib.zero_dequantize_blocks(
+        _ptr(codes), _ptr(blocks), bits, length, _ptr(dst), dtype, _stream()))
+
+
+class QuantRows:
+    """N block-quantised contribution rows: ``rows`` is a list of (codes,
+    blocks) device tensors (or integer addresses), all of ``bits`` bits."""
+
+    def __init__(self, rows, bits: int):
+        self.rows, self.bits = list(rows), bits
+
+    def tables(self):
+        c, n = _rows([r[0] for r in self.rows])
+        b, _ = _rows([r[1] for r in self.rows])
+        return c, b, n
+
+    @staticmethod
+    def alloc(nranks: int, length: int, bits: int, device):
+        """Code and block buffers for nranks rows of `length` elements."""
+        import torch
+        nbytes = max((zero_qcode_bytes(length, bits) + 15) // 16 * 16, 16)
+        nblk = max(zero_qblock_count(length), 1)
+        return QuantRows([(torch.empty(nbytes, dtype=torch.uint8, device=device),
+                           torch.empty(nblk * 8, dtype=torch.uint8, device=device))
+                          for _ in range(nranks)], bits)
+
+
+def zero_reduce_grads_q(q: QuantRows, valid_len: int, ctrl, g, ws) -> None:
+    c, b, n = q.tables()
+    _check("zero_reduce_grads_q", _lib.zero_reduce_grads_q(
+        c, b, q.bits, n, valid_len, _ptr(ctrl), _ptr(g), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream()))
+
+
+def zero_fused_step_q(q: QuantRows, pair, valid_len: int, gather, gather_dtype: int, offset: int,
+                      hp: Hparams, ctrl, ws) -> None:
+    c, b, n = q.tables()
+    st = _state(pair)
+    _check("zero_fused_step_q", _lib.zero_fused_step_q(
+        c, b, q.bits, n, ctypes.byref(st), valid_len, _ptr(gather), gather_dtype, offset,
+        ctypes.byref(hp), _ptr(ctrl), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+
+
 def zero_last_error() -> str:
     return _lib.zero_last_error().decode()
 
@@ -259,9 +326,10 @@ def read_ctrl(ctrl) -> dict:
 class ShardStep:
     """One rank's shard step over caller-provided device buffers.
 
-    contrib: [N, stride] 16-bit tensor, or a list of N row tensors (or device
-    addresses) taken by the row-table calls; gather: the full 16-bit parameter
-    buffer, this rank's slot at ``offset``.  ``state`` is the flat
+    contrib: [N, stride] 16-bit tensor, a list of N row tensors (or device
+    addresses) taken by the row-table calls, or a QuantRows of block-quantised
+    rows taken by the *_q calls; gather: the full 16-bit parameter buffer, this
+    rank's slot at ``offset``.  ``state`` is the flat
     (master, m, v) fp32 state of valid_len elements.  The two-pass path
     (clipping on) updates it in place through ``g``; the fused path keeps
     its double-buffered copy in ``pair`` (allocated here, loaded from
@@ -288,11 +356,15 @@ class ShardStep:
             zero_pair_store(state, self.pair, valid_len, self.ctrl)
 
     def step(self, contrib, gather) -> None:
+        quant = isinstance(contrib, QuantRows)
         table = isinstance(contrib, (list, tuple))
-        if table and len(contrib) != self.nranks:
-            raise ValueError(f"{len(contrib)} rows for {self.nranks} ranks")
+        if (table and len(contrib) != self.nranks) or (quant and len(contrib.rows) != self.nranks):
+            raise ValueError(f"contribution rows do not match {self.nranks} ranks")
         if self.fused:
-            if table:
+            if quant:
+                zero_fused_step_q(contrib, self.pair, self.valid_len, gather, self.gather_dtype,
+                                  self.offset, self.hp, self.ctrl, self.ws)
+            elif table:
                 zero_fused_step_rows(contrib, self.dtype, self.pair, self.valid_len, gather,
                                      self.gather_dtype, self.offset, self.hp, self.ctrl, self.ws)
             else:
@@ -303,7 +375,9 @@ class ShardStep:
             zero_fused_restore(self.pair, self.valid_len, gather, self.gather_dtype, self.offset,
                                self.ctrl)
         else:
-            if table:
+            if quant:
+                zero_reduce_grads_q(contrib, self.valid_len, self.ctrl, self.g, self.ws)
+            elif table:
                 zero_reduce_grads_rows(contrib, self.dtype, self.valid_len, self.ctrl, self.g,
                                        self.ws)
             else:

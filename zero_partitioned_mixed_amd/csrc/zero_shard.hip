@@ -228,6 +228,134 @@ __device__ __forceinline__ float sum_rows1(const RS& R, int n, int64_t i) {
     return acc;
 }
 
+// ---------------------------------------------------------------- contribution sources
+// What the streaming kernels sum: for the thread's 8 elements, the N rows'
+// values widened to fp32 and added in rank order k = 0..N-1.  A source
+// provides issue<NR> (start the first loads), finish<NR> (add them and
+// stream the rest) and sum1 (one element of a partial tile).
+//
+// Src16: 16-bit rows (fp16 or bf16), strided or through a row table.
+template <int DT, class RS>
+struct Src16 {
+    RS rows;
+    using Loads = RowLoads;
+    template <int NR>
+    __device__ __forceinline__ void issue(int n, const Runs& r, Loads& L) const {
+        sum_rows_issue<NR>(rows, n, r, L);
+    }
+    template <int NR>
+    __device__ __forceinline__ void finish(int n, const Runs& r, Loads& L, float acc[kVec]) const {
+        sum_rows_finish<DT, NR>(rows, n, r, L, acc);
+    }
+    __device__ __forceinline__ float sum1(int n, int64_t i) const { return sum_rows1<DT>(rows, n, i); }
+};
+
+// SrcQ: block-quantised rows (ZeRO++ gradient payloads).  Row k is codes[k]
+// (BITS = 8: one byte per element; BITS = 4: two elements per byte, the even
+// one in the low nibble) with one zero_qblock per ZERO_QBLOCK elements in
+// blocks[k]; both counted from the start of the shard, so the tile of a
+// workgroup is exactly one block of every row, and its parameters are
+// workgroup-uniform (indexed by blockIdx.x: the streaming kernels map tile
+// blockIdx.x to workgroup blockIdx.x).  Element value: scale * (code - zero),
+// one fp32 rounding, then added in rank order.
+static_assert(ZERO_QBLOCK == ZERO_TILE, "a quantisation block is one tile");
+
+struct QTable {
+    const uint8_t* codes[ZERO_MAX_RANKS];
+    const zero_qblock* blocks[ZERO_MAX_RANKS];
+};
+
+struct QRow {
+    uint32_t a, b;  // the four codes of run a and of run b
+};
+
+struct QLoads {
+    QRow w[8];
+    zero_qblock q[8];
+};
+
+template <int BITS>
+__device__ __forceinline__ QRow load_qrow(const uint8_t* __restrict__ base, const Runs& r) {
+    QRow w;
+    if constexpr (BITS == 8) {
+        w.a = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(base + r.a));
+        w.b = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(base + r.b));
+    } else {
+        w.a = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(base + (r.a >> 1)));
+        w.b = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(base + (r.b >> 1)));
+    }
+    return w;
+}
+
+template <int BITS>
+__device__ __forceinline__ int32_t code_at(uint32_t w, int j) {
+    return BITS == 8 ? (int32_t)((w >> (8 * j)) & 0xFFu) : (int32_t)((w >> (4 * j)) & 0xFu);
+}
+
+__device__ __forceinline__ float dequant(const zero_qblock& q, int32_t code) {
+    return q.scale * (float)(code - q.zero);
+}
+
+template <int BITS>
+__device__ __forceinline__ void add_qrow(float acc[kVec], const QRow& w, const zero_qblock& q) {
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) acc[j] = acc[j] + dequant(q, code_at<BITS>(w.a, j));
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) acc[kRun + j] = acc[kRun + j] + dequant(q, code_at<BITS>(w.b, j));
+}
+
+template <int BITS>
+struct SrcQ {
+    QTable t;
+    using Loads = QLoads;
+    __device__ __forceinline__ void load8(int k0, const Runs& r, Loads& L) const {
+        const int64_t blk = blockIdx.x;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            L.w[q] = load_qrow<BITS>(t.codes[k0 + q], r);
+            L.q[q] = t.blocks[k0 + q][blk];
+        }
+    }
+    __device__ __forceinline__ void add8(float acc[kVec], const Loads& L) const {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) add_qrow<BITS>(acc, L.w[q], L.q[q]);
+    }
+    template <int NR>
+    __device__ __forceinline__ void issue(int n, const Runs& r, Loads& L) const {
+        if (NR == 8 || n >= 8) load8(0, r, L);
+    }
+    template <int NR>
+    __device__ __forceinline__ void finish(int n, const Runs& r, Loads& L, float acc[kVec]) const {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) acc[j] = 0.0f;
+        if constexpr (NR == 8) {
+            add8(acc, L);
+            return;
+        }
+        int k = 0;
+        if (n >= 8) {
+            add8(acc, L);
+            for (k = 8; k + 8 <= n; k += 8) {
+                load8(k, r, L);
+                __builtin_amdgcn_sched_barrier(0);
+                add8(acc, L);
+            }
+        }
+        const int64_t blk = blockIdx.x;
+        for (; k < n; ++k) add_qrow<BITS>(acc, load_qrow<BITS>(t.codes[k], r), t.blocks[k][blk]);
+    }
+    __device__ __forceinline__ float sum1(int n, int64_t i) const {
+        float acc = 0.0f;
+        const int64_t blk = blockIdx.x;  // == i / ZERO_QBLOCK
+        for (int k = 0; k < n; ++k) {
+            const int32_t code = BITS == 8 ? (int32_t)t.codes[k][i]
+                                           : (int32_t)((t.codes[k][i >> 1] >> (4 * (i & 1))) & 0xFu);
+            acc = acc + dequant(t.blocks[k][blk], code);
+        }
+        return acc;
+    }
+};
+
 // ---------------------------------------------------------------- Adam element
 struct AdamK {
     float b1, b2, omb1, omb2, bc1, bc2, lr, eps, wd;
@@ -365,9 +493,9 @@ __global__ void ctrl_init_kernel(InitArgs a) {
     }
 }
 
-template <class RS>
+template <class SRC>
 struct ReduceArgs {
-    RS rows;
+    SRC src;
     int64_t len;
     const zero_ctrl* ctrl;
     float* g;
@@ -377,18 +505,18 @@ struct ReduceArgs {
 
 // Pass 1 of the two-pass step: g = fl32(sum_k C[k]) * inv, plus one partial
 // per tile.
-template <int DT, int NR, class RS>
-__global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs<RS> a) {
+template <int NR, class SRC>
+__global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs<SRC> a) {
     const float inv = (float)(1.0 / ((double)a.n * (double)a.ctrl->loss_scale));
     double ss = 0.0;
     uint32_t bad = 0;
     const Runs r = runs_of(blockIdx.x);
     if (r.b + kRun <= a.len) {
         float acc[kVec], out[kVec];
-        RowLoads L;
-        sum_rows_issue<NR>(a.rows, a.n, r, L);
+        typename SRC::Loads L;
+        a.src.template issue<NR>(a.n, r, L);
         __builtin_amdgcn_sched_barrier(0);
-        sum_rows_finish<DT, NR>(a.rows, a.n, r, L, acc);
+        a.src.template finish<NR>(a.n, r, L, acc);
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             bad |= __builtin_isfinite(acc[j]) ? 0u : 1u;
@@ -401,7 +529,7 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs<RS> a) {
         for (int j = 0; j < kVec; ++j) {
             const int64_t i = elem(r, j);
             if (i >= a.len) continue;
-            const float acc = sum_rows1<DT>(a.rows, a.n, i);
+            const float acc = a.src.sum1(a.n, i);
             bad |= __builtin_isfinite(acc) ? 0u : 1u;
             const float gj = acc * inv;
             ss += (double)gj * (double)gj;
@@ -636,9 +764,9 @@ __global__ void __launch_bounds__(kBlock) pack_kernel(PackArgs a) {
     }
 }
 
-template <class RS>
+template <class SRC>
 struct FusedArgs {
-    RS rows;
+    SRC src;
     float* pair[3];  // master, m, v in the paired layout
     uint16_t* slot;
     int64_t len;
@@ -650,8 +778,8 @@ struct FusedArgs {
 
 // Single pass: reduce + partial + Adam (read set cur, write set 1-cur of the
 // tile) + cast, one tile per workgroup.
-template <int DTI, int DTO, int GW, int NR, class RS>
-__global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs<RS> a) {
+template <int DTO, int GW, int NR, class SRC>
+__global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs<SRC> a) {
     const zero_ctrl* __restrict__ c = a.ctrl;
     const int cur = c->cur;
     const float inv = (float)(1.0 / ((double)a.n * (double)c->loss_scale));
@@ -667,13 +795,13 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs<RS> a) {
         const int64_t da = pair_index(r.a, cur ^ 1), db = da + 256;
         float acc[kVec], p[kVec], m[kVec], v[kVec];
         uint32_t h[kVec];
-        RowLoads L;
-        sum_rows_issue<NR>(a.rows, a.n, r, L);
+        typename SRC::Loads L;
+        a.src.template issue<NR>(a.n, r, L);
         load8(a.pair[0] + sa, a.pair[0] + sb, p);
         load8(a.pair[1] + sa, a.pair[1] + sb, m);
         load8(a.pair[2] + sa, a.pair[2] + sb, v);
         __builtin_amdgcn_sched_barrier(0);  // every load of the group is in flight first
-        sum_rows_finish<DTI, NR>(a.rows, a.n, r, L, acc);
+        a.src.template finish<NR>(a.n, r, L, acc);
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             bad |= __builtin_isfinite(acc[j]) ? 0u : 1u;
@@ -690,7 +818,7 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs<RS> a) {
         for (int j = 0; j < kVec; ++j) {
             const int64_t i = elem(r, j);
             if (i >= a.len) continue;
-            const float acc = sum_rows1<DTI>(a.rows, a.n, i);
+            const float acc = a.src.sum1(a.n, i);
             bad |= __builtin_isfinite(acc) ? 0u : 1u;
             const float gj = acc * inv;
             ss += (double)gj * (double)gj;
@@ -704,6 +832,159 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs<RS> a) {
         }
     }
     write_partial(a.ws, ss, bad);
+}
+
+// ---------------------------------------------------------------- block quantisation
+// One workgroup per block of ZERO_QBLOCK elements (one tile).  The block's
+// range [lo, hi] always contains 0: lo starts at +0 and is replaced only by
+// a strictly smaller finite value, hi likewise, so the result does not depend
+// on the order in which the lanes are combined.  Then
+//   S = (hi - lo) / Q (1 if 0), Z = clamp(rint(-lo / S)), q = clamp(rint(x / S) + Z),
+// every operation one fp32 rounding, rint half to even; a block with a
+// non-finite value, or whose S overflows, gets scale NaN, zero 0, codes 0.
+struct QuantArgs {
+    const uint16_t* src;
+    uint8_t* codes;
+    zero_qblock* blocks;
+    int64_t len;
+};
+
+__device__ __forceinline__ float take_lo(float a, float b) { return b < a ? b : a; }
+__device__ __forceinline__ float take_hi(float a, float b) { return b > a ? b : a; }
+
+// Range and non-finite flag of the workgroup's values, returned to every thread.
+__device__ __forceinline__ void block_range(float& lo, float& hi, uint32_t& bad) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        lo = take_lo(lo, __shfl_xor(lo, off, 64));
+        hi = take_hi(hi, __shfl_xor(hi, off, 64));
+        bad |= __shfl_xor(bad, off, 64);
+    }
+    constexpr int kW = kBlock / 64;
+    __shared__ float s_lo[kW], s_hi[kW];
+    __shared__ uint32_t s_bad[kW];
+    if ((threadIdx.x & 63) == 0) {
+        s_lo[threadIdx.x >> 6] = lo;
+        s_hi[threadIdx.x >> 6] = hi;
+        s_bad[threadIdx.x >> 6] = bad;
+    }
+    __syncthreads();
+    lo = 0.0f;
+    hi = 0.0f;
+    bad = 0u;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+        lo = take_lo(lo, s_lo[w]);
+        hi = take_hi(hi, s_hi[w]);
+        bad |= s_bad[w];
+    }
+}
+
+__device__ __forceinline__ float clamp_code(float r, float qmax) {
+    return r < 0.0f ? 0.0f : (r > qmax ? qmax : r);
+}
+
+template <int DT, int BITS>
+__global__ void __launch_bounds__(kBlock) quantize_kernel(QuantArgs a) {
+    constexpr float qmax = (float)((1 << BITS) - 1);
+    const Runs r = runs_of(blockIdx.x);
+    const bool full = r.b + kRun <= a.len;
+    float x[kVec];
+    if (full) {
+        const Row w = load_row(a.src, r);
+        x[0] = widen_lo<DT>(w.a.x); x[1] = widen_hi<DT>(w.a.x);
+        x[2] = widen_lo<DT>(w.a.y); x[3] = widen_hi<DT>(w.a.y);
+        x[4] = widen_lo<DT>(w.b.x); x[5] = widen_hi<DT>(w.b.x);
+        x[6] = widen_lo<DT>(w.b.y); x[7] = widen_hi<DT>(w.b.y);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            const int64_t i = elem(r, j);
+            x[j] = i < a.len ? widen1<DT>(a.src[i]) : 0.0f;  // 0 leaves the range unchanged
+        }
+    }
+    float lo = 0.0f, hi = 0.0f;
+    uint32_t bad = 0u;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+        if (!__builtin_isfinite(x[j])) {
+            bad = 1u;
+        } else {
+            lo = take_lo(lo, x[j]);
+            hi = take_hi(hi, x[j]);
+        }
+    }
+    block_range(lo, hi, bad);
+    float sc = (hi - lo) / qmax;
+    const bool ok = bad == 0u && __builtin_isfinite(sc);
+    if (sc == 0.0f) sc = 1.0f;
+    const float z = ok ? clamp_code(__builtin_rintf(-lo / sc), qmax) : 0.0f;
+    uint32_t c[kVec];
+#pragma unroll
+    for (int j = 0; j < kVec; ++j)
+        c[j] = ok ? (uint32_t)clamp_code(__builtin_rintf(x[j] / sc) + z, qmax) : 0u;
+    if (threadIdx.x == 0) {
+        zero_qblock q;
+        q.scale = ok ? sc : __builtin_nanf("");
+        q.zero = (int32_t)z;
+        a.blocks[blockIdx.x] = q;
+    }
+    if (full) {
+        if constexpr (BITS == 8) {
+            __builtin_nontemporal_store(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                                        reinterpret_cast<uint32_t*>(a.codes + r.a));
+            __builtin_nontemporal_store(c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24),
+                                        reinterpret_cast<uint32_t*>(a.codes + r.b));
+        } else {
+            __builtin_nontemporal_store((uint16_t)(c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12)),
+                                        reinterpret_cast<uint16_t*>(a.codes + (r.a >> 1)));
+            __builtin_nontemporal_store((uint16_t)(c[4] | (c[5] << 4) | (c[6] << 8) | (c[7] << 12)),
+                                        reinterpret_cast<uint16_t*>(a.codes + (r.b >> 1)));
+        }
+    } else if constexpr (BITS == 8) {
+        for (int j = 0; j < kVec; ++j) {
+            const int64_t i = elem(r, j);
+            if (i < a.len) a.codes[i] = (uint8_t)c[j];
+        }
+    } else {
+        // element pairs (2m, 2m + 1) never straddle a run, so each byte has one writer
+        for (int j = 0; j < kVec; j += 2) {
+            const int64_t i = elem(r, j);
+            if (i < a.len) a.codes[i >> 1] = (uint8_t)(c[j] | (i + 1 < a.len ? c[j + 1] << 4 : 0u));
+        }
+    }
+}
+
+struct DequantArgs {
+    const uint8_t* codes;
+    const zero_qblock* blocks;
+    uint16_t* dst;
+    int64_t len;
+};
+
+// dst = RNE16(scale * (code - zero)), one block per workgroup.
+template <int DT, int BITS>
+__global__ void __launch_bounds__(kBlock) dequantize_kernel(DequantArgs a) {
+    const Runs r = runs_of(blockIdx.x);
+    const zero_qblock q = a.blocks[blockIdx.x];
+    if (r.b + kRun <= a.len) {
+        const QRow w = load_qrow<BITS>(a.codes, r);
+        uint32_t h[kVec];
+#pragma unroll
+        for (int j = 0; j < kRun; ++j) {
+            h[j] = narrow<DT>(dequant(q, code_at<BITS>(w.a, j)));
+            h[kRun + j] = narrow<DT>(dequant(q, code_at<BITS>(w.b, j)));
+        }
+        store_slot<4>(a.dst, r, h);
+    } else {
+        for (int j = 0; j < kVec; ++j) {
+            const int64_t i = elem(r, j);
+            if (i >= a.len) continue;
+            const int32_t code = BITS == 8 ? (int32_t)a.codes[i]
+                                           : (int32_t)((a.codes[i >> 1] >> (4 * (i & 1))) & 0xFu);
+            a.dst[i] = (uint16_t)narrow<DT>(dequant(q, code));
+        }
+    }
 }
 
 // ---------------------------------------------------------------- host side
@@ -828,23 +1109,25 @@ int check_ctrl(const zero_ctrl* c, const char* what) {
 template <class Args>
 using Kernel = void (*)(Args);
 
-template <int GW, int NR, class RS>
-Kernel<FusedArgs<RS>> fused_for_nr(int dti, int dto) {
-    if (dti == ZERO_F16 && dto == ZERO_F16) return fused_kernel<ZERO_F16, ZERO_F16, GW, NR, RS>;
-    if (dti == ZERO_F16 && dto == ZERO_BF16) return fused_kernel<ZERO_F16, ZERO_BF16, GW, NR, RS>;
-    if (dti == ZERO_BF16 && dto == ZERO_F16) return fused_kernel<ZERO_BF16, ZERO_F16, GW, NR, RS>;
-    return fused_kernel<ZERO_BF16, ZERO_BF16, GW, NR, RS>;
+template <int GW, int NR, class SRC>
+Kernel<FusedArgs<SRC>> fused_for_nr(int dto) {
+    return dto == ZERO_F16 ? fused_kernel<ZERO_F16, GW, NR, SRC> : fused_kernel<ZERO_BF16, GW, NR, SRC>;
 }
 
-template <int GW, class RS>
-Kernel<FusedArgs<RS>> fused_for(int dti, int dto, int n) {
-    return n == 8 ? fused_for_nr<GW, 8, RS>(dti, dto) : fused_for_nr<GW, 0, RS>(dti, dto);
+// Fused kernel for a slot store width gw, output dtype dto and n rows.
+template <class SRC>
+Kernel<FusedArgs<SRC>> fused_for(int gw, int dto, int n) {
+    const bool n8 = n == 8;
+    switch (gw) {
+        case 4: return n8 ? fused_for_nr<4, 8, SRC>(dto) : fused_for_nr<4, 0, SRC>(dto);
+        case 2: return n8 ? fused_for_nr<2, 8, SRC>(dto) : fused_for_nr<2, 0, SRC>(dto);
+        default: return n8 ? fused_for_nr<1, 8, SRC>(dto) : fused_for_nr<1, 0, SRC>(dto);
+    }
 }
 
-template <class RS>
-Kernel<ReduceArgs<RS>> reduce_for(int dt, int n) {
-    if (n == 8) return dt == ZERO_F16 ? reduce_kernel<ZERO_F16, 8, RS> : reduce_kernel<ZERO_BF16, 8, RS>;
-    return dt == ZERO_F16 ? reduce_kernel<ZERO_F16, 0, RS> : reduce_kernel<ZERO_BF16, 0, RS>;
+template <class SRC>
+Kernel<ReduceArgs<SRC>> reduce_for(int n) {
+    return n == 8 ? reduce_kernel<8, SRC> : reduce_kernel<0, SRC>;
 }
 
 template <int DT>
@@ -881,13 +1164,12 @@ int launch(Kernel<Args> kernel, int64_t grid, int block, hipStream_t s, const Ar
     return ok();
 }
 
-// Checks and launches shared by the two fused entry points (the rows are
-// already checked).
-template <class RS>
-int fused_launch(const RS& rows, int32_t contrib_dtype, int32_t nranks, const zero_state* pair,
-                 int64_t valid_len, void* gather, int32_t gather_dtype, int64_t offset,
-                 const zero_hparams* hp, const zero_ctrl* ctrl, void* ws, size_t ws_bytes,
-                 void* stream, const char* what) {
+// Checks and launches shared by the fused entry points (the contribution
+// source is already checked).
+template <class SRC>
+int fused_launch(const SRC& src, int32_t nranks, const zero_state* pair, int64_t valid_len,
+                 void* gather, int32_t gather_dtype, int64_t offset, const zero_hparams* hp,
+                 const zero_ctrl* ctrl, void* ws, size_t ws_bytes, void* stream, const char* what) {
     int rc;
     if ((rc = check_state(pair, what)) != ZERO_OK) return rc;
     if ((rc = check_hp(hp)) != ZERO_OK) return rc;
@@ -897,18 +1179,55 @@ int fused_launch(const RS& rows, int32_t contrib_dtype, int32_t nranks, const ze
     if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
     if (valid_len == 0) return ok();
     uint16_t* slot = (uint16_t*)gather + offset;
-    const FusedArgs<RS> a{rows, {pair->master, pair->m, pair->v}, slot, valid_len, ctrl,
-                          (Partial*)ws, *hp, nranks};
-    Kernel<FusedArgs<RS>> k;
-    switch (store_width(slot)) {
-        case 4: k = fused_for<4, RS>(contrib_dtype, gather_dtype, nranks); break;
-        case 2: k = fused_for<2, RS>(contrib_dtype, gather_dtype, nranks); break;
-        default: k = fused_for<1, RS>(contrib_dtype, gather_dtype, nranks); break;
+    const FusedArgs<SRC> a{src, {pair->master, pair->m, pair->v}, slot, valid_len, ctrl,
+                           (Partial*)ws, *hp, nranks};
+    return launch(fused_for<SRC>(store_width(slot), gather_dtype, nranks), tiles_for(valid_len),
+                  kBlock, (hipStream_t)stream, a, what);
+}
+
+// Checks and launch shared by the reduce entry points (source already checked).
+template <class SRC>
+int reduce_launch(const SRC& src, int32_t nranks, int64_t valid_len, const zero_ctrl* ctrl,
+                  float* g, void* ws, size_t ws_bytes, void* stream, const char* what) {
+    int rc;
+    if ((rc = check_ctrl(ctrl, what)) != ZERO_OK) return rc;
+    if (g == nullptr) return fail(ZERO_EINVAL, "%s: null g", what);
+    if (!aligned16(g)) return fail(ZERO_EALIGN, "%s: g not 16-byte aligned", what);
+    if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
+    if (valid_len == 0) return ok();
+    const ReduceArgs<SRC> a{src, valid_len, ctrl, g, (Partial*)ws, nranks};
+    return launch(reduce_for<SRC>(nranks), tiles_for(valid_len), kBlock, (hipStream_t)stream, a,
+                  what);
+}
+
+// Quantised row tables: bits 8 or 4, nranks in [1, ZERO_MAX_RANKS], every
+// code row and block row non-null and 8-byte aligned.
+int check_qrows(const void* const* codes, const zero_qblock* const* blocks, int32_t bits,
+                int32_t n, int64_t len, QTable* out, const char* what) {
+    int rc;
+    if ((rc = check_len(len, what)) != ZERO_OK) return rc;
+    if (bits != 8 && bits != 4) return fail(ZERO_EINVAL, "%s: bits must be 8 or 4, not %d", what, bits);
+    if (n < 1 || n > ZERO_MAX_RANKS)
+        return fail(ZERO_EINVAL, "%s: nranks %d outside [1, %d]", what, n, ZERO_MAX_RANKS);
+    if (codes == nullptr || blocks == nullptr) return fail(ZERO_EINVAL, "%s: null row table", what);
+    for (int k = 0; k < ZERO_MAX_RANKS; ++k) {
+        out->codes[k] = nullptr;
+        out->blocks[k] = nullptr;
     }
-    return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, what);
+    for (int k = 0; k < n; ++k) {
+        if (codes[k] == nullptr || blocks[k] == nullptr)
+            return fail(ZERO_EINVAL, "%s: row %d is null", what, k);
+        if (((reinterpret_cast<uintptr_t>(codes[k]) | reinterpret_cast<uintptr_t>(blocks[k])) & 7u) != 0)
+            return fail(ZERO_EALIGN, "%s: row %d not 8-byte aligned", what, k);
+        out->codes[k] = (const uint8_t*)codes[k];
+        out->blocks[k] = blocks[k];
+    }
+    return ZERO_OK;
 }
 
 }  // namespace
+
+extern "C" {}  // namespace
 
 extern "C" {
 
@@ -953,36 +1272,38 @@ int zero_reduce_grads(const void* contrib, int32_t dtype, int32_t nranks, int64_
                       size_t ws_bytes, void* stream) {
     int rc;
     if ((rc = check_contrib(contrib, dtype, nranks, stride, valid_len)) != ZERO_OK) return rc;
-    if ((rc = check_ctrl(ctrl, "zero_reduce_grads")) != ZERO_OK) return rc;
-    if (g == nullptr) return fail(ZERO_EINVAL, "zero_reduce_grads: null g");
-    if (!aligned16(g)) return fail(ZERO_EALIGN, "zero_reduce_grads: g not 16-byte aligned");
-    if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
-    if (valid_len == 0) return ok();
-    const ReduceArgs<StridedRows> a{{(const uint16_t*)contrib, stride}, valid_len, ctrl, g,
-                                    (Partial*)ws, nranks};
-    return launch(reduce_for<StridedRows>(dtype, nranks), tiles_for(valid_len), kBlock,
-                  (hipStream_t)stream, a, "zero_reduce_grads");
+    const StridedRows rows{(const uint16_t*)contrib, stride};
+    const char* what = "zero_reduce_grads";
+    return dtype == ZERO_F16
+               ? reduce_launch(Src16<ZERO_F16, StridedRows>{rows}, nranks, valid_len, ctrl, g, ws,
+                               ws_bytes, stream, what)
+               : reduce_launch(Src16<ZERO_BF16, StridedRows>{rows}, nranks, valid_len, ctrl, g, ws,
+                               ws_bytes, stream, what);
 }
 
 int zero_reduce_grads_rows(const void* const* rows, int32_t dtype, int32_t nranks,
                            int64_t valid_len, const zero_ctrl* ctrl, float* g, void* ws,
                            size_t ws_bytes, void* stream) {
     int rc;
-    ReduceArgs<TableRows> a{};
-    if ((rc = check_rows(rows, dtype, nranks, valid_len, &a.rows, "zero_reduce_grads_rows")) != ZERO_OK)
-        return rc;
-    if ((rc = check_ctrl(ctrl, "zero_reduce_grads_rows")) != ZERO_OK) return rc;
-    if (g == nullptr) return fail(ZERO_EINVAL, "zero_reduce_grads_rows: null g");
-    if (!aligned16(g)) return fail(ZERO_EALIGN, "zero_reduce_grads_rows: g not 16-byte aligned");
-    if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
-    if (valid_len == 0) return ok();
-    a.len = valid_len;
-    a.ctrl = ctrl;
-    a.g = g;
-    a.ws = (Partial*)ws;
-    a.n = nranks;
-    return launch(reduce_for<TableRows>(dtype, nranks), tiles_for(valid_len), kBlock,
-                  (hipStream_t)stream, a, "zero_reduce_grads_rows");
+    const char* what = "zero_reduce_grads_rows";
+    TableRows t;
+    if ((rc = check_rows(rows, dtype, nranks, valid_len, &t, what)) != ZERO_OK) return rc;
+    return dtype == ZERO_F16
+               ? reduce_launch(Src16<ZERO_F16, TableRows>{t}, nranks, valid_len, ctrl, g, ws,
+                               ws_bytes, stream, what)
+               : reduce_launch(Src16<ZERO_BF16, TableRows>{t}, nranks, valid_len, ctrl, g, ws,
+                               ws_bytes, stream, what);
+}
+
+int zero_reduce_grads_q(const void* const* codes, const zero_qblock* const* blocks, int32_t bits,
+                        int32_t nranks, int64_t valid_len, const zero_ctrl* ctrl, float* g,
+                        void* ws, size_t ws_bytes, void* stream) {
+    int rc;
+    const char* what = "zero_reduce_grads_q";
+    QTable t;
+    if ((rc = check_qrows(codes, blocks, bits, nranks, valid_len, &t, what)) != ZERO_OK) return rc;
+    return bits == 8 ? reduce_launch(SrcQ<8>{t}, nranks, valid_len, ctrl, g, ws, ws_bytes, stream, what)
+                     : reduce_launch(SrcQ<4>{t}, nranks, valid_len, ctrl, g, ws, ws_bytes, stream, what);
 }
 
 int zero_grad_norm_overflow(int32_t nranks, void* const* ws, const int64_t* valid_len,
@@ -1063,9 +1384,13 @@ int zero_fused_step(const void* contrib, int32_t contrib_dtype, int32_t nranks, 
                     size_t ws_bytes, void* stream) {
     int rc;
     if ((rc = check_contrib(contrib, contrib_dtype, nranks, stride, valid_len)) != ZERO_OK) return rc;
-    return fused_launch(StridedRows{(const uint16_t*)contrib, stride}, contrib_dtype, nranks, pair,
-                        valid_len, gather, gather_dtype, offset, hp, ctrl, ws, ws_bytes, stream,
-                        "zero_fused_step");
+    const StridedRows rows{(const uint16_t*)contrib, stride};
+    const char* what = "zero_fused_step";
+    return contrib_dtype == ZERO_F16
+               ? fused_launch(Src16<ZERO_F16, StridedRows>{rows}, nranks, pair, valid_len, gather,
+                              gather_dtype, offset, hp, ctrl, ws, ws_bytes, stream, what)
+               : fused_launch(Src16<ZERO_BF16, StridedRows>{rows}, nranks, pair, valid_len, gather,
+                              gather_dtype, offset, hp, ctrl, ws, ws_bytes, stream, what);
 }
 
 int zero_fused_step_rows(const void* const* rows, int32_t contrib_dtype, int32_t nranks,
@@ -1073,11 +1398,75 @@ int zero_fused_step_rows(const void* const* rows, int32_t contrib_dtype, int32_t
                          int32_t gather_dtype, int64_t offset, const zero_hparams* hp,
                          const zero_ctrl* ctrl, void* ws, size_t ws_bytes, void* stream) {
     int rc;
+    const char* what = "zero_fused_step_rows";
     TableRows t;
-    if ((rc = check_rows(rows, contrib_dtype, nranks, valid_len, &t, "zero_fused_step_rows")) != ZERO_OK)
-        return rc;
-    return fused_launch(t, contrib_dtype, nranks, pair, valid_len, gather, gather_dtype, offset,
-                        hp, ctrl, ws, ws_bytes, stream, "zero_fused_step_rows");
+    if ((rc = check_rows(rows, contrib_dtype, nranks, valid_len, &t, what)) != ZERO_OK) return rc;
+    return contrib_dtype == ZERO_F16
+               ? fused_launch(Src16<ZERO_F16, TableRows>{t}, nranks, pair, valid_len, gather,
+                              gather_dtype, offset, hp, ctrl, ws, ws_bytes, stream, what)
+               : fused_launch(Src16<ZERO_BF16, TableRows>{t}, nranks, pair, valid_len, gather,
+                              gather_dtype, offset, hp, ctrl, ws, ws_bytes, stream, what);
+}
+
+int zero_fused_step_q(const void* const* codes, const zero_qblock* const* blocks, int32_t bits,
+                      int32_t nranks, const zero_state* pair, int64_t valid_len, void* gather,
+                      int32_t gather_dtype, int64_t offset, const zero_hparams* hp,
+                      const zero_ctrl* ctrl, void* ws, size_t ws_bytes, void* stream) {
+    int rc;
+    const char* what = "zero_fused_step_q";
+    QTable t;
+    if ((rc = check_qrows(codes, blocks, bits, nranks, valid_len, &t, what)) != ZERO_OK) return rc;
+    return bits == 8 ? fused_launch(SrcQ<8>{t}, nranks, pair, valid_len, gather, gather_dtype,
+                                    offset, hp, ctrl, ws, ws_bytes, stream, what)
+                     : fused_launch(SrcQ<4>{t}, nranks, pair, valid_len, gather, gather_dtype,
+                                    offset, hp, ctrl, ws, ws_bytes, stream, what);
+}
+
+size_t zero_qblock_count(int64_t len) { return (size_t)tiles_for(len); }
+
+size_t zero_qcode_bytes(int64_t len, int32_t bits) {
+    if (len <= 0) return 0;
+    return bits == 4 ? (size_t)((len + 1) / 2) : (size_t)len;
+}
+
+int zero_quantize_blocks(const void* src, int32_t dtype, int64_t len, int32_t bits, void* codes,
+                         zero_qblock* blocks, void* stream) {
+    int rc;
+    const char* what = "zero_quantize_blocks";
+    if ((rc = check_len(len, what)) != ZERO_OK) return rc;
+    if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, "%s: unknown dtype %d", what, dtype);
+    if (bits != 8 && bits != 4) return fail(ZERO_EINVAL, "%s: bits must be 8 or 4, not %d", what, bits);
+    if (src == nullptr || codes == nullptr || blocks == nullptr)
+        return fail(ZERO_EINVAL, "%s: null pointer", what);
+    if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(codes) |
+          reinterpret_cast<uintptr_t>(blocks)) & 7u) != 0)
+        return fail(ZERO_EALIGN, "%s: src, codes and blocks must be 8-byte aligned", what);
+    if (len == 0) return ok();
+    const QuantArgs a{(const uint16_t*)src, (uint8_t*)codes, blocks, len};
+    Kernel<QuantArgs> k;
+    if (dtype == ZERO_F16) k = bits == 8 ? quantize_kernel<ZERO_F16, 8> : quantize_kernel<ZERO_F16, 4>;
+    else k = bits == 8 ? quantize_kernel<ZERO_BF16, 8> : quantize_kernel<ZERO_BF16, 4>;
+    return launch(k, tiles_for(len), kBlock, (hipStream_t)stream, a, what);
+}
+
+int zero_dequantize_blocks(const void* codes, const zero_qblock* blocks, int32_t bits, int64_t len,
+                           void* dst, int32_t dtype, void* stream) {
+    int rc;
+    const char* what = "zero_dequantize_blocks";
+    if ((rc = check_len(len, what)) != ZERO_OK) return rc;
+    if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, "%s: unknown dtype %d", what, dtype);
+    if (bits != 8 && bits != 4) return fail(ZERO_EINVAL, "%s: bits must be 8 or 4, not %d", what, bits);
+    if (dst == nullptr || codes == nullptr || blocks == nullptr)
+        return fail(ZERO_EINVAL, "%s: null pointer", what);
+    if (((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(codes) |
+          reinterpret_cast<uintptr_t>(blocks)) & 7u) != 0)
+        return fail(ZERO_EALIGN, "%s: dst, codes and blocks must be 8-byte aligned", what);
+    if (len == 0) return ok();
+    const DequantArgs a{(const uint8_t*)codes, blocks, (uint16_t*)dst, len};
+    Kernel<DequantArgs> k;
+    if (dtype == ZERO_F16) k = bits == 8 ? dequantize_kernel<ZERO_F16, 8> : dequantize_kernel<ZERO_F16, 4>;
+    else k = bits == 8 ? dequantize_kernel<ZERO_BF16, 8> : dequantize_kernel<ZERO_BF16, 4>;
+    return launch(k, tiles_for(len), kBlock, (hipStream_t)stream, a, what);
 }
 
 int zero_fused_restore(const zero_state* pair, int64_t valid_len, void* gather, int32_t dtype,
