@@ -27,7 +27,6 @@ if ROOT not in sys.path:
 
 METRIC = "fused ZeRO shard step effective GB/s + % of HBM peak (1 MI355X)"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ("zero_partitioned_mixed_amd/csrc/zero_shard.hip", "include/zero_shard.h")
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "psi1.3e10_n8_dynscale"
 
@@ -36,35 +35,31 @@ def _fmt(x, nd=3):
     return float(f"{x:.{nd}g}") if x is not None else None
 
 
-def kernel_source_sha256() -> str:
-    """Digest of the library's kernel sources (comments and layout stripped,
-    so documentation edits do not count as kernel changes) and hipcc flags."""
-    import hashlib
-    import re
-
+def kernel_isa_digest(kernel: str):
+    """SHA-256 of the named kernel's machine code in the built library (from
+    libzero_shard.isa.json, which the build writes), or None."""
     from zero_partitioned_mixed_amd import build as zbuild
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        text = open(os.path.join(ROOT, rel)).read()
-        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-        text = re.sub(r"//[^\n]*", " ", text)
-        h.update(" ".join(text.split()).encode())
-    h.update(" ".join(zbuild.HIPCC_FLAGS[:-1]).encode())  # the include path varies by machine
-    return h.hexdigest()
+    try:
+        with open(zbuild.ISA_JSON) as f:
+            return json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(label: str, workload: str):
     """HBM bytes per launch from the committed PMC summary of this kernel and
-    workload, or None when there is none or the kernel source has changed
-    since the counters were taken."""
-    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.md")
+    workload, or None when there is none or when the profiled kernel's
+    machine code differs from the one in the built library (the counters
+    then describe another kernel)."""
+    path = os.path.join(PROFILES, f"{label}_{workload}_pmc.md")
     try:
         fields = {}
         for line in open(path):
             if ":" in line and line.startswith("- "):
                 k, v = line[2:].split(":", 1)
                 fields[k.strip()] = v.strip().strip("`")
-        if fields.get("source_sha256") != kernel_source_sha256():
+        digest = kernel_isa_digest(fields["kernel"])
+        if digest is None or fields.get("isa_sha256") != digest:
             return None
         return int(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
