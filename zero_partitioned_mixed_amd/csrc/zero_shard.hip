@@ -3,13 +3,19 @@
 // Every kernel here streams HBM: the work per element is a handful of fp32
 // operations against 26 + 2N bytes, so nothing is a contraction and nothing
 // uses the matrix cores.  The design points are
-//   * one workgroup per tile of ZERO_TILE = 2048 elements (256 threads x 8
-//     elements), launched as one grid over the whole shard: a block moves
-//     16-byte vectors (8 sixteen-bit or 4 fp32 values per access, 4 KiB per
-//     instruction per workgroup) for every stream it touches and retires, so
-//     the dispatcher keeps the active window of the shard compact, which is
-//     what lets HBM pages be reused across the streams;
-//   * non-temporal hints on every access: each byte is touched once per step;
+//   * one workgroup per tile of ZERO_TILE = 2048 elements (4 wave64s x 64
+//     lanes x 8 elements), launched as one grid over the whole shard, so
+//     workgroups retire in dispatch order and the active window of the shard
+//     stays compact (a grid-stride loop measured slower);
+//   * wave-contiguous lanes: lane l of wave w owns two runs of four elements,
+//     [512w + 4l, +4) and 256 elements later, so every memory instruction of a
+//     wave covers one contiguous span and fills whole cache lines;
+//   * every load of an element group is issued before its first use (a
+//     scheduling barrier keeps the compiler from sinking loads behind the
+//     arithmetic), with non-temporal hints: each byte is touched once a step;
+//   * the contributions come from a source: one [N, stride] buffer, a table
+//     of one pointer per row (peer-mapped slices), or block-quantised INT8 /
+//     INT4 rows (ZeRO++ payloads); the rest of the step is shared;
 //   * the fused path double-buffers the optimizer state with the two sets of
 //     a tile adjacent in memory, so reading one set and writing the other
 //     keeps the locality of an in-place update;
