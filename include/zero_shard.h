@@ -300,7 +300,9 @@ int zero_pair_load(const zero_state *pair, const zero_state *flat, int64_t valid
  *   dequantises to NaN and a downstream overflow check still fires.
  *   Codes: bits = 8, one byte per element; bits = 4, two per byte, the
  *   even-indexed element in the low nibble.
- * Pointers (codes, blocks, 16-bit src/dst) must be 8-byte aligned. */
+ * codes and blocks must be 8-byte aligned; a 16-bit src or dst needs only
+ * 2-byte alignment (a parameter slot at any offset), with vector accesses
+ * where its alignment allows. */
 
 /* Blocks of a quantised buffer of len elements: ceil(len / ZERO_QBLOCK). */
 size_t zero_qblock_count(int64_t len);

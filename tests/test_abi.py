@@ -189,10 +189,12 @@ def test_quantize_validation(Z):
     assert L.zero_quantize_blocks(FAKE, 1, 64, 3, FAKE, FAKE, None) == -1          # bits
     assert L.zero_quantize_blocks(FAKE, 7, 64, 8, FAKE, FAKE, None) == -1          # dtype
     assert L.zero_quantize_blocks(0, 1, 64, 8, FAKE, FAKE, None) == -1
-    assert L.zero_quantize_blocks(FAKE + 2, 1, 64, 8, FAKE, FAKE, None) == -2
+    assert L.zero_quantize_blocks(FAKE + 1, 1, 64, 8, FAKE, FAKE, None) == -2      # odd src
+    assert L.zero_quantize_blocks(FAKE + 2, 1, 64, 8, FAKE + 4, FAKE, None) == -2  # codes
     assert L.zero_quantize_blocks(FAKE, 1, 64, 4, FAKE + 4, FAKE, None) == -2
     assert L.zero_quantize_blocks(FAKE, 1, -5, 8, FAKE, FAKE, None) == -3
-    assert L.zero_dequantize_blocks(FAKE, FAKE, 4, 64, FAKE + 6, 1, None) == -2
+    assert L.zero_dequantize_blocks(FAKE, FAKE, 4, 64, FAKE + 7, 1, None) == -2    # odd dst
+    assert L.zero_dequantize_blocks(FAKE, FAKE + 2, 4, 64, FAKE + 6, 1, None) == -2  # blocks
     assert L.zero_dequantize_blocks(FAKE, FAKE, 2, 64, FAKE, 1, None) == -1
     assert L.zero_dequantize_blocks(FAKE, None, 8, 64, FAKE, 2, None) == -1
 

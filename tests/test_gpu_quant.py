@@ -148,3 +148,63 @@ def test_quantized_step_gpt2_sized(bits):
     H.assert_f32_close("v", v, rv)
     H.assert_16bit_within_ulp("slot", slot, rslot, w.dtype)
     H.log(f"gpt2 q{bits}: ok, norm {g.reports[-1]['norm']:.9g} (16-bit path: see parity tests)")
+
+
+@pytest.mark.parametrize("shift", [1, 2, 3])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantize_and_dequantize_unaligned(bits, shift):
+    """16-bit buffers at 2-, 4- and 6-byte offsets (a parameter slot at any
+    offset): the 16-bit loads and the narrower stores give the same codes and
+    values as the oracle."""
+    import torch
+    import zero_partitioned_mixed_amd as Z
+    length = 5 * 2048 + 333
+    src = O.from_f32(_values(length, seed=40 + shift), F16)
+    ref = O.quantize(src, F16, bits)
+    buf = torch.zeros(length + 8, dtype=torch.int16, device="cuda")
+    buf[shift:shift + length] = _to_gpu(src.view(np.int16))
+    q = Z.QuantRows.alloc(1, length, bits, torch.device("cuda", 0))
+    codes, blocks = q.rows[0]
+    Z.zero_quantize_blocks(buf[shift:], F16, length, bits, codes, blocks)
+    dst = torch.full((length + 8,), 7.0, dtype=torch.float16, device="cuda")
+    Z.zero_dequantize_blocks(codes, blocks, bits, length, dst[shift:], F16)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy()[:ref.codes.size], ref.codes)
+    got = dst.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = O.cast(O.dequantize(ref), F16)
+    seven = O.from_f32(np.array([7.0], np.float32), F16)[0]
+    assert np.array_equal(got[shift:shift + length], want)
+    assert np.all(got[:shift] == seven) and np.all(got[shift + length:] == seven)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantized_all_gather_of_updated_slot(bits):
+    """ZeRO++'s parameter path on one rank: after a fused step writes the
+    rank's 16-bit slot (at an odd offset of the full buffer), the slot is
+    block-quantised for the all-gather and dequantised on the receiving side
+    into the same place of a second full buffer.  Checked against the oracle's
+    step, quantiser and dequantiser."""
+    import torch
+    import zero_partitioned_mixed_amd as Z
+    w = small(7 * 30_001, 7, 5, steps=2)
+    c = Case(w, 5, 2)
+    _, off, valid = c.part
+    assert off % 2 == 1
+    g = H.GpuRun(c, full_gather=True)
+    g.run()
+    slot = g.gather[off:off + valid]
+    q = Z.QuantRows.alloc(1, valid, bits, slot.device)
+    codes, blocks = q.rows[0]
+    Z.zero_quantize_blocks(slot, F16, valid, bits, codes, blocks)
+    received = torch.zeros_like(g.gather)
+    Z.zero_dequantize_blocks(codes, blocks, bits, valid, received[off:], F16)
+    torch.cuda.synchronize()
+    reps = H.oracle_scalars(c)
+    _, _, _, oslot = H.oracle_elements(c, reps)
+    got_slot = slot.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got_slot, oslot)      # the step itself (fp16 slot) is exact here
+    ref = O.quantize(oslot, F16, bits)
+    assert np.array_equal(codes.cpu().numpy()[:ref.codes.size], ref.codes)
+    got = received.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got[off:off + valid], O.cast(O.dequantize(ref), F16))
+    assert not got[:off].any() and not got[off + valid:].any()

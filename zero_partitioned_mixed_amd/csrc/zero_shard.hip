@@ -929,13 +929,14 @@ __device__ __forceinline__ float clamp_code(float r, float qmax) {
     return r < 0.0f ? 0.0f : (r > qmax ? qmax : r);
 }
 
-template <int DT, int BITS>
+// VEC: src is 8-byte aligned (vector loads); otherwise 16-bit loads.
+template <int DT, int BITS, bool VEC>
 __global__ void __launch_bounds__(kBlock) quantize_kernel(QuantArgs a) {
     constexpr float qmax = (float)((1 << BITS) - 1);
     const Runs r = runs_of(blockIdx.x);
     const bool full = r.b + kRun <= a.len;
     float x[kVec];
-    if (full) {
+    if (VEC && full) {
         const Row w = load_row(a.src, r);
         x[0] = widen_lo<DT>(w.a.x); x[1] = widen_hi<DT>(w.a.x);
         x[2] = widen_lo<DT>(w.a.y); x[3] = widen_hi<DT>(w.a.y);
@@ -1007,8 +1008,9 @@ struct DequantArgs {
     int64_t len;
 };
 
-// dst = RNE16(scale * (code - zero)), one block per workgroup.
-template <int DT, int BITS>
+// dst = RNE16(scale * (code - zero)), one block per workgroup; GW is the
+// store width of dst as for the gather slot (4, 2 or 1 elements).
+template <int DT, int BITS, int GW>
 __global__ void __launch_bounds__(kBlock) dequantize_kernel(DequantArgs a) {
     const Runs r = runs_of(blockIdx.x);
     const zero_qblock q = a.blocks[blockIdx.x];
@@ -1020,7 +1022,7 @@ __global__ void __launch_bounds__(kBlock) dequantize_kernel(DequantArgs a) {
             h[j] = narrow<DT>(dequant(q, code_at<BITS>(w.a, j)));
             h[kRun + j] = narrow<DT>(dequant(q, code_at<BITS>(w.b, j)));
         }
-        store_slot<4>(a.dst, r, h);
+        store_slot<GW>(a.dst, r, h);
     } else {
         for (int j = 0; j < kVec; ++j) {
             const int64_t i = elem(r, j);
@@ -1168,6 +1170,20 @@ Kernel<FusedArgs<SRC>> fused_for(int gw, int dto, int n) {
         case 2: return n8 ? fused_for_nr<2, 8, SRC>(dto) : fused_for_nr<2, 0, SRC>(dto);
         default: return n8 ? fused_for_nr<1, 8, SRC>(dto) : fused_for_nr<1, 0, SRC>(dto);
     }
+}
+
+template <int DT, int BITS>
+Kernel<DequantArgs> dequant_for_bits(int gw) {
+    switch (gw) {
+        case 4: return dequantize_kernel<DT, BITS, 4>;
+        case 2: return dequantize_kernel<DT, BITS, 2>;
+        default: return dequantize_kernel<DT, BITS, 1>;
+    }
+}
+
+template <int DT>
+Kernel<DequantArgs> dequant_for(int bits, int gw) {
+    return bits == 8 ? dequant_for_bits<DT, 8>(gw) : dequant_for_bits<DT, 4>(gw);
 }
 
 template <class SRC>
@@ -1483,14 +1499,21 @@ int zero_quantize_blocks(const void* src, int32_t dtype, int64_t len, int32_t bi
     if (bits != 8 && bits != 4) return fail(ZERO_EINVAL, "%s: bits must be 8 or 4, not %d", what, bits);
     if (src == nullptr || codes == nullptr || blocks == nullptr)
         return fail(ZERO_EINVAL, "%s: null pointer", what);
-    if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(codes) |
-          reinterpret_cast<uintptr_t>(blocks)) & 7u) != 0)
-        return fail(ZERO_EALIGN, "%s: src, codes and blocks must be 8-byte aligned", what);
+    if (((reinterpret_cast<uintptr_t>(codes) | reinterpret_cast<uintptr_t>(blocks)) & 7u) != 0)
+        return fail(ZERO_EALIGN, "%s: codes and blocks must be 8-byte aligned", what);
+    if ((reinterpret_cast<uintptr_t>(src) & 1u) != 0)
+        return fail(ZERO_EALIGN, "%s: src not 2-byte aligned", what);
     if (len == 0) return ok();
     const QuantArgs a{(const uint16_t*)src, (uint8_t*)codes, blocks, len};
+    const bool vec = (reinterpret_cast<uintptr_t>(src) & 7u) == 0;
     Kernel<QuantArgs> k;
-    if (dtype == ZERO_F16) k = bits == 8 ? quantize_kernel<ZERO_F16, 8> : quantize_kernel<ZERO_F16, 4>;
-    else k = bits == 8 ? quantize_kernel<ZERO_BF16, 8> : quantize_kernel<ZERO_BF16, 4>;
+    if (dtype == ZERO_F16) {
+        if (bits == 8) k = vec ? quantize_kernel<ZERO_F16, 8, true> : quantize_kernel<ZERO_F16, 8, false>;
+        else k = vec ? quantize_kernel<ZERO_F16, 4, true> : quantize_kernel<ZERO_F16, 4, false>;
+    } else {
+        if (bits == 8) k = vec ? quantize_kernel<ZERO_BF16, 8, true> : quantize_kernel<ZERO_BF16, 8, false>;
+        else k = vec ? quantize_kernel<ZERO_BF16, 4, true> : quantize_kernel<ZERO_BF16, 4, false>;
+    }
     return launch(k, tiles_for(len), kBlock, (hipStream_t)stream, a, what);
 }
 
@@ -1503,14 +1526,14 @@ int zero_dequantize_blocks(const void* codes, const zero_qblock* blocks, int32_t
     if (bits != 8 && bits != 4) return fail(ZERO_EINVAL, "%s: bits must be 8 or 4, not %d", what, bits);
     if (dst == nullptr || codes == nullptr || blocks == nullptr)
         return fail(ZERO_EINVAL, "%s: null pointer", what);
-    if (((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(codes) |
-          reinterpret_cast<uintptr_t>(blocks)) & 7u) != 0)
-        return fail(ZERO_EALIGN, "%s: dst, codes and blocks must be 8-byte aligned", what);
+    if (((reinterpret_cast<uintptr_t>(codes) | reinterpret_cast<uintptr_t>(blocks)) & 7u) != 0)
+        return fail(ZERO_EALIGN, "%s: codes and blocks must be 8-byte aligned", what);
+    if ((reinterpret_cast<uintptr_t>(dst) & 1u) != 0)
+        return fail(ZERO_EALIGN, "%s: dst not 2-byte aligned", what);
     if (len == 0) return ok();
     const DequantArgs a{(const uint8_t*)codes, blocks, (uint16_t*)dst, len};
-    Kernel<DequantArgs> k;
-    if (dtype == ZERO_F16) k = bits == 8 ? dequantize_kernel<ZERO_F16, 8> : dequantize_kernel<ZERO_F16, 4>;
-    else k = bits == 8 ? dequantize_kernel<ZERO_BF16, 8> : dequantize_kernel<ZERO_BF16, 4>;
+    const Kernel<DequantArgs> k = dtype == ZERO_F16 ? dequant_for<ZERO_F16>(bits, store_width(dst))
+                                                    : dequant_for<ZERO_BF16>(bits, store_width(dst));
     return launch(k, tiles_for(len), kBlock, (hipStream_t)stream, a, what);
 }
 
