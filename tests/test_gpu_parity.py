@@ -115,6 +115,10 @@ SMALL = {
     "f16_fused_inf_in_padding": (small(100_003, 3, 2, steps=2), (Inject(1, 1, 33_340, np.inf),)),
     "bf16_twopass_inf_skip": (small(200_000, 8, 5, dtype=BF16, max_grad_norm=0.05, steps=4),
                               (Inject(2, 7, 12_345, np.inf),)),
+    "f16_fused_skip_offset_odd": (small(69_990, 7, 5, steps=3, scaler=2, contrib_scale=2.0 ** 10,
+                                        loss_scale=2.0 ** 10), (Inject(2, 3, 4_000, np.inf),)),
+    "bf16_fused_skip_offset_2mod4": (small(100_003, 3, 2, dtype=BF16, steps=3),
+                                     (Inject(2, 0, 2_049, np.nan),)),
     "f16_fused_dynamic_growth": (small(60_016, 4, 3, steps=6, scaler=2, growth_interval=2,
                                        contrib_scale=2.0 ** 12, loss_scale=2.0 ** 12),
                                  (Inject(4, 1, 5, np.inf),)),

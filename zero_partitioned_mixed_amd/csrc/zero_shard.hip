@@ -753,18 +753,28 @@ __global__ void __launch_bounds__(kBlock) cast_kernel(CastArgs a) {
 }
 
 // After a skipped fused step: gather slot <- RNE(current set of the paired
-// master).  A fixed small grid walks the tiles; with no skip every
-// workgroup returns after reading the flag.
-template <int DT>
+// master).  A fixed small grid walks the tiles (with no skip every workgroup
+// returns after reading the flag), with the cast's vector accesses.
+template <int DT, int GW>
 __global__ void __launch_bounds__(kBlock) restore_kernel(CastArgs a) {
     if (!a.ctrl->skip) return;
     const int cur = a.ctrl->cur;
     const int64_t ntile = (a.len + kTile - 1) / kTile;
     for (int64_t tile = blockIdx.x; tile < ntile; tile += gridDim.x) {
         const Runs r = runs_of(tile);
-        for (int j = 0; j < kVec; ++j) {
-            const int64_t i = elem(r, j);
-            if (i < a.len) a.slot[i] = (uint16_t)narrow<DT>(a.master[pair_index(i, cur)]);
+        if (r.b + kRun <= a.len) {
+            const int64_t sa = pair_index(r.a, cur);
+            float p[kVec];
+            uint32_t h[kVec];
+            load8(a.master + sa, a.master + sa + 256, p);
+#pragma unroll
+            for (int j = 0; j < kVec; ++j) h[j] = narrow<DT>(p[j]);
+            store_slot<GW>(a.slot, r, h);
+        } else {
+            for (int j = 0; j < kVec; ++j) {
+                const int64_t i = elem(r, j);
+                if (i < a.len) a.slot[i] = (uint16_t)narrow<DT>(a.master[pair_index(i, cur)]);
+            }
         }
     }
 }
@@ -1547,7 +1557,13 @@ int zero_fused_restore(const zero_state* pair, int64_t valid_len, void* gather, 
     if (valid_len == 0) return ok();
     CastArgs a{pair->master, (uint16_t*)gather + offset, valid_len, ctrl};
     const int64_t nt = tiles_for(valid_len);
-    Kernel<CastArgs> k = dtype == ZERO_F16 ? restore_kernel<ZERO_F16> : restore_kernel<ZERO_BF16>;
+    const int gw = store_width((uint16_t*)gather + offset);
+    Kernel<CastArgs> k;
+    switch (gw) {
+        case 4: k = dtype == ZERO_F16 ? restore_kernel<ZERO_F16, 4> : restore_kernel<ZERO_BF16, 4>; break;
+        case 2: k = dtype == ZERO_F16 ? restore_kernel<ZERO_F16, 2> : restore_kernel<ZERO_BF16, 2>; break;
+        default: k = dtype == ZERO_F16 ? restore_kernel<ZERO_F16, 1> : restore_kernel<ZERO_BF16, 1>; break;
+    }
     return launch(k, nt < kRestoreGrid ? nt : kRestoreGrid, kBlock, (hipStream_t)stream, a,
                   "zero_fused_restore");
 }
