@@ -162,12 +162,12 @@ def test_run_to_run_bitwise():
 
 
 # --------------------------------------------------------------------------- toy: all 32 shards
-def _toy(inject=None):
+def _toy(inject=None, w=None):
     import torch
     import oracle as O
     import synth
     import zero_partitioned_mixed_amd as Z
-    w = workloads.TOY
+    w = workloads.TOY if w is None else w
     n = w.nranks
     H.log(f"toy: psi={w.psi} N={n} all shards, steps={w.steps}, inject={inject}")
     gather = torch.empty(w.psi, dtype=torch.float16, device="cuda")
@@ -231,6 +231,22 @@ def test_toy_all_shards():
 
 def test_toy_overflow_on_one_rank_skips_all():
     _toy(inject=(2, 5, 3, 19_000))
+
+
+def test_64_ranks_combined_in_one_decision():
+    """ZERO_MAX_RANKS = 64 shards of a ragged buffer (the last one short)
+    stepped on one GPU with one shared decision per step."""
+    w = Workload(name="ranks64", psi=64 * 3_001 - 40, nranks=64, ranks=tuple(range(64)),
+                 dtype=F16, steps=2)
+    _toy(w=w)
+
+
+def test_max_contributions_in_one_buffer():
+    """ZERO_MAX_CONTRIB = 1024 contribution rows in one [N, stride] buffer
+    (128 chunks of eight rows in the generic loop), fused and two-pass."""
+    run_case(Case(small(1024 * 2_101, 1024, 1023), 1023, 2), "n1024_fused")
+    run_case(Case(small(1024 * 2_101, 1024, 5, dtype=BF16, max_grad_norm=0.01), 5, 2),
+             "n1024_two_pass")
 
 
 # --------------------------------------------------------------------------- full configs
