@@ -285,8 +285,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one rank's shard step on ONE GPU; this build has no multi-GPU "
-              "path (collectives are out of its scope). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one rank's shard step on ONE GPU; the library has no multi-GPU "
+              "path (collectives between GPUs are outside it). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
