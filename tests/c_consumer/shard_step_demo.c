@@ -1,0 +1,163 @@
+/* A plain C consumer of the shard-step C ABI (include/zero_shard.h): no Python,
+ * no torch.  Device memory comes from the HIP runtime's C API, inputs from the
+ * seeded host generator (libsynth_cpu), and every step of the path from
+ * libzero_shard.
+ *
+ *   shard_step_demo host        partition, size queries and argument checks
+ *                               (needs no GPU)
+ *   shard_step_demo gpu FILE    runs two ranks of a small workload on the GPU
+ *                               and writes their results to FILE for the test
+ *                               to compare with the oracle:
+ *     rank 2, fused path, dynamic loss scale, +inf in contribution 1 at step 2
+ *     rank 1, two-pass path, clipping at 0.01
+ *   both of Psi = 120,007 (fp16) over N = 3 ranks, 3 steps.
+ */
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "zero_shard.h"
+
+/* libsynth_cpu (the seeded input generator shared by both sides of the tests) */
+void synth_contrib_rows(uint64_t seed, uint32_t step, int32_t n, int32_t dtype, double sigma,
+                        double scale, uint64_t outlier_thresh, double outlier_mult, int64_t idx0,
+                        int64_t len, int64_t stride, uint16_t *out);
+void synth_master_range(uint64_t seed, double sigma, int64_t idx0, int64_t len, float *out);
+void synth_param_range(uint64_t seed, double sigma, int32_t dtype, int64_t idx0, int64_t len,
+                       uint16_t *out);
+
+enum { PSI = 120007, NR = 3, STEPS = 3 };
+static const double SCALE = 1024.0;
+
+#define HIP(x)                                                                          \
+    do {                                                                                \
+        hipError_t e_ = (x);                                                            \
+        if (e_ != hipSuccess) {                                                         \
+            fprintf(stderr, "%s:%d %s: %s\n", __FILE__, __LINE__, #x, hipGetErrorString(e_)); \
+            exit(3);                                                                    \
+        }                                                                               \
+    } while (0)
+
+#define ZERO(x)                                                                          \
+    do {                                                                                 \
+        int rc_ = (x);                                                                   \
+        if (rc_ != ZERO_OK) {                                                            \
+            fprintf(stderr, "%s:%d %s -> %d: %s\n", __FILE__, __LINE__, #x, rc_, zero_last_error()); \
+            exit(4);                                                                     \
+        }                                                                                \
+    } while (0)
+
+static int host_mode(void) {
+    int64_t shard, off, valid;
+    ZERO(zero_partition(PSI, NR, 2, &shard, &off, &valid));
+    if (shard != 40003 || off != 80006 || valid != 40001) return fprintf(stderr, "partition\n"), 1;
+    ZERO(zero_partition(10, 7, 6, &shard, &off, &valid));
+    if (shard != 2 || off != 12 || valid != 0) return fprintf(stderr, "empty rank\n"), 1;
+    if (zero_ctrl_bytes() != 128 || zero_workspace_bytes(4097) != (3 + 256) * 16 ||
+        zero_pair_elems(4097) != 6 * 2048 || zero_qcode_bytes(5, 4) != 3)
+        return fprintf(stderr, "sizes\n"), 1;
+    if (zero_partition(0, 3, 0, &shard, &off, &valid) != ZERO_EINVAL || zero_last_error()[0] == 0)
+        return fprintf(stderr, "error path\n"), 1;
+    if (zero_reduce_grads(NULL, ZERO_F16, 3, 64, 64, NULL, NULL, NULL, 0, NULL) != ZERO_EINVAL)
+        return fprintf(stderr, "validation\n"), 1;
+    printf("host ok\n");
+    return 0;
+}
+
+/* One rank's STEPS steps; appends ctrl after each step, then master, m, v
+ * (valid floats each) and the slot (valid 16-bit words) to f. */
+static void run_rank(FILE *f, int32_t rank, float max_grad_norm, int inject) {
+    int64_t shard, off, valid;
+    ZERO(zero_partition(PSI, NR, rank, &shard, &off, &valid));
+    const int64_t stride = (shard + 63) / 64 * 64;
+    const int fused = !(max_grad_norm > 0.0f);
+    zero_hparams hp = {1e-3f, 0.9f, 0.999f, 1e-8f, 0.0f, max_grad_norm,
+                       fused ? ZERO_SCALER_DYNAMIC : ZERO_SCALER_STATIC, 1.0f, 1000};
+    const float loss_scale = (float)SCALE;
+
+    uint16_t *C = malloc(sizeof(uint16_t) * NR * stride);
+    float *p0 = malloc(sizeof(float) * valid);
+    uint16_t *gather = malloc(sizeof(uint16_t) * PSI);
+    synth_master_range(0, 0.02, off, valid, p0);
+    synth_param_range(0, 0.02, ZERO_F16, 0, PSI, gather);
+
+    void *dC, *dG, *dCtrl, *dWs, *dg = NULL;
+    float *flat[3], *pair[3];
+    const size_t ws_bytes = zero_workspace_bytes(valid);
+    HIP(hipMalloc(&dC, sizeof(uint16_t) * NR * stride));
+    HIP(hipMalloc(&dG, sizeof(uint16_t) * PSI));
+    HIP(hipMalloc(&dCtrl, zero_ctrl_bytes()));
+    HIP(hipMalloc(&dWs, ws_bytes));
+    for (int q = 0; q < 3; ++q) {
+        HIP(hipMalloc((void **)&flat[q], sizeof(float) * valid));
+        HIP(hipMemset(flat[q], 0, sizeof(float) * valid));
+        HIP(hipMalloc((void **)&pair[q], sizeof(float) * zero_pair_elems(valid)));
+    }
+    HIP(hipMemcpy(flat[0], p0, sizeof(float) * valid, hipMemcpyHostToDevice));
+    HIP(hipMemcpy(dG, gather, sizeof(uint16_t) * PSI, hipMemcpyHostToDevice));
+    if (!fused) HIP(hipMalloc(&dg, sizeof(float) * valid));
+
+    zero_state st_flat = {flat[0], flat[1], flat[2]}, st_pair = {pair[0], pair[1], pair[2]};
+    ZERO(zero_ctrl_init(dCtrl, loss_scale, NULL));
+    if (fused) ZERO(zero_pair_store(&st_flat, &st_pair, valid, dCtrl, NULL));
+    for (uint32_t s = 1; s <= STEPS; ++s) {
+        synth_contrib_rows(0, s, NR, ZERO_F16, 1e-3, SCALE, 0, 100.0, off, valid, stride, C);
+        if (inject && s == 2) C[1 * stride + 123] = 0x7C00; /* +inf in contribution 1 */
+        HIP(hipMemcpy(dC, C, sizeof(uint16_t) * NR * stride, hipMemcpyHostToDevice));
+        void *ws_arr[1] = {dWs};
+        int64_t len_arr[1] = {valid};
+        zero_ctrl *ctrl_arr[1] = {dCtrl};
+        if (fused) {
+            ZERO(zero_fused_step(dC, ZERO_F16, NR, stride, &st_pair, valid, dG, ZERO_F16, off, &hp,
+                                 dCtrl, dWs, ws_bytes, NULL));
+            ZERO(zero_grad_norm_overflow(1, ws_arr, len_arr, ctrl_arr, &hp, 1, NULL));
+            ZERO(zero_fused_restore(&st_pair, valid, dG, ZERO_F16, off, dCtrl, NULL));
+        } else {
+            ZERO(zero_reduce_grads(dC, ZERO_F16, NR, stride, valid, dCtrl, dg, dWs, ws_bytes, NULL));
+            ZERO(zero_grad_norm_overflow(1, ws_arr, len_arr, ctrl_arr, &hp, 0, NULL));
+            ZERO(zero_adam_step(&st_flat, dg, valid, &hp, dCtrl, dG, ZERO_F16, off, NULL));
+        }
+        zero_ctrl c;
+        HIP(hipMemcpy(&c, dCtrl, sizeof c, hipMemcpyDeviceToHost));
+        fwrite(&c, sizeof c, 1, f);
+    }
+    if (fused) ZERO(zero_pair_load(&st_pair, &st_flat, valid, dCtrl, NULL));
+    HIP(hipDeviceSynchronize());
+    float *out = malloc(sizeof(float) * valid);
+    for (int q = 0; q < 3; ++q) {
+        HIP(hipMemcpy(out, flat[q], sizeof(float) * valid, hipMemcpyDeviceToHost));
+        fwrite(out, sizeof(float), (size_t)valid, f);
+    }
+    HIP(hipMemcpy(gather, dG, sizeof(uint16_t) * PSI, hipMemcpyDeviceToHost));
+    fwrite(gather + off, sizeof(uint16_t), (size_t)valid, f);
+    for (int q = 0; q < 3; ++q) {
+        HIP(hipFree(flat[q]));
+        HIP(hipFree(pair[q]));
+    }
+    HIP(hipFree(dC));
+    HIP(hipFree(dG));
+    HIP(hipFree(dCtrl));
+    HIP(hipFree(dWs));
+    if (dg) HIP(hipFree(dg));
+    free(C);
+    free(p0);
+    free(gather);
+    free(out);
+}
+
+int main(int argc, char **argv) {
+    if (argc >= 2 && strcmp(argv[1], "host") == 0) return host_mode();
+    if (argc >= 3 && strcmp(argv[1], "gpu") == 0) {
+        FILE *f = fopen(argv[2], "wb");
+        if (!f) return 2;
+        run_rank(f, 2, 0.0f, 1);
+        run_rank(f, 1, 0.01f, 0);
+        fclose(f);
+        printf("gpu ok\n");
+        return 0;
+    }
+    fprintf(stderr, "usage: %s host | gpu FILE\n", argv[0]);
+    return 2;
+}
