@@ -61,7 +61,7 @@ def measured_traffic(label: str, workload: str):
         digest = kernel_isa_digest(fields["kernel"])
         if digest is None or fields.get("isa_sha256") != digest:
             return None
-        return int(fields["traffic_bytes_per_launch"])
+        return int(fields["traffic_bytes_per_launch"]), fields["kernel"], digest
     except (OSError, KeyError, ValueError):
         return None
 
@@ -349,11 +349,16 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kern_name, "achieved": _fmt(kern_gbps, 5),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": _fmt(kern_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(kern_name, w.name),
+                     "traffic": None,
                      "kernel_ms": _fmt(kern_avg, 5), "bytes_per_launch": kern_bytes},
         "last_step": {"norm": ctrl["norm"], "skip": ctrl["skip"], "t": ctrl["t"],
                       "loss_scale": ctrl["loss_scale"]},
     }
+    measured = measured_traffic(kern_name, w.name)
+    if measured is not None:
+        traffic, profiled_kernel, digest = measured
+        out["roofline"].update(traffic=traffic, traffic_ratio=_fmt(traffic / kern_bytes, 5),
+                               traffic_kernel=profiled_kernel, traffic_isa_sha256=digest[:16])
     if red_ms:
         red_avg = sum(red_ms) / len(red_ms)
         red_bpe = 4 + (w.nranks * (args.quant / 8 + 8 / 2048) if args.quant else 2 * w.nranks)
