@@ -18,7 +18,7 @@ from synth.workloads import BF16, F16, Workload
 
 pytestmark = pytest.mark.gpu
 
-SEEDS = list(range(1, 65))
+SEEDS = list(range(1, 129))
 
 
 @pytest.fixture(scope="module", autouse=True)
