@@ -43,6 +43,13 @@
  *     where the call says otherwise.
  *   - Calls on different streams are independent as long as they use
  *     different ctrl blocks and workspaces.
+ *   - Sizes the library cannot see are the caller's to guarantee: a gather
+ *     buffer holds at least offset + valid_len elements; contribution rows
+ *     hold valid_len elements (and a [N, stride] buffer N * stride); g and
+ *     flat state arrays valid_len floats; paired state zero_pair_elems;
+ *     workspaces ws_bytes (checked against zero_workspace_bytes); quantised
+ *     codes zero_qcode_bytes and block records zero_qblock_count entries.
+ *     A buffer shorter than that is read or written out of bounds.
  */
 #ifndef ZERO_SHARD_H
 #define ZERO_SHARD_H
