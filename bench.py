@@ -123,7 +123,7 @@ def setup(w, torch, synth, Z, rows=False, qbits=0):
                 gather=gather, step=st, fused=fused)
 
 
-def timed_steps(b, steps, warmup, torch, Z):
+def timed_steps(b, steps, warmup, torch, Z, graph=False):
     """Warmup, then two timed passes of `steps` steps each on the same stream:
     the first with events only around the whole loop (the step time), the
     second with events also around each launch of the dominant kernel (the
@@ -136,10 +136,15 @@ def timed_steps(b, steps, warmup, torch, Z):
     for _ in range(warmup):
         st.step(contrib, gather)
     torch.cuda.synchronize()
+    run_step = lambda: st.step(contrib, gather)  # noqa: E731
+    if graph:  # one captured step, replayed: the step's scalars live on the device
+        g = st.capture(contrib, gather)
+        torch.cuda.synchronize()
+        run_step = g.replay
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(steps):
-        st.step(contrib, gather)
+        run_step()
     t1.record()
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
@@ -147,7 +152,7 @@ def timed_steps(b, steps, warmup, torch, Z):
     bounds = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     bounds[0].record()
     for i in range(steps):
-        st.step(contrib, gather)
+        run_step()
         bounds[i + 1].record()
     torch.cuda.synchronize()
     per_step = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(steps))
@@ -272,6 +277,8 @@ def main():
     ap.add_argument("--quant", type=int, choices=(0, 4, 8), default=0,
                     help="block-quantised (ZeRO++) INT8 or INT4 contributions through the "
                          "quantised calls")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step as one captured HIP graph replayed each step")
     ap.add_argument("--rows", action="store_true",
                     help="contribution rows in N separate allocations, through the row-table "
                          "calls (one pointer per row) instead of one [N, stride] buffer")
@@ -306,7 +313,8 @@ def main():
 
     w = workloads.BY_NAME[args.workload]
     b = setup(w, torch, synth, Z, rows=args.rows, qbits=args.quant)
-    ms_step, per_step, kern_ms, red_ms, ctrl = timed_steps(b, args.steps, args.warmup, torch, Z)
+    ms_step, per_step, kern_ms, red_ms, ctrl = timed_steps(b, args.steps, args.warmup, torch, Z,
+                                                           graph=args.graph)
     valid = b["valid"]
     bpe = quant_bytes_per_elem(w, args.quant) if args.quant else w.bytes_per_elem
     step_bytes = int(round(bpe * valid))
@@ -341,7 +349,8 @@ def main():
                    "contrib_dtype": "fp16" if w.dtype == Z.F16 else "bf16",
                    "bytes_per_elem": _fmt(bpe, 6), "step_bytes": step_bytes,
                    "contrib_layout": ("int%d_blocks" % args.quant if args.quant else
-                                      "row_table" if args.rows else "strided")},
+                                      "row_table" if args.rows else "strided"),
+                   "launch": "hip_graph" if args.graph else "stream"},
         "step_ms_median": _fmt(per_step[len(per_step) // 2], 5),
         "step_ms_min": _fmt(per_step[0], 5),
         "pct_hbm_peak": _fmt(100 * gbps / HBM_PEAK_GBPS, 4),

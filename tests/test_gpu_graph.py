@@ -1,0 +1,74 @@
+"""A whole shard step captured once in a HIP graph and replayed every step.
+
+All step-to-step scalars (t, loss scale, beta powers, skip, the current
+state set) live in the device ctrl block and every kernel argument is a fixed
+pointer, so one captured step serves every later step.  Each case runs the
+same steps eagerly and by replay, with the contributions refilled eagerly and
+a synchronisation between replays; every replay's ctrl and the final
+master/m/v/slot must equal the eager run's bit for bit, and the oracle's.
+"""
+import numpy as np
+import pytest
+
+import harness as H
+from harness import Case, Inject
+from synth import workloads
+from synth.workloads import BF16, F16, Workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import synth
+    synth.gpu()
+    import zero_partitioned_mixed_amd  # noqa: F401
+    yield
+
+
+def small(psi, n, rank, dtype=F16, steps=3, **kw):
+    return Workload(name="small", psi=psi, nranks=n, ranks=(rank,), dtype=dtype, steps=steps, **kw)
+
+
+CASES = {
+    "fused_skip_and_halve": Case(small(100_003, 3, 2, steps=5, scaler=2, contrib_scale=2.0 ** 10,
+                                       loss_scale=2.0 ** 10), 2, 5,
+                                 extra=(Inject(2, 1, 17_001, np.inf),)),
+    "two_pass_clip": Case(small(200_000, 8, 5, dtype=BF16, max_grad_norm=0.05, steps=4), 5, 4),
+    "fused_int8_rows": Case(small(64 * 1_000 + 37, 8, 7, steps=3), 7, 3, qbits=8),
+    "gpt2_sized": Case(workloads.GPT2, 7, 6),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_graph_replay_equals_eager(name):
+    import torch
+    c = CASES[name]
+    eager = H.GpuRun(c, full_gather=False)
+    eager.run()
+    g = H.GpuRun(c, full_gather=False)
+    src = g.qrows if g.qrows is not None else g.contrib
+    graph = g.step_obj.capture(src, g.gather)
+    torch.cuda.synchronize()
+    assert g.step_obj.ctrl_dict()["t"] == 0          # capturing ran nothing
+    for s in range(1, c.steps + 1):
+        g.fill(s)                                    # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        rep = g.step_obj.ctrl_dict()
+        assert rep == eager.reports[s - 1], (s, rep, eager.reports[s - 1])
+        g.reports.append(rep)
+    for a, b, what in zip(g.fetch(), eager.fetch(), ("master", "m", "v", "slot")):
+        assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8)), what
+    reps = H.oracle_scalars(c)
+    H.assert_reports(g.reports, reps)
+    if c.part[2] <= 1_000_000:
+        p, m, v, slot = g.fetch()
+        rp, rm, rv, rslot = H.oracle_elements(c, reps)
+        H.assert_f32_close("master", p, rp)
+        H.assert_16bit_within_ulp("slot", slot, rslot, c.w.dtype)
+    H.log(f"graph {name}: {c.steps} replays equal the eager steps; skips "
+          f"{[r['skip'] for r in g.reports]}")

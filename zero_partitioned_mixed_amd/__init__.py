@@ -387,6 +387,23 @@ class ShardStep:
             zero_adam_step(self.state, self.g, self.valid_len, self.hp, self.ctrl, gather,
                            self.gather_dtype, self.offset)
 
+    def capture(self, contrib, gather):
+        """Records one step (its two or three launches) into a HIP graph and
+        returns it (a torch.cuda.CUDAGraph); ``graph.replay()`` then runs a
+        step.  Every step-to-step scalar lives in the device ctrl block and every
+        argument is a fixed pointer, so the same graph serves every later step:
+        the caller refills ``contrib`` in place between replays.  Capturing
+        runs nothing."""
+        import torch
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                self.step(contrib, gather)
+        torch.cuda.current_stream().wait_stream(side)
+        return graph
+
     def current(self):
         """(master, m, v): the current state, flat (the fused path copies it
         out of the paired buffers into ``state``)."""
