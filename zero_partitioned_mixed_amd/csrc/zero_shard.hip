@@ -51,7 +51,6 @@ constexpr int64_t kFinPer = 16384;          // partials per first-level finalize
 constexpr int kRestoreGrid = 256;           // workgroups of the (usually idle) restore pass
 constexpr int64_t kMaxLen = int64_t(1) << 40;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
