@@ -29,16 +29,22 @@ def gpu():
     torch.cuda.empty_cache()
 
 
-def run_fullsize(w):
+_REPS = {}  # the oracle's per-step decisions, per workload (shared by the layouts)
+
+
+def run_fullsize(w, layout="strided"):
     import synth
     import torch
     c = Case(w, w.ranks[0], w.steps)
     shard, off, valid = c.part
-    H.log(f"{w.name}: shard {shard} at offset {off}, N={w.nranks}, {w.variant}, {w.steps} steps")
-    g = H.GpuRun(c, full_gather=True)
+    H.log(f"{w.name}: shard {shard} at offset {off}, N={w.nranks}, {w.variant}, {w.steps} steps, "
+          f"layout {layout}")
+    g = H.GpuRun(c, full_gather=True, layout=layout)
     g.run()
-    H.log(f"{w.name}: GPU steps done; oracle scalar pass over {valid} x {w.nranks} x {w.steps}")
-    reps = H.oracle_scalars(c)
+    if w.name not in _REPS:
+        H.log(f"{w.name}: GPU steps done; oracle scalar pass over {valid} x {w.nranks} x {w.steps}")
+        _REPS[w.name] = H.oracle_scalars(c)
+    reps = _REPS[w.name]
     stats = H.assert_reports(g.reports, reps)
     H.log(f"{w.name}: scalars ok {stats}; skips {[r['skip'] for r in reps]}")
     extra = [i.col + d for i in c.injections for d in (-1, 0, 1)]
@@ -66,3 +72,9 @@ def test_psi7e9_clip_two_pass_fullsize():
 
 def test_psi13e9_dynamic_scale_fused_fullsize():
     run_fullsize(workloads.P13B)
+
+
+def test_psi13e9_row_table_fullsize():
+    """The 13B shard with its eight contribution rows in eight separate
+    allocations, through zero_fused_step_rows (bench.py --rows)."""
+    run_fullsize(workloads.P13B, layout="rows")
