@@ -24,7 +24,10 @@
  * -ffp-contract=off, SSE scalar arithmetic).  The squared-norm is exact.
  *
  * Parity unpinned: Adam trajectories beyond the closed forms and the library
- * cross-check in the tests (the pages print none).
+ * cross-check in the tests (the pages print none).  Readings the pages leave
+ * open, each pinned by the tests only to the definition stated here: the
+ * clip coefficient's 1e-6, the loss scaler's skip/halve/grow schedule, and
+ * the quantisation's block size, zero-point form and rounding.
  */
 #include <math.h>
 #include <stdint.h>
