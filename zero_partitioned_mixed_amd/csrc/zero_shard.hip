@@ -587,6 +587,10 @@ __global__ void __launch_bounds__(kFinBlock) finalize_kernel(CombineArgs a) {
     const int64_t total = a.first[a.nranks];
     const int64_t lo = (int64_t)blockIdx.x * a.per;
     const int64_t hi = lo + a.per < total ? lo + a.per : total;
+    // the step's scalars, read now so their latency overlaps the reduction
+    // (nothing else writes them during this kernel; arrive is reset below)
+    zero_ctrl c;
+    if (threadIdx.x == 0) c = *a.ctrl[0];
     double ss = 0.0;
     uint32_t bad = 0;
     if (a.nranks == 1) {
@@ -643,7 +647,6 @@ __global__ void __launch_bounds__(kFinBlock) finalize_kernel(CombineArgs a) {
     }
     if (threadIdx.x != 0) return;
     const zero_hparams& hp = a.hp;
-    zero_ctrl c = *a.ctrl[0];
     c.arrive = 0u;
     c.sumsq = ss;
     c.norm = sqrt(ss);
