@@ -789,10 +789,31 @@ struct PackArgs {
 };
 
 // TO_PAIR: flat -> current set of the pair; otherwise current set -> flat.
+// Full tiles move 16-byte vectors (run a and run b sit 256 elements apart in
+// both layouts); the partial last tile goes element by element.
 template <bool TO_PAIR>
 __global__ void __launch_bounds__(kBlock) pack_kernel(PackArgs a) {
     const int cur = a.ctrl->cur;
     const Runs r = runs_of(blockIdx.x);
+    if (r.b + kRun <= a.len) {
+        const int64_t pa = pair_index(r.a, cur), pb = pa + 256;
+        float x[3][kVec];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            if (TO_PAIR)
+                load8(a.flat[q] + r.a, a.flat[q] + r.b, x[q]);
+            else
+                load8(a.pair[q] + pa, a.pair[q] + pb, x[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            if (TO_PAIR)
+                store8(a.pair[q] + pa, a.pair[q] + pb, x[q]);
+            else
+                store8(a.flat[q] + r.a, a.flat[q] + r.b, x[q]);
+        }
+        return;
+    }
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
         for (int j = 0; j < kVec; ++j) {
