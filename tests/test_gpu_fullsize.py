@@ -32,23 +32,25 @@ def gpu():
 _REPS = {}  # the oracle's per-step decisions, per workload (shared by the layouts)
 
 
-def run_fullsize(w, layout="strided"):
+def run_fullsize(w, layout="strided", qbits=0, steps=None, samples=65_536):
     import synth
     import torch
-    c = Case(w, w.ranks[0], w.steps)
+    c = Case(w, w.ranks[0], w.steps if steps is None else steps, qbits=qbits)
     shard, off, valid = c.part
-    H.log(f"{w.name}: shard {shard} at offset {off}, N={w.nranks}, {w.variant}, {w.steps} steps, "
-          f"layout {layout}")
+    H.log(f"{w.name}: shard {shard} at offset {off}, N={w.nranks}, {w.variant}, {c.steps} steps, "
+          f"layout {layout}, qbits {qbits}")
     g = H.GpuRun(c, full_gather=True, layout=layout)
     g.run()
-    if w.name not in _REPS:
-        H.log(f"{w.name}: GPU steps done; oracle scalar pass over {valid} x {w.nranks} x {w.steps}")
-        _REPS[w.name] = H.oracle_scalars(c)
-    reps = _REPS[w.name]
+    key = (w.name, qbits, c.steps)
+    if key not in _REPS:
+        H.log(f"{w.name}: GPU steps done; oracle scalar pass over {valid} x {w.nranks} x {c.steps}"
+              f" (qbits {qbits})")
+        _REPS[key] = H.oracle_scalars(c)
+    reps = _REPS[key]
     stats = H.assert_reports(g.reports, reps)
     H.log(f"{w.name}: scalars ok {stats}; skips {[r['skip'] for r in reps]}")
     extra = [i.col + d for i in c.injections for d in (-1, 0, 1)]
-    cols = H.sample_cols(valid, 65_536, seed=11, extra=extra)
+    cols = H.sample_cols(valid, samples, seed=11, extra=extra)
     p, m, v, slot = g.fetch(cols)
     rp, rm, rv, rslot = H.oracle_elements(c, reps, cols)
     stats["master"] = H.assert_f32_close("master", p, rp)
@@ -78,3 +80,12 @@ def test_psi13e9_row_table_fullsize():
     """The 13B shard with its eight contribution rows in eight separate
     allocations, through zero_fused_step_rows (bench.py --rows)."""
     run_fullsize(workloads.P13B, layout="rows")
+
+
+def test_psi13e9_int8_blocks_fullsize():
+    """The 13B shard with INT8 block-quantised contributions, through
+    zero_fused_step_q (bench.py --quant 8): its first two steps (the second
+    holds the injected +inf, so its block dequantises to NaN and the step is
+    skipped), decisions over the whole shard, elements on a sample with their
+    whole blocks."""
+    run_fullsize(workloads.P13B, qbits=8, steps=2, samples=2_000)
