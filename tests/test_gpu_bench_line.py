@@ -1,0 +1,43 @@
+"""bench.py keeps its contract: one JSON line with the fields the benchmark
+report needs, on a small workload (the GPT-2-sized shard, a few steps, a
+small CPU sample), run as a child process exactly as a user would."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.gpu
+def test_bench_prints_one_complete_json_line():
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "gpt2_psi124439808_n8",
+           "--steps", "5", "--warmup", "1", "--cpu-sample", str(1 << 20), "--no-copy"]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, r.stdout
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline", "pct_hbm_peak", "elements_per_s"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 5 and d["warmup"] == 1
+    assert d["unit"] == "GB/s" and d["higher_is_better"] is True and d["value"] > 0
+    assert d["config"]["workload"] == "gpt2_psi124439808_n8"
+    ro = d["roofline"]
+    for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert key in ro, key
+    assert ro["bound"] == "hbm" and ro["peak"] == 8000.0 and 0 < ro["frac"] < 1
+    assert abs(ro["frac"] - ro["achieved"] / ro["peak"]) < 1e-3
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["value"] > 0 and cb["sample"]
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # checked before anything touches the GPU, so this runs without one
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "ONE GPU" in r.stderr
