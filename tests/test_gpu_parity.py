@@ -119,6 +119,12 @@ SMALL = {
                                         loss_scale=2.0 ** 10), (Inject(2, 3, 4_000, np.inf),)),
     "bf16_fused_skip_offset_2mod4": (small(100_003, 3, 2, dtype=BF16, steps=3),
                                      (Inject(2, 0, 2_049, np.nan),)),
+    "f16_fused_zero_gradients": (small(100_003, 3, 2, contrib_sigma=0.0, weight_decay=0.01), ()),
+    "bf16_twopass_zero_gradients_clip": (small(100_003, 3, 1, dtype=BF16, contrib_sigma=0.0,
+                                               max_grad_norm=1.0), ()),
+    "f16_fused_skip_every_step_to_floor": (
+        small(60_016, 4, 3, steps=4, scaler=2, contrib_scale=4.0, loss_scale=4.0, min_scale=1.0),
+        tuple(Inject(s, s % 4, 100 * s, np.inf) for s in range(1, 5))),
     "f16_fused_dynamic_growth": (small(60_016, 4, 3, steps=6, scaler=2, growth_interval=2,
                                        contrib_scale=2.0 ** 12, loss_scale=2.0 ** 12),
                                  (Inject(4, 1, 5, np.inf),)),
