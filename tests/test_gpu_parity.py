@@ -293,3 +293,20 @@ def test_finalize_single_and_grouped(tiles):
     the grouped path (ranges, then the last group to arrive) runs."""
     w = small(tiles * 2048 - 1000, 1, 0, dtype=BF16, steps=2, max_grad_norm=0.5)
     run_case(Case(w, 0, 2), f"finalize_{tiles}_tiles", full=False)
+
+
+@pytest.mark.parametrize("pad", [8, 4096 + 24])
+@pytest.mark.parametrize("two_pass", [False, True])
+def test_row_strides_beyond_the_shard(pad, two_pass):
+    """Row strides that are any multiple of eight elements beyond the shard
+    (here shard + 8 and shard + 4120, neither a multiple of 64), with an inf
+    in every row's padding that must be ignored."""
+    kw = dict(max_grad_norm=0.02) if two_pass else {}
+    w = small(3 * 33_335 - 2, 3, 2, dtype=BF16, **kw)
+    c0 = Case(w, 2, 2)
+    valid = c0.part[2]
+    stride = (c0.part[0] + 63) // 64 * 64 + pad
+    extra = tuple(Inject(1, k, stride - 1, np.inf) for k in range(3))
+    c = Case(w, 2, 2, extra=extra, stride_pad=pad)
+    assert c.stride == stride and c.stride % 64 != 0 and stride - 1 >= valid
+    run_case(c, f"stride_pad_{pad}_{'two_pass' if two_pass else 'fused'}")
