@@ -130,22 +130,24 @@ def setup(w, torch, synth, Z, rows=False, qbits=0):
                 gather=gather, step=st, fused=fused)
 
 
-def timed_steps(b, steps, warmup, torch, Z, graph=False):
+def timed_steps(b, steps, warmup, torch, Z, graph=False, qg=None):
     """Warmup, then two timed passes of `steps` steps each on the same stream:
     the first with events only around the whole loop (the step time), the
     second with events also around each launch of the dominant kernel (the
     fused pass, or the Adam pass; plus the reduce pass on the two-pass path).
     Event records between kernels cost a few microseconds each, so they are
-    kept out of the loop that gives the step time."""
+    kept out of the loop that gives the step time.  With `qg` (a QGather) the
+    step writes the quantised all-gather payload instead of the 16-bit slot."""
     st, contrib, gather = b["step"], b["contrib"], b["gather"]
+    slot = None if qg is not None else gather
     table = isinstance(contrib, list)
     quant = isinstance(contrib, Z.QuantRows)
     for _ in range(warmup):
-        st.step(contrib, gather)
+        st.step(contrib, slot, qg)
     torch.cuda.synchronize()
-    run_step = lambda: st.step(contrib, gather)  # noqa: E731
+    run_step = lambda: st.step(contrib, slot, qg)  # noqa: E731
     if graph:  # one captured step, replayed: the step's scalars live on the device
-        g = st.capture(contrib, gather)
+        g = st.capture(contrib, slot, qg)
         torch.cuda.synchronize()
         run_step = g.replay
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -169,7 +171,14 @@ def timed_steps(b, steps, warmup, torch, Z, graph=False):
               for _ in range(steps)]
     hp, n, stride, valid, off = st.hp, st.nranks, st.stride, st.valid_len, st.offset
     for i in range(steps):
-        if b["fused"]:
+        if qg is not None:
+            ev[i][0].record()
+            Z.zero_fused_step_qgather(contrib, st.dtype, n, stride, st.pair, valid, None,
+                                      st.gather_dtype, off, qg, hp, st.ctrl, st.ws)
+            ev[i][1].record()
+            Z.zero_grad_norm_overflow([st.ws], [valid], [st.ctrl], hp, True)
+            Z.zero_fused_restore_q(st.pair, valid, None, st.gather_dtype, off, qg, st.ctrl)
+        elif b["fused"]:
             ev[i][0].record()
             if quant:
                 Z.zero_fused_step_q(contrib, st.pair, valid, gather, st.gather_dtype, off, hp,
@@ -284,6 +293,9 @@ def main():
     ap.add_argument("--quant", type=int, choices=(0, 4, 8), default=0,
                     help="block-quantised (ZeRO++) INT8 or INT4 contributions through the "
                          "quantised calls")
+    ap.add_argument("--qgather", type=int, choices=(0, 4, 8), default=0,
+                    help="the fused step writes the ZeRO++ INT8 or INT4 all-gather payload of "
+                         "the new parameters instead of the 16-bit slot")
     ap.add_argument("--graph", action="store_true",
                     help="time the step as one captured HIP graph replayed each step")
     ap.add_argument("--rows", action="store_true",
@@ -319,23 +331,31 @@ def main():
         return
 
     w = workloads.BY_NAME[args.workload]
+    if args.qgather and (args.rows or args.quant or w.max_grad_norm > 0):
+        print("--qgather takes the fused path over [N, stride] contributions only",
+              file=sys.stderr)
+        sys.exit(2)
     b = setup(w, torch, synth, Z, rows=args.rows, qbits=args.quant)
-    ms_step, per_step, kern_ms, red_ms, ctrl = timed_steps(b, args.steps, args.warmup, torch, Z,
-                                                           graph=args.graph)
     valid = b["valid"]
+    qg = Z.QGather.alloc(valid, args.qgather, torch.device("cuda", 0)) if args.qgather else None
+    ms_step, per_step, kern_ms, red_ms, ctrl = timed_steps(b, args.steps, args.warmup, torch, Z,
+                                                           graph=args.graph, qg=qg)
     bpe = quant_bytes_per_elem(w, args.quant) if args.quant else w.bytes_per_elem
+    if args.qgather:  # the 2-byte slot replaced by the codes and one 8-byte record per block
+        bpe = bpe - 2 + args.qgather / 8 + 8 / 2048
     step_bytes = int(round(bpe * valid))
     gbps = step_bytes / (ms_step * 1e-3) / 1e9
     kern_avg = sum(kern_ms) / len(kern_ms)
     if b["fused"]:
         kern_name = ("fused_kernel_q%d" % args.quant if args.quant else
+                     "fused_qgather_kernel_q%d" % args.qgather if args.qgather else
                      "fused_kernel_rows" if args.rows else "fused_kernel")
         kern_bytes = step_bytes
     else:
         kern_name = "adam_kernel"
         kern_bytes = (4 + 26) * valid  # g + master/m/v in and out + the 16-bit slot
     kern_gbps = kern_bytes / (kern_avg * 1e-3) / 1e9
-    del b
+    del b, qg
     torch.cuda.empty_cache()
 
     out = {
@@ -357,6 +377,8 @@ def main():
                    "bytes_per_elem": _fmt(bpe, 6), "step_bytes": step_bytes,
                    "contrib_layout": ("int%d_blocks" % args.quant if args.quant else
                                       "row_table" if args.rows else "strided"),
+                   "gather_payload": ("int%d_blocks" % args.qgather if args.qgather else
+                                      "16bit_slot"),
                    "launch": "hip_graph" if args.graph else "stream"},
         "step_ms_median": _fmt(per_step[len(per_step) // 2], 5),
         "step_ms_min": _fmt(per_step[0], 5),

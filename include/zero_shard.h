@@ -354,6 +354,37 @@ int zero_fused_step_q(const void *const *codes_dev, const zero_qblock *const *bl
                       const zero_hparams *hp, const zero_ctrl *ctrl_dev, void *ws_dev,
                       size_t ws_bytes, void *stream);
 
+/* zero_fused_step (strided rows) that also writes the quantised all-gather
+ * payload of the rank's new parameters ("CMU 11-868 L18", Other memory
+ * optimizations: ZeRO++ quantises the parameters block-wise to INT8 with a
+ * zero point for the forward all-gather).  Block b covers shard elements
+ * [b * ZERO_QBLOCK, ...), which is exactly one tile of the pass, so the
+ * block's range, record and codes come out of the same pass as the new
+ * parameters: codes_dev (zero_qcode_bytes(valid_len, bits)) and blocks_dev
+ * (zero_qblock_count(valid_len) records) equal, bit for bit, what
+ * zero_quantize_blocks(gather_dtype, bits) would write from the 16-bit slot
+ * after the step.  gather_dev may be NULL: then no 16-bit slot is written
+ * (every rank rebuilds the parameters from the gathered payload with
+ * zero_dequantize_blocks, this one included); gather_dtype still names the
+ * 16-bit format that is quantised.  bits is 8 (the page's choice) or 4.
+ * On a skipped step, zero_fused_restore_q (not zero_fused_restore) rewrites
+ * the slot and the payload.  Other arguments and errors as in zero_fused_step
+ * and zero_quantize_blocks (codes_dev and blocks_dev 8-byte aligned). */
+int zero_fused_step_qgather(const void *contrib_dev, int32_t contrib_dtype, int32_t nranks,
+                            int64_t stride, const zero_state *pair, int64_t valid_len,
+                            void *gather_dev, int32_t gather_dtype, int64_t offset, int32_t bits,
+                            void *codes_dev, zero_qblock *blocks_dev, const zero_hparams *hp,
+                            const zero_ctrl *ctrl_dev, void *ws_dev, size_t ws_bytes,
+                            void *stream);
+
+/* After a zero_fused_step_qgather's zero_grad_norm_overflow: if ctrl->skip,
+ * rewrite the slot (when gather_dev is not NULL) and the payload from the
+ * current master of the paired state, as the step would have written them;
+ * otherwise every workgroup returns at once. */
+int zero_fused_restore_q(const zero_state *pair, int64_t valid_len, void *gather_dev,
+                         int32_t dtype, int64_t offset, int32_t bits, void *codes_dev,
+                         zero_qblock *blocks_dev, const zero_ctrl *ctrl_dev, void *stream);
+
 /* Message for the last nonzero return on the calling thread ("" if none). */
 const char *zero_last_error(void);
 

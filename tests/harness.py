@@ -208,7 +208,8 @@ class GpuRun:
     The row copies are filled from the strided buffer, so all three hand the
     library the same values."""
 
-    def __init__(self, c: Case, full_gather: bool = True, layout: str = "strided"):
+    def __init__(self, c: Case, full_gather: bool = True, layout: str = "strided",
+                 qgather: int = 0, write_slot: bool = True):
         import torch
         import zero_partitioned_mixed_amd as Z
         self.c, self.Z, self.torch = c, Z, torch
@@ -242,6 +243,15 @@ class GpuRun:
         self.layout = layout
         self.rows = None
         self.qrows = None
+        # qgather = 8 or 4: the step also writes the quantised all-gather
+        # payload (zero_fused_step_qgather); write_slot=False passes no gather
+        self.qg = Z.QGather.alloc(valid, qgather, dev) if qgather else None
+        if self.qg is not None:
+            self.qg.codes.fill_(0xA5)   # canaries: every code byte and record must be written
+            self.qg.blocks.fill_(0xA5)
+        self.write_slot = write_slot
+        if not write_slot and not qgather:
+            raise ValueError("only a quantised-gather step may skip the 16-bit slot")
         n = w.nranks
         if c.qbits:
             self.qrows = Z.QuantRows.alloc(n, valid, c.qbits, dev)
@@ -275,7 +285,7 @@ class GpuRun:
             self.fill(s)
             src = self.qrows if self.qrows is not None else (
                 self.contrib if self.rows is None else self.rows)
-            self.step_obj.step(src, self.gather)
+            self.step_obj.step(src, self.gather if self.write_slot else None, self.qg)
             if record:
                 self.reports.append(self.step_obj.ctrl_dict())
         self.torch.cuda.synchronize()
@@ -298,20 +308,32 @@ class GpuRun:
         slot = slot.view(torch.int16).cpu().numpy().view(np.uint16)
         return out[0], out[1], out[2], slot
 
+    def qpayload(self):
+        """(codes, scales, zero points) of the quantised all-gather payload."""
+        q = self.qg
+        nblk = (self.valid + O.QBLOCK - 1) // O.QBLOCK
+        codes = q.codes.cpu().numpy()[:O.qcode_bytes(self.valid, q.bits)]
+        rec = q.blocks.cpu().numpy().view(np.uint8)[:8 * nblk]
+        return codes, rec.view(np.float32)[0::2], rec.view(np.int32)[1::2]
+
     def gather_bits(self, idx: np.ndarray) -> np.ndarray:
         torch = self.torch
         ix = torch.from_numpy(idx.astype(np.int64)).to(self.gather.device)
         return self.gather.index_select(0, ix).view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run_and_compare(c: Case, label: str, full: bool = True, layout: str = "strided"):
+def run_and_compare(c: Case, label: str, full: bool = True, layout: str = "strided",
+                    qgather: int = 0, write_slot: bool = True):
     """Runs case `c` on the GPU and checks every step's decisions and the final
     master/m/v/slot of the whole shard against the oracle; with `full`, also
-    that the gather buffer is unchanged outside the slot."""
+    that the gather buffer is unchanged outside the slot.  With `qgather`, the
+    quantised all-gather payload must equal, bit for bit, the oracle's
+    quantisation of the oracle's final slot; without `write_slot`, the whole
+    gather buffer must be unchanged."""
     log(f"{label}: psi={c.w.psi} N={c.w.nranks} rank={c.rank} dtype={c.w.dtype} "
         f"variant={c.w.variant} steps={c.steps} offset={c.part[1]} valid={c.part[2]} "
-        f"layout={layout} qbits={c.qbits}")
-    g = GpuRun(c, full_gather=full, layout=layout)
+        f"layout={layout} qbits={c.qbits} qgather={qgather} write_slot={write_slot}")
+    g = GpuRun(c, full_gather=full, layout=layout, qgather=qgather, write_slot=write_slot)
     g.run()
     ref_reps = oracle_scalars(c)
     stats = assert_reports(g.reports, ref_reps)
@@ -320,17 +342,29 @@ def run_and_compare(c: Case, label: str, full: bool = True, layout: str = "strid
     stats["master"] = assert_f32_close("master", p, rp)
     stats["m"] = assert_f32_close("m", m, rm)
     stats["v"] = assert_f32_close("v", v, rv)
-    stats["slot"] = assert_16bit_within_ulp("slot", slot, rslot, c.w.dtype)
-    if full:  # nothing outside the slot changed
-        w = c.w
-        _, off, valid = c.part
-        outside = np.r_[0:off, off + valid:w.psi]
+    if write_slot:
+        stats["slot"] = assert_16bit_within_ulp("slot", slot, rslot, c.w.dtype)
+    if qgather:
+        stats["qgather"] = assert_qpayload(g.qpayload(), O.quantize(rslot, c.w.dtype, qgather))
+    w = c.w
+    _, off, valid = c.part
+    if full:  # nothing outside the slot changed (nothing at all without a slot)
+        outside = np.r_[0:off, off + valid:w.psi] if write_slot else np.arange(w.psi)
         if outside.size:
             got = g.gather_bits(outside)
             ref = synth.param_range(w.seed, w.master_sigma, w.dtype, 0, w.psi)[outside]
             assert np.array_equal(got, ref), "gather buffer changed outside the slot"
     log(f"{label}: ok {stats}")
     return g, stats
+
+
+def assert_qpayload(got, ref) -> dict:
+    """Codes, scales (as bits) and zero points equal."""
+    codes, scale, zero = got
+    assert np.array_equal(codes, ref.codes[:O.qcode_bytes(ref.length, ref.bits)]), "codes differ"
+    assert np.array_equal(scale.view(np.uint32), ref.scale.view(np.uint32)), "scales differ"
+    assert np.array_equal(zero, ref.zero), "zero points differ"
+    return {"blocks": int(ref.scale.size), "nan_blocks": int(np.isnan(ref.scale).sum())}
 
 
 # ----------------------------------------------------------------------------- comparisons

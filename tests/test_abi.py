@@ -227,3 +227,54 @@ def _q_call(Z, fused, codes, blocks, bits=8, n=None, valid=64, g=FAKE, wsb=1 << 
 def test_quant_rows_validation(Z, fused, codes, blocks, kw, code, msg):
     assert _q_call(Z, fused, codes, blocks, **kw) == code
     assert msg in Z.zero_last_error()
+
+
+def _qg_call(Z, contrib_dtype=1, valid=64, gather=FAKE, gdt=1, bits=8, codes=FAKE, blocks=FAKE,
+             clip=0.0, wsb=1 << 16, ctrl=FAKE):
+    pair = Z.State(FAKE, FAKE + 65536, FAKE + 131072)
+    hp = Z.hparams(max_grad_norm=clip)
+    return Z._lib.zero_fused_step_qgather(FAKE, contrib_dtype, 8, 64, ctypes.byref(pair), valid,
+                                          gather, gdt, 0, bits, codes, blocks, ctypes.byref(hp),
+                                          ctrl, FAKE, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(bits=3), -1, "bits"),
+    (dict(bits=16), -1, "bits"),
+    (dict(codes=0), -1, "null codes"),
+    (dict(blocks=0), -1, "null codes"),
+    (dict(codes=FAKE + 4), -2, "8-byte"),
+    (dict(blocks=FAKE + 2), -2, "8-byte"),
+    (dict(gather=FAKE + 1), -2, "2-byte"),
+    (dict(gather=None, gdt=9), -1, "gather dtype"),
+    (dict(gdt=0), -1, "gather dtype"),
+    (dict(clip=1.0), -1, "two-pass"),
+    (dict(contrib_dtype=3), -1, "dtype"),
+    (dict(valid=-1), -3, "out of range"),
+    (dict(ctrl=0), -1, "null ctrl"),
+    (dict(wsb=16), -4, "workspace"),
+    # a NULL gather is accepted: validation runs on to the workspace check
+    (dict(gather=None, wsb=16), -4, "workspace"),
+])
+def test_fused_qgather_validation(Z, kw, code, msg):
+    assert _qg_call(Z, **kw) == code
+    assert msg in Z.zero_last_error()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(bits=5), -1, "bits"),
+    (dict(codes=0), -1, "null codes"),
+    (dict(blocks=FAKE + 4), -2, "8-byte"),
+    (dict(gather=None, dtype=9), -1, "gather dtype"),
+    (dict(gather=FAKE + 1), -2, "2-byte"),
+    (dict(ctrl=0), -1, "null ctrl"),
+    (dict(valid=-3), -3, "out of range"),
+])
+def test_fused_restore_q_validation(Z, kw, code, msg):
+    a = dict(valid=64, gather=FAKE, dtype=1, bits=8, codes=FAKE, blocks=FAKE, ctrl=FAKE)
+    a.update(kw)
+    pair = Z.State(FAKE, FAKE + 65536, FAKE + 131072)
+    rc = Z._lib.zero_fused_restore_q(ctypes.byref(pair), a["valid"], a["gather"], a["dtype"], 0,
+                                     a["bits"], a["codes"], a["blocks"], a["ctrl"], None)
+    assert rc == code
+    assert msg in Z.zero_last_error()

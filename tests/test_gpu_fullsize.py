@@ -32,14 +32,17 @@ def gpu():
 _REPS = {}  # the oracle's per-step decisions, per workload (shared by the layouts)
 
 
-def run_fullsize(w, layout="strided", qbits=0, steps=None, samples=65_536):
+def run_fullsize(w, layout="strided", qbits=0, steps=None, samples=65_536, qgather=0):
+    """qgather = 8 or 4: the step writes the quantised all-gather payload and
+    no 16-bit slot (bench.py --qgather); the payload is checked on whole
+    sampled blocks and the slot must stay as it was."""
     import synth
     import torch
     c = Case(w, w.ranks[0], w.steps if steps is None else steps, qbits=qbits)
     shard, off, valid = c.part
     H.log(f"{w.name}: shard {shard} at offset {off}, N={w.nranks}, {w.variant}, {c.steps} steps, "
-          f"layout {layout}, qbits {qbits}")
-    g = H.GpuRun(c, full_gather=True, layout=layout)
+          f"layout {layout}, qbits {qbits}, qgather {qgather}")
+    g = H.GpuRun(c, full_gather=True, layout=layout, qgather=qgather, write_slot=not qgather)
     g.run()
     key = (w.name, qbits, c.steps)
     if key not in _REPS:
@@ -56,7 +59,12 @@ def run_fullsize(w, layout="strided", qbits=0, steps=None, samples=65_536):
     stats["master"] = H.assert_f32_close("master", p, rp)
     stats["m"] = H.assert_f32_close("m", m, rm)
     stats["v"] = H.assert_f32_close("v", v, rv)
-    stats["slot"] = H.assert_16bit_within_ulp("slot", slot, rslot, w.dtype)
+    if qgather:
+        assert np.array_equal(slot, synth.param_at(w.seed, w.master_sigma, w.dtype, cols + off)), \
+            "the slot changed though the step wrote only the quantised payload"
+        stats["qgather"] = check_payload_blocks(g, c, reps, qgather)
+    else:
+        stats["slot"] = H.assert_16bit_within_ulp("slot", slot, rslot, w.dtype)
     rng = np.random.default_rng(5)
     outside = np.concatenate([np.arange(max(0, off - 4096), off),
                               np.arange(off + valid, min(w.psi, off + valid + 4096)),
@@ -66,6 +74,30 @@ def run_fullsize(w, layout="strided", qbits=0, steps=None, samples=65_536):
     H.log(f"{w.name}: ok {stats}")
     del g
     torch.cuda.empty_cache()
+
+
+def check_payload_blocks(g, c, reps, bits, nrandom=6):
+    """The first, last and injected-overflow blocks and a few random ones:
+    codes and records against the oracle's quantisation of its own new
+    16-bit parameters over each whole block."""
+    import oracle as O
+    _, _, valid = c.part
+    nblk = (valid + O.QBLOCK - 1) // O.QBLOCK
+    rng = np.random.default_rng(23)
+    picks = {0, nblk - 1, *(i.col // O.QBLOCK for i in c.injections),
+             *rng.integers(0, nblk, nrandom).tolist()}
+    for b in sorted(picks):
+        lo, hi = b * O.QBLOCK, min(valid, (b + 1) * O.QBLOCK)
+        cols = np.arange(lo, hi, dtype=np.int64)
+        _, _, _, rslot = H.oracle_elements(c, reps, cols)
+        ref = O.quantize(rslot, c.w.dtype, bits)
+        c0, c1 = O.qcode_bytes(lo, bits), O.qcode_bytes(hi, bits)
+        codes = g.qg.codes[c0:c1].cpu().numpy()
+        rec = g.qg.blocks[8 * b:8 * b + 8].cpu().numpy()
+        assert np.array_equal(codes, ref.codes[:c1 - c0]), f"block {b}: codes differ"
+        assert rec[:4].view(np.uint32)[0] == ref.scale.view(np.uint32)[0], f"block {b}: scale"
+        assert rec[4:].view(np.int32)[0] == ref.zero[0], f"block {b}: zero point"
+    return {"blocks_checked": len(picks)}
 
 
 def test_psi7e9_clip_two_pass_fullsize():
@@ -89,3 +121,12 @@ def test_psi13e9_int8_blocks_fullsize():
     skipped), decisions over the whole shard, elements on a sample with their
     whole blocks."""
     run_fullsize(workloads.P13B, qbits=8, steps=2, samples=2_000)
+
+
+def test_psi13e9_int8_gather_payload_fullsize():
+    """The 13B shard through zero_fused_step_qgather writing the INT8
+    all-gather payload and no 16-bit slot (bench.py --qgather 8): its five
+    steps, the second skipped by the injected +inf (zero_fused_restore_q then
+    rebuilds the payload from the kept master), decisions over the whole
+    shard, state on a sample, payload on whole sampled blocks."""
+    run_fullsize(workloads.P13B, qgather=8)

@@ -72,3 +72,39 @@ def test_graph_replay_equals_eager(name):
         H.assert_16bit_within_ulp("slot", slot, rslot, c.w.dtype)
     H.log(f"graph {name}: {c.steps} replays equal the eager steps; skips "
           f"{[r['skip'] for r in g.reports]}")
+
+
+@pytest.mark.parametrize("write_slot", [True, False])
+def test_graph_replay_with_quantised_gather_payload(write_slot):
+    """The fused step that writes the INT8 all-gather payload, captured once:
+    a skip at step 2 (zero_fused_restore_q rebuilds the payload inside the
+    replay), every replay's ctrl and the final state, slot and payload equal
+    to the eager run's bit for bit, the payload also to the oracle's."""
+    import torch
+    import oracle as O
+    c = Case(small(100_003, 3, 2, steps=4, scaler=2, contrib_scale=2.0 ** 10,
+                   loss_scale=2.0 ** 10), 2, 4, extra=(Inject(2, 2, 30_001, np.inf),))
+    eager = H.GpuRun(c, full_gather=False, qgather=8, write_slot=write_slot)
+    eager.run()
+    g = H.GpuRun(c, full_gather=False, qgather=8, write_slot=write_slot)
+    graph = g.step_obj.capture(g.contrib, g.gather if write_slot else None, g.qg)
+    torch.cuda.synchronize()
+    assert g.step_obj.ctrl_dict()["t"] == 0
+    for s in range(1, c.steps + 1):
+        g.fill(s)
+        graph.replay()
+        torch.cuda.synchronize()
+        rep = g.step_obj.ctrl_dict()
+        assert rep == eager.reports[s - 1], (s, rep, eager.reports[s - 1])
+        g.reports.append(rep)
+    for a, b, what in zip(g.fetch(), eager.fetch(), ("master", "m", "v", "slot")):
+        assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8)), what
+    for a, b, what in zip(g.qpayload(), eager.qpayload(), ("codes", "scales", "zeros")):
+        assert np.array_equal(np.ascontiguousarray(a).view(np.uint8),
+                              np.ascontiguousarray(b).view(np.uint8)), what
+    reps = H.oracle_scalars(c)
+    H.assert_reports(g.reports, reps)
+    _, _, _, rslot = H.oracle_elements(c, reps)
+    H.assert_qpayload(g.qpayload(), O.quantize(rslot, c.w.dtype, 8))
+    H.log(f"graph qgather write_slot={write_slot}: {c.steps} replays equal; skips "
+          f"{[r['skip'] for r in g.reports]}")

@@ -100,6 +100,12 @@ _sig = {
     "zero_fused_step_q": (ctypes.c_int, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _i32,
                                          ctypes.POINTER(State), _i64, _vp, _i32, _i64,
                                          ctypes.POINTER(Hparams), _vp, _vp, ctypes.c_size_t, _vp]),
+    "zero_fused_step_qgather": (ctypes.c_int, [_vp, _i32, _i32, _i64, ctypes.POINTER(State), _i64,
+                                               _vp, _i32, _i64, _i32, _vp, _vp,
+                                               ctypes.POINTER(Hparams), _vp, _vp, ctypes.c_size_t,
+                                               _vp]),
+    "zero_fused_restore_q": (ctypes.c_int, [ctypes.POINTER(State), _i64, _vp, _i32, _i64, _i32, _vp,
+                                            _vp, _vp, _vp]),
     "zero_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _sig.items():
@@ -312,6 +318,37 @@ def zero_fused_step_q(q: QuantRows, pair, valid_len: int, gather, gather_dtype: 
         ctypes.byref(hp), _ptr(ctrl), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
 
 
+class QGather:
+    """A rank's quantised all-gather payload: ``codes`` and ``blocks`` device
+    tensors holding ``bits``-bit block codes of ``length`` 16-bit parameters."""
+
+    def __init__(self, codes, blocks, bits: int, length: int):
+        self.codes, self.blocks, self.bits, self.length = codes, blocks, bits, length
+
+    @staticmethod
+    def alloc(length: int, bits: int, device):
+        (codes, blocks), = QuantRows.alloc(1, length, bits, device).rows
+        return QGather(codes, blocks, bits, length)
+
+
+def zero_fused_step_qgather(contrib, contrib_dtype: int, nranks: int, stride: int, pair,
+                            valid_len: int, gather, gather_dtype: int, offset: int, q: QGather,
+                            hp: Hparams, ctrl, ws) -> None:
+    st = _state(pair)
+    _check("zero_fused_step_qgather", _lib.zero_fused_step_qgather(
+        _ptr(contrib), contrib_dtype, nranks, stride, ctypes.byref(st), valid_len, _ptr(gather),
+        gather_dtype, offset, q.bits, _ptr(q.codes), _ptr(q.blocks), ctypes.byref(hp), _ptr(ctrl),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+
+
+def zero_fused_restore_q(pair, valid_len: int, gather, dtype: int, offset: int, q: QGather,
+                         ctrl) -> None:
+    st = _state(pair)
+    _check("zero_fused_restore_q", _lib.zero_fused_restore_q(
+        ctypes.byref(st), valid_len, _ptr(gather), dtype, offset, q.bits, _ptr(q.codes),
+        _ptr(q.blocks), _ptr(ctrl), _stream()))
+
+
 def zero_last_error() -> str:
     return _lib.zero_last_error().decode()
 
@@ -355,11 +392,25 @@ class ShardStep:
             self.pair = tuple(torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3))
             zero_pair_store(state, self.pair, valid_len, self.ctrl)
 
-    def step(self, contrib, gather) -> None:
+    def step(self, contrib, gather, qgather: QGather = None) -> None:
+        """One step.  With ``qgather`` (fused path, [N, stride] contributions)
+        the step also writes the quantised all-gather payload of the new
+        parameters, and ``gather`` may be None (no 16-bit slot written)."""
         quant = isinstance(contrib, QuantRows)
         table = isinstance(contrib, (list, tuple))
         if (table and len(contrib) != self.nranks) or (quant and len(contrib.rows) != self.nranks):
             raise ValueError(f"contribution rows do not match {self.nranks} ranks")
+        if qgather is not None:
+            if not self.fused or quant or table:
+                raise ValueError("a quantised all-gather payload needs the fused path over "
+                                 "[N, stride] contributions")
+            zero_fused_step_qgather(contrib, self.dtype, self.nranks, self.stride, self.pair,
+                                    self.valid_len, gather, self.gather_dtype, self.offset,
+                                    qgather, self.hp, self.ctrl, self.ws)
+            zero_grad_norm_overflow([self.ws], [self.valid_len], [self.ctrl], self.hp, True)
+            zero_fused_restore_q(self.pair, self.valid_len, gather, self.gather_dtype, self.offset,
+                                 qgather, self.ctrl)
+            return
         if self.fused:
             if quant:
                 zero_fused_step_q(contrib, self.pair, self.valid_len, gather, self.gather_dtype,
@@ -387,7 +438,7 @@ class ShardStep:
             zero_adam_step(self.state, self.g, self.valid_len, self.hp, self.ctrl, gather,
                            self.gather_dtype, self.offset)
 
-    def capture(self, contrib, gather):
+    def capture(self, contrib, gather, qgather: QGather = None):
         """Records one step (its two or three launches) into a HIP graph and
         returns it (a torch.cuda.CUDAGraph); ``graph.replay()`` then runs a
         step.  Every step-to-step scalar lives in the device ctrl block and every
@@ -400,7 +451,7 @@ class ShardStep:
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             with torch.cuda.graph(graph, stream=side):
-                self.step(contrib, gather)
+                self.step(contrib, gather, qgather)
         torch.cuda.current_stream().wait_stream(side)
         return graph
 

@@ -19,6 +19,9 @@
 //   * the fused path double-buffers the optimizer state with the two sets of
 //     a tile adjacent in memory, so reading one set and writing the other
 //     keeps the locality of an in-place update;
+//   * a quantisation block (ZeRO++) is one tile, so the fused step can also
+//     emit the block-quantised all-gather payload of the new parameters in
+//     the same pass: the block's range is one more workgroup reduction;
 //   * fp32 reduction in rank order k = 0..N-1 and each Adam operation rounded
 //     once in the written order (compiled with -ffp-contract=off, correctly
 //     rounded division and square root), so results are reproducible and
@@ -839,10 +842,39 @@ struct FusedArgs {
     int32_t n;
 };
 
-// Single pass: reduce + partial + Adam (read set cur, write set 1-cur of the
-// tile) + cast, one tile per workgroup.
-template <int DTO, int GW, int NR, class SRC>
-__global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs<SRC> a) {
+// The quantised all-gather payload a fused step may also write: codes and
+// block records of the new 16-bit parameters, and the slot's store width
+// (4, 2, 1, or 0 for no 16-bit slot), chosen at launch.
+struct QGatherOut {
+    uint8_t* codes;
+    zero_qblock* blocks;
+    int32_t gw;
+};
+
+constexpr int kGwRuntime = -1;  // slot store width taken from QGatherOut::gw
+
+// Slot store with the width chosen at launch (a workgroup-uniform branch).
+__device__ __forceinline__ void store_slot_rt(int gw, uint16_t* __restrict__ slot, const Runs& r,
+                                              const uint32_t h[kVec]) {
+    if (gw == 4)
+        store_slot<4>(slot, r, h);
+    else if (gw == 2)
+        store_slot<2>(slot, r, h);
+    else if (gw == 1)
+        store_slot<1>(slot, r, h);
+}
+
+template <int BITS>
+__device__ __forceinline__ void quant_tile(const float x[kVec], const Runs& r, bool full, int64_t len,
+                                           uint8_t* __restrict__ codes,
+                                           zero_qblock* __restrict__ blocks, int64_t blk);
+
+// Single pass over one tile: reduce + partial + Adam (read set cur, write set
+// 1-cur of the tile) + cast.  QB = 8 or 4 also quantises the tile's new
+// 16-bit parameters as one block (the payload of a quantised all-gather),
+// after the per-thread work so that every thread reaches the block's barrier.
+template <int DTO, int GW, int NR, class SRC, int QB>
+__device__ __forceinline__ void fused_tile(const FusedArgs<SRC>& a, const QGatherOut& qo) {
     const zero_ctrl* __restrict__ c = a.ctrl;
     const int cur = c->cur;
     const float inv = (float)(1.0 / ((double)a.n * (double)c->loss_scale));
@@ -851,6 +883,7 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs<SRC> a) {
     const Runs r = runs_of(blockIdx.x);
     double ss = 0.0;
     uint32_t bad = 0;
+    float xq[kVec];  // QB: the new 16-bit parameters widened to fp32, 0 past the end
     if (r.b + kRun <= a.len) {
         // run a and run b of one tile sit at the same distance from their
         // set's start in the paired layout
@@ -887,15 +920,22 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs<SRC> a) {
             ss += (double)gj * (double)gj;
             adam_elem(k, gj, p[j], m[j], v[j]);
             h[j] = narrow<DTO>(p[j]);
+            if constexpr (QB != 0) xq[j] = widen1<DTO>((uint16_t)h[j]);
         }
         store8(a.pair[0] + da, a.pair[0] + db, p);
         store8(a.pair[1] + da, a.pair[1] + db, m);
         store8(a.pair[2] + da, a.pair[2] + db, v);
-        store_slot<GW>(a.slot, r, h);
+        if constexpr (GW == kGwRuntime)
+            store_slot_rt(qo.gw, a.slot, r, h);
+        else
+            store_slot<GW>(a.slot, r, h);
     } else {
         for (int j = 0; j < kVec; ++j) {
             const int64_t i = elem(r, j);
-            if (i >= a.len) continue;
+            if (i >= a.len) {
+                if constexpr (QB != 0) xq[j] = 0.0f;
+                continue;
+            }
             const float acc = a.src.sum1(a.n, i);
             bad |= __builtin_isfinite(acc) ? 0u : 1u;
             const float gj = acc * inv;
@@ -906,10 +946,36 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs<SRC> a) {
             a.pair[0][di] = p;
             a.pair[1][di] = m;
             a.pair[2][di] = v;
-            a.slot[i] = (uint16_t)narrow<DTO>(p);
+            if constexpr (QB == 0) {
+                a.slot[i] = (uint16_t)narrow<DTO>(p);
+            } else {
+                const uint32_t hj = narrow<DTO>(p);
+                if (qo.gw != 0) a.slot[i] = (uint16_t)hj;
+                xq[j] = widen1<DTO>((uint16_t)hj);
+            }
         }
     }
+    if constexpr (QB != 0)
+        quant_tile<QB>(xq, r, r.b + kRun <= a.len, a.len, qo.codes, qo.blocks, blockIdx.x);
     write_partial(a.ws, ss, bad);
+}
+
+template <int DTO, int GW, int NR, class SRC>
+__global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs<SRC> a) {
+    fused_tile<DTO, GW, NR, SRC, 0>(a, QGatherOut{nullptr, nullptr, 0});
+}
+
+template <class SRC>
+struct FusedQArgs {
+    FusedArgs<SRC> f;
+    QGatherOut q;
+};
+
+// The fused step that also writes the quantised all-gather payload of the
+// new parameters (BITS = 8 or 4); the 16-bit slot is written when q.gw != 0.
+template <int DTO, int NR, class SRC, int BITS>
+__global__ void __launch_bounds__(kBlock) fused_qgather_kernel(FusedQArgs<SRC> a) {
+    fused_tile<DTO, kGwRuntime, NR, SRC, BITS>(a.f, a.q);
 }
 
 // ---------------------------------------------------------------- block quantisation
@@ -962,26 +1028,17 @@ __device__ __forceinline__ float clamp_code(float r, float qmax) {
     return r < 0.0f ? 0.0f : (r > qmax ? qmax : r);
 }
 
-// VEC: src is 8-byte aligned (vector loads); otherwise 16-bit loads.
-template <int DT, int BITS, bool VEC>
-__global__ void __launch_bounds__(kBlock) quantize_kernel(QuantArgs a) {
+// Quantises one block (one tile) from the thread's 8 values x (0 for
+// positions past len, which leaves the range unchanged): the block's range
+// over the whole workgroup, its record at blocks[blk], and the codes at the
+// thread's two runs.  Every thread of the workgroup must call it (it holds a
+// workgroup barrier); `full` says whether both of the thread's runs are inside
+// len.
+template <int BITS>
+__device__ __forceinline__ void quant_tile(const float x[kVec], const Runs& r, bool full, int64_t len,
+                                           uint8_t* __restrict__ codes,
+                                           zero_qblock* __restrict__ blocks, int64_t blk) {
     constexpr float qmax = (float)((1 << BITS) - 1);
-    const Runs r = runs_of(blockIdx.x);
-    const bool full = r.b + kRun <= a.len;
-    float x[kVec];
-    if (VEC && full) {
-        const Row w = load_row(a.src, r);
-        x[0] = widen_lo<DT>(w.a.x); x[1] = widen_hi<DT>(w.a.x);
-        x[2] = widen_lo<DT>(w.a.y); x[3] = widen_hi<DT>(w.a.y);
-        x[4] = widen_lo<DT>(w.b.x); x[5] = widen_hi<DT>(w.b.x);
-        x[6] = widen_lo<DT>(w.b.y); x[7] = widen_hi<DT>(w.b.y);
-    } else {
-#pragma unroll
-        for (int j = 0; j < kVec; ++j) {
-            const int64_t i = elem(r, j);
-            x[j] = i < a.len ? widen1<DT>(a.src[i]) : 0.0f;  // 0 leaves the range unchanged
-        }
-    }
     float lo = 0.0f, hi = 0.0f;
     uint32_t bad = 0u;
 #pragma unroll
@@ -1006,31 +1063,104 @@ __global__ void __launch_bounds__(kBlock) quantize_kernel(QuantArgs a) {
         zero_qblock q;
         q.scale = ok ? sc : __builtin_nanf("");
         q.zero = (int32_t)z;
-        a.blocks[blockIdx.x] = q;
+        blocks[blk] = q;
     }
     if (full) {
         if constexpr (BITS == 8) {
             __builtin_nontemporal_store(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                                        reinterpret_cast<uint32_t*>(a.codes + r.a));
+                                        reinterpret_cast<uint32_t*>(codes + r.a));
             __builtin_nontemporal_store(c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24),
-                                        reinterpret_cast<uint32_t*>(a.codes + r.b));
+                                        reinterpret_cast<uint32_t*>(codes + r.b));
         } else {
             __builtin_nontemporal_store((uint16_t)(c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12)),
-                                        reinterpret_cast<uint16_t*>(a.codes + (r.a >> 1)));
+                                        reinterpret_cast<uint16_t*>(codes + (r.a >> 1)));
             __builtin_nontemporal_store((uint16_t)(c[4] | (c[5] << 4) | (c[6] << 8) | (c[7] << 12)),
-                                        reinterpret_cast<uint16_t*>(a.codes + (r.b >> 1)));
+                                        reinterpret_cast<uint16_t*>(codes + (r.b >> 1)));
         }
     } else if constexpr (BITS == 8) {
         for (int j = 0; j < kVec; ++j) {
             const int64_t i = elem(r, j);
-            if (i < a.len) a.codes[i] = (uint8_t)c[j];
+            if (i < len) codes[i] = (uint8_t)c[j];
         }
     } else {
         // element pairs (2m, 2m + 1) never straddle a run, so each byte has one writer
         for (int j = 0; j < kVec; j += 2) {
             const int64_t i = elem(r, j);
-            if (i < a.len) a.codes[i >> 1] = (uint8_t)(c[j] | (i + 1 < a.len ? c[j + 1] << 4 : 0u));
+            if (i < len) codes[i >> 1] = (uint8_t)(c[j] | (i + 1 < len ? c[j + 1] << 4 : 0u));
         }
+    }
+}
+
+// VEC: src is 8-byte aligned (vector loads); otherwise 16-bit loads.
+template <int DT, int BITS, bool VEC>
+__global__ void __launch_bounds__(kBlock) quantize_kernel(QuantArgs a) {
+    const Runs r = runs_of(blockIdx.x);
+    const bool full = r.b + kRun <= a.len;
+    float x[kVec];
+    if (VEC && full) {
+        const Row w = load_row(a.src, r);
+        x[0] = widen_lo<DT>(w.a.x); x[1] = widen_hi<DT>(w.a.x);
+        x[2] = widen_lo<DT>(w.a.y); x[3] = widen_hi<DT>(w.a.y);
+        x[4] = widen_lo<DT>(w.b.x); x[5] = widen_hi<DT>(w.b.x);
+        x[6] = widen_lo<DT>(w.b.y); x[7] = widen_hi<DT>(w.b.y);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            const int64_t i = elem(r, j);
+            x[j] = i < a.len ? widen1<DT>(a.src[i]) : 0.0f;  // 0 leaves the range unchanged
+        }
+    }
+    quant_tile<BITS>(x, r, full, a.len, a.codes, a.blocks, blockIdx.x);
+}
+
+struct RestoreQArgs {
+    const float* master;  // paired master
+    uint16_t* slot;       // NULL when gw == 0
+    int64_t len;
+    const zero_ctrl* ctrl;
+    QGatherOut q;
+};
+
+// After a skipped fused step that wrote a quantised all-gather payload: the
+// slot (when gw != 0) and the payload rebuilt from the current set of the
+// paired master, exactly as the step would have written them.  A fixed small
+// grid walks the tiles; with no skip every workgroup returns after reading
+// the flag (uniform per workgroup, so the barriers below are reached by all
+// or none of its threads).
+template <int DT, int BITS>
+__global__ void __launch_bounds__(kBlock) restore_q_kernel(RestoreQArgs a) {
+    if (!a.ctrl->skip) return;
+    const int cur = a.ctrl->cur;
+    const int64_t ntile = (a.len + kTile - 1) / kTile;
+    for (int64_t tile = blockIdx.x; tile < ntile; tile += gridDim.x) {
+        const Runs r = runs_of(tile);
+        const bool full = r.b + kRun <= a.len;
+        float x[kVec];
+        if (full) {
+            const int64_t sa = pair_index(r.a, cur);
+            float p[kVec];
+            uint32_t h[kVec];
+            load8(a.master + sa, a.master + sa + 256, p);
+#pragma unroll
+            for (int j = 0; j < kVec; ++j) {
+                h[j] = narrow<DT>(p[j]);
+                x[j] = widen1<DT>((uint16_t)h[j]);
+            }
+            store_slot_rt(a.q.gw, a.slot, r, h);
+        } else {
+            for (int j = 0; j < kVec; ++j) {
+                const int64_t i = elem(r, j);
+                if (i >= a.len) {
+                    x[j] = 0.0f;
+                    continue;
+                }
+                const uint32_t hj = narrow<DT>(a.master[pair_index(i, cur)]);
+                if (a.q.gw != 0) a.slot[i] = (uint16_t)hj;
+                x[j] = widen1<DT>((uint16_t)hj);
+            }
+        }
+        quant_tile<BITS>(x, r, full, a.len, a.q.codes, a.q.blocks, tile);
+        __syncthreads();  // the next tile's block range reuses the same LDS
     }
 }
 
@@ -1319,9 +1449,50 @@ int check_qrows(const void* const* codes, const zero_qblock* const* blocks, int3
     return ZERO_OK;
 }
 
-}  // namespace
+// Output of a quantised all-gather payload: bits 8 or 4, codes and blocks
+// non-null and 8-byte aligned.
+int check_qout(int32_t bits, const void* codes, const zero_qblock* blocks, const char* what) {
+    if (bits != 8 && bits != 4) return fail(ZERO_EINVAL, "%s: bits must be 8 or 4, not %d", what, bits);
+    if (codes == nullptr || blocks == nullptr) return fail(ZERO_EINVAL, "%s: null codes or blocks", what);
+    if (((reinterpret_cast<uintptr_t>(codes) | reinterpret_cast<uintptr_t>(blocks)) & 7u) != 0)
+        return fail(ZERO_EALIGN, "%s: codes and blocks must be 8-byte aligned", what);
+    return ZERO_OK;
+}
 
-extern "C" {}  // namespace
+// The 16-bit slot of a step that also writes a quantised payload: optional
+// (gather NULL writes no slot), the dtype always names the parameters' format.
+int check_opt_slot(const void* gather, int32_t dtype, int64_t offset) {
+    if (gather != nullptr) return check_slot(gather, dtype, offset);
+    if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, "unknown gather dtype %d", dtype);
+    return ZERO_OK;
+}
+
+template <int DT, int BITS>
+Kernel<FusedQArgs<Src16<DT, StridedRows>>> fused_qgather_bits(int dto, int n) {
+    using S = Src16<DT, StridedRows>;
+    if (n == 8)
+        return dto == ZERO_F16 ? fused_qgather_kernel<ZERO_F16, 8, S, BITS>
+                               : fused_qgather_kernel<ZERO_BF16, 8, S, BITS>;
+    return dto == ZERO_F16 ? fused_qgather_kernel<ZERO_F16, 0, S, BITS>
+                           : fused_qgather_kernel<ZERO_BF16, 0, S, BITS>;
+}
+
+template <int DT>
+int fused_qgather_launch(const StridedRows& rows, int32_t nranks, const zero_state* pair,
+                         int64_t valid_len, void* gather, int32_t gather_dtype, int64_t offset,
+                         int32_t bits, void* codes, zero_qblock* blocks, const zero_hparams* hp,
+                         const zero_ctrl* ctrl, void* ws, void* stream, const char* what) {
+    uint16_t* slot = gather == nullptr ? nullptr : (uint16_t*)gather + offset;
+    const FusedQArgs<Src16<DT, StridedRows>> a{
+        {Src16<DT, StridedRows>{rows}, {pair->master, pair->m, pair->v}, slot, valid_len, ctrl,
+         (Partial*)ws, *hp, nranks},
+        {(uint8_t*)codes, blocks, slot == nullptr ? 0 : store_width(slot)}};
+    const auto k = bits == 8 ? fused_qgather_bits<DT, 8>(gather_dtype, nranks)
+                             : fused_qgather_bits<DT, 4>(gather_dtype, nranks);
+    return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, what);
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -1589,6 +1760,53 @@ int zero_fused_restore(const zero_state* pair, int64_t valid_len, void* gather, 
     }
     return launch(k, nt < kRestoreGrid ? nt : kRestoreGrid, kBlock, (hipStream_t)stream, a,
                   "zero_fused_restore");
+}
+
+int zero_fused_step_qgather(const void* contrib, int32_t contrib_dtype, int32_t nranks,
+                            int64_t stride, const zero_state* pair, int64_t valid_len, void* gather,
+                            int32_t gather_dtype, int64_t offset, int32_t bits, void* codes,
+                            zero_qblock* blocks, const zero_hparams* hp, const zero_ctrl* ctrl,
+                            void* ws, size_t ws_bytes, void* stream) {
+    int rc;
+    const char* what = "zero_fused_step_qgather";
+    if ((rc = check_contrib(contrib, contrib_dtype, nranks, stride, valid_len)) != ZERO_OK) return rc;
+    if ((rc = check_state(pair, what)) != ZERO_OK) return rc;
+    if ((rc = check_hp(hp)) != ZERO_OK) return rc;
+    if (hp->max_grad_norm > 0.0f) return fail(ZERO_EINVAL, "%s: clipping needs the two-pass path", what);
+    if ((rc = check_ctrl(ctrl, what)) != ZERO_OK) return rc;
+    if ((rc = check_opt_slot(gather, gather_dtype, offset)) != ZERO_OK) return rc;
+    if ((rc = check_qout(bits, codes, blocks, what)) != ZERO_OK) return rc;
+    if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
+    if (valid_len == 0) return ok();
+    const StridedRows rows{(const uint16_t*)contrib, stride};
+    return contrib_dtype == ZERO_F16
+               ? fused_qgather_launch<ZERO_F16>(rows, nranks, pair, valid_len, gather, gather_dtype,
+                                                offset, bits, codes, blocks, hp, ctrl, ws, stream, what)
+               : fused_qgather_launch<ZERO_BF16>(rows, nranks, pair, valid_len, gather, gather_dtype,
+                                                 offset, bits, codes, blocks, hp, ctrl, ws, stream, what);
+}
+
+int zero_fused_restore_q(const zero_state* pair, int64_t valid_len, void* gather, int32_t dtype,
+                         int64_t offset, int32_t bits, void* codes, zero_qblock* blocks,
+                         const zero_ctrl* ctrl, void* stream) {
+    int rc;
+    const char* what = "zero_fused_restore_q";
+    if ((rc = check_len(valid_len, what)) != ZERO_OK) return rc;
+    if ((rc = check_state(pair, what)) != ZERO_OK) return rc;
+    if ((rc = check_ctrl(ctrl, what)) != ZERO_OK) return rc;
+    if ((rc = check_opt_slot(gather, dtype, offset)) != ZERO_OK) return rc;
+    if ((rc = check_qout(bits, codes, blocks, what)) != ZERO_OK) return rc;
+    if (valid_len == 0) return ok();
+    uint16_t* slot = gather == nullptr ? nullptr : (uint16_t*)gather + offset;
+    const RestoreQArgs a{pair->master, slot, valid_len, ctrl,
+                         {(uint8_t*)codes, blocks, slot == nullptr ? 0 : store_width(slot)}};
+    Kernel<RestoreQArgs> k;
+    if (dtype == ZERO_F16)
+        k = bits == 8 ? restore_q_kernel<ZERO_F16, 8> : restore_q_kernel<ZERO_F16, 4>;
+    else
+        k = bits == 8 ? restore_q_kernel<ZERO_BF16, 8> : restore_q_kernel<ZERO_BF16, 4>;
+    const int64_t nt = tiles_for(valid_len);
+    return launch(k, nt < kRestoreGrid ? nt : kRestoreGrid, kBlock, (hipStream_t)stream, a, what);
 }
 
 static int pair_copy(const zero_state* flat, const zero_state* pair, int64_t valid_len,
