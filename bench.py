@@ -171,7 +171,7 @@ def timed_steps(b, steps, warmup, torch, Z, graph=False, qg=None):
               for _ in range(steps)]
     hp, n, stride, valid, off = st.hp, st.nranks, st.stride, st.valid_len, st.offset
     for i in range(steps):
-        if qg is not None:
+        if qg is not None and b["fused"]:
             ev[i][0].record()
             Z.zero_fused_step_qgather(contrib, st.dtype, n, stride, st.pair, valid, None,
                                       st.gather_dtype, off, qg, hp, st.ctrl, st.ws)
@@ -203,7 +203,11 @@ def timed_steps(b, steps, warmup, torch, Z, graph=False, qg=None):
             ev_red[i][1].record()
             Z.zero_grad_norm_overflow([st.ws], [valid], [st.ctrl], hp, False)
             ev[i][0].record()
-            Z.zero_adam_step(st.state, st.g, valid, hp, st.ctrl, gather, st.gather_dtype, off)
+            if qg is not None:
+                Z.zero_adam_step_qgather(st.state, st.g, valid, hp, st.ctrl, None,
+                                         st.gather_dtype, off, qg)
+            else:
+                Z.zero_adam_step(st.state, st.g, valid, hp, st.ctrl, gather, st.gather_dtype, off)
             ev[i][1].record()
     torch.cuda.synchronize()
     kern_ms = [a.elapsed_time(c) for a, c in ev]
@@ -294,8 +298,8 @@ def main():
                     help="block-quantised (ZeRO++) INT8 or INT4 contributions through the "
                          "quantised calls")
     ap.add_argument("--qgather", type=int, choices=(0, 4, 8), default=0,
-                    help="the fused step writes the ZeRO++ INT8 or INT4 all-gather payload of "
-                         "the new parameters instead of the 16-bit slot")
+                    help="the step writes the ZeRO++ INT8 or INT4 all-gather payload of the new "
+                         "parameters instead of the 16-bit slot")
     ap.add_argument("--graph", action="store_true",
                     help="time the step as one captured HIP graph replayed each step")
     ap.add_argument("--rows", action="store_true",
@@ -331,9 +335,8 @@ def main():
         return
 
     w = workloads.BY_NAME[args.workload]
-    if args.qgather and (args.rows or args.quant or w.max_grad_norm > 0):
-        print("--qgather takes the fused path over [N, stride] contributions only",
-              file=sys.stderr)
+    if args.qgather and (args.rows or args.quant):
+        print("--qgather takes [N, stride] 16-bit contributions only", file=sys.stderr)
         sys.exit(2)
     b = setup(w, torch, synth, Z, rows=args.rows, qbits=args.quant)
     valid = b["valid"]
@@ -351,6 +354,9 @@ def main():
                      "fused_qgather_kernel_q%d" % args.qgather if args.qgather else
                      "fused_kernel_rows" if args.rows else "fused_kernel")
         kern_bytes = step_bytes
+    elif args.qgather:
+        kern_name = "adam_qgather_kernel_q%d" % args.qgather
+        kern_bytes = int(round((4 + 24 + args.qgather / 8 + 8 / 2048) * valid))  # payload, no slot
     else:
         kern_name = "adam_kernel"
         kern_bytes = (4 + 26) * valid  # g + master/m/v in and out + the 16-bit slot

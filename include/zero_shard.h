@@ -242,6 +242,20 @@ int zero_adam_step(const zero_state *state, const float *g_dev, int64_t valid_le
                    const zero_hparams *hp, const zero_ctrl *ctrl_dev, void *gather_dev,
                    int32_t gather_dtype, int64_t offset, void *stream);
 
+/* zero_adam_step that also writes the quantised all-gather payload of the
+ * new parameters (ZeRO++, "CMU 11-868 L18", Other memory optimizations; see
+ * zero_fused_step_qgather): codes_dev and blocks_dev equal, bit for bit,
+ * what zero_quantize_blocks(gather_dtype, bits) would write from the 16-bit
+ * slot after the step.  gather_dev may be NULL (no 16-bit slot written);
+ * gather_dtype always names the 16-bit format that is quantised.  A skipped
+ * step writes nothing, so slot and payload keep the previous step's values.
+ * Errors: as zero_adam_step, plus EINVAL (bits not 8 or 4, null codes or
+ * blocks, gather dtype) and EALIGN (codes or blocks not 8-byte aligned). */
+int zero_adam_step_qgather(const zero_state *state, const float *g_dev, int64_t valid_len,
+                           const zero_hparams *hp, const zero_ctrl *ctrl_dev, void *gather_dev,
+                           int32_t gather_dtype, int64_t offset, int32_t bits, void *codes_dev,
+                           zero_qblock *blocks_dev, void *stream);
+
 /* Cast ("CMU 11-868 L18", Mechanism 1 steps 5-6; lesson Stage 1 step 4):
  * gather_dev[offset + i] = RNE_dtype(master_dev[i]) for i < valid_len,
  * unconditionally (also used to fill the initial parameters). */

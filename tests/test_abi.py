@@ -278,3 +278,26 @@ def test_fused_restore_q_validation(Z, kw, code, msg):
                                      a["bits"], a["codes"], a["blocks"], a["ctrl"], None)
     assert rc == code
     assert msg in Z.zero_last_error()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(bits=2), -1, "bits"),
+    (dict(codes=0), -1, "null codes"),
+    (dict(blocks=FAKE + 4), -2, "8-byte"),
+    (dict(gather=None, gdt=0), -1, "gather dtype"),
+    (dict(gather=FAKE + 1), -2, "2-byte"),
+    (dict(g=0), -1, "null g"),
+    (dict(g=FAKE + 8), -2, "g not 16-byte"),
+    (dict(ctrl=0), -1, "null ctrl"),
+    (dict(valid=-2), -3, "out of range"),
+])
+def test_adam_qgather_validation(Z, kw, code, msg):
+    a = dict(valid=64, g=FAKE, gather=FAKE, gdt=1, bits=8, codes=FAKE, blocks=FAKE, ctrl=FAKE)
+    a.update(kw)
+    s0 = Z.State(FAKE, FAKE + 256, FAKE + 512)
+    hp = Z.hparams(max_grad_norm=1.0)
+    rc = Z._lib.zero_adam_step_qgather(ctypes.byref(s0), a["g"], a["valid"], ctypes.byref(hp),
+                                       a["ctrl"], a["gather"], a["gdt"], 0, a["bits"], a["codes"],
+                                       a["blocks"], None)
+    assert rc == code
+    assert msg in Z.zero_last_error()

@@ -106,6 +106,9 @@ _sig = {
                                                _vp]),
     "zero_fused_restore_q": (ctypes.c_int, [ctypes.POINTER(State), _i64, _vp, _i32, _i64, _i32, _vp,
                                             _vp, _vp, _vp]),
+    "zero_adam_step_qgather": (ctypes.c_int, [ctypes.POINTER(State), _vp, _i64,
+                                              ctypes.POINTER(Hparams), _vp, _vp, _i32, _i64, _i32,
+                                              _vp, _vp, _vp]),
     "zero_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _sig.items():
@@ -349,6 +352,14 @@ def zero_fused_restore_q(pair, valid_len: int, gather, dtype: int, offset: int, 
         _ptr(q.blocks), _ptr(ctrl), _stream()))
 
 
+def zero_adam_step_qgather(state, g, valid_len: int, hp: Hparams, ctrl, gather,
+                           gather_dtype: int, offset: int, q: QGather) -> None:
+    st = _state(state)
+    _check("zero_adam_step_qgather", _lib.zero_adam_step_qgather(
+        ctypes.byref(st), _ptr(g), valid_len, ctypes.byref(hp), _ptr(ctrl), _ptr(gather),
+        gather_dtype, offset, q.bits, _ptr(q.codes), _ptr(q.blocks), _stream()))
+
+
 def zero_last_error() -> str:
     return _lib.zero_last_error().decode()
 
@@ -393,16 +404,30 @@ class ShardStep:
             zero_pair_store(state, self.pair, valid_len, self.ctrl)
 
     def step(self, contrib, gather, qgather: QGather = None) -> None:
-        """One step.  With ``qgather`` (fused path, [N, stride] contributions)
-        the step also writes the quantised all-gather payload of the new
-        parameters, and ``gather`` may be None (no 16-bit slot written)."""
+        """One step.  With ``qgather`` the step also writes the quantised
+        all-gather payload of the new parameters, and ``gather`` may be None
+        (no 16-bit slot written); the fused path then takes [N, stride]
+        contributions only."""
         quant = isinstance(contrib, QuantRows)
         table = isinstance(contrib, (list, tuple))
         if (table and len(contrib) != self.nranks) or (quant and len(contrib.rows) != self.nranks):
             raise ValueError(f"contribution rows do not match {self.nranks} ranks")
+        if qgather is not None and not self.fused:
+            if quant:
+                zero_reduce_grads_q(contrib, self.valid_len, self.ctrl, self.g, self.ws)
+            elif table:
+                zero_reduce_grads_rows(contrib, self.dtype, self.valid_len, self.ctrl, self.g,
+                                       self.ws)
+            else:
+                zero_reduce_grads(contrib, self.dtype, self.nranks, self.stride, self.valid_len,
+                                  self.ctrl, self.g, self.ws)
+            zero_grad_norm_overflow([self.ws], [self.valid_len], [self.ctrl], self.hp, False)
+            zero_adam_step_qgather(self.state, self.g, self.valid_len, self.hp, self.ctrl, gather,
+                                   self.gather_dtype, self.offset, qgather)
+            return
         if qgather is not None:
-            if not self.fused or quant or table:
-                raise ValueError("a quantised all-gather payload needs the fused path over "
+            if quant or table:
+                raise ValueError("the fused step with a quantised all-gather payload takes "
                                  "[N, stride] contributions")
             zero_fused_step_qgather(contrib, self.dtype, self.nranks, self.stride, self.pair,
                                     self.valid_len, gather, self.gather_dtype, self.offset,

@@ -681,6 +681,33 @@ __global__ void __launch_bounds__(kFinBlock) finalize_kernel(CombineArgs a) {
     for (int q = 0; q < a.nranks; ++q) *a.ctrl[q] = c;
 }
 
+// The quantised all-gather payload a fused step may also write: codes and
+// block records of the new 16-bit parameters, and the slot's store width
+// (4, 2, 1, or 0 for no 16-bit slot), chosen at launch.
+struct QGatherOut {
+    uint8_t* codes;
+    zero_qblock* blocks;
+    int32_t gw;
+};
+
+constexpr int kGwRuntime = -1;  // slot store width taken from QGatherOut::gw
+
+// Slot store with the width chosen at launch (a workgroup-uniform branch).
+__device__ __forceinline__ void store_slot_rt(int gw, uint16_t* __restrict__ slot, const Runs& r,
+                                              const uint32_t h[kVec]) {
+    if (gw == 4)
+        store_slot<4>(slot, r, h);
+    else if (gw == 2)
+        store_slot<2>(slot, r, h);
+    else if (gw == 1)
+        store_slot<1>(slot, r, h);
+}
+
+template <int BITS>
+__device__ __forceinline__ void quant_tile(const float x[kVec], const Runs& r, bool full, int64_t len,
+                                           uint8_t* __restrict__ codes,
+                                           zero_qblock* __restrict__ blocks, int64_t blk);
+
 struct AdamArgs {
     float* master;
     float* m;
@@ -692,14 +719,19 @@ struct AdamArgs {
     zero_hparams hp;
 };
 
-// Pass 2 of the two-pass step: Adam in place (+ cast into the gather slot).
-template <int DT, int GW>
-__global__ void __launch_bounds__(kBlock) adam_kernel(AdamArgs a) {
+// Pass 2 of the two-pass step over one tile: Adam in place (+ cast into the
+// gather slot).  QB = 8 or 4 also quantises the tile's new 16-bit parameters
+// as one block of the all-gather payload.  A skipped step returns from every
+// workgroup (the flag is the same for all its threads) before writing
+// anything, so slot and payload keep the previous step's values.
+template <int DT, int GW, int QB>
+__device__ __forceinline__ void adam_tile(const AdamArgs& a, const QGatherOut& qo) {
     const zero_ctrl* __restrict__ c = a.ctrl;
     if (c->skip) return;
     const float clip = c->clip;
     const AdamK k = make_adam(a.hp, c->beta1_pow, c->beta2_pow);
     const Runs r = runs_of(blockIdx.x);
+    float xq[kVec];  // QB: the new 16-bit parameters widened to fp32, 0 past the end
     if (r.b + kRun <= a.len) {
         float g[kVec], p[kVec], m[kVec], v[kVec];
         uint32_t h[kVec];
@@ -712,23 +744,55 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(AdamArgs a) {
         for (int j = 0; j < kVec; ++j) {
             adam_elem(k, g[j] * clip, p[j], m[j], v[j]);
             h[j] = narrow<DT>(p[j]);
+            if constexpr (QB != 0) xq[j] = widen1<DT>((uint16_t)h[j]);
         }
         store8(a.master + r.a, a.master + r.b, p);
         store8(a.m + r.a, a.m + r.b, m);
         store8(a.v + r.a, a.v + r.b, v);
-        if constexpr (GW > 0) store_slot<GW>(a.slot, r, h);
+        if constexpr (GW == kGwRuntime)
+            store_slot_rt(qo.gw, a.slot, r, h);
+        else if constexpr (GW > 0)
+            store_slot<GW>(a.slot, r, h);
     } else {
         for (int j = 0; j < kVec; ++j) {
             const int64_t i = elem(r, j);
-            if (i >= a.len) continue;
+            if (i >= a.len) {
+                if constexpr (QB != 0) xq[j] = 0.0f;
+                continue;
+            }
             float p = a.master[i], m = a.m[i], v = a.v[i];
             adam_elem(k, a.g[i] * clip, p, m, v);
             a.master[i] = p;
             a.m[i] = m;
             a.v[i] = v;
-            if constexpr (GW > 0) a.slot[i] = (uint16_t)narrow<DT>(p);
+            if constexpr (QB == 0) {
+                if constexpr (GW > 0) a.slot[i] = (uint16_t)narrow<DT>(p);
+            } else {
+                const uint32_t hj = narrow<DT>(p);
+                if (qo.gw != 0) a.slot[i] = (uint16_t)hj;
+                xq[j] = widen1<DT>((uint16_t)hj);
+            }
         }
     }
+    if constexpr (QB != 0)
+        quant_tile<QB>(xq, r, r.b + kRun <= a.len, a.len, qo.codes, qo.blocks, blockIdx.x);
+}
+
+template <int DT, int GW>
+__global__ void __launch_bounds__(kBlock) adam_kernel(AdamArgs a) {
+    adam_tile<DT, GW, 0>(a, QGatherOut{nullptr, nullptr, 0});
+}
+
+struct AdamQArgs {
+    AdamArgs a;
+    QGatherOut q;
+};
+
+// Pass 2 that also writes the quantised all-gather payload (BITS = 8 or 4);
+// the 16-bit slot is written when q.gw != 0.
+template <int DT, int BITS>
+__global__ void __launch_bounds__(kBlock) adam_qgather_kernel(AdamQArgs a) {
+    adam_tile<DT, kGwRuntime, BITS>(a.a, a.q);
 }
 
 struct CastArgs {
@@ -841,33 +905,6 @@ struct FusedArgs {
     zero_hparams hp;
     int32_t n;
 };
-
-// The quantised all-gather payload a fused step may also write: codes and
-// block records of the new 16-bit parameters, and the slot's store width
-// (4, 2, 1, or 0 for no 16-bit slot), chosen at launch.
-struct QGatherOut {
-    uint8_t* codes;
-    zero_qblock* blocks;
-    int32_t gw;
-};
-
-constexpr int kGwRuntime = -1;  // slot store width taken from QGatherOut::gw
-
-// Slot store with the width chosen at launch (a workgroup-uniform branch).
-__device__ __forceinline__ void store_slot_rt(int gw, uint16_t* __restrict__ slot, const Runs& r,
-                                              const uint32_t h[kVec]) {
-    if (gw == 4)
-        store_slot<4>(slot, r, h);
-    else if (gw == 2)
-        store_slot<2>(slot, r, h);
-    else if (gw == 1)
-        store_slot<1>(slot, r, h);
-}
-
-template <int BITS>
-__device__ __forceinline__ void quant_tile(const float x[kVec], const Runs& r, bool full, int64_t len,
-                                           uint8_t* __restrict__ codes,
-                                           zero_qblock* __restrict__ blocks, int64_t blk);
 
 // Single pass over one tile: reduce + partial + Adam (read set cur, write set
 // 1-cur of the tile) + cast.  QB = 8 or 4 also quantises the tile's new
@@ -1626,6 +1663,32 @@ int zero_adam_step(const zero_state* state, const float* g, int64_t valid_len,
     Kernel<AdamArgs> k = gather != nullptr && gather_dtype == ZERO_BF16 ? adam_for<ZERO_BF16>(gw)
                                                               : adam_for<ZERO_F16>(gw);
     return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, "zero_adam_step");
+}
+
+int zero_adam_step_qgather(const zero_state* state, const float* g, int64_t valid_len,
+                           const zero_hparams* hp, const zero_ctrl* ctrl, void* gather,
+                           int32_t gather_dtype, int64_t offset, int32_t bits, void* codes,
+                           zero_qblock* blocks, void* stream) {
+    int rc;
+    const char* what = "zero_adam_step_qgather";
+    if ((rc = check_len(valid_len, what)) != ZERO_OK) return rc;
+    if ((rc = check_state(state, what)) != ZERO_OK) return rc;
+    if ((rc = check_hp(hp)) != ZERO_OK) return rc;
+    if ((rc = check_ctrl(ctrl, what)) != ZERO_OK) return rc;
+    if (g == nullptr) return fail(ZERO_EINVAL, "%s: null g", what);
+    if (!aligned16(g)) return fail(ZERO_EALIGN, "%s: g not 16-byte aligned", what);
+    if ((rc = check_opt_slot(gather, gather_dtype, offset)) != ZERO_OK) return rc;
+    if ((rc = check_qout(bits, codes, blocks, what)) != ZERO_OK) return rc;
+    if (valid_len == 0) return ok();
+    uint16_t* slot = gather == nullptr ? nullptr : (uint16_t*)gather + offset;
+    const AdamQArgs a{{state->master, state->m, state->v, g, slot, valid_len, ctrl, *hp},
+                      {(uint8_t*)codes, blocks, slot == nullptr ? 0 : store_width(slot)}};
+    Kernel<AdamQArgs> k;
+    if (gather_dtype == ZERO_F16)
+        k = bits == 8 ? adam_qgather_kernel<ZERO_F16, 8> : adam_qgather_kernel<ZERO_F16, 4>;
+    else
+        k = bits == 8 ? adam_qgather_kernel<ZERO_BF16, 8> : adam_qgather_kernel<ZERO_BF16, 4>;
+    return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, what);
 }
 
 int zero_cast_to_gather(const float* master, int64_t valid_len, void* gather, int32_t dtype,
