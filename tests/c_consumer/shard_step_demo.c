@@ -5,12 +5,14 @@
  *
  *   shard_step_demo host        partition, size queries and argument checks
  *                               (needs no GPU)
- *   shard_step_demo gpu FILE    runs two ranks of a small workload on the GPU
- *                               and writes their results to FILE for the test
- *                               to compare with the oracle:
+ *   shard_step_demo gpu FILE    runs four ranks' steps of a small workload on
+ *                               the GPU and writes their results to FILE for
+ *                               the test to compare with the oracle:
  *     rank 2, fused path, dynamic loss scale, +inf in contribution 1 at step 2
  *     rank 1, two-pass path, clipping at 0.01
- *   both of Psi = 120,007 (fp16) over N = 3 ranks, 3 steps.
+ *     rank 0, fused path as rank 2, writing only the INT8 all-gather payload
+ *     rank 2, two-pass path as rank 1, writing the slot and an INT4 payload
+ *   all of Psi = 120,007 (fp16) over N = 3 ranks, 3 steps.
  */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -67,8 +69,11 @@ static int host_mode(void) {
 }
 
 /* One rank's STEPS steps; appends ctrl after each step, then master, m, v
- * (valid floats each) and the slot (valid 16-bit words) to f. */
-static void run_rank(FILE *f, int32_t rank, float max_grad_norm, int inject) {
+ * (valid floats each), the slot (valid 16-bit words) unless slot is 0, and
+ * with qbits (8 or 4) the quantised all-gather payload: codes
+ * (zero_qcode_bytes) and block records (zero_qblock_count of them). */
+static void run_rank(FILE *f, int32_t rank, float max_grad_norm, int inject, int slot,
+                     int32_t qbits) {
     int64_t shard, off, valid;
     ZERO(zero_partition(PSI, NR, rank, &shard, &off, &valid));
     const int64_t stride = (shard + 63) / 64 * 64;
@@ -98,6 +103,14 @@ static void run_rank(FILE *f, int32_t rank, float max_grad_norm, int inject) {
     HIP(hipMemcpy(flat[0], p0, sizeof(float) * valid, hipMemcpyHostToDevice));
     HIP(hipMemcpy(dG, gather, sizeof(uint16_t) * PSI, hipMemcpyHostToDevice));
     if (!fused) HIP(hipMalloc(&dg, sizeof(float) * valid));
+    void *dCodes = NULL, *dBlocks = NULL;
+    const size_t code_bytes = qbits ? zero_qcode_bytes(valid, qbits) : 0;
+    const size_t nblk = qbits ? zero_qblock_count(valid) : 0;
+    if (qbits) {
+        HIP(hipMalloc(&dCodes, code_bytes));
+        HIP(hipMalloc(&dBlocks, nblk * sizeof(zero_qblock)));
+    }
+    void *slot_dev = slot ? dG : NULL; /* NULL: no 16-bit slot is written */
 
     zero_state st_flat = {flat[0], flat[1], flat[2]}, st_pair = {pair[0], pair[1], pair[2]};
     ZERO(zero_ctrl_init(dCtrl, loss_scale, NULL));
@@ -109,7 +122,14 @@ static void run_rank(FILE *f, int32_t rank, float max_grad_norm, int inject) {
         void *ws_arr[1] = {dWs};
         int64_t len_arr[1] = {valid};
         zero_ctrl *ctrl_arr[1] = {dCtrl};
-        if (fused) {
+        if (fused && qbits) {
+            ZERO(zero_fused_step_qgather(dC, ZERO_F16, NR, stride, &st_pair, valid, slot_dev,
+                                         ZERO_F16, off, qbits, dCodes, dBlocks, &hp, dCtrl, dWs,
+                                         ws_bytes, NULL));
+            ZERO(zero_grad_norm_overflow(1, ws_arr, len_arr, ctrl_arr, &hp, 1, NULL));
+            ZERO(zero_fused_restore_q(&st_pair, valid, slot_dev, ZERO_F16, off, qbits, dCodes,
+                                      dBlocks, dCtrl, NULL));
+        } else if (fused) {
             ZERO(zero_fused_step(dC, ZERO_F16, NR, stride, &st_pair, valid, dG, ZERO_F16, off, &hp,
                                  dCtrl, dWs, ws_bytes, NULL));
             ZERO(zero_grad_norm_overflow(1, ws_arr, len_arr, ctrl_arr, &hp, 1, NULL));
@@ -117,7 +137,11 @@ static void run_rank(FILE *f, int32_t rank, float max_grad_norm, int inject) {
         } else {
             ZERO(zero_reduce_grads(dC, ZERO_F16, NR, stride, valid, dCtrl, dg, dWs, ws_bytes, NULL));
             ZERO(zero_grad_norm_overflow(1, ws_arr, len_arr, ctrl_arr, &hp, 0, NULL));
-            ZERO(zero_adam_step(&st_flat, dg, valid, &hp, dCtrl, dG, ZERO_F16, off, NULL));
+            if (qbits)
+                ZERO(zero_adam_step_qgather(&st_flat, dg, valid, &hp, dCtrl, slot_dev, ZERO_F16, off,
+                                            qbits, dCodes, dBlocks, NULL));
+            else
+                ZERO(zero_adam_step(&st_flat, dg, valid, &hp, dCtrl, dG, ZERO_F16, off, NULL));
         }
         zero_ctrl c;
         HIP(hipMemcpy(&c, dCtrl, sizeof c, hipMemcpyDeviceToHost));
@@ -130,8 +154,22 @@ static void run_rank(FILE *f, int32_t rank, float max_grad_norm, int inject) {
         HIP(hipMemcpy(out, flat[q], sizeof(float) * valid, hipMemcpyDeviceToHost));
         fwrite(out, sizeof(float), (size_t)valid, f);
     }
-    HIP(hipMemcpy(gather, dG, sizeof(uint16_t) * PSI, hipMemcpyDeviceToHost));
-    fwrite(gather + off, sizeof(uint16_t), (size_t)valid, f);
+    if (slot) {
+        HIP(hipMemcpy(gather, dG, sizeof(uint16_t) * PSI, hipMemcpyDeviceToHost));
+        fwrite(gather + off, sizeof(uint16_t), (size_t)valid, f);
+    }
+    if (qbits) {
+        unsigned char *codes = malloc(code_bytes);
+        zero_qblock *blocks = malloc(nblk * sizeof(zero_qblock));
+        HIP(hipMemcpy(codes, dCodes, code_bytes, hipMemcpyDeviceToHost));
+        HIP(hipMemcpy(blocks, dBlocks, nblk * sizeof(zero_qblock), hipMemcpyDeviceToHost));
+        fwrite(codes, 1, code_bytes, f);
+        fwrite(blocks, sizeof(zero_qblock), nblk, f);
+        free(codes);
+        free(blocks);
+        HIP(hipFree(dCodes));
+        HIP(hipFree(dBlocks));
+    }
     for (int q = 0; q < 3; ++q) {
         HIP(hipFree(flat[q]));
         HIP(hipFree(pair[q]));
@@ -152,8 +190,10 @@ int main(int argc, char **argv) {
     if (argc >= 3 && strcmp(argv[1], "gpu") == 0) {
         FILE *f = fopen(argv[2], "wb");
         if (!f) return 2;
-        run_rank(f, 2, 0.0f, 1);
-        run_rank(f, 1, 0.01f, 0);
+        run_rank(f, 2, 0.0f, 1, 1, 0);
+        run_rank(f, 1, 0.01f, 0, 1, 0);
+        run_rank(f, 0, 0.0f, 1, 0, 8);
+        run_rank(f, 2, 0.01f, 0, 1, 4);
         fclose(f);
         printf("gpu ok\n");
         return 0;
