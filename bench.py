@@ -47,10 +47,10 @@ def kernel_isa_digest(kernel: str):
 
 
 def measured_traffic(label: str, workload: str):
-    """HBM bytes per launch from the committed PMC summary of this kernel and
-    workload, or None when there is none or when the profiled kernel's
-    machine code differs from the one in the built library (the counters
-    then describe another kernel)."""
+    """HBM bytes per pass (one call of the entry point, all its launches) from
+    the committed PMC summary of this kernel and workload, or None when there
+    is none or when the profiled kernel's machine code differs from the one in
+    the built library (the counters then describe another kernel)."""
     path = os.path.join(PROFILES, f"{label}_{workload}_pmc.md")
     try:
         fields = {}
@@ -61,7 +61,7 @@ def measured_traffic(label: str, workload: str):
         digest = kernel_isa_digest(fields["kernel"])
         if digest is None or fields.get("isa_sha256") != digest:
             return None
-        return int(fields["traffic_bytes_per_launch"]), fields["kernel"], digest
+        return int(fields["traffic_bytes_per_pass"]), fields["kernel"], digest
     except (OSError, KeyError, ValueError):
         return None
 
@@ -73,7 +73,7 @@ def quant_bytes_per_elem(w, bits: int) -> float:
     return w.bytes_per_elem - 2 * w.nranks + w.nranks * (bits / 8 + 8 / 2048)
 
 
-def setup(w, torch, synth, Z, rows=False, qbits=0):
+def setup(w, torch, synth, Z, rows=False, qbits=0, bucket=0):
     """Buffers of the measured rank, inputs generated in HBM.  With `rows`, the
     N contribution rows live in N separate allocations and the step goes
     through the row-table calls; with `qbits`, the rows are block-quantised
@@ -98,7 +98,7 @@ def setup(w, torch, synth, Z, rows=False, qbits=0):
                    max_grad_norm=w.max_grad_norm, scaler=w.scaler, min_scale=w.min_scale,
                    growth_interval=w.growth_interval)
     st = Z.ShardStep(w.nranks, stride, valid, off, w.dtype, w.dtype, hp, state0, g,
-                     w.loss_scale)
+                     w.loss_scale, bucket=bucket)
     if fused:  # the flat state is only needed to load the paired copy
         torch.cuda.synchronize()
         del state0, p0
@@ -140,8 +140,6 @@ def timed_steps(b, steps, warmup, torch, Z, graph=False, qg=None):
     step writes the quantised all-gather payload instead of the 16-bit slot."""
     st, contrib, gather = b["step"], b["contrib"], b["gather"]
     slot = None if qg is not None else gather
-    table = isinstance(contrib, list)
-    quant = isinstance(contrib, Z.QuantRows)
     for _ in range(warmup):
         st.step(contrib, slot, qg)
     torch.cuda.synchronize()
@@ -169,45 +167,20 @@ def timed_steps(b, steps, warmup, torch, Z, graph=False, qg=None):
           for _ in range(steps)]
     ev_red = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
-    hp, n, stride, valid, off = st.hp, st.nranks, st.stride, st.valid_len, st.offset
     for i in range(steps):
-        if qg is not None and b["fused"]:
+        if b["fused"]:  # the fused launches (one per piece), then decision and restore
             ev[i][0].record()
-            Z.zero_fused_step_qgather(contrib, st.dtype, n, stride, st.pair, valid, None,
-                                      st.gather_dtype, off, qg, hp, st.ctrl, st.ws)
+            st.run_pieces(contrib, slot, qg)
             ev[i][1].record()
-            Z.zero_grad_norm_overflow([st.ws], [valid], [st.ctrl], hp, True)
-            Z.zero_fused_restore_q(st.pair, valid, None, st.gather_dtype, off, qg, st.ctrl)
-        elif b["fused"]:
-            ev[i][0].record()
-            if quant:
-                Z.zero_fused_step_q(contrib, st.pair, valid, gather, st.gather_dtype, off, hp,
-                                    st.ctrl, st.ws)
-            elif table:
-                Z.zero_fused_step_rows(contrib, st.dtype, st.pair, valid, gather,
-                                       st.gather_dtype, off, hp, st.ctrl, st.ws)
-            else:
-                Z.zero_fused_step(contrib, st.dtype, n, stride, st.pair, valid, gather,
-                                  st.gather_dtype, off, hp, st.ctrl, st.ws)
-            ev[i][1].record()
-            Z.zero_grad_norm_overflow([st.ws], [valid], [st.ctrl], hp, True)
-            Z.zero_fused_restore(st.pair, valid, gather, st.gather_dtype, off, st.ctrl)
-        else:
+            st.decide()
+            st.complete(slot, qg)
+        else:  # the reduce launches (one per piece), the decision, then the Adam pass
             ev_red[i][0].record()
-            if quant:
-                Z.zero_reduce_grads_q(contrib, valid, st.ctrl, st.g, st.ws)
-            elif table:
-                Z.zero_reduce_grads_rows(contrib, st.dtype, valid, st.ctrl, st.g, st.ws)
-            else:
-                Z.zero_reduce_grads(contrib, st.dtype, n, stride, valid, st.ctrl, st.g, st.ws)
+            st.run_pieces(contrib, slot, qg)
             ev_red[i][1].record()
-            Z.zero_grad_norm_overflow([st.ws], [valid], [st.ctrl], hp, False)
+            st.decide()
             ev[i][0].record()
-            if qg is not None:
-                Z.zero_adam_step_qgather(st.state, st.g, valid, hp, st.ctrl, None,
-                                         st.gather_dtype, off, qg)
-            else:
-                Z.zero_adam_step(st.state, st.g, valid, hp, st.ctrl, gather, st.gather_dtype, off)
+            st.complete(slot, qg)
             ev[i][1].record()
     torch.cuda.synchronize()
     kern_ms = [a.elapsed_time(c) for a, c in ev]
@@ -300,6 +273,10 @@ def main():
     ap.add_argument("--qgather", type=int, choices=(0, 4, 8), default=0,
                     help="the step writes the ZeRO++ INT8 or INT4 all-gather payload of the new "
                          "parameters instead of the 16-bit slot")
+    ap.add_argument("--bucket", type=int, default=0,
+                    help="the shard's gradient arrives in pieces of this many elements (rounded "
+                         "down to a multiple of 2048), each reduced or stepped by its own launch; "
+                         "the pages' reduce_bucket_size is 5e8")
     ap.add_argument("--graph", action="store_true",
                     help="time the step as one captured HIP graph replayed each step")
     ap.add_argument("--rows", action="store_true",
@@ -338,7 +315,13 @@ def main():
     if args.qgather and (args.rows or args.quant):
         print("--qgather takes [N, stride] 16-bit contributions only", file=sys.stderr)
         sys.exit(2)
-    b = setup(w, torch, synth, Z, rows=args.rows, qbits=args.quant)
+    bucket = args.bucket // Z.TILE * Z.TILE
+    if args.bucket and not bucket:
+        print("--bucket must be at least 2048 elements", file=sys.stderr)
+        sys.exit(2)
+    b = setup(w, torch, synth, Z, rows=args.rows, qbits=args.quant, bucket=bucket)
+    b_pieces = b["step"].pieces()
+    pieces = len(b_pieces)
     valid = b["valid"]
     qg = Z.QGather.alloc(valid, args.qgather, torch.device("cuda", 0)) if args.qgather else None
     ms_step, per_step, kern_ms, red_ms, ctrl = timed_steps(b, args.steps, args.warmup, torch, Z,
@@ -385,6 +368,7 @@ def main():
                                       "row_table" if args.rows else "strided"),
                    "gather_payload": ("int%d_blocks" % args.qgather if args.qgather else
                                       "16bit_slot"),
+                   "bucket_elems": bucket, "calls_per_pass": pieces,
                    "launch": "hip_graph" if args.graph else "stream"},
         "step_ms_median": _fmt(per_step[len(per_step) // 2], 5),
         "step_ms_min": _fmt(per_step[0], 5),
@@ -394,11 +378,13 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": _fmt(kern_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None,
-                     "kernel_ms": _fmt(kern_avg, 5), "bytes_per_launch": kern_bytes},
+                     "kernel_ms": _fmt(kern_avg, 5), "bytes_per_pass": kern_bytes,
+                     "launches_per_pass": sum(Z.launches(n) for _, n in b_pieces)},
         "last_step": {"norm": ctrl["norm"], "skip": ctrl["skip"], "t": ctrl["t"],
                       "loss_scale": ctrl["loss_scale"]},
     }
-    measured = measured_traffic(kern_name, w.name)
+    # the committed counters cover the pass issued as one call
+    measured = measured_traffic(kern_name, w.name) if pieces == 1 else None
     if measured is not None:
         traffic, profiled_kernel, digest = measured
         out["roofline"].update(traffic=traffic, traffic_ratio=_fmt(traffic / kern_bytes, 5),

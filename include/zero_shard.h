@@ -129,6 +129,12 @@ typedef struct zero_ctrl {
  * double-buffered state interleaves its two sets tile by tile. */
 #define ZERO_TILE 2048
 
+/* Most tiles per kernel launch: a streaming pass (reduce, fused step, Adam)
+ * over valid_len elements is issued as ceil(ceil(valid_len / ZERO_TILE) /
+ * ZERO_LAUNCH_TILES) consecutive launches on the caller's stream, which a
+ * profiler lists one by one.  The results are those of one launch. */
+#define ZERO_LAUNCH_TILES 16384
+
 /* One rank's fp32 optimizer state: master weights, Adam m, Adam v.
  * Flat form (two-pass path, pack/unpack): valid_len contiguous floats each.
  * Paired form (fused path): zero_pair_elems(valid_len) floats each, holding
@@ -152,6 +158,30 @@ typedef struct zero_state {
  * null output pointer. */
 int zero_partition(int64_t psi, int32_t nranks, int32_t rank, int64_t *shard_len,
                    int64_t *offset, int64_t *valid_len);
+
+/* Bytes of the device workspace per tile of ZERO_TILE elements: the first
+ * level of the norm and overflow reduction keeps one partial per tile. */
+#define ZERO_PARTIAL_BYTES 16
+
+/* Buckets (paper summary 3.4, Stage 2, bucketization: gradients are reduced
+ * bucket by bucket as the backward pass produces them; "ZeRO Stage 1/2/3"
+ * guide, section 5: reduce_bucket_size).  The per-element calls
+ * (zero_reduce_grads and its _rows/_q forms, zero_fused_step and its
+ * _rows/_q/_qgather forms) may be issued as several calls over consecutive
+ * pieces of one shard, each piece [b0, b0 + len) starting at a multiple of
+ * ZERO_TILE, as the pieces arrive.  The call for a piece takes every
+ * per-element pointer advanced by b0 elements (contribution rows, g, the
+ * 16-bit slot's offset; the paired state arrays by 2 * b0 floats; INT8 codes
+ * by b0 bytes, INT4 codes by b0 / 2, block records by b0 / ZERO_TILE), and
+ * the workspace advanced by (b0 / ZERO_TILE) * ZERO_PARTIAL_BYTES bytes with
+ * ws_bytes reduced by as much; ctrl, hparams and the row stride stay the
+ * same.  After the last piece, zero_grad_norm_overflow over the whole
+ * workspace and valid_len, then the rest of the step over the whole shard
+ * (zero_adam_step or zero_adam_step_qgather; zero_fused_restore or
+ * zero_fused_restore_q), complete the step: the results equal those of one
+ * call over the whole shard, bit for bit.  On the fused path each piece's Adam update
+ * can therefore run as soon as its gradient has arrived; the skip decision
+ * still waits for the last piece. */
 
 /* sizeof(zero_ctrl); allocate that many bytes of device memory per rank. */
 size_t zero_ctrl_bytes(void);

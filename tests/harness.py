@@ -209,7 +209,7 @@ class GpuRun:
     library the same values."""
 
     def __init__(self, c: Case, full_gather: bool = True, layout: str = "strided",
-                 qgather: int = 0, write_slot: bool = True):
+                 qgather: int = 0, write_slot: bool = True, bucket: int = 0):
         import torch
         import zero_partitioned_mixed_amd as Z
         self.c, self.Z, self.torch = c, Z, torch
@@ -236,7 +236,7 @@ class GpuRun:
                        weight_decay=w.weight_decay, max_grad_norm=w.max_grad_norm,
                        scaler=w.scaler, min_scale=w.min_scale, growth_interval=w.growth_interval)
         self.step_obj = Z.ShardStep(w.nranks, c.stride, valid, self.gather_off, w.dtype, w.dtype,
-                                    hp, self.state0, self.g, w.loss_scale)
+                                    hp, self.state0, self.g, w.loss_scale, bucket=bucket)
         self.reports = []
         if layout not in ROW_LAYOUTS:
             raise ValueError(layout)
@@ -323,7 +323,7 @@ class GpuRun:
 
 
 def run_and_compare(c: Case, label: str, full: bool = True, layout: str = "strided",
-                    qgather: int = 0, write_slot: bool = True):
+                    qgather: int = 0, write_slot: bool = True, bucket: int = 0):
     """Runs case `c` on the GPU and checks every step's decisions and the final
     master/m/v/slot of the whole shard against the oracle; with `full`, also
     that the gather buffer is unchanged outside the slot.  With `qgather`, the
@@ -332,8 +332,10 @@ def run_and_compare(c: Case, label: str, full: bool = True, layout: str = "strid
     gather buffer must be unchanged."""
     log(f"{label}: psi={c.w.psi} N={c.w.nranks} rank={c.rank} dtype={c.w.dtype} "
         f"variant={c.w.variant} steps={c.steps} offset={c.part[1]} valid={c.part[2]} "
-        f"layout={layout} qbits={c.qbits} qgather={qgather} write_slot={write_slot}")
-    g = GpuRun(c, full_gather=full, layout=layout, qgather=qgather, write_slot=write_slot)
+        f"layout={layout} qbits={c.qbits} qgather={qgather} write_slot={write_slot} "
+        f"bucket={bucket}")
+    g = GpuRun(c, full_gather=full, layout=layout, qgather=qgather, write_slot=write_slot,
+               bucket=bucket)
     g.run()
     ref_reps = oracle_scalars(c)
     stats = assert_reports(g.reports, ref_reps)

@@ -1,0 +1,58 @@
+"""Shards longer than one launch of a streaming pass.
+
+The library issues each streaming pass (reduce, fused step, Adam) as
+consecutive launches of at most 2^25 elements (16,384 tiles) with its
+pointers advanced per launch.  These shards cross that boundary, with a ragged
+second launch, and are checked in full against the oracle: every step's
+decisions and every element of master, m, v, slot and quantised payload.  An
+overflow is injected right after the boundary.
+"""
+import numpy as np
+import pytest
+
+import harness as H
+from harness import Case, Inject
+from synth.workloads import BF16, F16, Workload
+
+pytestmark = pytest.mark.gpu
+
+CHUNK = 16384 * 2048
+SHARD = CHUNK + 3 * 2048 + 77  # a second, ragged launch
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import synth
+    synth.gpu()
+    import zero_partitioned_mixed_amd  # noqa: F401
+    yield
+    torch.cuda.empty_cache()
+
+
+def two_chunk(dtype=F16, steps=3, **kw):
+    return Workload(name="two_chunk", psi=2 * SHARD, nranks=2, ranks=(1,), dtype=dtype,
+                    steps=steps, **kw)
+
+
+DYN = dict(scaler=2, contrib_scale=2.0 ** 10, loss_scale=2.0 ** 10)
+
+# name: (case, payload bits, 16-bit slot)
+CASES = {
+    "fused_skip_after_boundary": (Case(two_chunk(**DYN), 1, 3,
+                                       extra=(Inject(2, 1, CHUNK + 5, np.inf),)), 0, True),
+    "two_pass_clip": (Case(two_chunk(dtype=BF16, max_grad_norm=0.5), 1, 3), 0, True),
+    "fused_int8_payload_no_slot": (Case(two_chunk(**DYN), 1, 3,
+                                        extra=(Inject(2, 0, CHUNK + 2048, np.inf),)), 8, False),
+    "two_pass_int4_payload": (Case(two_chunk(dtype=BF16, max_grad_norm=0.5), 1, 2), 4, True),
+    "fused_int8_contributions": (Case(two_chunk(steps=2), 1, 2, qbits=8), 0, True),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_shard_over_two_launches(name):
+    c, qbits, slot = CASES[name]
+    assert c.part[2] == SHARD
+    H.run_and_compare(c, name, qgather=qbits, write_slot=slot)

@@ -22,8 +22,9 @@ import numpy as np
 import pytest
 
 import harness as H
+from harness import Case, Inject
 from synth import workloads
-from synth.workloads import F16
+from synth.workloads import BF16, F16, Workload
 
 pytestmark = pytest.mark.gpu
 
@@ -193,3 +194,56 @@ def test_bucketed_reduce_equals_one_shot():
         assert np.array_equal(g0.view(np.uint32), g1.view(np.uint32))
         assert c1["sumsq"] == c0["sumsq"] and c1["clip"] == c0["clip"] and c1["t"] == c0["t"]
     H.log(f"bucketed reduce: norm {c0['norm']:.12g}, clip {c0['clip']}")
+
+
+DYN = dict(scaler=2, contrib_scale=2.0 ** 10, loss_scale=2.0 ** 10)
+
+
+def _bsmall(psi, n, rank, dtype=F16, steps=3, **kw):
+    return Workload(name="small", psi=psi, nranks=n, ranks=(rank,), dtype=dtype, steps=steps, **kw)
+
+
+# name: (case, bucket elements, layout, payload bits, 16-bit slot)
+BUCKETED = {
+    "fused_skip": (Case(_bsmall(8 * 50_001, 8, 7, steps=4, **DYN), 7, 4,
+                        extra=(Inject(2, 3, 45_000, np.inf),)), 2048 * 5, "strided", 0, True),
+    "fused_n3_ragged": (Case(_bsmall(100_003, 3, 2), 2, 3), 2048 * 3, "strided", 0, True),
+    "two_pass_clip": (Case(_bsmall(200_000, 8, 5, dtype=BF16, max_grad_norm=0.05), 5, 3),
+                      2048 * 4, "strided", 0, True),
+    "fused_rows": (Case(_bsmall(8 * 50_001, 8, 6), 6, 3), 2048 * 7, "rows", 0, True),
+    "fused_int8_rows": (Case(_bsmall(8 * 50_001, 8, 6), 6, 3, qbits=8), 2048 * 6, "strided", 0,
+                        True),
+    "fused_int4_payload_no_slot": (Case(_bsmall(8 * 50_001, 8, 7, steps=4, **DYN), 7, 4,
+                                        extra=(Inject(3, 0, 2048 * 10 + 5, np.inf),)),
+                                   2048 * 5, "strided", 4, False),
+    "two_pass_int8_payload": (Case(_bsmall(100_003, 3, 2, max_grad_norm=0.02), 2, 3),
+                              2048, "strided", 8, True),
+}
+
+
+@pytest.mark.parametrize("name", list(BUCKETED))
+def test_bucketed_step_equals_one_call(name):
+    """ShardStep(bucket=B): the step issued piece by piece (each piece's
+    reduce, or each piece's whole fused step, as its gradient arrives; the
+    decision after the last piece) is bit-identical to one call per step:
+    every step's ctrl, the final state, slot and payload.  One case is also
+    run against the oracle directly."""
+    c, bucket, layout, qbits, slot = BUCKETED[name]
+    runs = []
+    for b in (0, bucket):
+        g = H.GpuRun(c, full_gather=True, layout=layout, qgather=qbits, write_slot=slot, bucket=b)
+        assert len(g.step_obj.pieces()) == (1 if b == 0 else -(-c.part[2] // bucket))
+        g.run()
+        runs.append(g)
+    a, b = runs
+    assert repr(a.reports) == repr(b.reports)
+    for x, y in zip(a.fetch(), b.fetch()):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+    if qbits:
+        for x, y in zip(a.qpayload(), b.qpayload()):
+            assert np.array_equal(np.ascontiguousarray(x).view(np.uint8),
+                                  np.ascontiguousarray(y).view(np.uint8))
+    H.log(f"bucketed {name}: {len(b.step_obj.pieces())} pieces of {bucket} equal one call; "
+          f"skips {[r['skip'] for r in b.reports]}")
+    if name == "fused_skip":
+        H.run_and_compare(c, "bucketed fused_skip vs oracle", bucket=bucket)

@@ -55,6 +55,15 @@ class Ctrl(ctypes.Structure):
 
 TILE = 2048  # ZERO_TILE
 QBLOCK = 2048  # ZERO_QBLOCK
+PARTIAL_BYTES = 16  # ZERO_PARTIAL_BYTES
+LAUNCH_TILES = 16384  # ZERO_LAUNCH_TILES
+
+
+def launches(valid_len: int) -> int:
+    """Kernel launches one call of a streaming pass over valid_len elements
+    is issued as."""
+    tiles = -(-valid_len // TILE)
+    return -(-tiles // LAUNCH_TILES)
 
 
 class State(ctypes.Structure):
@@ -154,6 +163,13 @@ def _rows(rows):
         else:
             ptrs.append(_ptr(r).value)
     return (_vp * max(len(ptrs), 1))(*ptrs), len(ptrs)
+
+
+def _at(x, nbytes: int):
+    """x advanced by nbytes: an integer device address, or a 1-D tensor sliced."""
+    if isinstance(x, int):
+        return x + nbytes
+    return x[nbytes // x.element_size():]
 
 
 def _state(s) -> State:
@@ -333,6 +349,11 @@ class QGather:
         (codes, blocks), = QuantRows.alloc(1, length, bits, device).rows
         return QGather(codes, blocks, bits, length)
 
+    def at(self, b0: int):
+        """The payload from element b0 on (b0 a multiple of TILE)."""
+        return QGather(_at(self.codes, b0 * self.bits // 8), _at(self.blocks, b0 // QBLOCK * 8),
+                       self.bits, self.length - b0)
+
 
 def zero_fused_step_qgather(contrib, contrib_dtype: int, nranks: int, stride: int, pair,
                             valid_len: int, gather, gather_dtype: int, offset: int, q: QGather,
@@ -382,11 +403,19 @@ class ShardStep:
     (clipping on) updates it in place through ``g``; the fused path keeps
     its double-buffered copy in ``pair`` (allocated here, loaded from
     ``state``) and ``current()`` copies the current set back out.
+
+    ``bucket`` (a multiple of TILE elements; 0 for none): the shard's gradient
+    arrives in consecutive pieces of that many elements, and each piece is
+    reduced (two-pass) or fully stepped (fused) by its own calls before the
+    decision over the whole shard; bit-identical to one call per step.
     """
 
     def __init__(self, nranks, stride, valid_len, offset, dtype, gather_dtype, hp: Hparams,
-                 state, g=None, loss_scale=1.0):
+                 state, g=None, loss_scale=1.0, bucket: int = 0):
         import torch
+        if bucket < 0 or bucket % TILE:
+            raise ValueError(f"bucket must be a multiple of {TILE} elements")
+        self.bucket = bucket
         self.nranks, self.stride, self.valid_len, self.offset = nranks, stride, valid_len, offset
         self.dtype, self.gather_dtype, self.hp = dtype, gather_dtype, hp
         self.state, self.g = state, g
@@ -403,63 +432,88 @@ class ShardStep:
             self.pair = tuple(torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3))
             zero_pair_store(state, self.pair, valid_len, self.ctrl)
 
+    def pieces(self):
+        """(first element, length) of each piece one step is issued in."""
+        b, n = self.bucket, self.valid_len
+        if not b or n <= b:
+            return [(0, n)]
+        return [(b0, min(b, n - b0)) for b0 in range(0, n, b)]
+
+    @staticmethod
+    def _contrib_at(contrib, b0: int):
+        if isinstance(contrib, QuantRows):
+            return QuantRows([(_at(c, b0 * contrib.bits // 8), _at(k, b0 // QBLOCK * 8))
+                              for c, k in contrib.rows], contrib.bits)
+        if isinstance(contrib, (list, tuple)):
+            return [_at(r, 2 * b0) for r in contrib]
+        return contrib[:, b0:]
+
     def step(self, contrib, gather, qgather: QGather = None) -> None:
         """One step.  With ``qgather`` the step also writes the quantised
         all-gather payload of the new parameters, and ``gather`` may be None
         (no 16-bit slot written); the fused path then takes [N, stride]
         contributions only."""
+        self.run_pieces(contrib, gather, qgather)
+        self.decide()
+        self.complete(gather, qgather)
+
+    def run_pieces(self, contrib, gather, qgather: QGather = None) -> None:
+        """The per-element launches of a step, one per piece: the reduce
+        (two-pass) or the whole fused step (fused path)."""
         quant = isinstance(contrib, QuantRows)
         table = isinstance(contrib, (list, tuple))
         if (table and len(contrib) != self.nranks) or (quant and len(contrib.rows) != self.nranks):
             raise ValueError(f"contribution rows do not match {self.nranks} ranks")
-        if qgather is not None and not self.fused:
-            if quant:
-                zero_reduce_grads_q(contrib, self.valid_len, self.ctrl, self.g, self.ws)
-            elif table:
-                zero_reduce_grads_rows(contrib, self.dtype, self.valid_len, self.ctrl, self.g,
-                                       self.ws)
+        if qgather is not None and self.fused and (quant or table):
+            raise ValueError("the fused step with a quantised all-gather payload takes "
+                             "[N, stride] contributions")
+        hp, ctrl = self.hp, self.ctrl
+        pieces = self.pieces()
+        for b0, ln in pieces:
+            if len(pieces) == 1:
+                c, ws, off, q = contrib, self.ws, self.offset, qgather
             else:
-                zero_reduce_grads(contrib, self.dtype, self.nranks, self.stride, self.valid_len,
-                                  self.ctrl, self.g, self.ws)
-            zero_grad_norm_overflow([self.ws], [self.valid_len], [self.ctrl], self.hp, False)
-            zero_adam_step_qgather(self.state, self.g, self.valid_len, self.hp, self.ctrl, gather,
-                                   self.gather_dtype, self.offset, qgather)
-            return
-        if qgather is not None:
-            if quant or table:
-                raise ValueError("the fused step with a quantised all-gather payload takes "
-                                 "[N, stride] contributions")
-            zero_fused_step_qgather(contrib, self.dtype, self.nranks, self.stride, self.pair,
-                                    self.valid_len, gather, self.gather_dtype, self.offset,
-                                    qgather, self.hp, self.ctrl, self.ws)
-            zero_grad_norm_overflow([self.ws], [self.valid_len], [self.ctrl], self.hp, True)
+                c, ws = self._contrib_at(contrib, b0), _at(self.ws, b0 // TILE * PARTIAL_BYTES)
+                off, q = self.offset + b0, None if qgather is None else qgather.at(b0)
+            if self.fused:
+                pair = self.pair if b0 == 0 else tuple(_at(t, 8 * b0) for t in self.pair)
+                if q is not None:
+                    zero_fused_step_qgather(c, self.dtype, self.nranks, self.stride, pair, ln,
+                                            gather, self.gather_dtype, off, q, hp, ctrl, ws)
+                elif quant:
+                    zero_fused_step_q(c, pair, ln, gather, self.gather_dtype, off, hp, ctrl, ws)
+                elif table:
+                    zero_fused_step_rows(c, self.dtype, pair, ln, gather, self.gather_dtype, off,
+                                         hp, ctrl, ws)
+                else:
+                    zero_fused_step(c, self.dtype, self.nranks, self.stride, pair, ln, gather,
+                                    self.gather_dtype, off, hp, ctrl, ws)
+            else:
+                g = self.g if b0 == 0 else _at(self.g, 4 * b0)
+                if quant:
+                    zero_reduce_grads_q(c, ln, ctrl, g, ws)
+                elif table:
+                    zero_reduce_grads_rows(c, self.dtype, ln, ctrl, g, ws)
+                else:
+                    zero_reduce_grads(c, self.dtype, self.nranks, self.stride, ln, ctrl, g, ws)
+
+    def decide(self) -> None:
+        """Norm, overflow and the step's decisions over the whole shard."""
+        zero_grad_norm_overflow([self.ws], [self.valid_len], [self.ctrl], self.hp, self.fused)
+
+    def complete(self, gather, qgather: QGather = None) -> None:
+        """The rest of the step: the Adam pass (two-pass path), or the restore
+        of slot and payload after a skipped fused step."""
+        if self.fused and qgather is not None:
             zero_fused_restore_q(self.pair, self.valid_len, gather, self.gather_dtype, self.offset,
                                  qgather, self.ctrl)
-            return
-        if self.fused:
-            if quant:
-                zero_fused_step_q(contrib, self.pair, self.valid_len, gather, self.gather_dtype,
-                                  self.offset, self.hp, self.ctrl, self.ws)
-            elif table:
-                zero_fused_step_rows(contrib, self.dtype, self.pair, self.valid_len, gather,
-                                     self.gather_dtype, self.offset, self.hp, self.ctrl, self.ws)
-            else:
-                zero_fused_step(contrib, self.dtype, self.nranks, self.stride, self.pair,
-                                self.valid_len, gather, self.gather_dtype, self.offset, self.hp,
-                                self.ctrl, self.ws)
-            zero_grad_norm_overflow([self.ws], [self.valid_len], [self.ctrl], self.hp, True)
+        elif self.fused:
             zero_fused_restore(self.pair, self.valid_len, gather, self.gather_dtype, self.offset,
                                self.ctrl)
+        elif qgather is not None:
+            zero_adam_step_qgather(self.state, self.g, self.valid_len, self.hp, self.ctrl, gather,
+                                   self.gather_dtype, self.offset, qgather)
         else:
-            if quant:
-                zero_reduce_grads_q(contrib, self.valid_len, self.ctrl, self.g, self.ws)
-            elif table:
-                zero_reduce_grads_rows(contrib, self.dtype, self.valid_len, self.ctrl, self.g,
-                                       self.ws)
-            else:
-                zero_reduce_grads(contrib, self.dtype, self.nranks, self.stride, self.valid_len,
-                                  self.ctrl, self.g, self.ws)
-            zero_grad_norm_overflow([self.ws], [self.valid_len], [self.ctrl], self.hp, False)
             zero_adam_step(self.state, self.g, self.valid_len, self.hp, self.ctrl, gather,
                            self.gather_dtype, self.offset)
 

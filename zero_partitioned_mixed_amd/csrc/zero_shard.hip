@@ -52,6 +52,7 @@ constexpr int kFinBlock = 1024;             // threads per finalize workgroup
 constexpr int kFinGroups = 256;             // most first-level groups of the finalize
 constexpr int64_t kFinPer = 16384;          // partials per first-level finalize group
 constexpr int kRestoreGrid = 256;           // workgroups of the (usually idle) restore pass
+constexpr int64_t kChunkTiles = ZERO_LAUNCH_TILES;  // most tiles per launch of a streaming pass
 constexpr int64_t kMaxLen = int64_t(1) << 40;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -62,7 +63,7 @@ struct Partial {
     uint32_t nonfinite;
     uint32_t pad;
 };
-static_assert(sizeof(Partial) == 16, "partial layout");
+static_assert(sizeof(Partial) == ZERO_PARTIAL_BYTES, "one workspace partial per tile");
 static_assert(sizeof(zero_ctrl) == 128, "ctrl layout");
 
 int64_t tiles_for(int64_t len) { return len <= 0 ? 0 : (len + kTile - 1) / kTile; }
@@ -1425,6 +1426,98 @@ int launch(Kernel<Args> kernel, int64_t grid, int block, hipStream_t s, const Ar
     return ok();
 }
 
+// A streaming pass over a long shard is issued as consecutive launches of at
+// most kChunkTiles tiles, each with every per-element pointer advanced to its
+// first element (the same arithmetic as the bucket contract in the header, so
+// the results are those of one launch, bit for bit).  In one launch of
+// several hundred thousand workgroups the slowest ones fall further and
+// further behind and the set of tiles in flight spreads over more memory; a
+// new launch every 16,384 tiles keeps it compact (the 13B fused step: 1-5%
+// shorter, most on boxes where the buffers landed on slower memory).
+// at(x, b0): x advanced by b0 elements of the shard (b0 a multiple of kTile).
+StridedRows at(StridedRows r, int64_t b0) {
+    r.base += b0;
+    return r;
+}
+
+TableRows at(TableRows t, int64_t b0) {
+    for (int k = 0; k < ZERO_MAX_RANKS; ++k)
+        if (t.p[k] != nullptr) t.p[k] += b0;
+    return t;
+}
+
+template <int DT, class RS>
+Src16<DT, RS> at(Src16<DT, RS> s, int64_t b0) {
+    s.rows = at(s.rows, b0);
+    return s;
+}
+
+template <int BITS>
+SrcQ<BITS> at(SrcQ<BITS> s, int64_t b0) {
+    for (int k = 0; k < ZERO_MAX_RANKS; ++k) {
+        if (s.t.codes[k] != nullptr) s.t.codes[k] += b0 * BITS / 8;
+        if (s.t.blocks[k] != nullptr) s.t.blocks[k] += b0 / kTile;
+    }
+    return s;
+}
+
+QGatherOut at(QGatherOut q, int64_t b0, int bits) {
+    q.codes += b0 * bits / 8;
+    q.blocks += b0 / kTile;
+    return q;
+}
+
+template <class SRC>
+FusedArgs<SRC> at(FusedArgs<SRC> a, int64_t b0, int64_t len) {
+    a.src = at(a.src, b0);
+    for (int q = 0; q < 3; ++q) a.pair[q] += 2 * b0;
+    if (a.slot != nullptr) a.slot += b0;
+    a.len = len;
+    a.ws += b0 / kTile;
+    return a;
+}
+
+template <class SRC>
+ReduceArgs<SRC> at(ReduceArgs<SRC> a, int64_t b0, int64_t len) {
+    a.src = at(a.src, b0);
+    a.len = len;
+    a.g += b0;
+    a.ws += b0 / kTile;
+    return a;
+}
+
+AdamArgs at(AdamArgs a, int64_t b0, int64_t len) {
+    a.master += b0;
+    a.m += b0;
+    a.v += b0;
+    a.g += b0;
+    if (a.slot != nullptr) a.slot += b0;
+    a.len = len;
+    return a;
+}
+
+// Launches kernel over len elements in chunks; at(args, b0, n) gives the
+// arguments of the chunk [b0, b0 + n).  A launch error stops the loop, with
+// the earlier chunks already enqueued.
+template <class Args, class At>
+int launch_chunked(Kernel<Args> kernel, const Args& args, int64_t len, hipStream_t s,
+                   const char* what, At&& at_chunk) {
+    constexpr int64_t chunk = kChunkTiles * kTile;
+    for (int64_t b0 = 0; b0 < len; b0 += chunk) {
+        const int64_t n = len - b0 < chunk ? len - b0 : chunk;
+        const int rc = launch(kernel, tiles_for(n), kBlock, s, at_chunk(args, b0, n), what);
+        if (rc != ZERO_OK) return rc;
+    }
+    return ok();
+}
+
+template <class Args>
+int launch_chunked(Kernel<Args> kernel, const Args& args, int64_t len, hipStream_t s,
+                   const char* what) {
+    return launch_chunked(kernel, args, len, s, what,
+                          [](const Args& a, int64_t b0, int64_t n) { return at(a, b0, n); });
+}
+
 // Checks and launches shared by the fused entry points (the contribution
 // source is already checked).
 template <class SRC>
@@ -1442,8 +1535,8 @@ int fused_launch(const SRC& src, int32_t nranks, const zero_state* pair, int64_t
     uint16_t* slot = (uint16_t*)gather + offset;
     const FusedArgs<SRC> a{src, {pair->master, pair->m, pair->v}, slot, valid_len, ctrl,
                            (Partial*)ws, *hp, nranks};
-    return launch(fused_for<SRC>(store_width(slot), gather_dtype, nranks), tiles_for(valid_len),
-                  kBlock, (hipStream_t)stream, a, what);
+    return launch_chunked(fused_for<SRC>(store_width(slot), gather_dtype, nranks), a, valid_len,
+                          (hipStream_t)stream, what);
 }
 
 // Checks and launch shared by the reduce entry points (source already checked).
@@ -1457,8 +1550,7 @@ int reduce_launch(const SRC& src, int32_t nranks, int64_t valid_len, const zero_
     if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
     if (valid_len == 0) return ok();
     const ReduceArgs<SRC> a{src, valid_len, ctrl, g, (Partial*)ws, nranks};
-    return launch(reduce_for<SRC>(nranks), tiles_for(valid_len), kBlock, (hipStream_t)stream, a,
-                  what);
+    return launch_chunked(reduce_for<SRC>(nranks), a, valid_len, (hipStream_t)stream, what);
 }
 
 // Quantised row tables: bits 8 or 4, nranks in [1, ZERO_MAX_RANKS], every
@@ -1526,7 +1618,11 @@ int fused_qgather_launch(const StridedRows& rows, int32_t nranks, const zero_sta
         {(uint8_t*)codes, blocks, slot == nullptr ? 0 : store_width(slot)}};
     const auto k = bits == 8 ? fused_qgather_bits<DT, 8>(gather_dtype, nranks)
                              : fused_qgather_bits<DT, 4>(gather_dtype, nranks);
-    return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, what);
+    using A = FusedQArgs<Src16<DT, StridedRows>>;
+    return launch_chunked(k, a, valid_len, (hipStream_t)stream, what,
+                          [bits](const A& x, int64_t b0, int64_t n) {
+                              return A{at(x.f, b0, n), at(x.q, b0, bits)};
+                          });
 }
 
 }  // namespace
@@ -1662,7 +1758,7 @@ int zero_adam_step(const zero_state* state, const float* g, int64_t valid_len,
     AdamArgs a{state->master, state->m, state->v, g, slot, valid_len, ctrl, *hp};
     Kernel<AdamArgs> k = gather != nullptr && gather_dtype == ZERO_BF16 ? adam_for<ZERO_BF16>(gw)
                                                               : adam_for<ZERO_F16>(gw);
-    return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, "zero_adam_step");
+    return launch_chunked(k, a, valid_len, (hipStream_t)stream, "zero_adam_step");
 }
 
 int zero_adam_step_qgather(const zero_state* state, const float* g, int64_t valid_len,
@@ -1688,7 +1784,10 @@ int zero_adam_step_qgather(const zero_state* state, const float* g, int64_t vali
         k = bits == 8 ? adam_qgather_kernel<ZERO_F16, 8> : adam_qgather_kernel<ZERO_F16, 4>;
     else
         k = bits == 8 ? adam_qgather_kernel<ZERO_BF16, 8> : adam_qgather_kernel<ZERO_BF16, 4>;
-    return launch(k, tiles_for(valid_len), kBlock, (hipStream_t)stream, a, what);
+    return launch_chunked(k, a, valid_len, (hipStream_t)stream, what,
+                          [bits](const AdamQArgs& x, int64_t b0, int64_t n) {
+                              return AdamQArgs{at(x.a, b0, n), at(x.q, b0, bits)};
+                          });
 }
 
 int zero_cast_to_gather(const float* master, int64_t valid_len, void* gather, int32_t dtype,
