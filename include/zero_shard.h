@@ -21,7 +21,11 @@
  *   "zero-stages-simulation" README: flat partitioning into N near-equal
  *     contiguous chunks, GPU r owns chunk r;
  *   "ZeRO: Memory Optimization for Large Models" (lesson), Stage 1 and 2;
- *   "ZeRO Stage 1/2/3" guide, section 5 (AdamW with weight decay).
+ *   "ZeRO Stage 1/2/3" guide, section 5 (AdamW with weight decay, the
+ *     reduce bucket size);
+ *   "CMU 11-868 L18", Other memory optimizations (ZeRO++ block-quantised
+ *     payloads); paper summary 3.4, Stage 2 bucketization (gradients reduced
+ *     bucket by bucket during the backward pass).
  *
  * Conventions for every call below.
  *   - Pointers named *_dev are device pointers (hipMalloc'd or torch tensors);
@@ -30,9 +34,12 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls that touch device memory only enqueue work on `stream` and return;
  *     they never synchronise.  Results are visible after the caller syncs.
- *   - Arguments are validated before anything is enqueued.  On a nonzero
- *     return nothing was enqueued and nothing was written; zero_last_error()
- *     describes the problem.  Faults inside kernels surface at the next sync.
+ *   - Arguments are validated before anything is enqueued: on an argument
+ *     error (EINVAL, EALIGN, ERANGE, ESPACE) nothing was enqueued and nothing
+ *     was written.  EHIP (the runtime refused a launch) can follow earlier
+ *     launches of the same call (a pass is issued as several launches, see
+ *     ZERO_LAUNCH_TILES).  zero_last_error() describes the problem.  Faults
+ *     inside kernels surface at the next sync.
  *   - 16-bit data is passed as raw storage (uint16 bit patterns); `dtype`
  *     selects ZERO_F16 (IEEE binary16) or ZERO_BF16 (bfloat16).
  *   - Element counts and offsets are int64 (Psi reaches 1.3e10 elements).
@@ -179,9 +186,9 @@ int zero_partition(int64_t psi, int32_t nranks, int32_t rank, int64_t *shard_len
  * workspace and valid_len, then the rest of the step over the whole shard
  * (zero_adam_step or zero_adam_step_qgather; zero_fused_restore or
  * zero_fused_restore_q), complete the step: the results equal those of one
- * call over the whole shard, bit for bit.  On the fused path each piece's Adam update
- * can therefore run as soon as its gradient has arrived; the skip decision
- * still waits for the last piece. */
+ * call over the whole shard, bit for bit.  On the fused path each piece's
+ * Adam update can therefore run as soon as its gradient has arrived; the
+ * skip decision still waits for the last piece. */
 
 /* sizeof(zero_ctrl); allocate that many bytes of device memory per rank. */
 size_t zero_ctrl_bytes(void);
