@@ -63,6 +63,15 @@ constexpr int64_t kChunkTiles = ZERO_LAUNCH_TILES;  // most tiles per launch of 
 // ran 4.5% faster and the 7B two-pass step 3% faster than at six per CU; one
 // per CU was 23% slower.
 constexpr unsigned kResidencyLds = 64 * 1024;
+// Three workgroups per CU (more than a quarter, at most a third of the LDS)
+// for the passes with quantised data.  Those that also quantise the
+// all-gather payload wait at one more workgroup barrier per tile (the block's
+// range): the 13B step took 10.9 ms at three per CU against 11.2 at six and
+// 11.5 at two.  Those over quantised contributions load each row's block
+// record through the scalar cache: INT8 rows 9.34 ms at three per CU, 9.28
+// at six, 9.55 at two; INT4 rows 7.82, 7.87 and 8.11.
+constexpr unsigned kResidencyLdsQ = 48 * 1024;
+
 constexpr int64_t kMaxLen = int64_t(1) << 40;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -1436,6 +1445,16 @@ int launch(Kernel<Args> kernel, int64_t grid, int block, hipStream_t s, const Ar
     return ok();
 }
 
+// LDS reserved per workgroup of a pass over each kind of contribution source.
+template <class SRC>
+struct Residency {
+    static constexpr unsigned lds = kResidencyLds;
+};
+template <int BITS>
+struct Residency<SrcQ<BITS>> {
+    static constexpr unsigned lds = kResidencyLdsQ;
+};
+
 // A streaming pass over a long shard is issued as consecutive launches of at
 // most kChunkTiles tiles, each with every per-element pointer advanced to its
 // first element (the same arithmetic as the bucket contract in the header, so
@@ -1511,12 +1530,11 @@ AdamArgs at(AdamArgs a, int64_t b0, int64_t len) {
 // the earlier chunks already enqueued.
 template <class Args, class At>
 int launch_chunked(Kernel<Args> kernel, const Args& args, int64_t len, hipStream_t s,
-                   const char* what, At&& at_chunk) {
+                   const char* what, At&& at_chunk, unsigned lds = kResidencyLds) {
     constexpr int64_t chunk = kChunkTiles * kTile;
     for (int64_t b0 = 0; b0 < len; b0 += chunk) {
         const int64_t n = len - b0 < chunk ? len - b0 : chunk;
-        const int rc = launch(kernel, tiles_for(n), kBlock, s, at_chunk(args, b0, n), what,
-                              kResidencyLds);
+        const int rc = launch(kernel, tiles_for(n), kBlock, s, at_chunk(args, b0, n), what, lds);
         if (rc != ZERO_OK) return rc;
     }
     return ok();
@@ -1524,9 +1542,10 @@ int launch_chunked(Kernel<Args> kernel, const Args& args, int64_t len, hipStream
 
 template <class Args>
 int launch_chunked(Kernel<Args> kernel, const Args& args, int64_t len, hipStream_t s,
-                   const char* what) {
-    return launch_chunked(kernel, args, len, s, what,
-                          [](const Args& a, int64_t b0, int64_t n) { return at(a, b0, n); });
+                   const char* what, unsigned lds = kResidencyLds) {
+    return launch_chunked(
+        kernel, args, len, s, what, [](const Args& a, int64_t b0, int64_t n) { return at(a, b0, n); },
+        lds);
 }
 
 // Checks and launches shared by the fused entry points (the contribution
@@ -1547,7 +1566,7 @@ int fused_launch(const SRC& src, int32_t nranks, const zero_state* pair, int64_t
     const FusedArgs<SRC> a{src, {pair->master, pair->m, pair->v}, slot, valid_len, ctrl,
                            (Partial*)ws, *hp, nranks};
     return launch_chunked(fused_for<SRC>(store_width(slot), gather_dtype, nranks), a, valid_len,
-                          (hipStream_t)stream, what);
+                          (hipStream_t)stream, what, Residency<SRC>::lds);
 }
 
 // Checks and launch shared by the reduce entry points (source already checked).
@@ -1561,7 +1580,8 @@ int reduce_launch(const SRC& src, int32_t nranks, int64_t valid_len, const zero_
     if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
     if (valid_len == 0) return ok();
     const ReduceArgs<SRC> a{src, valid_len, ctrl, g, (Partial*)ws, nranks};
-    return launch_chunked(reduce_for<SRC>(nranks), a, valid_len, (hipStream_t)stream, what);
+    return launch_chunked(reduce_for<SRC>(nranks), a, valid_len, (hipStream_t)stream, what,
+                          Residency<SRC>::lds);
 }
 
 // Quantised row tables: bits 8 or 4, nranks in [1, ZERO_MAX_RANKS], every
@@ -1633,7 +1653,8 @@ int fused_qgather_launch(const StridedRows& rows, int32_t nranks, const zero_sta
     return launch_chunked(k, a, valid_len, (hipStream_t)stream, what,
                           [bits](const A& x, int64_t b0, int64_t n) {
                               return A{at(x.f, b0, n), at(x.q, b0, bits)};
-                          });
+                          },
+                          kResidencyLdsQ);
 }
 
 }  // namespace
@@ -1798,7 +1819,8 @@ int zero_adam_step_qgather(const zero_state* state, const float* g, int64_t vali
     return launch_chunked(k, a, valid_len, (hipStream_t)stream, what,
                           [bits](const AdamQArgs& x, int64_t b0, int64_t n) {
                               return AdamQArgs{at(x.a, b0, n), at(x.q, b0, bits)};
-                          });
+                          },
+                          kResidencyLdsQ);
 }
 
 int zero_cast_to_gather(const float* master, int64_t valid_len, void* gather, int32_t dtype,
@@ -1891,7 +1913,7 @@ int zero_quantize_blocks(const void* src, int32_t dtype, int64_t len, int32_t bi
         if (bits == 8) k = vec ? quantize_kernel<ZERO_BF16, 8, true> : quantize_kernel<ZERO_BF16, 8, false>;
         else k = vec ? quantize_kernel<ZERO_BF16, 4, true> : quantize_kernel<ZERO_BF16, 4, false>;
     }
-    return launch(k, tiles_for(len), kBlock, (hipStream_t)stream, a, what, kResidencyLds);
+    return launch(k, tiles_for(len), kBlock, (hipStream_t)stream, a, what);
 }
 
 int zero_dequantize_blocks(const void* codes, const zero_qblock* blocks, int32_t bits, int64_t len,
@@ -1911,7 +1933,7 @@ int zero_dequantize_blocks(const void* codes, const zero_qblock* blocks, int32_t
     const DequantArgs a{(const uint8_t*)codes, blocks, (uint16_t*)dst, len};
     const Kernel<DequantArgs> k = dtype == ZERO_F16 ? dequant_for<ZERO_F16>(bits, store_width(dst))
                                                     : dequant_for<ZERO_BF16>(bits, store_width(dst));
-    return launch(k, tiles_for(len), kBlock, (hipStream_t)stream, a, what, kResidencyLds);
+    return launch(k, tiles_for(len), kBlock, (hipStream_t)stream, a, what);
 }
 
 int zero_fused_restore(const zero_state* pair, int64_t valid_len, void* gather, int32_t dtype,
