@@ -54,23 +54,28 @@ constexpr int kFinGroups = 256;             // most first-level groups of the fi
 constexpr int64_t kFinPer = 16384;          // partials per first-level finalize group
 constexpr int kRestoreGrid = 256;           // workgroups of the (usually idle) restore pass
 constexpr int64_t kChunkTiles = ZERO_LAUNCH_TILES;  // most tiles per launch of a streaming pass
-// LDS reserved (and left unused) by each streaming workgroup: more than a
-// third and at most half of a CU's 160 KB, so that two workgroups, eight
-// waves, are resident per CU.  Each wave already has every load of its group
-// in flight, so two workgroups per CU (512 tiles over the chip) still cover
-// HBM latency, and the smaller set of tiles in flight reads and writes DRAM
-// with more locality: in one process on the same buffers the 13B fused step
-// ran 4.5% faster and the 7B two-pass step 3% faster than at six per CU; one
-// per CU was 23% slower.
-constexpr unsigned kResidencyLds = 64 * 1024;
-// Three workgroups per CU (more than a quarter, at most a third of the LDS)
-// for the passes with quantised data.  Those that also quantise the
-// all-gather payload wait at one more workgroup barrier per tile (the block's
-// range): the 13B step took 10.9 ms at three per CU against 11.2 at six and
-// 11.5 at two.  Those over quantised contributions load each row's block
-// record through the scalar cache: INT8 rows 9.34 ms at three per CU, 9.28
-// at six, 9.55 at two; INT4 rows 7.82, 7.87 and 8.11.
-constexpr unsigned kResidencyLdsQ = 48 * 1024;
+// Workgroups resident per CU, set by the LDS each streaming workgroup reserves
+// (and leaves unused) out of a CU's 160 KB.  Each wave already has every
+// load of its group in flight, so few workgroups per CU still cover HBM
+// latency, and fewer tiles in flight read and write DRAM with more locality.
+// The best count differs by pass.  Without a reservation the registers allow
+// six per CU for the 16-bit fused kernels and eight for the others; in one
+// process on the same buffers:
+//   fused step over 16-bit rows: two per CU; the 13B step 4.5% faster than
+//     without a reservation, one per CU 23% slower;
+//   Adam pass: two per CU (the 7B step 3% faster, mostly here);
+//   reduce over 16-bit rows: three per CU; the 7B step 7.08 ms, against
+//     7.18 without a reservation and 7.32 at two;
+//   passes that also quantise the all-gather payload wait at one more
+//     workgroup barrier per tile: three per CU; the 13B step 10.9 ms against
+//     11.2 without a reservation and 11.5 at two;
+//   passes over quantised contributions load each row's block record through
+//     the scalar cache: no reservation; INT8 rows 9.28 ms against 9.34 at
+//     three and 9.55 at two, their reduce 6.05 against 6.21 at three.
+constexpr unsigned kLdsTwoPerCu = 64 * 1024;    // more than a third, at most half
+constexpr unsigned kLdsThreePerCu = 48 * 1024;  // more than a quarter, at most a third
+constexpr unsigned kResidencyLds = kLdsTwoPerCu;     // fused (16-bit rows) and Adam passes
+constexpr unsigned kResidencyLdsQ = kLdsThreePerCu;  // passes writing the all-gather payload
 
 constexpr int64_t kMaxLen = int64_t(1) << 40;
 
@@ -1445,14 +1450,16 @@ int launch(Kernel<Args> kernel, int64_t grid, int block, hipStream_t s, const Ar
     return ok();
 }
 
-// LDS reserved per workgroup of a pass over each kind of contribution source.
+// LDS reserved per workgroup of the fused and reduce passes, by source.
 template <class SRC>
 struct Residency {
-    static constexpr unsigned lds = kResidencyLds;
+    static constexpr unsigned fused = kLdsTwoPerCu;
+    static constexpr unsigned reduce = kLdsThreePerCu;
 };
 template <int BITS>
 struct Residency<SrcQ<BITS>> {
-    static constexpr unsigned lds = kResidencyLdsQ;
+    static constexpr unsigned fused = 0;
+    static constexpr unsigned reduce = 0;
 };
 
 // A streaming pass over a long shard is issued as consecutive launches of at
@@ -1566,7 +1573,7 @@ int fused_launch(const SRC& src, int32_t nranks, const zero_state* pair, int64_t
     const FusedArgs<SRC> a{src, {pair->master, pair->m, pair->v}, slot, valid_len, ctrl,
                            (Partial*)ws, *hp, nranks};
     return launch_chunked(fused_for<SRC>(store_width(slot), gather_dtype, nranks), a, valid_len,
-                          (hipStream_t)stream, what, Residency<SRC>::lds);
+                          (hipStream_t)stream, what, Residency<SRC>::fused);
 }
 
 // Checks and launch shared by the reduce entry points (source already checked).
@@ -1581,7 +1588,7 @@ int reduce_launch(const SRC& src, int32_t nranks, int64_t valid_len, const zero_
     if (valid_len == 0) return ok();
     const ReduceArgs<SRC> a{src, valid_len, ctrl, g, (Partial*)ws, nranks};
     return launch_chunked(reduce_for<SRC>(nranks), a, valid_len, (hipStream_t)stream, what,
-                          Residency<SRC>::lds);
+                          Residency<SRC>::reduce);
 }
 
 // Quantised row tables: bits 8 or 4, nranks in [1, ZERO_MAX_RANKS], every
