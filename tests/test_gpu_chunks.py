@@ -39,20 +39,30 @@ def two_chunk(dtype=F16, steps=3, **kw):
 
 DYN = dict(scaler=2, contrib_scale=2.0 ** 10, loss_scale=2.0 ** 10)
 
-# name: (case, payload bits, 16-bit slot)
+# name: (case, payload bits, 16-bit slot, contribution layout)
 CASES = {
     "fused_skip_after_boundary": (Case(two_chunk(**DYN), 1, 3,
-                                       extra=(Inject(2, 1, CHUNK + 5, np.inf),)), 0, True),
-    "two_pass_clip": (Case(two_chunk(dtype=BF16, max_grad_norm=0.5), 1, 3), 0, True),
+                                       extra=(Inject(2, 1, CHUNK + 5, np.inf),)), 0, True,
+                                  "strided"),
+    "two_pass_clip": (Case(two_chunk(dtype=BF16, max_grad_norm=0.5), 1, 3), 0, True, "strided"),
     "fused_int8_payload_no_slot": (Case(two_chunk(**DYN), 1, 3,
-                                        extra=(Inject(2, 0, CHUNK + 2048, np.inf),)), 8, False),
-    "two_pass_int4_payload": (Case(two_chunk(dtype=BF16, max_grad_norm=0.5), 1, 2), 4, True),
-    "fused_int8_contributions": (Case(two_chunk(steps=2), 1, 2, qbits=8), 0, True),
+                                        extra=(Inject(2, 0, CHUNK + 2048, np.inf),)), 8, False,
+                                   "strided"),
+    "fused_int4_payload": (Case(two_chunk(steps=2), 1, 2), 4, True, "strided"),
+    "two_pass_int4_payload": (Case(two_chunk(dtype=BF16, max_grad_norm=0.5), 1, 2), 4, True,
+                              "strided"),
+    "fused_int8_contributions": (Case(two_chunk(steps=2), 1, 2, qbits=8), 0, True, "strided"),
+    "fused_int4_contributions": (Case(two_chunk(steps=2), 1, 2, qbits=4), 0, True, "strided"),
+    "two_pass_int8_contributions": (Case(two_chunk(dtype=BF16, max_grad_norm=0.5, steps=2), 1, 2,
+                                         qbits=8), 0, True, "strided"),
+    "fused_row_table": (Case(two_chunk(steps=2), 1, 2), 0, True, "rows"),
+    "two_pass_row_table_shifted": (Case(two_chunk(dtype=BF16, max_grad_norm=0.5, steps=2), 1, 2),
+                                   0, True, "rows_shifted"),
 }
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_shard_over_two_launches(name):
-    c, qbits, slot = CASES[name]
+    c, qbits, slot, layout = CASES[name]
     assert c.part[2] == SHARD
-    H.run_and_compare(c, name, qgather=qbits, write_slot=slot)
+    H.run_and_compare(c, name, layout=layout, qgather=qbits, write_slot=slot)
