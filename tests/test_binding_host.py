@@ -1,0 +1,83 @@
+"""Host-side logic of the Python binding, without a GPU: the constants that
+mirror include/zero_shard.h, the number of launches a pass is issued as, and
+the pieces and pointer advances of a bucketed step (the header's bucket
+contract: every per-element pointer advanced by the piece's first element,
+codes by bytes, block records by whole blocks)."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def Z():
+    import zero_partitioned_mixed_amd as Z
+    return Z
+
+
+def _header_define(name):
+    text = open(os.path.join(ROOT, "include", "zero_shard.h")).read()
+    m = re.search(rf"^#define {name} (\d+)", text, re.M)
+    assert m, name
+    return int(m.group(1))
+
+
+def test_constants_match_header(Z):
+    assert Z.TILE == _header_define("ZERO_TILE")
+    assert Z.QBLOCK == _header_define("ZERO_QBLOCK")
+    assert Z.PARTIAL_BYTES == _header_define("ZERO_PARTIAL_BYTES")
+    assert Z.LAUNCH_TILES == _header_define("ZERO_LAUNCH_TILES")
+    assert Z.MAX_RANKS == _header_define("ZERO_MAX_RANKS")
+    # one workspace partial per tile: the workspace grows by PARTIAL_BYTES per tile
+    assert Z.zero_workspace_bytes(3 * Z.TILE) - Z.zero_workspace_bytes(Z.TILE) == 2 * Z.PARTIAL_BYTES
+
+
+@pytest.mark.parametrize("valid,expected", [
+    (0, 0), (1, 1), (2048, 1), (16384 * 2048, 1), (16384 * 2048 + 1, 2),
+    (1_625_000_000, 49), (875_000_000, 27), (15_554_976, 1), (23_437_500, 1),
+])
+def test_launches_per_pass(Z, valid, expected):
+    assert Z.launches(valid) == expected
+
+
+def _step(Z, valid, bucket):
+    st = object.__new__(Z.ShardStep)   # no device state: only the piece logic is used
+    st.valid_len, st.bucket = valid, bucket
+    return st
+
+
+@pytest.mark.parametrize("valid,bucket", [
+    (0, 0), (5, 0), (5, 2048), (2048, 2048), (2049, 2048), (100_003, 2048 * 3),
+    (1_625_000_000, 499_998_720),
+])
+def test_pieces_cover_the_shard_in_order(Z, valid, bucket):
+    pieces = _step(Z, valid, bucket).pieces()
+    assert pieces[0][0] == 0
+    assert sum(n for _, n in pieces) == valid
+    for (b0, n), (b1, _) in zip(pieces, pieces[1:]):
+        assert b1 == b0 + n and b0 % Z.TILE == 0 and b1 % Z.TILE == 0
+    if bucket and valid > bucket:
+        assert all(n == bucket for _, n in pieces[:-1]) and 0 < pieces[-1][1] <= bucket
+    else:
+        assert pieces == [(0, valid)]
+
+
+def test_bucket_must_be_whole_tiles(Z):
+    hp = Z.hparams()
+    with pytest.raises(ValueError):
+        Z.ShardStep(8, 64, 64, 0, Z.F16, Z.F16, hp, (None, None, None), bucket=1000)
+
+
+def test_piece_pointer_advances(Z):
+    b0 = 3 * Z.TILE
+    rows = Z.ShardStep._contrib_at([1 << 20, 1 << 24], b0)
+    assert rows == [(1 << 20) + 2 * b0, (1 << 24) + 2 * b0]        # 16-bit elements
+    for bits, code_bytes in ((8, b0), (4, b0 // 2)):
+        q = Z.ShardStep._contrib_at(Z.QuantRows([(1 << 20, 1 << 22)], bits), b0)
+        assert q.bits == bits
+        assert q.rows == [((1 << 20) + code_bytes, (1 << 22) + 8 * (b0 // Z.QBLOCK))]
+        g = Z.QGather(1 << 20, 1 << 22, bits, 100_000).at(b0)
+        assert (g.codes, g.blocks, g.bits, g.length) == \
+            ((1 << 20) + code_bytes, (1 << 22) + 8 * (b0 // Z.QBLOCK), bits, 100_000 - b0)
