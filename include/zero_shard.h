@@ -285,7 +285,9 @@ int zero_adam_step(const zero_state *state, const float *g_dev, int64_t valid_le
  * what zero_quantize_blocks(gather_dtype, bits) would write from the 16-bit
  * slot after the step.  gather_dev may be NULL (no 16-bit slot written);
  * gather_dtype always names the 16-bit format that is quantised.  A skipped
- * step writes nothing, so slot and payload keep the previous step's values.
+ * step writes nothing, so slot and payload keep the previous step's values;
+ * the caller initialises the payload with the slot (zero_quantize_blocks
+ * over the initial slot), since the first step may be skipped.
  * Errors: as zero_adam_step, plus EINVAL (bits not 8 or 4, null codes or
  * blocks, gather dtype) and EALIGN (codes or blocks not 8-byte aligned). */
 int zero_adam_step_qgather(const zero_state *state, const float *g_dev, int64_t valid_len,

@@ -246,9 +246,15 @@ class GpuRun:
         # qgather = 8 or 4: the step also writes the quantised all-gather
         # payload (zero_fused_step_qgather); write_slot=False passes no gather
         self.qg = Z.QGather.alloc(valid, qgather, dev) if qgather else None
-        if self.qg is not None:
-            self.qg.codes.fill_(0xA5)   # canaries: every code byte and record must be written
+        if self.qg is not None and fused:
+            # canaries: the step or the restore writes every code byte and record
+            self.qg.codes.fill_(0xA5)
             self.qg.blocks.fill_(0xA5)
+        elif self.qg is not None and valid:
+            # the two-pass path writes nothing on a skipped step, so the payload
+            # starts as the caller's would: the initial slot, quantised
+            Z.zero_quantize_blocks(self.gather[self.gather_off:], w.dtype, valid, qgather,
+                                   self.qg.codes, self.qg.blocks)
         self.write_slot = write_slot
         if not write_slot and not qgather:
             raise ValueError("only a quantised-gather step may skip the 16-bit slot")

@@ -6,8 +6,11 @@ the 16-bit format, the path (fused, or two-pass with a clip threshold that
 may or may not bind), the loss scaler, the contribution hand-over (one
 buffer, a row table, rows at 8-byte-aligned starts, INT8 or INT4 blocks), the
 step count, the weight decay, outliers, and sometimes an inf or NaN in one
-contribution.  The bars are those of the fixed cases.  The draw uses its own
-numpy generator; the data come from the seeded input generator as always.
+contribution.  A second draw per seed (its own generator, so the first draw
+stays as it was) adds the quantised all-gather payload (INT8 or INT4, with
+or without the 16-bit slot) and bucketed steps (pieces of a few tiles).  The
+bars are those of the fixed cases.  The data come from the seeded input
+generator as always.
 """
 import numpy as np
 import pytest
@@ -62,7 +65,21 @@ def draw(seed: int):
     return Case(w, rank, steps, extra=extra, qbits=qbits), layout
 
 
+def draw_options(seed: int, c: Case, layout: str):
+    """(payload bits, write the 16-bit slot, bucket elements) for a case."""
+    rng = np.random.default_rng(5000 + seed)
+    fused = c.w.max_grad_norm <= 0
+    qgather = int(rng.choice([0, 0, 0, 8, 4]))
+    if fused and (c.qbits or layout != "strided"):
+        qgather = 0   # the fused payload step takes [N, stride] contributions
+    write_slot = not qgather or bool(rng.random() < 0.5)
+    bucket = int(rng.choice([0, 0, 0, 1, 2, 5])) * 2048
+    return qgather, write_slot, bucket
+
+
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_case(seed):
     c, layout = draw(seed)
-    H.run_and_compare(c, f"random{seed}", full=True, layout=layout)
+    qgather, write_slot, bucket = draw_options(seed, c, layout)
+    H.run_and_compare(c, f"random{seed}", full=True, layout=layout, qgather=qgather,
+                      write_slot=write_slot, bucket=bucket)
