@@ -5,9 +5,10 @@
 // uses the matrix cores.  The design points are
 //   * one workgroup per tile of ZERO_TILE = 2048 elements (4 wave64s x 64
 //     lanes x 8 elements), launched as full grids of at most 16,384 tiles,
-//     with two workgroups resident per CU, so that the set of tiles in flight
-//     stays compact (a grid-stride loop, one grid over a whole 13B shard and
-//     six workgroups per CU all measured slower);
+//     with few workgroups resident per CU (two or three, by pass), so that
+//     the set of tiles in flight stays compact (a grid-stride loop, one grid
+//     over a whole 13B shard and six or eight workgroups per CU all measured
+//     slower);
 //   * wave-contiguous lanes: lane l of wave w owns two runs of four elements,
 //     [512w + 4l, +4) and 256 elements later, so every memory instruction of a
 //     wave covers one contiguous span and fills whole cache lines;
