@@ -196,7 +196,7 @@ def oracle_elements(c: Case, reps: list[dict], cols: np.ndarray | None = None):
 ROW_LAYOUTS = ("strided", "rows", "rows_shifted")
 
 
-class GpuRun:
+class DeviceRun:
     """One rank's buffers in HBM and its steps through the C ABI.
 
     layout: how the contribution rows are handed to the library.
@@ -340,7 +340,7 @@ def run_and_compare(c: Case, label: str, full: bool = True, layout: str = "strid
         f"variant={c.w.variant} steps={c.steps} offset={c.part[1]} valid={c.part[2]} "
         f"layout={layout} qbits={c.qbits} qgather={qgather} write_slot={write_slot} "
         f"bucket={bucket}")
-    g = GpuRun(c, full_gather=full, layout=layout, qgather=qgather, write_slot=write_slot,
+    g = DeviceRun(c, full_gather=full, layout=layout, qgather=qgather, write_slot=write_slot,
                bucket=bucket)
     g.run()
     ref_reps = oracle_scalars(c)

@@ -43,7 +43,7 @@ def run_fullsize(w, layout="strided", qbits=0, steps=None, samples=65_536, qgath
     shard, off, valid = c.part
     H.log(f"{w.name}: shard {shard} at offset {off}, N={w.nranks}, {w.variant}, {c.steps} steps, "
           f"layout {layout}, qbits {qbits}, qgather {qgather}")
-    g = H.GpuRun(c, full_gather=True, layout=layout, qgather=qgather, write_slot=not qgather)
+    g = H.DeviceRun(c, full_gather=True, layout=layout, qgather=qgather, write_slot=not qgather)
     g.run()
     key = (w.name, qbits, c.steps)
     if key not in _REPS:

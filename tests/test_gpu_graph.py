@@ -47,9 +47,9 @@ CASES = {
 def test_graph_replay_equals_eager(name):
     import torch
     c = CASES[name]
-    eager = H.GpuRun(c, full_gather=False)
+    eager = H.DeviceRun(c, full_gather=False)
     eager.run()
-    g = H.GpuRun(c, full_gather=False)
+    g = H.DeviceRun(c, full_gather=False)
     src = g.qrows if g.qrows is not None else g.contrib
     graph = g.step_obj.capture(src, g.gather)
     torch.cuda.synchronize()
@@ -87,9 +87,9 @@ def test_graph_replay_with_quantised_gather_payload(write_slot, clip):
     c = Case(small(100_003, 3, 2, steps=4, scaler=2, contrib_scale=2.0 ** 10,
                    loss_scale=2.0 ** 10, max_grad_norm=clip), 2, 4,
              extra=(Inject(2, 2, 30_001, np.inf),))
-    eager = H.GpuRun(c, full_gather=False, qgather=8, write_slot=write_slot)
+    eager = H.DeviceRun(c, full_gather=False, qgather=8, write_slot=write_slot)
     eager.run()
-    g = H.GpuRun(c, full_gather=False, qgather=8, write_slot=write_slot)
+    g = H.DeviceRun(c, full_gather=False, qgather=8, write_slot=write_slot)
     graph = g.step_obj.capture(g.contrib, g.gather if write_slot else None, g.qg)
     torch.cuda.synchronize()
     assert g.step_obj.ctrl_dict()["t"] == 0

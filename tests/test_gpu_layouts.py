@@ -231,7 +231,7 @@ def test_bucketed_step_equals_one_call(name):
     c, bucket, layout, qbits, slot = BUCKETED[name]
     runs = []
     for b in (0, bucket):
-        g = H.GpuRun(c, full_gather=True, layout=layout, qgather=qbits, write_slot=slot, bucket=b)
+        g = H.DeviceRun(c, full_gather=True, layout=layout, qgather=qbits, write_slot=slot, bucket=b)
         assert len(g.step_obj.pieces()) == (1 if b == 0 else -(-c.part[2] // bucket))
         g.run()
         runs.append(g)

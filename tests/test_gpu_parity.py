@@ -144,7 +144,7 @@ def test_empty_tail_rank():
     w = small(10, 7, 6)
     c = Case(w, 6, 2)
     assert c.part == (2, 12, 0)
-    g = H.GpuRun(c)
+    g = H.DeviceRun(c)
     before = g.gather.clone()
     g.run()
     assert torch.equal(g.gather.view(torch.int16), before.view(torch.int16))
@@ -157,7 +157,7 @@ def test_run_to_run_bitwise():
     w = small(300_007, 8, 6, dtype=BF16, max_grad_norm=0.02)
     outs = []
     for _ in range(2):
-        g = H.GpuRun(Case(w, 6, 3))
+        g = H.DeviceRun(Case(w, 6, 3))
         g.run()
         outs.append((g.fetch(), [r["sumsq"] for r in g.reports]))
     (a, sa), (b, sb) = outs

@@ -95,9 +95,9 @@ def test_qgather_step_equals_step_then_quantize(name, w, extra, bits):
     import zero_partitioned_mixed_amd as Z
     c = Case(w, w.ranks[0], w.steps, extra=tuple(extra))
     H.log(f"qgather vs step+quantize {name} bits={bits}: part {c.part}")
-    a = H.GpuRun(c, full_gather=True, qgather=bits)
+    a = H.DeviceRun(c, full_gather=True, qgather=bits)
     a.run()
-    b = H.GpuRun(c, full_gather=True)
+    b = H.DeviceRun(c, full_gather=True)
     b.run()
     assert repr(a.reports) == repr(b.reports)  # exact for floats, and NaN norms compare equal
     for x, y in zip(a.fetch(), b.fetch()):

@@ -136,7 +136,7 @@ def test_quantized_step_gpt2_sized(bits):
     blocks around each sampled column)."""
     w = workloads.GPT2
     c = Case(w, w.ranks[0], w.steps, qbits=bits)
-    g = H.GpuRun(c, full_gather=False)
+    g = H.DeviceRun(c, full_gather=False)
     g.run()
     reps = H.oracle_scalars(c)
     H.assert_reports(g.reports, reps)
@@ -190,7 +190,7 @@ def test_quantized_all_gather_of_updated_slot(bits):
     c = Case(w, 5, 2)
     _, off, valid = c.part
     assert off % 2 == 1
-    g = H.GpuRun(c, full_gather=True)
+    g = H.DeviceRun(c, full_gather=True)
     g.run()
     slot = g.gather[off:off + valid]
     q = Z.QuantRows.alloc(1, valid, bits, slot.device)

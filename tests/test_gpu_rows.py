@@ -66,7 +66,7 @@ def test_row_table_small(name, layout):
     w, extra = CASES[name]
     c = Case(w, w.ranks[0], w.steps, extra=tuple(extra))
     g, _ = H.run_and_compare(c, f"{name}/{layout}", full=True, layout=layout)
-    ref = H.GpuRun(c, full_gather=True, layout="strided")
+    ref = H.DeviceRun(c, full_gather=True, layout="strided")
     ref.run()
     _assert_same(g, ref, name)
 
@@ -78,7 +78,7 @@ def test_row_table_aliased_rows():
     import zero_partitioned_mixed_amd as Z
     w = small(4 * 9_001, 4, 1)
     c = Case(w, 1, 1)
-    g = H.GpuRun(c, full_gather=False, layout="strided")
+    g = H.DeviceRun(c, full_gather=False, layout="strided")
     g.fill(1)
     dup = g.contrib.clone()
     dup[2] = dup[0]
@@ -105,9 +105,9 @@ def test_row_table_gpt2_sized():
     step and oracle elements on a sample."""
     w = workloads.GPT2
     c = Case(w, w.ranks[0], w.steps)
-    g = H.GpuRun(c, full_gather=False, layout="rows")
+    g = H.DeviceRun(c, full_gather=False, layout="rows")
     g.run()
-    ref = H.GpuRun(c, full_gather=False, layout="strided")
+    ref = H.DeviceRun(c, full_gather=False, layout="strided")
     ref.run()
     _assert_same(g, ref, "gpt2 rows")
     reps = H.oracle_scalars(c)
