@@ -58,7 +58,7 @@ static int host_mode(void) {
     ZERO(zero_partition(10, 7, 6, &shard, &off, &valid));
     if (shard != 2 || off != 12 || valid != 0) return fprintf(stderr, "empty rank\n"), 1;
     if (zero_ctrl_bytes() != 128 || zero_workspace_bytes(4097) != (3 + 256) * 16 ||
-        zero_pair_elems(4097) != 6 * 2048 || zero_qcode_bytes(5, 4) != 3)
+        zero_pair_elems(4097) != 18 * 2048 || zero_qcode_bytes(5, 4) != 3)
         return fprintf(stderr, "sizes\n"), 1;
     if (zero_partition(0, 3, 0, &shard, &off, &valid) != ZERO_EINVAL || zero_last_error()[0] == 0)
         return fprintf(stderr, "error path\n"), 1;
@@ -89,16 +89,18 @@ static void run_rank(FILE *f, int32_t rank, float max_grad_norm, int inject, int
     synth_param_range(0, 0.02, ZERO_F16, 0, PSI, gather);
 
     void *dC, *dG, *dCtrl, *dWs, *dg = NULL;
-    float *flat[3], *pair[3];
+    float *flat[3], *pair[3], *pair_buf;
     const size_t ws_bytes = zero_workspace_bytes(valid);
     HIP(hipMalloc(&dC, sizeof(uint16_t) * NR * stride));
     HIP(hipMalloc(&dG, sizeof(uint16_t) * PSI));
     HIP(hipMalloc(&dCtrl, zero_ctrl_bytes()));
     HIP(hipMalloc(&dWs, ws_bytes));
+    /* the paired state is one buffer; m and v start one and two tiles into it */
+    HIP(hipMalloc((void **)&pair_buf, sizeof(float) * zero_pair_elems(valid)));
     for (int q = 0; q < 3; ++q) {
         HIP(hipMalloc((void **)&flat[q], sizeof(float) * valid));
         HIP(hipMemset(flat[q], 0, sizeof(float) * valid));
-        HIP(hipMalloc((void **)&pair[q], sizeof(float) * zero_pair_elems(valid)));
+        pair[q] = pair_buf + q * ZERO_TILE;
     }
     HIP(hipMemcpy(flat[0], p0, sizeof(float) * valid, hipMemcpyHostToDevice));
     HIP(hipMemcpy(dG, gather, sizeof(uint16_t) * PSI, hipMemcpyHostToDevice));
@@ -170,10 +172,8 @@ static void run_rank(FILE *f, int32_t rank, float max_grad_norm, int inject, int
         HIP(hipFree(dCodes));
         HIP(hipFree(dBlocks));
     }
-    for (int q = 0; q < 3; ++q) {
-        HIP(hipFree(flat[q]));
-        HIP(hipFree(pair[q]));
-    }
+    for (int q = 0; q < 3; ++q) HIP(hipFree(flat[q]));
+    HIP(hipFree(pair_buf));
     HIP(hipFree(dC));
     HIP(hipFree(dG));
     HIP(hipFree(dCtrl));

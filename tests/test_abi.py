@@ -66,13 +66,19 @@ def test_workspace_and_pair_sizes(Z):
     assert Z.zero_workspace_bytes(2048) == 257 * 16
     assert Z.zero_workspace_bytes(2049) == 258 * 16
     assert Z.zero_workspace_bytes(1_625_000_000) == (793_458 + 256) * 16
+    # one buffer: per tile two sets of master, m and v
     assert Z.zero_pair_elems(0) == 0
-    assert Z.zero_pair_elems(1) == 2 * 2048
-    assert Z.zero_pair_elems(4096) == 4 * 2048
-    assert Z.zero_pair_elems(4097) == 6 * 2048
+    assert Z.zero_pair_elems(1) == 6 * 2048
+    assert Z.zero_pair_elems(4096) == 12 * 2048
+    assert Z.zero_pair_elems(4097) == 18 * 2048
 
 
 FAKE = 1 << 20  # a 16-byte aligned non-null address, never dereferenced
+
+
+def _pair(Z):
+    """A well-formed paired state at FAKE: m and v 2048 floats apart."""
+    return Z.State(FAKE, FAKE + 4 * 2048, FAKE + 8 * 2048)
 
 
 def _reduce(Z, contrib=FAKE, dtype=1, n=8, stride=64, valid=64, ctrl=FAKE, g=FAKE, ws=FAKE,
@@ -91,17 +97,23 @@ def test_reduce_validation(Z, kw, code):
     assert Z.zero_last_error() != ""
 
 
-def test_fused_rejects_clipping_and_aliasing(Z):
-    pair = Z.State(FAKE, FAKE + 65536, FAKE + 131072)
+def test_fused_rejects_clipping_and_a_bad_paired_state(Z):
+    pair = _pair(Z)
     hp = Z.hparams(max_grad_norm=1.0)
     rc = Z._lib.zero_fused_step(FAKE, 1, 8, 64, ctypes.byref(pair), 64, FAKE, 1, 0,
                                 ctypes.byref(hp), FAKE, FAKE, 1 << 20, None)
     assert rc == -1 and "two-pass" in Z.zero_last_error()
     hp = Z.hparams()
-    alias = Z.State(FAKE, FAKE, FAKE + 131072)
-    rc = Z._lib.zero_fused_step(FAKE, 1, 8, 64, ctypes.byref(alias), 64, FAKE, 1, 0,
+    # a paired state is one buffer: m and v one and two tiles of 2048 floats past master
+    for bad in (Z.State(FAKE, FAKE, FAKE + 16384), Z.State(FAKE, FAKE + 65536, FAKE + 131072),
+                Z.State(FAKE, FAKE + 8192, FAKE + 8192), Z.State(FAKE, FAKE + 8192, 0)):
+        rc = Z._lib.zero_fused_step(FAKE, 1, 8, 64, ctypes.byref(bad), 64, FAKE, 1, 0,
+                                    ctypes.byref(hp), FAKE, FAKE, 1 << 20, None)
+        assert rc == -1 and "one buffer" in Z.zero_last_error()
+    odd = Z.State(FAKE + 4, FAKE + 4 + 8192, FAKE + 4 + 16384)
+    rc = Z._lib.zero_fused_step(FAKE, 1, 8, 64, ctypes.byref(odd), 64, FAKE, 1, 0,
                                 ctypes.byref(hp), FAKE, FAKE, 1 << 20, None)
-    assert rc == -1 and "distinct" in Z.zero_last_error()
+    assert rc == -2
     rc = Z._lib.zero_fused_step(FAKE, 1, 8, 64, ctypes.byref(pair), 64, FAKE, 1, 0,
                                 ctypes.byref(hp), FAKE, FAKE, 16, None)
     assert rc == -4  # workspace too small
@@ -146,7 +158,7 @@ def _rows_call(Z, fused, rows, n=None, dtype=1, valid=64, ctrl=FAKE, g=FAKE, wsb
     arr = (ctypes.c_void_p * max(len(rows), 1))(*rows) if rows is not None else None
     if not fused:
         return Z._lib.zero_reduce_grads_rows(arr, dtype, n, valid, ctrl, g, FAKE, wsb, None)
-    pair = Z.State(FAKE, FAKE + 65536, FAKE + 131072)
+    pair = _pair(Z)
     hp = Z.hparams()
     return Z._lib.zero_fused_step_rows(arr, dtype, n, ctypes.byref(pair), valid, FAKE, 1, 0,
                                        ctypes.byref(hp), ctrl, FAKE, wsb, None)
@@ -205,7 +217,7 @@ def _q_call(Z, fused, codes, blocks, bits=8, n=None, valid=64, g=FAKE, wsb=1 << 
     ba = (ctypes.c_void_p * max(len(blocks), 1))(*blocks) if blocks is not None else None
     if not fused:
         return Z._lib.zero_reduce_grads_q(ca, ba, bits, n, valid, FAKE, g, FAKE, wsb, None)
-    pair = Z.State(FAKE, FAKE + 65536, FAKE + 131072)
+    pair = _pair(Z)
     hp = Z.hparams()
     return Z._lib.zero_fused_step_q(ca, ba, bits, n, ctypes.byref(pair), valid, FAKE, 1, 0,
                                     ctypes.byref(hp), FAKE, FAKE, wsb, None)
@@ -231,7 +243,7 @@ def test_quant_rows_validation(Z, fused, codes, blocks, kw, code, msg):
 
 def _qg_call(Z, contrib_dtype=1, valid=64, gather=FAKE, gdt=1, bits=8, codes=FAKE, blocks=FAKE,
              clip=0.0, wsb=1 << 16, ctrl=FAKE):
-    pair = Z.State(FAKE, FAKE + 65536, FAKE + 131072)
+    pair = _pair(Z)
     hp = Z.hparams(max_grad_norm=clip)
     return Z._lib.zero_fused_step_qgather(FAKE, contrib_dtype, 8, 64, ctypes.byref(pair), valid,
                                           gather, gdt, 0, bits, codes, blocks, ctypes.byref(hp),
@@ -273,7 +285,7 @@ def test_fused_qgather_validation(Z, kw, code, msg):
 def test_fused_restore_q_validation(Z, kw, code, msg):
     a = dict(valid=64, gather=FAKE, dtype=1, bits=8, codes=FAKE, blocks=FAKE, ctrl=FAKE)
     a.update(kw)
-    pair = Z.State(FAKE, FAKE + 65536, FAKE + 131072)
+    pair = _pair(Z)
     rc = Z._lib.zero_fused_restore_q(ctypes.byref(pair), a["valid"], a["gather"], a["dtype"], 0,
                                      a["bits"], a["codes"], a["blocks"], a["ctrl"], None)
     assert rc == code

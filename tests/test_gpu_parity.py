@@ -273,7 +273,8 @@ def test_pair_store_load_round_trip():
     dev = torch.device("cuda", 0)
     for n in (1, 7, 2048, 2049, 100_003):
         flat = tuple(torch.randn(n, device=dev) for _ in range(3))
-        pair = tuple(torch.full((Z.zero_pair_elems(n),), float("nan"), device=dev) for _ in range(3))
+        pair = Z.paired_state(n, dev)
+        pair[0].fill_(float("nan"))
         ctrl = torch.empty(Z.zero_ctrl_bytes(), dtype=torch.uint8, device=dev)
         Z.zero_ctrl_init(ctrl, 1.0)
         Z.zero_pair_store(flat, pair, n, ctrl)
@@ -281,10 +282,11 @@ def test_pair_store_load_round_trip():
         Z.zero_pair_load(pair, back, n, ctrl)
         for a, b in zip(flat, back):
             assert torch.equal(a, b)
-        # set 0 of each tile holds the data, set 1 is untouched
-        p = pair[0].view(-1, 2, 2048)
-        assert torch.isnan(p[:, 1, :]).all()
-        assert torch.equal(p[:, 0, :].reshape(-1)[:n], flat[0])
+        # one buffer [tile][set][master|m|v][2048]: set 0 holds the data, set 1 is untouched
+        p = pair[0][:Z.zero_pair_elems(n)].view(-1, 2, 3, 2048)
+        assert torch.isnan(p[:, 1]).all()
+        for q in range(3):
+            assert torch.equal(p[:, 0, q].reshape(-1)[:n], flat[q])
 
 
 @pytest.mark.parametrize("tiles", [16384, 16385])

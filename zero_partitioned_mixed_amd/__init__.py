@@ -203,6 +203,16 @@ def zero_pair_elems(valid_len: int) -> int:
     return _lib.zero_pair_elems(valid_len)
 
 
+def paired_state(valid_len: int, device):
+    """A paired (fused-path) state: one fp32 buffer of zero_pair_elems
+    floats, returned as the (master, m, v) views the paired calls take (m and
+    v start ZERO_TILE and 2 * ZERO_TILE floats into the buffer)."""
+    import torch
+    buf = torch.empty(max(zero_pair_elems(valid_len), 3 * TILE), dtype=torch.float32,
+                      device=device)
+    return buf, buf[TILE:], buf[2 * TILE:]
+
+
 def zero_ctrl_init(ctrl, loss_scale: float) -> None:
     _check("zero_ctrl_init", _lib.zero_ctrl_init(_ptr(ctrl), loss_scale, _stream()))
 
@@ -428,8 +438,7 @@ class ShardStep:
         zero_ctrl_init(self.ctrl, loss_scale)
         self.pair = None
         if self.fused:
-            n = max(zero_pair_elems(valid_len), 4)
-            self.pair = tuple(torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3))
+            self.pair = paired_state(valid_len, dev)
             zero_pair_store(state, self.pair, valid_len, self.ctrl)
 
     def pieces(self):
@@ -476,7 +485,7 @@ class ShardStep:
                 c, ws = self._contrib_at(contrib, b0), _at(self.ws, b0 // TILE * PARTIAL_BYTES)
                 off, q = self.offset + b0, None if qgather is None else qgather.at(b0)
             if self.fused:
-                pair = self.pair if b0 == 0 else tuple(_at(t, 8 * b0) for t in self.pair)
+                pair = self.pair if b0 == 0 else tuple(_at(t, 4 * 6 * b0) for t in self.pair)
                 if q is not None:
                     zero_fused_step_qgather(c, self.dtype, self.nranks, self.stride, pair, ln,
                                             gather, self.gather_dtype, off, q, hp, ctrl, ws)

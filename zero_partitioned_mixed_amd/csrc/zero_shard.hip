@@ -111,10 +111,15 @@ __device__ __forceinline__ Runs runs_of(int64_t tile) {
     return Runs{a, a + 256};
 }
 
-// Index of shard element i of set s in a paired state array (ZERO_TILE interleave).
-__device__ __forceinline__ int64_t pair_index(int64_t i, int s) {
+// The paired state is one buffer: per tile, set 0 then set 1, each set
+// master, m, v of ZERO_TILE floats ([tile][set][master|m|v][ZERO_TILE]).  The
+// three array pointers of a paired zero_state are the buffer and the buffer
+// plus one and two ZERO_TILE, so pair_index gives the offset of shard element
+// i of set s from any of them.
+constexpr int64_t kPairTile = 6 * kTile;  // floats of one tile's two sets
+__device__ __host__ __forceinline__ int64_t pair_index(int64_t i, int s) {
     const int64_t tile = i / kTile;
-    return tile * 2 * kTile + (int64_t)s * kTile + (i - tile * kTile);
+    return tile * kPairTile + (int64_t)s * 3 * kTile + (i - tile * kTile);
 }
 
 // Element j (0..7) of the thread's group: run a for j < 4, run b otherwise.
@@ -1353,6 +1358,18 @@ int check_state(const zero_state* s, const char* what) {
     return ZERO_OK;
 }
 
+// A paired state: one buffer, with m and v at one and two ZERO_TILE past it.
+int check_pair(const zero_state* s, const char* what) {
+    if (s == nullptr || s->master == nullptr)
+        return fail(ZERO_EINVAL, "%s: null paired state", what);
+    if (!aligned16(s->master))
+        return fail(ZERO_EALIGN, "%s: paired state not 16-byte aligned", what);
+    if (s->m != s->master + kTile || s->v != s->master + 2 * kTile)
+        return fail(ZERO_EINVAL, "%s: a paired state is one buffer with m = master + ZERO_TILE and "
+                    "v = master + 2 * ZERO_TILE", what);
+    return ZERO_OK;
+}
+
 int check_ws(const void* ws, size_t ws_bytes, int64_t len) {
     const size_t need = zero_workspace_bytes(len);
     if (ws == nullptr) return fail(ZERO_EINVAL, "workspace pointer is null");
@@ -1507,7 +1524,7 @@ QGatherOut at(QGatherOut q, int64_t b0, int bits) {
 template <class SRC>
 FusedArgs<SRC> at(FusedArgs<SRC> a, int64_t b0, int64_t len) {
     a.src = at(a.src, b0);
-    for (int q = 0; q < 3; ++q) a.pair[q] += 2 * b0;
+    for (int q = 0; q < 3; ++q) a.pair[q] += b0 / kTile * kPairTile;
     if (a.slot != nullptr) a.slot += b0;
     a.len = len;
     a.ws += b0 / kTile;
@@ -1563,7 +1580,7 @@ int fused_launch(const SRC& src, int32_t nranks, const zero_state* pair, int64_t
                  void* gather, int32_t gather_dtype, int64_t offset, const zero_hparams* hp,
                  const zero_ctrl* ctrl, void* ws, size_t ws_bytes, void* stream, const char* what) {
     int rc;
-    if ((rc = check_state(pair, what)) != ZERO_OK) return rc;
+    if ((rc = check_pair(pair, what)) != ZERO_OK) return rc;
     if ((rc = check_hp(hp)) != ZERO_OK) return rc;
     if (hp->max_grad_norm > 0.0f) return fail(ZERO_EINVAL, "%s: clipping needs the two-pass path", what);
     if ((rc = check_ctrl(ctrl, what)) != ZERO_OK) return rc;
@@ -1693,7 +1710,7 @@ size_t zero_workspace_bytes(int64_t valid_len) {
 }
 
 size_t zero_pair_elems(int64_t valid_len) {
-    return (size_t)(2 * tiles_for(valid_len) * kTile);
+    return (size_t)(tiles_for(valid_len) * kPairTile);
 }
 
 int zero_ctrl_init(zero_ctrl* ctrl, float loss_scale, void* stream) {
@@ -1948,7 +1965,7 @@ int zero_fused_restore(const zero_state* pair, int64_t valid_len, void* gather, 
                        int64_t offset, const zero_ctrl* ctrl, void* stream) {
     int rc;
     if ((rc = check_len(valid_len, "zero_fused_restore")) != ZERO_OK) return rc;
-    if ((rc = check_state(pair, "zero_fused_restore")) != ZERO_OK) return rc;
+    if ((rc = check_pair(pair, "zero_fused_restore")) != ZERO_OK) return rc;
     if ((rc = check_ctrl(ctrl, "zero_fused_restore")) != ZERO_OK) return rc;
     if ((rc = check_slot(gather, dtype, offset)) != ZERO_OK) return rc;
     if (valid_len == 0) return ok();
@@ -1973,7 +1990,7 @@ int zero_fused_step_qgather(const void* contrib, int32_t contrib_dtype, int32_t 
     int rc;
     const char* what = "zero_fused_step_qgather";
     if ((rc = check_contrib(contrib, contrib_dtype, nranks, stride, valid_len)) != ZERO_OK) return rc;
-    if ((rc = check_state(pair, what)) != ZERO_OK) return rc;
+    if ((rc = check_pair(pair, what)) != ZERO_OK) return rc;
     if ((rc = check_hp(hp)) != ZERO_OK) return rc;
     if (hp->max_grad_norm > 0.0f) return fail(ZERO_EINVAL, "%s: clipping needs the two-pass path", what);
     if ((rc = check_ctrl(ctrl, what)) != ZERO_OK) return rc;
@@ -1995,7 +2012,7 @@ int zero_fused_restore_q(const zero_state* pair, int64_t valid_len, void* gather
     int rc;
     const char* what = "zero_fused_restore_q";
     if ((rc = check_len(valid_len, what)) != ZERO_OK) return rc;
-    if ((rc = check_state(pair, what)) != ZERO_OK) return rc;
+    if ((rc = check_pair(pair, what)) != ZERO_OK) return rc;
     if ((rc = check_ctrl(ctrl, what)) != ZERO_OK) return rc;
     if ((rc = check_opt_slot(gather, dtype, offset)) != ZERO_OK) return rc;
     if ((rc = check_qout(bits, codes, blocks, what)) != ZERO_OK) return rc;
@@ -2017,7 +2034,7 @@ static int pair_copy(const zero_state* flat, const zero_state* pair, int64_t val
     int rc;
     if ((rc = check_len(valid_len, what)) != ZERO_OK) return rc;
     if ((rc = check_state(flat, what)) != ZERO_OK) return rc;
-    if ((rc = check_state(pair, what)) != ZERO_OK) return rc;
+    if ((rc = check_pair(pair, what)) != ZERO_OK) return rc;
     if ((rc = check_ctrl(ctrl, what)) != ZERO_OK) return rc;
     if (valid_len == 0) return ok();
     PackArgs a{{flat->master, flat->m, flat->v}, {pair->master, pair->m, pair->v}, valid_len, ctrl};
