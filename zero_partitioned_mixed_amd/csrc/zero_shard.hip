@@ -70,9 +70,12 @@ constexpr int64_t kChunkTiles = ZERO_LAUNCH_TILES;  // most tiles per launch of 
 //   passes that also quantise the all-gather payload wait at one more
 //     workgroup barrier per tile: three per CU; the 13B step 10.9 ms against
 //     11.2 without a reservation and 11.5 at two;
-//   passes over quantised contributions load each row's block record through
-//     the scalar cache: no reservation; INT8 rows 9.28 ms against 9.34 at
-//     three and 9.55 at two, their reduce 6.05 against 6.21 at three.
+//   fused step over quantised contributions: two per CU; INT8 rows 9.41 ms
+//     against 9.63 at three and 9.78 without a reservation, INT4 rows 8.26
+//     against 8.37 and 8.50;
+//   reduce over quantised contributions, which loads each row's block record
+//     through the scalar cache and touches no paired state: no reservation;
+//     the 7B step over INT8 rows 6.05 ms against 6.21 at three.
 constexpr unsigned kLdsTwoPerCu = 64 * 1024;    // more than a third, at most half
 constexpr unsigned kLdsThreePerCu = 48 * 1024;  // more than a quarter, at most a third
 constexpr unsigned kResidencyLds = kLdsTwoPerCu;     // fused (16-bit rows) and Adam passes
@@ -1476,7 +1479,7 @@ struct Residency {
 };
 template <int BITS>
 struct Residency<SrcQ<BITS>> {
-    static constexpr unsigned fused = 0;
+    static constexpr unsigned fused = kLdsTwoPerCu;
     static constexpr unsigned reduce = 0;
 };
 
