@@ -411,8 +411,9 @@ class ShardStep:
     rank's slot at ``offset``.  ``state`` is the flat
     (master, m, v) fp32 state of valid_len elements.  The two-pass path
     (clipping on) updates it in place through ``g``; the fused path keeps
-    its double-buffered copy in ``pair`` (allocated here, loaded from
-    ``state``) and ``current()`` copies the current set back out.
+    its double-buffered copy in ``pair`` (one interleaved buffer allocated
+    here by paired_state(), loaded from ``state``) and ``current()`` copies
+    the current set back out.
 
     ``bucket`` (a multiple of TILE elements; 0 for none): the shard's gradient
     arrives in consecutive pieces of that many elements, and each piece is
