@@ -312,9 +312,6 @@ def main():
         return
 
     w = workloads.BY_NAME[args.workload]
-    if args.qgather and (args.rows or args.quant):
-        print("--qgather takes [N, stride] 16-bit contributions only", file=sys.stderr)
-        sys.exit(2)
     bucket = args.bucket // Z.TILE * Z.TILE
     if args.bucket and not bucket:
         print("--bucket must be at least 2048 elements", file=sys.stderr)
@@ -334,8 +331,10 @@ def main():
     kern_avg = sum(kern_ms) / len(kern_ms)
     if b["fused"]:
         kern_name = ("fused_kernel_q%d" % args.quant if args.quant else
-                     "fused_qgather_kernel_q%d" % args.qgather if args.qgather else
                      "fused_kernel_rows" if args.rows else "fused_kernel")
+        if args.qgather:
+            kern_name = ("fused_qgather_kernel_q%d" % args.qgather if kern_name == "fused_kernel"
+                         else "%s_qgather%d" % (kern_name, args.qgather))
         kern_bytes = step_bytes
     elif args.qgather:
         kern_name = "adam_qgather_kernel_q%d" % args.qgather

@@ -437,7 +437,33 @@ int zero_fused_step_qgather(const void *contrib_dev, int32_t contrib_dtype, int3
                             const zero_ctrl *ctrl_dev, void *ws_dev, size_t ws_bytes,
                             void *stream);
 
-/* After a zero_fused_step_qgather's zero_grad_norm_overflow: if ctrl->skip,
+/* zero_fused_step_qgather with the contribution rows given as a table of row
+ * pointers (rows_dev as in zero_reduce_grads_rows, nranks <= ZERO_MAX_RANKS).
+ * Bit-identical to zero_fused_step_qgather on the same rows. */
+int zero_fused_step_rows_qgather(const void *const *rows_dev, int32_t contrib_dtype,
+                                 int32_t nranks, const zero_state *pair, int64_t valid_len,
+                                 void *gather_dev, int32_t gather_dtype, int64_t offset,
+                                 int32_t bits, void *codes_dev, zero_qblock *blocks_dev,
+                                 const zero_hparams *hp, const zero_ctrl *ctrl_dev, void *ws_dev,
+                                 size_t ws_bytes, void *stream);
+
+/* zero_fused_step_qgather over quantised contributions (qcodes_dev,
+ * qblocks_dev and qbits as codes_dev, blocks_dev and bits of
+ * zero_reduce_grads_q): ZeRO++ end to end in one pass, with the gradient
+ * reduce-scatter arriving as INT8 or INT4 blocks and the parameters leaving
+ * as the bits-bit all-gather payload (codes_dev, blocks_dev).  The two widths
+ * are independent.  Other arguments and errors as in zero_fused_step_q and
+ * zero_fused_step_qgather. */
+int zero_fused_step_q_qgather(const void *const *qcodes_dev, const zero_qblock *const *qblocks_dev,
+                              int32_t qbits, int32_t nranks, const zero_state *pair,
+                              int64_t valid_len, void *gather_dev, int32_t gather_dtype,
+                              int64_t offset, int32_t bits, void *codes_dev,
+                              zero_qblock *blocks_dev, const zero_hparams *hp,
+                              const zero_ctrl *ctrl_dev, void *ws_dev, size_t ws_bytes,
+                              void *stream);
+
+/* After a zero_fused_step_qgather's (or its _rows/_q form's)
+ * zero_grad_norm_overflow: if ctrl->skip,
  * rewrite the slot (when gather_dev is not NULL) and the payload from the
  * current master of the paired state, as the step would have written them;
  * otherwise every workgroup returns at once. */

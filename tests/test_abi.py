@@ -241,15 +241,25 @@ def test_quant_rows_validation(Z, fused, codes, blocks, kw, code, msg):
     assert msg in Z.zero_last_error()
 
 
-def _qg_call(Z, contrib_dtype=1, valid=64, gather=FAKE, gdt=1, bits=8, codes=FAKE, blocks=FAKE,
-             clip=0.0, wsb=1 << 16, ctrl=FAKE):
+def _qg_call(Z, form="strided", contrib_dtype=1, valid=64, gather=FAKE, gdt=1, bits=8,
+             codes=FAKE, blocks=FAKE, clip=0.0, wsb=1 << 16, ctrl=FAKE, table=None, qbits=8):
     pair = _pair(Z)
     hp = Z.hparams(max_grad_norm=clip)
-    return Z._lib.zero_fused_step_qgather(FAKE, contrib_dtype, 8, 64, ctypes.byref(pair), valid,
-                                          gather, gdt, 0, bits, codes, blocks, ctypes.byref(hp),
-                                          ctrl, FAKE, wsb, None)
+    tail = (gather, gdt, 0, bits, codes, blocks, ctypes.byref(hp), ctrl, FAKE, wsb, None)
+    if form == "strided":
+        return Z._lib.zero_fused_step_qgather(FAKE, contrib_dtype, 8, 64, ctypes.byref(pair),
+                                              valid, *tail)
+    rows = [FAKE] * 4 if table is None else table
+    arr = (ctypes.c_void_p * max(len(rows), 1))(*rows)
+    if form == "rows":
+        return Z._lib.zero_fused_step_rows_qgather(arr, contrib_dtype, len(rows),
+                                                   ctypes.byref(pair), valid, *tail)
+    blk = (ctypes.c_void_p * max(len(rows), 1))(*([FAKE] * len(rows)))
+    return Z._lib.zero_fused_step_q_qgather(arr, blk, qbits, len(rows), ctypes.byref(pair), valid,
+                                            *tail)
 
 
+@pytest.mark.parametrize("form", ["strided", "rows", "q"])
 @pytest.mark.parametrize("kw,code,msg", [
     (dict(bits=3), -1, "bits"),
     (dict(bits=16), -1, "bits"),
@@ -268,8 +278,25 @@ def _qg_call(Z, contrib_dtype=1, valid=64, gather=FAKE, gdt=1, bits=8, codes=FAK
     # a NULL gather is accepted: validation runs on to the workspace check
     (dict(gather=None, wsb=16), -4, "workspace"),
 ])
-def test_fused_qgather_validation(Z, kw, code, msg):
-    assert _qg_call(Z, **kw) == code
+def test_fused_qgather_validation(Z, form, kw, code, msg):
+    if form == "q" and "contrib_dtype" in kw:
+        pytest.skip("quantised contributions carry no 16-bit dtype")
+    assert _qg_call(Z, form, **kw) == code
+    assert msg in Z.zero_last_error()
+
+
+@pytest.mark.parametrize("form,kw,code,msg", [
+    ("rows", dict(table=[FAKE, 0, FAKE]), -1, "row 1 is null"),
+    ("rows", dict(table=[FAKE, FAKE + 4]), -2, "row 1 not 8-byte"),
+    ("rows", dict(table=[FAKE] * 65), -1, "outside"),
+    ("q", dict(qbits=2), -1, "bits"),
+    ("q", dict(table=[FAKE, FAKE + 4]), -2, "row 1 not 8-byte"),
+    ("q", dict(table=[0, FAKE]), -1, "row 0 is null"),
+])
+def test_fused_qgather_source_validation(Z, form, kw, code, msg):
+    """The row-table and quantised-row forms check their source as the
+    corresponding plain fused calls do."""
+    assert _qg_call(Z, form, **kw) == code
     assert msg in Z.zero_last_error()
 
 

@@ -58,6 +58,11 @@ CASES = {
     "fused_row_table": (Case(two_chunk(steps=2), 1, 2), 0, True, "rows"),
     "two_pass_row_table_shifted": (Case(two_chunk(dtype=BF16, max_grad_norm=0.5, steps=2), 1, 2),
                                    0, True, "rows_shifted"),
+    "fused_int8_contributions_int4_payload": (Case(two_chunk(steps=2), 1, 2, qbits=8), 4, True,
+                                              "strided"),
+    "fused_row_table_int8_payload_skip": (Case(two_chunk(**DYN), 1, 3,
+                                               extra=(Inject(2, 1, CHUNK + 5, np.inf),)), 8,
+                                          False, "rows"),
 }
 
 

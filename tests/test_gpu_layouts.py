@@ -218,6 +218,11 @@ BUCKETED = {
                                    2048 * 5, "strided", 4, False),
     "two_pass_int8_payload": (Case(_bsmall(100_003, 3, 2, max_grad_norm=0.02), 2, 3),
                               2048, "strided", 8, True),
+    "fused_int4_rows_int8_payload": (Case(_bsmall(8 * 50_001, 8, 6, steps=4, **DYN), 6, 4,
+                                          qbits=4, extra=(Inject(2, 5, 2048 * 9 + 3, np.nan),)),
+                                     2048 * 6, "strided", 8, True),
+    "fused_row_table_int4_payload": (Case(_bsmall(8 * 50_001, 8, 7), 7, 3), 2048 * 7, "rows", 4,
+                                     False),
 }
 
 

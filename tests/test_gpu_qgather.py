@@ -1,5 +1,6 @@
 """GPU parity of the steps that also write the quantised all-gather payload
-of the new parameters (zero_fused_step_qgather with zero_fused_restore_q, and
+of the new parameters (zero_fused_step_qgather and its row-table and
+quantised-contribution forms, with zero_fused_restore_q; and
 zero_adam_step_qgather on the two-pass path).
 
 "CMU 11-868 L18", Other memory optimizations: ZeRO++ quantises the
@@ -78,6 +79,35 @@ def test_qgather_step_matches_oracle(name):
     w, bits, write_slot, extra = CASES[name]
     c = Case(w, w.ranks[0], w.steps, extra=tuple(extra))
     H.run_and_compare(c, name, qgather=bits, write_slot=write_slot)
+
+
+# ZeRO++ end to end: the contributions as a row table or as INT8/INT4 blocks,
+# the payload leaving the same pass.
+# name: (workload, contribution bits (0: 16-bit), layout, payload bits, slot, injections)
+SOURCES = {
+    "rows_f16_n8_q8": (small(200_000, 8, 3), 0, "rows", 8, True, ()),
+    "rows_shifted_bf16_n7_odd_offset_q4": (small(7 * 30_001, 7, 5, dtype=BF16), 0,
+                                           "rows_shifted", 4, True, ()),
+    "rows_f16_skip_no_slot_q8": (small(100_003, 3, 2, steps=4, **DYN), 0, "rows", 8, False,
+                                 (Inject(2, 1, 17_001, np.inf),)),
+    "q8_in_q8_out_f16_n8": (small(200_000, 8, 3), 8, "strided", 8, True, ()),
+    "q8_in_q4_out_bf16_n3_tail": (small(100_003, 3, 2, dtype=BF16), 8, "strided", 4, True, ()),
+    "q4_in_q8_out_f16_n7_odd_offset": (small(7 * 30_001, 7, 5), 4, "strided", 8, True, ()),
+    "q4_in_q4_out_no_slot_bf16_n64": (small(64 * 1_000 + 37, 64, 63, dtype=BF16), 4, "strided",
+                                      4, False, ()),
+    "q8_in_q8_out_skip_last": (small(100_003, 3, 2, steps=3, **DYN), 8, "strided", 8, True,
+                               (Inject(3, 0, 33_000, -np.inf),)),
+    "q8_in_q8_out_twopass_clip": (small(200_000, 8, 5, dtype=BF16, max_grad_norm=0.05), 8,
+                                  "strided", 8, True, ()),
+    "rows_twopass_clip_q4": (small(100_003, 3, 1, max_grad_norm=0.02), 0, "rows", 4, True, ()),
+}
+
+
+@pytest.mark.parametrize("name", list(SOURCES))
+def test_qgather_from_other_sources_matches_oracle(name):
+    w, qbits, layout, bits, write_slot, extra = SOURCES[name]
+    c = Case(w, w.ranks[0], w.steps, extra=tuple(extra), qbits=qbits)
+    H.run_and_compare(c, name, layout=layout, qgather=bits, write_slot=write_slot)
 
 
 @pytest.mark.parametrize("bits", [8, 4])

@@ -68,10 +68,7 @@ def draw(seed: int):
 def draw_options(seed: int, c: Case, layout: str):
     """(payload bits, write the 16-bit slot, bucket elements) for a case."""
     rng = np.random.default_rng(5000 + seed)
-    fused = c.w.max_grad_norm <= 0
     qgather = int(rng.choice([0, 0, 0, 8, 4]))
-    if fused and (c.qbits or layout != "strided"):
-        qgather = 0   # the fused payload step takes [N, stride] contributions
     write_slot = not qgather or bool(rng.random() < 0.5)
     bucket = int(rng.choice([0, 0, 0, 1, 2, 5])) * 2048
     return qgather, write_slot, bucket

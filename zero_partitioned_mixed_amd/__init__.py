@@ -113,6 +113,14 @@ _sig = {
                                                _vp, _i32, _i64, _i32, _vp, _vp,
                                                ctypes.POINTER(Hparams), _vp, _vp, ctypes.c_size_t,
                                                _vp]),
+    "zero_fused_step_rows_qgather": (ctypes.c_int, [ctypes.POINTER(_vp), _i32, _i32,
+                                                    ctypes.POINTER(State), _i64, _vp, _i32, _i64,
+                                                    _i32, _vp, _vp, ctypes.POINTER(Hparams), _vp,
+                                                    _vp, ctypes.c_size_t, _vp]),
+    "zero_fused_step_q_qgather": (ctypes.c_int, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32,
+                                                 _i32, ctypes.POINTER(State), _i64, _vp, _i32,
+                                                 _i64, _i32, _vp, _vp, ctypes.POINTER(Hparams),
+                                                 _vp, _vp, ctypes.c_size_t, _vp]),
     "zero_fused_restore_q": (ctypes.c_int, [ctypes.POINTER(State), _i64, _vp, _i32, _i64, _i32, _vp,
                                             _vp, _vp, _vp]),
     "zero_adam_step_qgather": (ctypes.c_int, [ctypes.POINTER(State), _vp, _i64,
@@ -375,6 +383,27 @@ def zero_fused_step_qgather(contrib, contrib_dtype: int, nranks: int, stride: in
         _ptr(ws), ws.numel() * ws.element_size(), _stream()))
 
 
+def zero_fused_step_rows_qgather(rows, contrib_dtype: int, pair, valid_len: int, gather,
+                                 gather_dtype: int, offset: int, q: QGather, hp: Hparams, ctrl,
+                                 ws) -> None:
+    arr, n = _rows(rows)
+    st = _state(pair)
+    _check("zero_fused_step_rows_qgather", _lib.zero_fused_step_rows_qgather(
+        arr, contrib_dtype, n, ctypes.byref(st), valid_len, _ptr(gather), gather_dtype, offset,
+        q.bits, _ptr(q.codes), _ptr(q.blocks), ctypes.byref(hp), _ptr(ctrl), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream()))
+
+
+def zero_fused_step_q_qgather(qr: QuantRows, pair, valid_len: int, gather, gather_dtype: int,
+                              offset: int, q: QGather, hp: Hparams, ctrl, ws) -> None:
+    c, b, n = qr.tables()
+    st = _state(pair)
+    _check("zero_fused_step_q_qgather", _lib.zero_fused_step_q_qgather(
+        c, b, qr.bits, n, ctypes.byref(st), valid_len, _ptr(gather), gather_dtype, offset, q.bits,
+        _ptr(q.codes), _ptr(q.blocks), ctypes.byref(hp), _ptr(ctrl), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream()))
+
+
 def zero_fused_restore_q(pair, valid_len: int, gather, dtype: int, offset: int, q: QGather,
                          ctrl) -> None:
     st = _state(pair)
@@ -461,8 +490,7 @@ class ShardStep:
     def step(self, contrib, gather, qgather: QGather = None) -> None:
         """One step.  With ``qgather`` the step also writes the quantised
         all-gather payload of the new parameters, and ``gather`` may be None
-        (no 16-bit slot written); the fused path then takes [N, stride]
-        contributions only."""
+        (no 16-bit slot written)."""
         self.run_pieces(contrib, gather, qgather)
         self.decide()
         self.complete(gather, qgather)
@@ -474,9 +502,6 @@ class ShardStep:
         table = isinstance(contrib, (list, tuple))
         if (table and len(contrib) != self.nranks) or (quant and len(contrib.rows) != self.nranks):
             raise ValueError(f"contribution rows do not match {self.nranks} ranks")
-        if qgather is not None and self.fused and (quant or table):
-            raise ValueError("the fused step with a quantised all-gather payload takes "
-                             "[N, stride] contributions")
         hp, ctrl = self.hp, self.ctrl
         pieces = self.pieces()
         for b0, ln in pieces:
@@ -487,7 +512,13 @@ class ShardStep:
                 off, q = self.offset + b0, None if qgather is None else qgather.at(b0)
             if self.fused:
                 pair = self.pair if b0 == 0 else tuple(_at(t, 4 * 6 * b0) for t in self.pair)
-                if q is not None:
+                if q is not None and quant:
+                    zero_fused_step_q_qgather(c, pair, ln, gather, self.gather_dtype, off, q, hp,
+                                              ctrl, ws)
+                elif q is not None and table:
+                    zero_fused_step_rows_qgather(c, self.dtype, pair, ln, gather,
+                                                 self.gather_dtype, off, q, hp, ctrl, ws)
+                elif q is not None:
                     zero_fused_step_qgather(c, self.dtype, self.nranks, self.stride, pair, ln,
                                             gather, self.gather_dtype, off, q, hp, ctrl, ws)
                 elif quant:

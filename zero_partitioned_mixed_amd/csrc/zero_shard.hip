@@ -1471,15 +1471,20 @@ int launch(Kernel<Args> kernel, int64_t grid, int block, hipStream_t s, const Ar
     return ok();
 }
 
-// LDS reserved per workgroup of the fused and reduce passes, by source.
+// LDS reserved per workgroup of the fused, fused-with-payload and reduce
+// passes, by source.  Over quantised rows the payload pass runs best with no
+// reservation (13B shard, INT4 rows: 8.14 against 8.43 ms at three per CU and
+// 9.52 ms at two; INT8 rows: equal at none and three per CU).
 template <class SRC>
 struct Residency {
     static constexpr unsigned fused = kLdsTwoPerCu;
+    static constexpr unsigned fused_q = kResidencyLdsQ;
     static constexpr unsigned reduce = kLdsThreePerCu;
 };
 template <int BITS>
 struct Residency<SrcQ<BITS>> {
     static constexpr unsigned fused = kLdsTwoPerCu;
+    static constexpr unsigned fused_q = 0;
     static constexpr unsigned reduce = 0;
 };
 
@@ -1655,34 +1660,44 @@ int check_opt_slot(const void* gather, int32_t dtype, int64_t offset) {
     return ZERO_OK;
 }
 
-template <int DT, int BITS>
-Kernel<FusedQArgs<Src16<DT, StridedRows>>> fused_qgather_bits(int dto, int n) {
-    using S = Src16<DT, StridedRows>;
+template <class SRC, int BITS>
+Kernel<FusedQArgs<SRC>> fused_qgather_bits(int dto, int n) {
     if (n == 8)
-        return dto == ZERO_F16 ? fused_qgather_kernel<ZERO_F16, 8, S, BITS>
-                               : fused_qgather_kernel<ZERO_BF16, 8, S, BITS>;
-    return dto == ZERO_F16 ? fused_qgather_kernel<ZERO_F16, 0, S, BITS>
-                           : fused_qgather_kernel<ZERO_BF16, 0, S, BITS>;
+        return dto == ZERO_F16 ? fused_qgather_kernel<ZERO_F16, 8, SRC, BITS>
+                               : fused_qgather_kernel<ZERO_BF16, 8, SRC, BITS>;
+    return dto == ZERO_F16 ? fused_qgather_kernel<ZERO_F16, 0, SRC, BITS>
+                           : fused_qgather_kernel<ZERO_BF16, 0, SRC, BITS>;
 }
 
-template <int DT>
-int fused_qgather_launch(const StridedRows& rows, int32_t nranks, const zero_state* pair,
-                         int64_t valid_len, void* gather, int32_t gather_dtype, int64_t offset,
-                         int32_t bits, void* codes, zero_qblock* blocks, const zero_hparams* hp,
-                         const zero_ctrl* ctrl, void* ws, void* stream, const char* what) {
+// Checks and launch shared by the fused entry points that also write the
+// quantised all-gather payload (the contribution source is already checked).
+template <class SRC>
+int fused_qgather_launch(const SRC& src, int32_t nranks, const zero_state* pair, int64_t valid_len,
+                         void* gather, int32_t gather_dtype, int64_t offset, int32_t bits,
+                         void* codes, zero_qblock* blocks, const zero_hparams* hp,
+                         const zero_ctrl* ctrl, void* ws, size_t ws_bytes, void* stream,
+                         const char* what) {
+    int rc;
+    if ((rc = check_pair(pair, what)) != ZERO_OK) return rc;
+    if ((rc = check_hp(hp)) != ZERO_OK) return rc;
+    if (hp->max_grad_norm > 0.0f) return fail(ZERO_EINVAL, "%s: clipping needs the two-pass path", what);
+    if ((rc = check_ctrl(ctrl, what)) != ZERO_OK) return rc;
+    if ((rc = check_opt_slot(gather, gather_dtype, offset)) != ZERO_OK) return rc;
+    if ((rc = check_qout(bits, codes, blocks, what)) != ZERO_OK) return rc;
+    if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
+    if (valid_len == 0) return ok();
     uint16_t* slot = gather == nullptr ? nullptr : (uint16_t*)gather + offset;
-    const FusedQArgs<Src16<DT, StridedRows>> a{
-        {Src16<DT, StridedRows>{rows}, {pair->master, pair->m, pair->v}, slot, valid_len, ctrl,
-         (Partial*)ws, *hp, nranks},
-        {(uint8_t*)codes, blocks, slot == nullptr ? 0 : store_width(slot)}};
-    const auto k = bits == 8 ? fused_qgather_bits<DT, 8>(gather_dtype, nranks)
-                             : fused_qgather_bits<DT, 4>(gather_dtype, nranks);
-    using A = FusedQArgs<Src16<DT, StridedRows>>;
+    using A = FusedQArgs<SRC>;
+    const A a{{src, {pair->master, pair->m, pair->v}, slot, valid_len, ctrl, (Partial*)ws, *hp,
+               nranks},
+              {(uint8_t*)codes, blocks, slot == nullptr ? 0 : store_width(slot)}};
+    const Kernel<A> k = bits == 8 ? fused_qgather_bits<SRC, 8>(gather_dtype, nranks)
+                                  : fused_qgather_bits<SRC, 4>(gather_dtype, nranks);
     return launch_chunked(k, a, valid_len, (hipStream_t)stream, what,
                           [bits](const A& x, int64_t b0, int64_t n) {
                               return A{at(x.f, b0, n), at(x.q, b0, bits)};
                           },
-                          kResidencyLdsQ);
+                          Residency<SRC>::fused_q);
 }
 
 }  // namespace
@@ -1993,20 +2008,49 @@ int zero_fused_step_qgather(const void* contrib, int32_t contrib_dtype, int32_t 
     int rc;
     const char* what = "zero_fused_step_qgather";
     if ((rc = check_contrib(contrib, contrib_dtype, nranks, stride, valid_len)) != ZERO_OK) return rc;
-    if ((rc = check_pair(pair, what)) != ZERO_OK) return rc;
-    if ((rc = check_hp(hp)) != ZERO_OK) return rc;
-    if (hp->max_grad_norm > 0.0f) return fail(ZERO_EINVAL, "%s: clipping needs the two-pass path", what);
-    if ((rc = check_ctrl(ctrl, what)) != ZERO_OK) return rc;
-    if ((rc = check_opt_slot(gather, gather_dtype, offset)) != ZERO_OK) return rc;
-    if ((rc = check_qout(bits, codes, blocks, what)) != ZERO_OK) return rc;
-    if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
-    if (valid_len == 0) return ok();
     const StridedRows rows{(const uint16_t*)contrib, stride};
     return contrib_dtype == ZERO_F16
-               ? fused_qgather_launch<ZERO_F16>(rows, nranks, pair, valid_len, gather, gather_dtype,
-                                                offset, bits, codes, blocks, hp, ctrl, ws, stream, what)
-               : fused_qgather_launch<ZERO_BF16>(rows, nranks, pair, valid_len, gather, gather_dtype,
-                                                 offset, bits, codes, blocks, hp, ctrl, ws, stream, what);
+               ? fused_qgather_launch(Src16<ZERO_F16, StridedRows>{rows}, nranks, pair, valid_len,
+                                      gather, gather_dtype, offset, bits, codes, blocks, hp, ctrl,
+                                      ws, ws_bytes, stream, what)
+               : fused_qgather_launch(Src16<ZERO_BF16, StridedRows>{rows}, nranks, pair, valid_len,
+                                      gather, gather_dtype, offset, bits, codes, blocks, hp, ctrl,
+                                      ws, ws_bytes, stream, what);
+}
+
+int zero_fused_step_rows_qgather(const void* const* rows, int32_t contrib_dtype, int32_t nranks,
+                                 const zero_state* pair, int64_t valid_len, void* gather,
+                                 int32_t gather_dtype, int64_t offset, int32_t bits, void* codes,
+                                 zero_qblock* blocks, const zero_hparams* hp,
+                                 const zero_ctrl* ctrl, void* ws, size_t ws_bytes, void* stream) {
+    int rc;
+    const char* what = "zero_fused_step_rows_qgather";
+    TableRows t;
+    if ((rc = check_rows(rows, contrib_dtype, nranks, valid_len, &t, what)) != ZERO_OK) return rc;
+    return contrib_dtype == ZERO_F16
+               ? fused_qgather_launch(Src16<ZERO_F16, TableRows>{t}, nranks, pair, valid_len, gather,
+                                      gather_dtype, offset, bits, codes, blocks, hp, ctrl, ws,
+                                      ws_bytes, stream, what)
+               : fused_qgather_launch(Src16<ZERO_BF16, TableRows>{t}, nranks, pair, valid_len,
+                                      gather, gather_dtype, offset, bits, codes, blocks, hp, ctrl,
+                                      ws, ws_bytes, stream, what);
+}
+
+int zero_fused_step_q_qgather(const void* const* qcodes, const zero_qblock* const* qblocks,
+                              int32_t qbits, int32_t nranks, const zero_state* pair,
+                              int64_t valid_len, void* gather, int32_t gather_dtype, int64_t offset,
+                              int32_t bits, void* codes, zero_qblock* blocks, const zero_hparams* hp,
+                              const zero_ctrl* ctrl, void* ws, size_t ws_bytes, void* stream) {
+    int rc;
+    const char* what = "zero_fused_step_q_qgather";
+    QTable t;
+    if ((rc = check_qrows(qcodes, qblocks, qbits, nranks, valid_len, &t, what)) != ZERO_OK) return rc;
+    return qbits == 8 ? fused_qgather_launch(SrcQ<8>{t}, nranks, pair, valid_len, gather,
+                                             gather_dtype, offset, bits, codes, blocks, hp, ctrl, ws,
+                                             ws_bytes, stream, what)
+                      : fused_qgather_launch(SrcQ<4>{t}, nranks, pair, valid_len, gather,
+                                             gather_dtype, offset, bits, codes, blocks, hp, ctrl, ws,
+                                             ws_bytes, stream, what);
 }
 
 int zero_fused_restore_q(const zero_state* pair, int64_t valid_len, void* gather, int32_t dtype,
