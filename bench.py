@@ -319,6 +319,7 @@ def main():
     b = setup(w, torch, synth, Z, rows=args.rows, qbits=args.quant, bucket=bucket)
     b_pieces = b["step"].pieces()
     pieces = len(b_pieces)
+    row_pass_n = w.nranks if b["fused"] else 0  # the timed pass reads the N rows (fused) or not
     valid = b["valid"]
     qg = Z.QGather.alloc(valid, args.qgather, torch.device("cuda", 0)) if args.qgather else None
     ms_step, per_step, kern_ms, red_ms, ctrl = timed_steps(b, args.steps, args.warmup, torch, Z,
@@ -378,7 +379,7 @@ def main():
                      "frac": _fmt(kern_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None,
                      "kernel_ms": _fmt(kern_avg, 5), "bytes_per_pass": kern_bytes,
-                     "launches_per_pass": sum(Z.launches(n) for _, n in b_pieces)},
+                     "launches_per_pass": sum(Z.launches(n, row_pass_n) for _, n in b_pieces)},
         "last_step": {"norm": ctrl["norm"], "skip": ctrl["skip"], "t": ctrl["t"],
                       "loss_scale": ctrl["loss_scale"]},
     }

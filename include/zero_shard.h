@@ -137,11 +137,16 @@ typedef struct zero_ctrl {
  * double-buffered state interleaves its two sets tile by tile. */
 #define ZERO_TILE 2048
 
-/* Most tiles per kernel launch: a streaming pass (reduce, fused step, Adam)
- * over valid_len elements is issued as ceil(ceil(valid_len / ZERO_TILE) /
- * ZERO_LAUNCH_TILES) consecutive launches on the caller's stream, which a
- * profiler lists one by one.  The results are those of one launch. */
+/* Launch sizes: a streaming pass (reduce, fused step, Adam) over valid_len
+ * elements is issued as ceil(ceil(valid_len / ZERO_TILE) / T) consecutive
+ * launches of at most T tiles on the caller's stream, which a profiler lists
+ * one by one; the results are those of one launch.  T = ZERO_LAUNCH_TILES
+ * for the Adam passes; for a pass that reads N contribution rows (reduce and
+ * fused step, every source) T = ZERO_LAUNCH_ROW_TILES / N, clamped to
+ * [ZERO_LAUNCH_MIN_TILES, ZERO_LAUNCH_TILES] (zero_launch_tiles). */
 #define ZERO_LAUNCH_TILES 16384
+#define ZERO_LAUNCH_ROW_TILES 131072
+#define ZERO_LAUNCH_MIN_TILES 2048
 
 /* One rank's fp32 optimizer state: master weights, Adam m, Adam v.
  * Flat form (two-pass path, pack/unpack): three arrays of valid_len
@@ -206,6 +211,10 @@ size_t zero_ctrl_bytes(void);
  * for the second level of the reduction (about 0.8% of the shard's fp16
  * size). */
 size_t zero_workspace_bytes(int64_t valid_len);
+
+/* Most tiles per launch T of a pass that reads nranks contribution rows, as
+ * defined with ZERO_LAUNCH_TILES; nranks <= 0 gives the Adam passes' T. */
+int64_t zero_launch_tiles(int32_t nranks);
 
 /* Floats of the one buffer of a paired (fused-path) state for valid_len
  * elements: 6 * ceil(valid_len / ZERO_TILE) * ZERO_TILE. */

@@ -30,7 +30,6 @@ def gpu():
 
 
 _REPS = {}  # the oracle's per-step decisions, per workload (shared by the layouts)
-CHUNK = 16384 * 2048  # elements per launch of a streaming pass in the library
 
 
 def run_fullsize(w, layout="strided", qbits=0, steps=None, samples=65_536, qgather=0):
@@ -54,8 +53,11 @@ def run_fullsize(w, layout="strided", qbits=0, steps=None, samples=65_536, qgath
     stats = H.assert_reports(g.reports, reps)
     H.log(f"{w.name}: scalars ok {stats}; skips {[r['skip'] for r in reps]}")
     extra = [i.col + d for i in c.injections for d in (-1, 0, 1)]
-    # both sides of every boundary between the library's launches of 2^25 elements
-    extra += [b + d for b in range(CHUNK, valid, CHUNK) for d in (-2049, -1, 0, 1, 2048)]
+    # both sides of every boundary between the library's launches: of the pass
+    # over the N rows and of the Adam pass (two-pass path)
+    import zero_partitioned_mixed_amd as Z
+    for chunk in {Z.launch_tiles(w.nranks) * Z.TILE, Z.launch_tiles(0) * Z.TILE}:
+        extra += [b + d for b in range(chunk, valid, chunk) for d in (-2049, -1, 0, 1, 2048)]
     cols = H.sample_cols(valid, samples, seed=11, extra=extra)
     p, m, v, slot = g.fetch(cols)
     rp, rm, rv, rslot = H.oracle_elements(c, reps, cols)

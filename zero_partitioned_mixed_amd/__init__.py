@@ -57,13 +57,23 @@ TILE = 2048  # ZERO_TILE
 QBLOCK = 2048  # ZERO_QBLOCK
 PARTIAL_BYTES = 16  # ZERO_PARTIAL_BYTES
 LAUNCH_TILES = 16384  # ZERO_LAUNCH_TILES
+LAUNCH_ROW_TILES = 131072  # ZERO_LAUNCH_ROW_TILES
+LAUNCH_MIN_TILES = 2048  # ZERO_LAUNCH_MIN_TILES
 
 
-def launches(valid_len: int) -> int:
+def launch_tiles(nranks: int = 0) -> int:
+    """Most tiles per launch of a pass that reads nranks contribution rows
+    (0: the Adam passes); the library's zero_launch_tiles."""
+    if nranks <= 0:
+        return LAUNCH_TILES
+    return min(LAUNCH_TILES, max(LAUNCH_MIN_TILES, LAUNCH_ROW_TILES // nranks))
+
+
+def launches(valid_len: int, nranks: int = 0) -> int:
     """Kernel launches one call of a streaming pass over valid_len elements
-    is issued as."""
+    is issued as (nranks as in launch_tiles)."""
     tiles = -(-valid_len // TILE)
-    return -(-tiles // LAUNCH_TILES)
+    return -(-tiles // launch_tiles(nranks))
 
 
 class State(ctypes.Structure):
@@ -126,6 +136,7 @@ _sig = {
     "zero_adam_step_qgather": (ctypes.c_int, [ctypes.POINTER(State), _vp, _i64,
                                               ctypes.POINTER(Hparams), _vp, _vp, _i32, _i64, _i32,
                                               _vp, _vp, _vp]),
+    "zero_launch_tiles": (ctypes.c_int64, [_i32]),
     "zero_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _sig.items():

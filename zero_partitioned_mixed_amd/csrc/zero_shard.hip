@@ -4,11 +4,11 @@
 // operations against 26 + 2N bytes, so nothing is a contraction and nothing
 // uses the matrix cores.  The design points are
 //   * one workgroup per tile of ZERO_TILE = 2048 elements (4 wave64s x 64
-//     lanes x 8 elements), launched as full grids of at most 16,384 tiles,
-//     with few workgroups resident per CU (two or three, by pass), so that
-//     the set of tiles in flight stays compact (a grid-stride loop, one grid
-//     over a whole 13B shard and six or eight workgroups per CU all measured
-//     slower);
+//     lanes x 8 elements), launched as full grids of at most 16,384 tiles
+//     (2^17 / N over N > 8 contribution rows), with few workgroups resident
+//     per CU (two or three, by pass), so that the set of tiles in flight
+//     stays compact (a grid-stride loop, one grid over a whole 13B shard and
+//     six or eight workgroups per CU all measured slower);
 //   * wave-contiguous lanes: lane l of wave w owns two runs of four elements,
 //     [512w + 4l, +4) and 256 elements later, so every memory instruction of a
 //     wave covers one contiguous span and fills whole cache lines;
@@ -54,7 +54,6 @@ constexpr int kFinBlock = 1024;             // threads per finalize workgroup
 constexpr int kFinGroups = 256;             // most first-level groups of the finalize
 constexpr int64_t kFinPer = 16384;          // partials per first-level finalize group
 constexpr int kRestoreGrid = 256;           // workgroups of the (usually idle) restore pass
-constexpr int64_t kChunkTiles = ZERO_LAUNCH_TILES;  // most tiles per launch of a streaming pass
 // Workgroups resident per CU, set by the LDS each streaming workgroup reserves
 // (and leaves unused) out of a CU's 160 KB.  Each wave already has every
 // load of its group in flight, so few workgroups per CU still cover HBM
@@ -1489,13 +1488,26 @@ struct Residency<SrcQ<BITS>> {
 };
 
 // A streaming pass over a long shard is issued as consecutive launches of at
-// most kChunkTiles tiles, each with every per-element pointer advanced to its
-// first element (the same arithmetic as the bucket contract in the header, so
-// the results are those of one launch, bit for bit).  In one launch of
-// several hundred thousand workgroups the slowest ones fall further and
-// further behind and the set of tiles in flight spreads over more memory; a
-// new launch every 16,384 tiles keeps it compact (the 13B fused step: 1-5%
-// shorter, most on boxes where the buffers landed on slower memory).
+// most launch_tiles(N) tiles, each with every per-element pointer advanced to
+// its first element (the same arithmetic as the bucket contract in the
+// header, so the results are those of one launch, bit for bit).  In one launch
+// of many thousands of workgroups the slowest ones fall further and further
+// behind and the set of tiles in flight spreads over more memory; a new launch
+// every 16,384 tiles keeps it compact (the 13B fused step: 1-5% shorter, most
+// on boxes where the buffers landed on slower memory).  The memory that drift
+// spreads over grows with the rows each tile reads, so a pass over N rows
+// starts a new launch every 2^17 / N tiles: in one process, the best launch
+// size was 2,048 tiles at N = 64 (+7% against 16,384), 4,096 at N = 32
+// (+1.5%), flat from 8,192 up at N = 16, and 16,384-32,768 (within 1%) at
+// N <= 8.  Below 2,048 tiles the launches' fill and drain cost more than the
+// compact window gains.
+int64_t launch_tiles(int32_t nranks) {
+    if (nranks <= 0) return ZERO_LAUNCH_TILES;
+    const int64_t t = ZERO_LAUNCH_ROW_TILES / nranks;
+    return t > ZERO_LAUNCH_TILES ? ZERO_LAUNCH_TILES
+                                 : t < ZERO_LAUNCH_MIN_TILES ? ZERO_LAUNCH_MIN_TILES : t;
+}
+
 // at(x, b0): x advanced by b0 elements of the shard (b0 a multiple of kTile).
 StridedRows at(StridedRows r, int64_t b0) {
     r.base += b0;
@@ -1558,13 +1570,13 @@ AdamArgs at(AdamArgs a, int64_t b0, int64_t len) {
     return a;
 }
 
-// Launches kernel over len elements in chunks; at(args, b0, n) gives the
-// arguments of the chunk [b0, b0 + n).  A launch error stops the loop, with
-// the earlier chunks already enqueued.
+// Launches kernel over len elements in chunks of at most `tiles` tiles;
+// at(args, b0, n) gives the arguments of the chunk [b0, b0 + n).  A launch
+// error stops the loop, with the earlier chunks already enqueued.
 template <class Args, class At>
-int launch_chunked(Kernel<Args> kernel, const Args& args, int64_t len, hipStream_t s,
-                   const char* what, At&& at_chunk, unsigned lds = kResidencyLds) {
-    constexpr int64_t chunk = kChunkTiles * kTile;
+int launch_chunked(Kernel<Args> kernel, const Args& args, int64_t len, int64_t tiles,
+                   hipStream_t s, const char* what, At&& at_chunk, unsigned lds = kResidencyLds) {
+    const int64_t chunk = tiles * kTile;
     for (int64_t b0 = 0; b0 < len; b0 += chunk) {
         const int64_t n = len - b0 < chunk ? len - b0 : chunk;
         const int rc = launch(kernel, tiles_for(n), kBlock, s, at_chunk(args, b0, n), what, lds);
@@ -1574,11 +1586,11 @@ int launch_chunked(Kernel<Args> kernel, const Args& args, int64_t len, hipStream
 }
 
 template <class Args>
-int launch_chunked(Kernel<Args> kernel, const Args& args, int64_t len, hipStream_t s,
-                   const char* what, unsigned lds = kResidencyLds) {
+int launch_chunked(Kernel<Args> kernel, const Args& args, int64_t len, int64_t tiles,
+                   hipStream_t s, const char* what, unsigned lds = kResidencyLds) {
     return launch_chunked(
-        kernel, args, len, s, what, [](const Args& a, int64_t b0, int64_t n) { return at(a, b0, n); },
-        lds);
+        kernel, args, len, tiles, s, what,
+        [](const Args& a, int64_t b0, int64_t n) { return at(a, b0, n); }, lds);
 }
 
 // Checks and launches shared by the fused entry points (the contribution
@@ -1599,7 +1611,7 @@ int fused_launch(const SRC& src, int32_t nranks, const zero_state* pair, int64_t
     const FusedArgs<SRC> a{src, {pair->master, pair->m, pair->v}, slot, valid_len, ctrl,
                            (Partial*)ws, *hp, nranks};
     return launch_chunked(fused_for<SRC>(store_width(slot), gather_dtype, nranks), a, valid_len,
-                          (hipStream_t)stream, what, Residency<SRC>::fused);
+                          launch_tiles(nranks), (hipStream_t)stream, what, Residency<SRC>::fused);
 }
 
 // Checks and launch shared by the reduce entry points (source already checked).
@@ -1613,8 +1625,8 @@ int reduce_launch(const SRC& src, int32_t nranks, int64_t valid_len, const zero_
     if ((rc = check_ws(ws, ws_bytes, valid_len)) != ZERO_OK) return rc;
     if (valid_len == 0) return ok();
     const ReduceArgs<SRC> a{src, valid_len, ctrl, g, (Partial*)ws, nranks};
-    return launch_chunked(reduce_for<SRC>(nranks), a, valid_len, (hipStream_t)stream, what,
-                          Residency<SRC>::reduce);
+    return launch_chunked(reduce_for<SRC>(nranks), a, valid_len, launch_tiles(nranks),
+                          (hipStream_t)stream, what, Residency<SRC>::reduce);
 }
 
 // Quantised row tables: bits 8 or 4, nranks in [1, ZERO_MAX_RANKS], every
@@ -1693,7 +1705,7 @@ int fused_qgather_launch(const SRC& src, int32_t nranks, const zero_state* pair,
               {(uint8_t*)codes, blocks, slot == nullptr ? 0 : store_width(slot)}};
     const Kernel<A> k = bits == 8 ? fused_qgather_bits<SRC, 8>(gather_dtype, nranks)
                                   : fused_qgather_bits<SRC, 4>(gather_dtype, nranks);
-    return launch_chunked(k, a, valid_len, (hipStream_t)stream, what,
+    return launch_chunked(k, a, valid_len, launch_tiles(nranks), (hipStream_t)stream, what,
                           [bits](const A& x, int64_t b0, int64_t n) {
                               return A{at(x.f, b0, n), at(x.q, b0, bits)};
                           },
@@ -1726,6 +1738,8 @@ size_t zero_ctrl_bytes(void) { return sizeof(zero_ctrl); }
 size_t zero_workspace_bytes(int64_t valid_len) {
     return (size_t)(tiles_for(valid_len) + kFinGroups) * sizeof(Partial);
 }
+
+int64_t zero_launch_tiles(int32_t nranks) { return launch_tiles(nranks); }
 
 size_t zero_pair_elems(int64_t valid_len) {
     return (size_t)(tiles_for(valid_len) * kPairTile);
@@ -1833,7 +1847,8 @@ int zero_adam_step(const zero_state* state, const float* g, int64_t valid_len,
     AdamArgs a{state->master, state->m, state->v, g, slot, valid_len, ctrl, *hp};
     Kernel<AdamArgs> k = gather != nullptr && gather_dtype == ZERO_BF16 ? adam_for<ZERO_BF16>(gw)
                                                               : adam_for<ZERO_F16>(gw);
-    return launch_chunked(k, a, valid_len, (hipStream_t)stream, "zero_adam_step");
+    return launch_chunked(k, a, valid_len, launch_tiles(0), (hipStream_t)stream,
+                          "zero_adam_step");
 }
 
 int zero_adam_step_qgather(const zero_state* state, const float* g, int64_t valid_len,
@@ -1859,7 +1874,7 @@ int zero_adam_step_qgather(const zero_state* state, const float* g, int64_t vali
         k = bits == 8 ? adam_qgather_kernel<ZERO_F16, 8> : adam_qgather_kernel<ZERO_F16, 4>;
     else
         k = bits == 8 ? adam_qgather_kernel<ZERO_BF16, 8> : adam_qgather_kernel<ZERO_BF16, 4>;
-    return launch_chunked(k, a, valid_len, (hipStream_t)stream, what,
+    return launch_chunked(k, a, valid_len, launch_tiles(0), (hipStream_t)stream, what,
                           [bits](const AdamQArgs& x, int64_t b0, int64_t n) {
                               return AdamQArgs{at(x.a, b0, n), at(x.q, b0, bits)};
                           },
