@@ -144,6 +144,7 @@ def gpu():
     if _gpu is None:
         if not os.path.exists(_GPU_LIB):
             raise RuntimeError(f"{_GPU_LIB} is not built; run __graft_entry__.build()")
+        import torch  # noqa: F401  (its HIP runtime first: one runtime in the process)
         L = ctypes.CDLL(_GPU_LIB)
         u64, u32, i32, i64, f64, vp = (ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int32,
                                        ctypes.c_int64, ctypes.c_double, ctypes.c_void_p)

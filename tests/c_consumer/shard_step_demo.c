@@ -5,13 +5,15 @@
  *
  *   shard_step_demo host        partition, size queries and argument checks
  *                               (needs no GPU)
- *   shard_step_demo gpu FILE    runs four ranks' steps of a small workload on
+ *   shard_step_demo gpu FILE    runs five ranks' steps of a small workload on
  *                               the GPU and writes their results to FILE for
  *                               the test to compare with the oracle:
  *     rank 2, fused path, dynamic loss scale, +inf in contribution 1 at step 2
  *     rank 1, two-pass path, clipping at 0.01
  *     rank 0, fused path as rank 2, writing only the INT8 all-gather payload
  *     rank 2, two-pass path as rank 1, writing the slot and an INT4 payload
+ *     rank 1, fused path as rank 2 over INT8-quantised contributions, writing
+ *       only the INT8 payload (ZeRO++ end to end)
  *   all of Psi = 120,007 (fp16) over N = 3 ranks, 3 steps.
  */
 #include <hip/hip_runtime_api.h>
@@ -71,9 +73,11 @@ static int host_mode(void) {
 /* One rank's STEPS steps; appends ctrl after each step, then master, m, v
  * (valid floats each), the slot (valid 16-bit words) unless slot is 0, and
  * with qbits (8 or 4) the quantised all-gather payload: codes
- * (zero_qcode_bytes) and block records (zero_qblock_count of them). */
+ * (zero_qcode_bytes) and block records (zero_qblock_count of them).  With
+ * cbits (8 or 4, fused path only) each contribution row is block-quantised on
+ * the device (zero_quantize_blocks) and the step reads the quantised rows. */
 static void run_rank(FILE *f, int32_t rank, float max_grad_norm, int inject, int slot,
-                     int32_t qbits) {
+                     int32_t qbits, int32_t cbits) {
     int64_t shard, off, valid;
     ZERO(zero_partition(PSI, NR, rank, &shard, &off, &valid));
     const int64_t stride = (shard + 63) / 64 * 64;
@@ -113,6 +117,13 @@ static void run_rank(FILE *f, int32_t rank, float max_grad_norm, int inject, int
         HIP(hipMalloc(&dBlocks, nblk * sizeof(zero_qblock)));
     }
     void *slot_dev = slot ? dG : NULL; /* NULL: no 16-bit slot is written */
+    void *qc[NR] = {NULL}, *qb[NR] = {NULL}; /* quantised contribution rows */
+    if (cbits) {
+        for (int k = 0; k < NR; ++k) {
+            HIP(hipMalloc(&qc[k], zero_qcode_bytes(valid, cbits)));
+            HIP(hipMalloc(&qb[k], zero_qblock_count(valid) * sizeof(zero_qblock)));
+        }
+    }
 
     zero_state st_flat = {flat[0], flat[1], flat[2]}, st_pair = {pair[0], pair[1], pair[2]};
     ZERO(zero_ctrl_init(dCtrl, loss_scale, NULL));
@@ -124,7 +135,17 @@ static void run_rank(FILE *f, int32_t rank, float max_grad_norm, int inject, int
         void *ws_arr[1] = {dWs};
         int64_t len_arr[1] = {valid};
         zero_ctrl *ctrl_arr[1] = {dCtrl};
-        if (fused && qbits) {
+        if (cbits) {
+            for (int k = 0; k < NR; ++k)
+                ZERO(zero_quantize_blocks((uint16_t *)dC + k * stride, ZERO_F16, valid, cbits, qc[k],
+                                          (zero_qblock *)qb[k], NULL));
+            ZERO(zero_fused_step_q_qgather((const void *const *)qc, (const zero_qblock *const *)qb,
+                                           cbits, NR, &st_pair, valid, slot_dev, ZERO_F16, off,
+                                           qbits, dCodes, dBlocks, &hp, dCtrl, dWs, ws_bytes, NULL));
+            ZERO(zero_grad_norm_overflow(1, ws_arr, len_arr, ctrl_arr, &hp, 1, NULL));
+            ZERO(zero_fused_restore_q(&st_pair, valid, slot_dev, ZERO_F16, off, qbits, dCodes,
+                                      dBlocks, dCtrl, NULL));
+        } else if (fused && qbits) {
             ZERO(zero_fused_step_qgather(dC, ZERO_F16, NR, stride, &st_pair, valid, slot_dev,
                                          ZERO_F16, off, qbits, dCodes, dBlocks, &hp, dCtrl, dWs,
                                          ws_bytes, NULL));
@@ -172,6 +193,10 @@ static void run_rank(FILE *f, int32_t rank, float max_grad_norm, int inject, int
         HIP(hipFree(dCodes));
         HIP(hipFree(dBlocks));
     }
+    for (int k = 0; k < NR && cbits; ++k) {
+        HIP(hipFree(qc[k]));
+        HIP(hipFree(qb[k]));
+    }
     for (int q = 0; q < 3; ++q) HIP(hipFree(flat[q]));
     HIP(hipFree(pair_buf));
     HIP(hipFree(dC));
@@ -190,10 +215,11 @@ int main(int argc, char **argv) {
     if (argc >= 3 && strcmp(argv[1], "gpu") == 0) {
         FILE *f = fopen(argv[2], "wb");
         if (!f) return 2;
-        run_rank(f, 2, 0.0f, 1, 1, 0);
-        run_rank(f, 1, 0.01f, 0, 1, 0);
-        run_rank(f, 0, 0.0f, 1, 0, 8);
-        run_rank(f, 2, 0.01f, 0, 1, 4);
+        run_rank(f, 2, 0.0f, 1, 1, 0, 0);
+        run_rank(f, 1, 0.01f, 0, 1, 0, 0);
+        run_rank(f, 0, 0.0f, 1, 0, 8, 0);
+        run_rank(f, 2, 0.01f, 0, 1, 4, 0);
+        run_rank(f, 1, 0.0f, 1, 0, 8, 8);
         fclose(f);
         printf("gpu ok\n");
         return 0;

@@ -3,8 +3,11 @@ mirror include/zero_shard.h, the number of launches a pass is issued as, and
 the pieces and pointer advances of a bucketed step (the header's bucket
 contract: every per-element pointer advanced by the piece's first element,
 codes by bytes, block records by whole blocks)."""
+import json
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
@@ -94,3 +97,17 @@ def test_piece_pointer_advances(Z):
         g = Z.QGather(1 << 20, 1 << 22, bits, 100_000).at(b0)
         assert (g.codes, g.blocks, g.bits, g.length) == \
             ((1 << 20) + code_bytes, (1 << 22) + 8 * (b0 // Z.QBLOCK), bits, 100_000 - b0)
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Imported before torch, the binding and the device input generator still
+    leave one HIP runtime in the process (torch's): with two, the library's
+    runtime finds no device."""
+    code = ("import zero_partitioned_mixed_amd, synth; synth.gpu(); import torch; "
+            "import json; print(json.dumps(sorted({l.split()[-1] for l in open('/proc/self/maps') "
+            "if 'libamdhip64' in l})))")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    paths = json.loads(r.stdout.strip().splitlines()[-1])
+    assert len(paths) == 1, paths

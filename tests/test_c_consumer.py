@@ -6,9 +6,10 @@ CPU: the program's host mode (partition, size queries, argument checks).
 GPU: rank 2 of Psi = 120,007 over N = 3 (fp16) on the fused path with a
 dynamic loss scale and an +inf in contribution 1 at step 2 (a skip), and
 rank 1 on the two-pass path with clipping at 0.01, three steps each; then
-rank 0 as the first but writing only the INT8 all-gather payload, and rank 2
-as the second writing the slot and an INT4 payload.  Every step's decisions,
-the final master/m/v, the slot and the payload against the oracle.
+rank 0 as the first but writing only the INT8 all-gather payload, rank 2 as
+the second writing the slot and an INT4 payload, and rank 1 as the first over
+INT8-quantised contributions writing only the INT8 payload.  Every step's
+decisions, the final master/m/v, the slot and the payload against the oracle.
 """
 import os
 import subprocess
@@ -42,16 +43,16 @@ def _cases():
     common = dict(psi=120_007, nranks=3, dtype=F16, steps=3, contrib_scale=1024.0,
                   loss_scale=1024.0)
 
-    def fused(rank):
+    def fused(rank, qbits=0):
         return Case(Workload(name=f"c_fused_r{rank}", ranks=(rank,), scaler=2, **common), rank, 3,
-                    extra=(Inject(2, 1, 123, np.inf),))
+                    extra=(Inject(2, 1, 123, np.inf),), qbits=qbits)
 
     def two_pass(rank):
         return Case(Workload(name=f"c_two_pass_r{rank}", ranks=(rank,), scaler=1,
                              max_grad_norm=0.01, **common), rank, 3)
 
     return [(fused(2), True, 0), (two_pass(1), True, 0), (fused(0), False, 8),
-            (two_pass(2), True, 4)]
+            (two_pass(2), True, 4), (fused(1, qbits=8), False, 8)]
 
 
 @pytest.mark.gpu
@@ -94,4 +95,4 @@ def test_c_program_steps_match_oracle(tmp_path):
                               O.quantize(oslot, F16, qbits))
         H.log(f"{c.w.name}: C program matches the oracle; skips {[x['skip'] for x in reports]}")
     assert pos == len(raw)
-    assert [x["skip"] for x in reports] == [0, 0, 0]
+    assert [x["skip"] for x in reports] == [0, 1, 0]  # the last case's inf block skips step 2

@@ -74,23 +74,26 @@ def test_graph_replay_equals_eager(name):
           f"{[r['skip'] for r in g.reports]}")
 
 
+@pytest.mark.parametrize("qbits", [0, 8])
 @pytest.mark.parametrize("clip", [0.0, 0.02])
 @pytest.mark.parametrize("write_slot", [True, False])
-def test_graph_replay_with_quantised_gather_payload(write_slot, clip):
+def test_graph_replay_with_quantised_gather_payload(write_slot, clip, qbits):
     """The step that writes the INT8 all-gather payload (fused, or two-pass
-    with clipping), captured once: a skip at step 2 (on the fused path
-    zero_fused_restore_q rebuilds the payload inside the replay), every
-    replay's ctrl and the final state, slot and payload equal to the eager
-    run's bit for bit, the payload also to the oracle's."""
+    with clipping; over 16-bit or INT8 contributions), captured once: a skip
+    at step 2 (on the fused path zero_fused_restore_q rebuilds the payload
+    inside the replay), every replay's ctrl and the final state, slot and
+    payload equal to the eager run's bit for bit, the payload also to the
+    oracle's."""
     import torch
     import oracle as O
     c = Case(small(100_003, 3, 2, steps=4, scaler=2, contrib_scale=2.0 ** 10,
                    loss_scale=2.0 ** 10, max_grad_norm=clip), 2, 4,
-             extra=(Inject(2, 2, 30_001, np.inf),))
+             extra=(Inject(2, 2, 30_001, np.inf),), qbits=qbits)
     eager = H.DeviceRun(c, full_gather=False, qgather=8, write_slot=write_slot)
     eager.run()
     g = H.DeviceRun(c, full_gather=False, qgather=8, write_slot=write_slot)
-    graph = g.step_obj.capture(g.contrib, g.gather if write_slot else None, g.qg)
+    src = g.qrows if g.qrows is not None else g.contrib
+    graph = g.step_obj.capture(src, g.gather if write_slot else None, g.qg)
     torch.cuda.synchronize()
     assert g.step_obj.ctrl_dict()["t"] == 0
     for s in range(1, c.steps + 1):
@@ -109,5 +112,5 @@ def test_graph_replay_with_quantised_gather_payload(write_slot, clip):
     H.assert_reports(g.reports, reps)
     _, _, _, rslot = H.oracle_elements(c, reps)
     H.assert_qpayload(g.qpayload(), O.quantize(rslot, c.w.dtype, 8))
-    H.log(f"graph qgather write_slot={write_slot} clip={clip}: {c.steps} replays equal; "
-          f"skips {[r['skip'] for r in g.reports]}")
+    H.log(f"graph qgather write_slot={write_slot} clip={clip} qbits={qbits}: {c.steps} replays "
+          f"equal; skips {[r['skip'] for r in g.reports]}")

@@ -27,6 +27,12 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                       "(hipcc --offload-arch=gfx950); there is no fallback path")
 
+# torch first: its HIP runtime must be the one in the process when this library
+# loads.  The library asks for libamdhip64.so.7, which resolves to torch's
+# bundled runtime once that is loaded; loaded the other way round, the process
+# holds two HIP runtimes and this library's finds no device.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 _vp = ctypes.c_void_p
