@@ -68,7 +68,8 @@ constexpr int kRestoreGrid = 256;           // workgroups of the (usually idle) 
 //     7.18 without a reservation and 7.32 at two;
 //   passes that also quantise the all-gather payload wait at one more
 //     workgroup barrier per tile: three per CU; the 13B step 10.9 ms against
-//     11.2 without a reservation and 11.5 at two;
+//     11.2 without a reservation and 11.5 at two; over quantised
+//     contributions no reservation (Residency below);
 //   fused step over quantised contributions: two per CU; INT8 rows 9.41 ms
 //     against 9.63 at three and 9.78 without a reservation, INT4 rows 8.26
 //     against 8.37 and 8.50;
