@@ -448,7 +448,9 @@ int zero_fused_step_qgather(const void *contrib_dev, int32_t contrib_dtype, int3
 
 /* zero_fused_step_qgather with the contribution rows given as a table of row
  * pointers (rows_dev as in zero_reduce_grads_rows, nranks <= ZERO_MAX_RANKS).
- * Bit-identical to zero_fused_step_qgather on the same rows. */
+ * Bit-identical to zero_fused_step_qgather on the same rows.  Errors: those
+ * of zero_fused_step_rows for the table, then those of
+ * zero_fused_step_qgather for the rest. */
 int zero_fused_step_rows_qgather(const void *const *rows_dev, int32_t contrib_dtype,
                                  int32_t nranks, const zero_state *pair, int64_t valid_len,
                                  void *gather_dev, int32_t gather_dtype, int64_t offset,
@@ -461,8 +463,9 @@ int zero_fused_step_rows_qgather(const void *const *rows_dev, int32_t contrib_dt
  * zero_reduce_grads_q): ZeRO++ end to end in one pass, with the gradient
  * reduce-scatter arriving as INT8 or INT4 blocks and the parameters leaving
  * as the bits-bit all-gather payload (codes_dev, blocks_dev).  The two widths
- * are independent.  Other arguments and errors as in zero_fused_step_q and
- * zero_fused_step_qgather. */
+ * are independent.  Errors: those of zero_fused_step_q for the quantised
+ * rows (qbits, tables, 8-byte alignment), then those of
+ * zero_fused_step_qgather for the rest. */
 int zero_fused_step_q_qgather(const void *const *qcodes_dev, const zero_qblock *const *qblocks_dev,
                               int32_t qbits, int32_t nranks, const zero_state *pair,
                               int64_t valid_len, void *gather_dev, int32_t gather_dtype,

@@ -82,6 +82,9 @@ MANY_ROWS = {
              extra=(Inject(2, 40, T64 + 3, np.inf),)), 0, True, "strided", 3),
     "n64_two_pass_clip": (Case(many_rows(64, T64 + 4099, max_grad_norm=0.5), 63, 2), 0, True,
                           "strided", 2),
+    "n64_two_pass_int4_rows_int8_payload": (Case(many_rows(64, T64 + 2048 * 3 + 9,
+                                                           max_grad_norm=0.5), 63, 2, qbits=4), 8,
+                                            False, "strided", 2),
     "n24_fused_int8_rows_int4_payload": (Case(many_rows(24, T24 + 2048 + 5), 23, 2, qbits=8), 4,
                                          True, "strided", 2),
     "n24_fused_row_table": (Case(many_rows(24, 2 * T24 + 1, dtype=F16), 23, 2), 0, True, "rows",
