@@ -111,3 +111,50 @@ def test_one_hip_runtime_whatever_the_import_order():
     assert r.returncode == 0, r.stderr[-2000:]
     paths = json.loads(r.stdout.strip().splitlines()[-1])
     assert len(paths) == 1, paths
+
+
+ENTRY_POINTS = ["zero_fused_step", "zero_fused_step_rows", "zero_fused_step_q",
+                "zero_fused_step_qgather", "zero_fused_step_rows_qgather",
+                "zero_fused_step_q_qgather", "zero_reduce_grads", "zero_reduce_grads_rows",
+                "zero_reduce_grads_q", "zero_grad_norm_overflow", "zero_fused_restore",
+                "zero_fused_restore_q", "zero_adam_step", "zero_adam_step_qgather"]
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("source", ["strided", "rows", "quant"])
+@pytest.mark.parametrize("payload", [False, True])
+def test_shard_step_routes_each_form_to_its_call(Z, monkeypatch, fused, source, payload):
+    """ShardStep.step issues, for every contribution form, payload choice and
+    path, the calls the header pairs with them: the per-element pass, the
+    decision, then the restore (fused) or the Adam pass (two-pass)."""
+    calls = []
+    for name in ENTRY_POINTS:
+        monkeypatch.setattr(Z, name, lambda *a, _n=name, **k: calls.append(_n))
+    st = object.__new__(Z.ShardStep)
+    st.bucket, st.nranks, st.stride, st.valid_len, st.offset = 0, 2, 4096, 4096, 0
+    st.dtype = st.gather_dtype = Z.F16
+    st.hp = Z.hparams(max_grad_norm=0.0 if fused else 1.0)
+    st.fused = fused
+    st.state, st.g, st.ctrl, st.ws = ("m0", "m1", "m2"), "g", "ctrl", "ws"
+    st.pair = ("p0", "p1", "p2") if fused else None
+    contrib = {"strided": object(), "rows": [1 << 20, 1 << 21],
+               "quant": Z.QuantRows([(1 << 20, 1 << 22), (1 << 21, 1 << 23)], 8)}[source]
+    qg = Z.QGather(1 << 24, 1 << 25, 8, 4096) if payload else None
+    st.step(contrib, "gather", qg)
+    suffix = {"strided": "", "rows": "_rows", "quant": "_q"}[source]
+    if fused:
+        first = "zero_fused_step" + suffix + ("_qgather" if payload else "")
+        last = "zero_fused_restore_q" if payload else "zero_fused_restore"
+    else:
+        first = "zero_reduce_grads" + suffix
+        last = "zero_adam_step_qgather" if payload else "zero_adam_step"
+    assert calls == [first, "zero_grad_norm_overflow", last]
+
+
+def test_shard_step_rejects_a_row_count_mismatch(Z):
+    st = object.__new__(Z.ShardStep)
+    st.nranks, st.fused = 3, True
+    with pytest.raises(ValueError):
+        st.run_pieces([1 << 20, 1 << 21], "gather")
+    with pytest.raises(ValueError):
+        st.run_pieces(Z.QuantRows([(1 << 20, 1 << 22)], 4), "gather")
