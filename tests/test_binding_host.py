@@ -130,13 +130,7 @@ def test_shard_step_routes_each_form_to_its_call(Z, monkeypatch, fused, source, 
     calls = []
     for name in ENTRY_POINTS:
         monkeypatch.setattr(Z, name, lambda *a, _n=name, **k: calls.append(_n))
-    st = object.__new__(Z.ShardStep)
-    st.bucket, st.nranks, st.stride, st.valid_len, st.offset = 0, 2, 4096, 4096, 0
-    st.dtype = st.gather_dtype = Z.F16
-    st.hp = Z.hparams(max_grad_norm=0.0 if fused else 1.0)
-    st.fused = fused
-    st.state, st.g, st.ctrl, st.ws = ("m0", "m1", "m2"), "g", "ctrl", "ws"
-    st.pair = ("p0", "p1", "p2") if fused else None
+    st = _fake_step(Z, fused)
     contrib = {"strided": object(), "rows": [1 << 20, 1 << 21],
                "quant": Z.QuantRows([(1 << 20, 1 << 22), (1 << 21, 1 << 23)], 8)}[source]
     qg = Z.QGather(1 << 24, 1 << 25, 8, 4096) if payload else None
@@ -158,3 +152,39 @@ def test_shard_step_rejects_a_row_count_mismatch(Z):
         st.run_pieces([1 << 20, 1 << 21], "gather")
     with pytest.raises(ValueError):
         st.run_pieces(Z.QuantRows([(1 << 20, 1 << 22)], 4), "gather")
+
+
+def _fake_step(Z, fused, clip=1.0):
+    st = object.__new__(Z.ShardStep)
+    st.bucket, st.nranks, st.stride, st.valid_len, st.offset = 0, 2, 4096, 4096, 0
+    st.dtype = st.gather_dtype = Z.F16
+    st.hp = Z.hparams(max_grad_norm=0.0 if fused else clip)
+    st.fused = fused
+    st.state, st.g, st.ctrl, st.ws = ("m0", "m1", "m2"), "g", "ctrl", "ws"
+    st.pair = ("p0", "p1", "p2") if fused else None
+    return st
+
+
+def test_multi_shard_step_runs_every_rank_then_one_decision(Z, monkeypatch):
+    """Each rank's per-element pass (its own form and payload), one combined
+    decision, then each rank's restore."""
+    calls = []
+    for name in ENTRY_POINTS:
+        monkeypatch.setattr(Z, name, lambda *a, _n=name, **k: calls.append(_n))
+    multi = Z.MultiShardStep([_fake_step(Z, True), _fake_step(Z, True)])
+    qrows = Z.QuantRows([(1 << 20, 1 << 22), (1 << 21, 1 << 23)], 8)
+    multi.step([object(), qrows], "gather", [None, Z.QGather(1 << 24, 1 << 25, 8, 4096)])
+    assert calls == ["zero_fused_step", "zero_fused_step_q_qgather", "zero_grad_norm_overflow",
+                     "zero_fused_restore", "zero_fused_restore_q"]
+
+
+def test_multi_shard_step_validation(Z):
+    with pytest.raises(ValueError):
+        Z.MultiShardStep([])
+    with pytest.raises(ValueError):  # one decision, one set of hyperparameters
+        Z.MultiShardStep([_fake_step(Z, False, 1.0), _fake_step(Z, False, 0.5)])
+    multi = Z.MultiShardStep([_fake_step(Z, True), _fake_step(Z, True)])
+    with pytest.raises(ValueError):
+        multi.step([object()], "gather")
+    with pytest.raises(ValueError):
+        multi.step([object(), object()], "gather", [None])

@@ -605,28 +605,27 @@ class ShardStep:
 
 class MultiShardStep:
     """Several ranks' shard steps on one GPU whose norm and overflow decisions
-    are combined across the ranks (the scalar all-reduce between ranks)."""
+    are combined across the ranks (the scalar all-reduce between ranks).  The
+    ranks share one path and one set of hyperparameters; each takes its own
+    contributions (any form ShardStep takes) and optional payload."""
 
     def __init__(self, steps: list):
         if not 1 <= len(steps) <= MAX_RANKS:
             raise ValueError("between 1 and 64 ranks")
+        first = bytes(steps[0].hp)
+        if any(bytes(s.hp) != first for s in steps):
+            raise ValueError("the ranks of one decision share their hyperparameters")
         self.steps = steps
         self.fused = steps[0].fused
 
-    def step(self, contribs, gather) -> None:
+    def step(self, contribs, gather, qgathers=None) -> None:
         ss = self.steps
-        if self.fused:
-            for s, c in zip(ss, contribs):
-                zero_fused_step(c, s.dtype, s.nranks, s.stride, s.pair, s.valid_len, gather,
-                                s.gather_dtype, s.offset, s.hp, s.ctrl, s.ws)
-        else:
-            for s, c in zip(ss, contribs):
-                zero_reduce_grads(c, s.dtype, s.nranks, s.stride, s.valid_len, s.ctrl, s.g, s.ws)
+        qgathers = [None] * len(ss) if qgathers is None else list(qgathers)
+        if len(contribs) != len(ss) or len(qgathers) != len(ss):
+            raise ValueError(f"one contribution set and payload per rank ({len(ss)})")
+        for s, c, q in zip(ss, contribs, qgathers):
+            s.run_pieces(c, gather, q)
         zero_grad_norm_overflow([s.ws for s in ss], [s.valid_len for s in ss],
                                 [s.ctrl for s in ss], ss[0].hp, self.fused)
-        for s in ss:
-            if self.fused:
-                zero_fused_restore(s.pair, s.valid_len, gather, s.gather_dtype, s.offset, s.ctrl)
-            else:
-                zero_adam_step(s.state, s.g, s.valid_len, s.hp, s.ctrl, gather, s.gather_dtype,
-                               s.offset)
+        for s, q in zip(ss, qgathers):
+            s.complete(gather, q)
