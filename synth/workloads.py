@@ -43,7 +43,12 @@ class Workload:
     growth_interval: int = 1000
     inject_inf: tuple = ()        # (step, k, element-in-shard) triples set to +inf
     seed: int = 0
+    gather_dtype: int = 0         # 16-bit format of the gathered parameters; 0: as dtype
     note: str = field(default="", compare=False)
+
+    @property
+    def slot_dtype(self) -> int:
+        return self.gather_dtype or self.dtype
 
     @property
     def shard(self) -> int:

@@ -184,11 +184,11 @@ def oracle_elements(c: Case, reps: list[dict], cols: np.ndarray | None = None):
         v = np.concatenate([x[2] for x in parts]) if parts else np.zeros(0, np.float32)
         idx = None
     if any(not r["skip"] for r in reps):
-        slot = O.cast(p, w.dtype)
+        slot = O.cast(p, w.slot_dtype)
     elif idx is not None:  # never applied: the initial 16-bit parameters
-        slot = O.cast(synth.master_at(w.seed, w.master_sigma, idx), w.dtype)
+        slot = O.cast(synth.master_at(w.seed, w.master_sigma, idx), w.slot_dtype)
     else:
-        slot = O.cast(synth.master_range(w.seed, w.master_sigma, off, valid), w.dtype)
+        slot = O.cast(synth.master_range(w.seed, w.master_sigma, off, valid), w.slot_dtype)
     return p, m, v, slot
 
 
@@ -229,14 +229,16 @@ class DeviceRun:
         self.g = None if fused else torch.empty(n_state, dtype=torch.float32, device=dev)
         self.gather_len = w.psi if full_gather else valid
         self.gather_off = off if full_gather else 0
-        self.gather = torch.empty(max(self.gather_len, 1), dtype=tdt, device=dev)
-        synth.gpu_param_range(self.gather, w.seed, w.master_sigma, w.dtype,
+        gdt = torch.float16 if w.slot_dtype == F16 else torch.bfloat16
+        self.gather = torch.empty(max(self.gather_len, 1), dtype=gdt, device=dev)
+        synth.gpu_param_range(self.gather, w.seed, w.master_sigma, w.slot_dtype,
                               0 if full_gather else off)
         hp = Z.hparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                        weight_decay=w.weight_decay, max_grad_norm=w.max_grad_norm,
                        scaler=w.scaler, min_scale=w.min_scale, growth_interval=w.growth_interval)
-        self.step_obj = Z.ShardStep(w.nranks, c.stride, valid, self.gather_off, w.dtype, w.dtype,
-                                    hp, self.state0, self.g, w.loss_scale, bucket=bucket)
+        self.step_obj = Z.ShardStep(w.nranks, c.stride, valid, self.gather_off, w.dtype,
+                                    w.slot_dtype, hp, self.state0, self.g, w.loss_scale,
+                                    bucket=bucket)
         self.reports = []
         if layout not in ROW_LAYOUTS:
             raise ValueError(layout)
@@ -253,7 +255,7 @@ class DeviceRun:
         elif self.qg is not None and valid:
             # the two-pass path writes nothing on a skipped step, so the payload
             # starts as the caller's would: the initial slot, quantised
-            Z.zero_quantize_blocks(self.gather[self.gather_off:], w.dtype, valid, qgather,
+            Z.zero_quantize_blocks(self.gather[self.gather_off:], w.slot_dtype, valid, qgather,
                                    self.qg.codes, self.qg.blocks)
         self.write_slot = write_slot
         if not write_slot and not qgather:
@@ -351,16 +353,17 @@ def run_and_compare(c: Case, label: str, full: bool = True, layout: str = "strid
     stats["m"] = assert_f32_close("m", m, rm)
     stats["v"] = assert_f32_close("v", v, rv)
     if write_slot:
-        stats["slot"] = assert_16bit_within_ulp("slot", slot, rslot, c.w.dtype)
+        stats["slot"] = assert_16bit_within_ulp("slot", slot, rslot, c.w.slot_dtype)
     if qgather:
-        stats["qgather"] = assert_qpayload(g.qpayload(), O.quantize(rslot, c.w.dtype, qgather))
+        stats["qgather"] = assert_qpayload(g.qpayload(),
+                                           O.quantize(rslot, c.w.slot_dtype, qgather))
     w = c.w
     _, off, valid = c.part
     if full:  # nothing outside the slot changed (nothing at all without a slot)
         outside = np.r_[0:off, off + valid:w.psi] if write_slot else np.arange(w.psi)
         if outside.size:
             got = g.gather_bits(outside)
-            ref = synth.param_range(w.seed, w.master_sigma, w.dtype, 0, w.psi)[outside]
+            ref = synth.param_range(w.seed, w.master_sigma, w.slot_dtype, 0, w.psi)[outside]
             assert np.array_equal(got, ref), "gather buffer changed outside the slot"
     log(f"{label}: ok {stats}")
     return g, stats

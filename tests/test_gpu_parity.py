@@ -137,6 +137,38 @@ def test_small_cases(name):
     run_case(Case(w, w.ranks[0], w.steps, extra=tuple(extra)), name)
 
 
+DYN = dict(scaler=2, contrib_scale=2.0 ** 10, loss_scale=2.0 ** 10)
+
+# Contributions in one 16-bit format, the gathered parameters in the other.
+# name: (workload, contribution bits (0: 16-bit), layout, payload bits, injections)
+MIXED = {
+    "f16_in_bf16_slot_fused_skip": (small(8 * 25_007, 8, 3, steps=4, gather_dtype=BF16, **DYN),
+                                    0, "strided", 0, (Inject(2, 6, 10_001, np.inf),)),
+    "bf16_in_f16_slot_fused_n3_odd": (small(100_003, 3, 2, dtype=BF16, gather_dtype=F16), 0,
+                                      "strided", 0, ()),
+    "f16_in_bf16_slot_two_pass_clip": (small(200_000, 8, 5, max_grad_norm=0.05,
+                                             gather_dtype=BF16), 0, "strided", 0, ()),
+    "bf16_in_f16_slot_two_pass_n64": (small(64 * 1_000 + 37, 64, 63, dtype=BF16,
+                                            max_grad_norm=0.05, gather_dtype=F16), 0,
+                                      "strided", 0, ()),
+    "f16_rows_in_bf16_slot_int8_payload": (small(8 * 25_007, 8, 6, gather_dtype=BF16), 0, "rows",
+                                           8, ()),
+    "bf16_int4_rows_in_f16_slot_int8_payload": (small(8 * 25_007, 8, 7, dtype=BF16,
+                                                      gather_dtype=F16), 4, "strided", 8, ()),
+}
+
+
+@pytest.mark.parametrize("name", list(MIXED))
+def test_mixed_formats(name):
+    """The slot's 16-bit format differs from the contributions': every kernel
+    instantiation with the two formats apart, against the oracle (slot and
+    payload in the slot's format)."""
+    w, qbits, layout, payload, extra = MIXED[name]
+    assert w.slot_dtype != w.dtype
+    H.run_and_compare(Case(w, w.ranks[0], w.steps, extra=tuple(extra), qbits=qbits), name,
+                      layout=layout, qgather=payload)
+
+
 def test_empty_tail_rank():
     import torch
     import zero_partitioned_mixed_amd as Z
