@@ -8,10 +8,13 @@ buffer, a row table, rows at 8-byte-aligned starts, INT8 or INT4 blocks), the
 step count, the weight decay, outliers, and sometimes an inf or NaN in one
 contribution.  A second draw per seed (its own generator, so the first draw
 stays as it was) adds the quantised all-gather payload (INT8 or INT4, with
-or without the 16-bit slot) and bucketed steps (pieces of a few tiles).  The
+or without the 16-bit slot), bucketed steps (pieces of a few tiles) and the
+slot's 16-bit format (the other one in about a quarter of the cases).  The
 bars are those of the fixed cases.  The data come from the seeded input
 generator as always.
 """
+from dataclasses import replace
+
 import numpy as np
 import pytest
 
@@ -66,17 +69,22 @@ def draw(seed: int):
 
 
 def draw_options(seed: int, c: Case, layout: str):
-    """(payload bits, write the 16-bit slot, bucket elements) for a case."""
+    """(payload bits, write the 16-bit slot, bucket elements, slot format) for
+    a case; the slot format is the other 16-bit format for about one case in
+    four."""
     rng = np.random.default_rng(5000 + seed)
     qgather = int(rng.choice([0, 0, 0, 8, 4]))
     write_slot = not qgather or bool(rng.random() < 0.5)
     bucket = int(rng.choice([0, 0, 0, 1, 2, 5])) * 2048
-    return qgather, write_slot, bucket
+    other = BF16 if c.w.dtype == F16 else F16
+    gather_dtype = other if rng.random() < 0.25 else c.w.dtype
+    return qgather, write_slot, bucket, gather_dtype
 
 
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_case(seed):
     c, layout = draw(seed)
-    qgather, write_slot, bucket = draw_options(seed, c, layout)
+    qgather, write_slot, bucket, gather_dtype = draw_options(seed, c, layout)
+    c = replace(c, w=replace(c.w, gather_dtype=gather_dtype))
     H.run_and_compare(c, f"random{seed}", full=True, layout=layout, qgather=qgather,
                       write_slot=write_slot, bucket=bucket)
