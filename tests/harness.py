@@ -258,8 +258,8 @@ class DeviceRun:
             Z.zero_quantize_blocks(self.gather[self.gather_off:], w.slot_dtype, valid, qgather,
                                    self.qg.codes, self.qg.blocks)
         self.write_slot = write_slot
-        if not write_slot and not qgather:
-            raise ValueError("only a quantised-gather step may skip the 16-bit slot")
+        if not write_slot and not qgather and fused:
+            raise ValueError("the fused step without a payload writes the 16-bit slot")
         n = w.nranks
         if c.qbits:
             self.qrows = Z.QuantRows.alloc(n, valid, c.qbits, dev)

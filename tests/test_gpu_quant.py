@@ -150,29 +150,31 @@ def test_quantized_step_gpt2_sized(bits):
     H.log(f"gpt2 q{bits}: ok, norm {g.reports[-1]['norm']:.9g} (16-bit path: see parity tests)")
 
 
+@pytest.mark.parametrize("dtype", [F16, BF16])
 @pytest.mark.parametrize("shift", [1, 2, 3])
 @pytest.mark.parametrize("bits", [8, 4])
-def test_quantize_and_dequantize_unaligned(bits, shift):
+def test_quantize_and_dequantize_unaligned(bits, shift, dtype):
     """16-bit buffers at 2-, 4- and 6-byte offsets (a parameter slot at any
-    offset): the 16-bit loads and the narrower stores give the same codes and
-    values as the oracle."""
+    offset), in both formats: the 16-bit loads and the narrower stores give
+    the same codes and values as the oracle."""
     import torch
     import zero_partitioned_mixed_amd as Z
     length = 5 * 2048 + 333
-    src = O.from_f32(_values(length, seed=40 + shift), F16)
-    ref = O.quantize(src, F16, bits)
+    src = O.from_f32(_values(length, seed=40 + shift), dtype)
+    ref = O.quantize(src, dtype, bits)
     buf = torch.zeros(length + 8, dtype=torch.int16, device="cuda")
     buf[shift:shift + length] = _to_gpu(src.view(np.int16))
     q = Z.QuantRows.alloc(1, length, bits, torch.device("cuda", 0))
     codes, blocks = q.rows[0]
-    Z.zero_quantize_blocks(buf[shift:], F16, length, bits, codes, blocks)
-    dst = torch.full((length + 8,), 7.0, dtype=torch.float16, device="cuda")
-    Z.zero_dequantize_blocks(codes, blocks, bits, length, dst[shift:], F16)
+    Z.zero_quantize_blocks(buf[shift:], dtype, length, bits, codes, blocks)
+    tdt = torch.float16 if dtype == F16 else torch.bfloat16
+    dst = torch.full((length + 8,), 7.0, dtype=tdt, device="cuda")
+    Z.zero_dequantize_blocks(codes, blocks, bits, length, dst[shift:], dtype)
     torch.cuda.synchronize()
     assert np.array_equal(codes.cpu().numpy()[:ref.codes.size], ref.codes)
     got = dst.view(torch.int16).cpu().numpy().view(np.uint16)
-    want = O.cast(O.dequantize(ref), F16)
-    seven = O.from_f32(np.array([7.0], np.float32), F16)[0]
+    want = O.cast(O.dequantize(ref), dtype)
+    seven = O.from_f32(np.array([7.0], np.float32), dtype)[0]
     assert np.array_equal(got[shift:shift + length], want)
     assert np.all(got[:shift] == seven) and np.all(got[shift + length:] == seven)
 

@@ -1443,7 +1443,7 @@ Kernel<AdamArgs> adam_for(int gw) {
         case 4: return adam_kernel<DT, 4>;
         case 2: return adam_kernel<DT, 2>;
         case 1: return adam_kernel<DT, 1>;
-        default: return adam_kernel<DT, 0>;
+        default: return adam_kernel<ZERO_F16, 0>;  // no slot: the format is not used
     }
 }
 
