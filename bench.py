@@ -379,7 +379,8 @@ def main():
                      "frac": _fmt(kern_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None,
                      "kernel_ms": _fmt(kern_avg, 5), "bytes_per_pass": kern_bytes,
-                     "launches_per_pass": sum(Z.launches(n, row_pass_n) for _, n in b_pieces)},
+                     "launches_per_pass": sum(Z.launches(n, row_pass_n, payload=bool(
+                         args.qgather) and row_pass_n > 0) for _, n in b_pieces)},
         "last_step": {"norm": ctrl["norm"], "skip": ctrl["skip"], "t": ctrl["t"],
                       "loss_scale": ctrl["loss_scale"]},
     }

@@ -141,12 +141,15 @@ typedef struct zero_ctrl {
  * elements is issued as ceil(ceil(valid_len / ZERO_TILE) / T) consecutive
  * launches of at most T tiles on the caller's stream, which a profiler lists
  * one by one; the results are those of one launch.  T = ZERO_LAUNCH_TILES
- * for the Adam passes; for a pass that reads N contribution rows (reduce and
- * fused step, every source) T = ZERO_LAUNCH_ROW_TILES / N, clamped to
- * [ZERO_LAUNCH_MIN_TILES, ZERO_LAUNCH_TILES] (zero_launch_tiles). */
-#define ZERO_LAUNCH_TILES 16384
+ * for the Adam passes and for a pass that reads N <= 8 contribution rows;
+ * over N > 8 rows (reduce and fused step, every source) T =
+ * max(ZERO_LAUNCH_MIN_TILES, ZERO_LAUNCH_ROW_TILES / N) (zero_launch_tiles).
+ * The fused step that also writes the quantised all-gather payload takes at
+ * most ZERO_LAUNCH_PAYLOAD_TILES of those. */
+#define ZERO_LAUNCH_TILES 32768
 #define ZERO_LAUNCH_ROW_TILES 131072
 #define ZERO_LAUNCH_MIN_TILES 2048
+#define ZERO_LAUNCH_PAYLOAD_TILES 16384
 
 /* One rank's fp32 optimizer state: master weights, Adam m, Adam v.
  * Flat form (two-pass path, pack/unpack): three arrays of valid_len

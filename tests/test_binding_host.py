@@ -34,19 +34,28 @@ def test_constants_match_header(Z):
     assert Z.LAUNCH_TILES == _header_define("ZERO_LAUNCH_TILES")
     assert Z.LAUNCH_ROW_TILES == _header_define("ZERO_LAUNCH_ROW_TILES")
     assert Z.LAUNCH_MIN_TILES == _header_define("ZERO_LAUNCH_MIN_TILES")
+    assert Z.LAUNCH_PAYLOAD_TILES == _header_define("ZERO_LAUNCH_PAYLOAD_TILES")
     assert Z.MAX_RANKS == _header_define("ZERO_MAX_RANKS")
     # one workspace partial per tile: the workspace grows by PARTIAL_BYTES per tile
     assert Z.zero_workspace_bytes(3 * Z.TILE) - Z.zero_workspace_bytes(Z.TILE) == 2 * Z.PARTIAL_BYTES
 
 
 @pytest.mark.parametrize("valid,nranks,expected", [
-    (0, 0, 0), (1, 0, 1), (2048, 0, 1), (16384 * 2048, 0, 1), (16384 * 2048 + 1, 0, 2),
-    (1_625_000_000, 0, 49), (1_625_000_000, 8, 49), (875_000_000, 8, 27),
+    (0, 0, 0), (1, 0, 1), (2048, 0, 1), (32768 * 2048, 0, 1), (32768 * 2048 + 1, 0, 2),
+    (1_625_000_000, 0, 25), (1_625_000_000, 8, 25), (875_000_000, 8, 14),
     (15_554_976, 8, 1), (23_437_500, 64, 6), (23_437_500, 0, 1), (23_437_500, 32, 3),
     (5461 * 2048, 24, 1), (5461 * 2048 + 1, 24, 2), (2048 * 2048 + 1, 1024, 2),
+    (14563 * 2048 + 1, 9, 2),
 ])
 def test_launches_per_pass(Z, valid, nranks, expected):
     assert Z.launches(valid, nranks) == expected
+
+
+@pytest.mark.parametrize("valid,nranks,expected", [
+    (1_625_000_000, 8, 49), (16384 * 2048 + 1, 1, 2), (23_437_500, 64, 6), (8192 * 2048, 16, 1),
+])
+def test_launches_of_the_fused_payload_pass(Z, valid, nranks, expected):
+    assert Z.launches(valid, nranks, payload=True) == expected
 
 
 def test_launch_tiles_match_the_library(Z):
@@ -54,8 +63,8 @@ def test_launch_tiles_match_the_library(Z):
     library's own, for every row count a call accepts and beyond."""
     for n in list(range(-2, 1100)) + [4096, 1 << 20]:
         assert Z.launch_tiles(n) == Z._lib.zero_launch_tiles(n), n
-    assert [Z.launch_tiles(n) for n in (1, 8, 9, 16, 24, 32, 64, 65, 1024)] == \
-        [16384, 16384, 14563, 8192, 5461, 4096, 2048, 2048, 2048]
+    assert [Z.launch_tiles(n) for n in (0, 1, 8, 9, 16, 24, 32, 64, 65, 1024)] == \
+        [32768, 32768, 32768, 14563, 8192, 5461, 4096, 2048, 2048, 2048]
 
 
 def _step(Z, valid, bucket):

@@ -1,7 +1,7 @@
 """Shards longer than one launch of a streaming pass.
 
 The library issues each streaming pass (reduce, fused step, Adam) as
-consecutive launches of at most 2^25 elements (16,384 tiles) with its
+consecutive launches of at most 2^26 elements (32,768 tiles) with its
 pointers advanced per launch; a pass that reads N > 8 contribution rows
 launches 2^17 / N tiles at a time (at least 2,048).  These shards cross those
 boundaries, with a ragged last launch, and are checked in full against the
@@ -17,7 +17,7 @@ from synth.workloads import BF16, F16, Workload
 
 pytestmark = pytest.mark.gpu
 
-CHUNK = 16384 * 2048
+CHUNK = 32768 * 2048
 SHARD = CHUNK + 3 * 2048 + 77  # a second, ragged launch
 
 

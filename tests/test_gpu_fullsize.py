@@ -54,9 +54,10 @@ def run_fullsize(w, layout="strided", qbits=0, steps=None, samples=65_536, qgath
     H.log(f"{w.name}: scalars ok {stats}; skips {[r['skip'] for r in reps]}")
     extra = [i.col + d for i in c.injections for d in (-1, 0, 1)]
     # both sides of every boundary between the library's launches: of the pass
-    # over the N rows and of the Adam pass (two-pass path)
+    # over the N rows (with the payload or not) and of the Adam pass
     import zero_partitioned_mixed_amd as Z
-    for chunk in {Z.launch_tiles(w.nranks) * Z.TILE, Z.launch_tiles(0) * Z.TILE}:
+    for chunk in {Z.launch_tiles(w.nranks, payload=bool(qgather)) * Z.TILE,
+                  Z.launch_tiles(0) * Z.TILE}:
         extra += [b + d for b in range(chunk, valid, chunk) for d in (-2049, -1, 0, 1, 2048)]
     cols = H.sample_cols(valid, samples, seed=11, extra=extra)
     p, m, v, slot = g.fetch(cols)

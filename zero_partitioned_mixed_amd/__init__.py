@@ -62,24 +62,25 @@ class Ctrl(ctypes.Structure):
 TILE = 2048  # ZERO_TILE
 QBLOCK = 2048  # ZERO_QBLOCK
 PARTIAL_BYTES = 16  # ZERO_PARTIAL_BYTES
-LAUNCH_TILES = 16384  # ZERO_LAUNCH_TILES
+LAUNCH_TILES = 32768  # ZERO_LAUNCH_TILES
 LAUNCH_ROW_TILES = 131072  # ZERO_LAUNCH_ROW_TILES
 LAUNCH_MIN_TILES = 2048  # ZERO_LAUNCH_MIN_TILES
+LAUNCH_PAYLOAD_TILES = 16384  # ZERO_LAUNCH_PAYLOAD_TILES
 
 
-def launch_tiles(nranks: int = 0) -> int:
+def launch_tiles(nranks: int = 0, payload: bool = False) -> int:
     """Most tiles per launch of a pass that reads nranks contribution rows
-    (0: the Adam passes); the library's zero_launch_tiles."""
-    if nranks <= 0:
-        return LAUNCH_TILES
-    return min(LAUNCH_TILES, max(LAUNCH_MIN_TILES, LAUNCH_ROW_TILES // nranks))
+    (0: the Adam passes); the library's zero_launch_tiles.  payload: the fused
+    step that also writes the quantised all-gather payload."""
+    t = LAUNCH_TILES if nranks <= 8 else max(LAUNCH_MIN_TILES, LAUNCH_ROW_TILES // nranks)
+    return min(t, LAUNCH_PAYLOAD_TILES) if payload else t
 
 
-def launches(valid_len: int, nranks: int = 0) -> int:
+def launches(valid_len: int, nranks: int = 0, payload: bool = False) -> int:
     """Kernel launches one call of a streaming pass over valid_len elements
-    is issued as (nranks as in launch_tiles)."""
+    is issued as (nranks and payload as in launch_tiles)."""
     tiles = -(-valid_len // TILE)
-    return -(-tiles // launch_tiles(nranks))
+    return -(-tiles // launch_tiles(nranks, payload))
 
 
 class State(ctypes.Structure):

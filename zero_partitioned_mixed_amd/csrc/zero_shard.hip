@@ -4,7 +4,7 @@
 // operations against 26 + 2N bytes, so nothing is a contraction and nothing
 // uses the matrix cores.  The design points are
 //   * one workgroup per tile of ZERO_TILE = 2048 elements (4 wave64s x 64
-//     lanes x 8 elements), launched as full grids of at most 16,384 tiles
+//     lanes x 8 elements), launched as full grids of at most 32,768 tiles
 //     (2^17 / N over N > 8 contribution rows), with few workgroups resident
 //     per CU (two or three, by pass), so that the set of tiles in flight
 //     stays compact (a grid-stride loop, one grid over a whole 13B shard and
@@ -1494,19 +1494,20 @@ struct Residency<SrcQ<BITS>> {
 // header, so the results are those of one launch, bit for bit).  In one launch
 // of many thousands of workgroups the slowest ones fall further and further
 // behind and the set of tiles in flight spreads over more memory; a new launch
-// every 16,384 tiles keeps it compact (the 13B fused step: 1-5% shorter, most
-// on boxes where the buffers landed on slower memory).  The memory that drift
-// spreads over grows with the rows each tile reads, so a pass over N rows
-// starts a new launch every 2^17 / N tiles: in one process, the best launch
-// size was 2,048 tiles at N = 64 (+7% against 16,384), 4,096 at N = 32
-// (+1.5%), flat from 8,192 up at N = 16, and 16,384-32,768 (within 1%) at
-// N <= 8.  Below 2,048 tiles the launches' fill and drain cost more than the
-// compact window gains.
+// every few tens of thousands of tiles keeps it compact (the 13B fused step:
+// 1-7% shorter than one launch).  The memory that drift spreads over grows
+// with the rows each tile reads, so the best launch size falls as N grows: in
+// one process per shape, 2,048 tiles at N = 64 (+7% against 16,384), 4,096 at
+// N = 32 (+1.5%), flat from 8,192 up at N = 16; at N <= 8 and in the Adam
+// passes 32,768 (0.5-0.9% ahead of 16,384 on two boxes), except the fused
+// step that also writes the payload, which waits at one more workgroup
+// barrier per tile: 16,384 (INT4 payload 1.4% ahead, INT8 equal).  Below
+// 2,048 tiles the launches' fill and drain cost more than the compact window
+// gains.
 int64_t launch_tiles(int32_t nranks) {
-    if (nranks <= 0) return ZERO_LAUNCH_TILES;
+    if (nranks <= 8) return ZERO_LAUNCH_TILES;
     const int64_t t = ZERO_LAUNCH_ROW_TILES / nranks;
-    return t > ZERO_LAUNCH_TILES ? ZERO_LAUNCH_TILES
-                                 : t < ZERO_LAUNCH_MIN_TILES ? ZERO_LAUNCH_MIN_TILES : t;
+    return t < ZERO_LAUNCH_MIN_TILES ? ZERO_LAUNCH_MIN_TILES : t;
 }
 
 // at(x, b0): x advanced by b0 elements of the shard (b0 a multiple of kTile).
@@ -1706,7 +1707,10 @@ int fused_qgather_launch(const SRC& src, int32_t nranks, const zero_state* pair,
               {(uint8_t*)codes, blocks, slot == nullptr ? 0 : store_width(slot)}};
     const Kernel<A> k = bits == 8 ? fused_qgather_bits<SRC, 8>(gather_dtype, nranks)
                                   : fused_qgather_bits<SRC, 4>(gather_dtype, nranks);
-    return launch_chunked(k, a, valid_len, launch_tiles(nranks), (hipStream_t)stream, what,
+    const int64_t tiles = launch_tiles(nranks);
+    return launch_chunked(k, a, valid_len,
+                          tiles < ZERO_LAUNCH_PAYLOAD_TILES ? tiles : ZERO_LAUNCH_PAYLOAD_TILES,
+                          (hipStream_t)stream, what,
                           [bits](const A& x, int64_t b0, int64_t n) {
                               return A{at(x.f, b0, n), at(x.q, b0, bits)};
                           },
