@@ -24,7 +24,7 @@ from synth.workloads import BF16, F16, Workload
 
 pytestmark = pytest.mark.gpu
 
-SEEDS = list(range(1, 129))
+SEEDS = list(range(1, 257))
 
 
 @pytest.fixture(scope="module", autouse=True)
