@@ -18,8 +18,9 @@
  *     (paper-graph summary), 3.4: model-state analysis (16 Psi bill), Stage 1
  *     (Pos) and Stage 2 (Pos+g), and the residual-state note on gradient-norm
  *     buffers;
- *   "zero-stages-simulation" README: flat partitioning into N near-equal
- *     contiguous chunks, GPU r owns chunk r;
+ *   "zero-stages-simulation" README, partitioning paragraph: the flattened
+ *     buffer is cut into N contiguous pieces of (almost) the same length and
+ *     rank r holds piece r;
  *   "ZeRO: Memory Optimization for Large Models" (lesson), Stage 1 and 2;
  *   "ZeRO Stage 1/2/3" guide, section 5 (AdamW with weight decay, the
  *     reduce bucket size);
@@ -100,12 +101,16 @@ typedef struct {
  * weight decay:  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g*g;
  * p = p - lr ((m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps) + wd p),
  * every operation rounded to fp32, b^t a running fp64 product.
- * max_grad_norm > 0 turns clipping on: when norm > max_grad_norm, g is
- * multiplied by max_grad_norm / (norm + 1e-6).
+ * max_grad_norm > 0 turns clipping on: g is multiplied by
+ * min(1, max_grad_norm / (norm + 1e-6)), the coefficient formed in fp64 and
+ * rounded to fp32 (the rule of torch.nn.utils.clip_grad_norm_ given an fp64
+ * norm).
  * scaler: NONE keeps S = 1; STATIC keeps the initial S; DYNAMIC halves S
  * (not below min_scale) on a skipped step and doubles it after
- * growth_interval consecutive applied steps.  A step whose reduced gradient
- * holds inf or NaN is always skipped. */
+ * growth_interval consecutive applied steps, unless the doubled value is
+ * not finite, when S stays (torch._amp_update_scale_'s schedule, plus the
+ * min_scale floor).  A step whose reduced gradient holds inf or NaN is
+ * always skipped. */
 typedef struct zero_hparams {
     float lr, beta1, beta2, eps, weight_decay, max_grad_norm;
     int32_t scaler;
@@ -127,7 +132,7 @@ typedef struct zero_ctrl {
     int32_t nonfinite;  /* last step: 1 if any reduced element was inf/NaN */
     int32_t skip;       /* last step was skipped (state, slot and t unchanged) */
     int32_t t;          /* applied optimizer steps */
-    int32_t good_steps; /* applied steps since the loss scale last changed */
+    int32_t good_steps; /* applied steps since the last skip or doubling point */
     int32_t cur;        /* fused path: which set of the paired state is current */
     uint32_t arrive;    /* internal: arrival counter of the norm reduction, 0 between calls */
     uint32_t reserved[15];
@@ -284,10 +289,11 @@ int zero_grad_norm_overflow(int32_t nranks, void *const *ws_dev, const int64_t *
                             zero_ctrl *const *ctrl_dev, const zero_hparams *hp,
                             int32_t pingpong, void *stream);
 
-/* Adam on the owned slice ("CMU 11-868 L18", Mechanism 1 step 4: each GPU
- * updates only its part of the FP32 variance, momentum and parameters;
- * paper summary 3.4 Stage 1), fused with the cast into the gather slot
- * (step 5: the updated FP32 parameters are copied to FP16).
+/* Adam on the owned slice ("CMU 11-868 L18", Mechanism 1 step 4: the rank's
+ * fp32 master weights and both Adam moments are the only optimizer state it
+ * touches; paper summary 3.4 Stage 1), fused with the cast into the gather
+ * slot (Mechanism 1 step 5: the new master weights, rounded to the 16-bit
+ * format).
  * Two-pass path: runs after zero_reduce_grads and zero_grad_norm_overflow
  * (pingpong = 0), reads g_dev and ctrl (skip, clip, t, beta powers), updates
  * state in place.  When gather_dev is not NULL, writes

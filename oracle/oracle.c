@@ -24,10 +24,13 @@
  * -ffp-contract=off, SSE scalar arithmetic).  The squared-norm is exact.
  *
  * Parity unpinned: Adam trajectories beyond the closed forms and the library
- * cross-check in the tests (the pages print none).  Readings the pages leave
- * open, each pinned by the tests only to the definition stated here: the
- * clip coefficient's 1e-6, the loss scaler's skip/halve/grow schedule, and
- * the quantisation's block size, zero-point form and rounding.
+ * cross-check in the tests (the pages print none), and the quantisation's
+ * block size, zero-point form and rounding (the page fixes none of them; the
+ * tests pin the oracle to the definition stated here and to arithmetic).
+ * The clip rule and the loss scaler's schedule are readings too (the pages
+ * give neither); the tests pin them to PyTorch's own routines on the CPU
+ * (clip_grads_with_norm_, _amp_update_scale_), with the one departure
+ * stated above oracle_finalize: the scale never drops below min_scale.
  */
 #include <math.h>
 #include <stdint.h>
@@ -140,9 +143,9 @@ void oracle_from_f32_bits_range(uint32_t b0, int64_t n, int32_t dtype, uint16_t 
 }
 
 /* ------------------------------------------------------------------------ */
-/* Partition.  Every flattened tensor is split into N near-equal contiguous   */
-/* chunks and rank r owns chunk r ([sim] partitioning paragraph; [pg] 3.4     */
-/* Stage 1, process r updates only partition r; [grasp] Stage 1 step 3).     */
+/* Partition.  The flat buffer is cut into N contiguous pieces of (almost)    */
+/* the same length, piece r belonging to rank r ([sim] partitioning          */
+/* paragraph; [pg] 3.4 Stage 1; [grasp] Stage 1 step 3).                      */
 /* Equal ceil(Psi/N) chunks, so the tail ranks are short or empty.            */
 /* ------------------------------------------------------------------------ */
 int oracle_partition(int64_t psi, int32_t nranks, int32_t rank, int64_t *shard, int64_t *offset,
@@ -249,10 +252,13 @@ double oracle_sumsq_value(const oracle_sumsq *a) {
 /* or clipping rule; mixed precision is cited to Micikevicius et al. ([pg] 3.4 */
 /* "16 Psi baseline").  Readings taken: a step whose reduced gradient holds    */
 /* inf/NaN is skipped (parameters, moments and step count unchanged); the      */
-/* dynamic scaler halves S (not below min_scale) on a skipped step and doubles */
-/* it after growth_interval consecutive finite steps; clipping multiplies g by */
-/* max/(norm + 1e-6) when norm > max.  The bias-correction powers beta^t are   */
-/* running binary64 products, one factor per applied step.                     */
+/* dynamic scaler halves S (not below min_scale) on a skipped step and, after  */
+/* growth_interval consecutive finite steps, doubles it unless the doubled     */
+/* value is not finite (then S stays; the run count restarts either way);      */
+/* unlike PyTorch's scaler, S never drops below min_scale;                     */
+/* clipping multiplies g by min(1, max/(norm + 1e-6)), the coefficient formed  */
+/* in binary64 and rounded once to binary32.  The bias-correction powers       */
+/* beta^t are running binary64 products, one factor per applied step.          */
 /* ------------------------------------------------------------------------ */
 typedef struct {
     float lr, beta1, beta2, eps, weight_decay, max_grad_norm;
@@ -300,14 +306,17 @@ void oracle_finalize(const oracle_hparams *hp, oracle_scalars *st, int32_t nonfi
         } else {
             st->good += 1;
             if (st->good == hp->growth_interval) {
-                st->scale = st->scale * 2.0f;
+                float twice = st->scale * 2.0f;
+                if (isfinite(twice)) st->scale = twice;
                 st->good = 0;
             }
         }
     }
     if (!rep->skip) {
-        if (hp->max_grad_norm > 0.0f && rep->norm > (double)hp->max_grad_norm)
-            rep->clip = (float)((double)hp->max_grad_norm / (rep->norm + 1e-6));
+        if (hp->max_grad_norm > 0.0f) {
+            double coef = (double)hp->max_grad_norm / (rep->norm + 1e-6);
+            if (coef < 1.0) rep->clip = (float)coef;
+        }
         st->t += 1;
         st->pow1 = st->pow1 * (double)hp->beta1;
         st->pow2 = st->pow2 * (double)hp->beta2;
@@ -315,8 +324,8 @@ void oracle_finalize(const oracle_hparams *hp, oracle_scalars *st, int32_t nonfi
 }
 
 /* ------------------------------------------------------------------------ */
-/* Adam on the owned slice.  Each GPU updates only its part of the fp32        */
-/* variance, momentum and parameters ([cmu] Mechanism 1 step 4; [pg] 3.4       */
+/* Adam on the owned slice: the rank's fp32 master weights and both moments    */
+/* are the only optimizer state it touches ([cmu] Mechanism 1 step 4; [pg] 3.4 */
 /* Stage 1; [grasp] Stage 1 step 3).  The pages cite Kingma and Ba and name    */
 /* AdamW with weight_decay ([bea] section 5) without printing the update, so   */
 /* the textbook bias-corrected form is used, epsilon outside the square root,  */
@@ -343,7 +352,7 @@ void oracle_adam(float *p, float *m, float *v, const float *g, int64_t len,
 }
 
 /* ------------------------------------------------------------------------ */
-/* Cast.  The updated fp32 parameters are copied to the 16-bit format in the   */
+/* Cast.  The new master weights, rounded to the 16-bit format, go into the   */
 /* rank's slot of the full parameter buffer that the all-gather fills ([cmu]   */
 /* Mechanism 1 steps 5-6; [grasp] Stage 1 step 4).                              */
 /* ------------------------------------------------------------------------ */

@@ -84,12 +84,13 @@ def test_c_program_steps_match_oracle(tmp_path):
             pos += nb + 8 * nblk
         reps = H.oracle_scalars(c)
         H.assert_reports(reports, reps)
+        exact = H.same_clips(reports, reps)
         p, m, v, oslot = H.oracle_elements(c, reps)
-        H.assert_f32_close("master", arrays[0], p)
-        H.assert_f32_close("m", arrays[1], m)
-        H.assert_f32_close("v", arrays[2], v)
+        H.assert_f32_close("master", arrays[0], p, exact)
+        H.assert_f32_close("m", arrays[1], m, exact)
+        H.assert_f32_close("v", arrays[2], v, exact)
         if has_slot:
-            H.assert_16bit_within_ulp("slot", slot, oslot, F16)
+            H.assert_16bit_within_ulp("slot", slot, oslot, F16, exact)
         if qbits:
             H.assert_qpayload((codes, rec.view(np.float32)[0::2], rec.view(np.int32)[1::2]),
                               O.quantize(oslot, F16, qbits))

@@ -65,11 +65,14 @@ def test_graph_replay_equals_eager(name):
         assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8)), what
     reps = H.oracle_scalars(c)
     H.assert_reports(g.reports, reps)
+    exact = H.same_clips(g.reports, reps)
     if c.part[2] <= 1_000_000:
         p, m, v, slot = g.fetch()
         rp, rm, rv, rslot = H.oracle_elements(c, reps)
-        H.assert_f32_close("master", p, rp)
-        H.assert_16bit_within_ulp("slot", slot, rslot, c.w.dtype)
+        H.assert_f32_close("master", p, rp, exact)
+        H.assert_f32_close("m", m, rm, exact)
+        H.assert_f32_close("v", v, rv, exact)
+        H.assert_16bit_within_ulp("slot", slot, rslot, c.w.dtype, exact)
     H.log(f"graph {name}: {c.steps} replays equal the eager steps; skips "
           f"{[r['skip'] for r in g.reports]}")
 

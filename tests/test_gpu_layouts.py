@@ -13,7 +13,9 @@ toy workload (Psi = 637,824, N = 32, 3 steps):
   ZeRO-2  every rank reduces only its slice (fused path, shared decisions);
   ZeRO-3  as ZeRO-2, but each rank's 16-bit output is a shard-local buffer.
 
-All four must agree bit for bit, and with the oracle.  The bucketed reduce
+All four must agree bit for bit, and with the oracle: on the plain toy run,
+and on a run with clipping, a dynamic loss scale and an overflow at step 2,
+where every layout takes the two-pass path and skips step 2.  The bucketed reduce
 (the reduce-scatter arriving in tile-aligned buckets during backward, paper
 summary 3.4 Stage 2, bucketization) must equal the one-shot reduce bit for
 bit, norm included.
@@ -40,34 +42,61 @@ def gpu():
     yield
 
 
-def _toy_layout(stage):
+# Two runs of the toy workload: the plain one (3 steps, fused path where
+# clipping is off), and one with clipping, a dynamic loss scale and an
+# overflow (+inf in contribution 5 at global element 400,000, step 2): every
+# layout then takes the two-pass path, the clip coefficient depends on the
+# global norm, and all ranks must skip step 2 together.
+TOY_RUNS = {
+    "plain": dict(hp={}, loss_scale=1.0, contrib_scale=1.0, steps=3, inject={}),
+    "clip_skip": dict(hp=dict(max_grad_norm=1e-4, scaler=2, min_scale=1.0), loss_scale=2.0 ** 10,
+                      contrib_scale=2.0 ** 10, steps=4, inject={2: (5, 400_000)}),
+}
+
+
+def _toy_layout(stage, run):
+    """The toy workload laid out as ZeRO-``stage``: (master, m, v, 16-bit
+    params, the ctrl of every step)."""
     import torch
     import synth
     import zero_partitioned_mixed_amd as Z
     w = workloads.TOY
     n, psi = w.nranks, w.psi
+    cfg = TOY_RUNS[run]
     dev = torch.device("cuda", 0)
-    hp = Z.hparams(lr=w.lr)
+    hp = Z.hparams(lr=w.lr, **cfg["hp"])
+    fused = hp.max_grad_norm <= 0
     p_full = torch.empty(psi, dtype=torch.float32, device=dev)
     synth.gpu_master_range(p_full, w.seed, w.master_sigma, 0)
     parts = [Z.zero_partition(psi, n, r) for r in range(n)]
 
     def fill(buf, step, off, valid):
-        synth.gpu_contrib_rows(buf, w.seed, step, F16, w.contrib_sigma, 1.0, 0.0, 100.0, off, valid)
+        synth.gpu_contrib_rows(buf, w.seed, step, F16, w.contrib_sigma, cfg["contrib_scale"], 0.0,
+                               100.0, off, valid)
+        if step in cfg["inject"]:
+            k, col = cfg["inject"][step]
+            if off <= col < off + valid:
+                buf[k, col - off] = float("inf")
 
+    def flat(valid, src=None):
+        return (p_full[src:src + valid].clone() if src is not None else p_full,
+                torch.zeros(valid, device=dev), torch.zeros(valid, device=dev))
+
+    ctrls = []
     if stage == 0:
         stride = (psi + 63) // 64 * 64
         C = torch.empty((n, stride), dtype=torch.float16, device=dev)
         gather = torch.empty(psi, dtype=torch.float16, device=dev)
         synth.gpu_param_range(gather, w.seed, w.master_sigma, F16, 0)
-        st = Z.ShardStep(n, stride, psi, 0, F16, F16, hp,
-                         (p_full, torch.zeros_like(p_full), torch.zeros_like(p_full)))
-        for s in range(1, w.steps + 1):
+        g = None if fused else torch.empty(psi, dtype=torch.float32, device=dev)
+        st = Z.ShardStep(n, stride, psi, 0, F16, F16, hp, flat(psi), g, cfg["loss_scale"])
+        for s in range(1, cfg["steps"] + 1):
             fill(C, s, 0, psi)
             st.step(C, gather)
+            ctrls.append(st.ctrl_dict())
         master, m, v = [t.cpu().numpy() for t in st.current()]
         params = gather.view(torch.int16).cpu().numpy().view(np.uint16)
-        return master, m, v, params, st.ctrl_dict()
+        return master, m, v, params, ctrls
 
     if stage == 1:
         stride = (psi + 63) // 64 * 64
@@ -77,31 +106,31 @@ def _toy_layout(stage):
         synth.gpu_param_range(gather, w.seed, w.master_sigma, F16, 0)
         ctrl = torch.empty(Z.zero_ctrl_bytes(), dtype=torch.uint8, device=dev)
         ws = torch.empty(Z.zero_workspace_bytes(psi), dtype=torch.uint8, device=dev)
-        Z.zero_ctrl_init(ctrl, 1.0)
-        states = [(p_full[off:off + valid].clone(), torch.zeros(valid, device=dev),
-                   torch.zeros(valid, device=dev)) for _, off, valid in parts]
-        for s in range(1, w.steps + 1):
+        Z.zero_ctrl_init(ctrl, cfg["loss_scale"])
+        states = [flat(valid, off) for _, off, valid in parts]
+        for s in range(1, cfg["steps"] + 1):
             fill(C, s, 0, psi)
             Z.zero_reduce_grads(C, F16, n, stride, psi, ctrl, g, ws)  # all-reduce mean
             Z.zero_grad_norm_overflow([ws], [psi], [ctrl], hp, False)
             for (_, off, valid), st in zip(parts, states):  # each rank: its slice
                 Z.zero_adam_step(st, g[off:off + valid], valid, hp, ctrl, gather, F16, off)
+            ctrls.append(Z.read_ctrl(ctrl))
         master = np.concatenate([st[0].cpu().numpy() for st in states])
         m = np.concatenate([st[1].cpu().numpy() for st in states])
         v = np.concatenate([st[2].cpu().numpy() for st in states])
         params = gather.view(torch.int16).cpu().numpy().view(np.uint16)
-        return master, m, v, params, Z.read_ctrl(ctrl)
+        return master, m, v, params, ctrls
 
-    # stages 2 and 3: one fused shard step per rank with shared decisions
+    # stages 2 and 3: one shard step per rank with shared decisions
     local = stage == 3
     gather = torch.empty(psi, dtype=torch.float16, device=dev)
     synth.gpu_param_range(gather, w.seed, w.master_sigma, F16, 0)
     steps, contribs, outs = [], [], []
     for _, off, valid in parts:
         stride = (valid + 63) // 64 * 64
-        st = Z.ShardStep(n, stride, valid, 0 if local else off, F16, F16, hp,
-                         (p_full[off:off + valid].clone(), torch.zeros(valid, device=dev),
-                          torch.zeros(valid, device=dev)))
+        g = None if fused else torch.empty(valid, dtype=torch.float32, device=dev)
+        st = Z.ShardStep(n, stride, valid, 0 if local else off, F16, F16, hp, flat(valid, off), g,
+                         cfg["loss_scale"])
         steps.append(st)
         contribs.append(torch.empty((n, stride), dtype=torch.float16, device=dev))
         if local:
@@ -109,19 +138,26 @@ def _toy_layout(stage):
             synth.gpu_param_range(o, w.seed, w.master_sigma, F16, off)
             outs.append(o)
     multi = Z.MultiShardStep(steps)
-    for s in range(1, w.steps + 1):
+    for s in range(1, cfg["steps"] + 1):
         for (_, off, valid), c in zip(parts, contribs):
             fill(c, s, off, valid)
         if local:  # each rank writes its own shard-local buffer
             for st, c, o in zip(steps, contribs, outs):
-                Z.zero_fused_step(c, F16, n, st.stride, st.pair, st.valid_len, o, F16, 0, hp,
-                                  st.ctrl, st.ws)
+                if fused:
+                    Z.zero_fused_step(c, F16, n, st.stride, st.pair, st.valid_len, o, F16, 0, hp,
+                                      st.ctrl, st.ws)
+                else:
+                    Z.zero_reduce_grads(c, F16, n, st.stride, st.valid_len, st.ctrl, st.g, st.ws)
             Z.zero_grad_norm_overflow([st.ws for st in steps], [st.valid_len for st in steps],
-                                      [st.ctrl for st in steps], hp, True)
+                                      [st.ctrl for st in steps], hp, fused)
             for st, o in zip(steps, outs):
-                Z.zero_fused_restore(st.pair, st.valid_len, o, F16, 0, st.ctrl)
+                if fused:
+                    Z.zero_fused_restore(st.pair, st.valid_len, o, F16, 0, st.ctrl)
+                else:
+                    Z.zero_adam_step(st.state, st.g, st.valid_len, hp, st.ctrl, o, F16, 0)
         else:
             multi.step(contribs, gather)
+        ctrls.append(steps[0].ctrl_dict())
     cur = [st.current() for st in steps]
     master = np.concatenate([c[0].cpu().numpy() for c in cur])
     m = np.concatenate([c[1].cpu().numpy() for c in cur])
@@ -130,29 +166,62 @@ def _toy_layout(stage):
         params = np.concatenate([o.view(torch.int16).cpu().numpy().view(np.uint16) for o in outs])
     else:
         params = gather.view(torch.int16).cpu().numpy().view(np.uint16)
-    return master, m, v, params, steps[0].ctrl_dict()
+    return master, m, v, params, ctrls
 
 
-def test_zero_stage_layouts_bitwise_equal_on_gpu():
+@pytest.mark.parametrize("run", list(TOY_RUNS))
+def test_zero_stage_layouts_bitwise_equal_on_gpu(run):
+    """All four layouts bit for bit equal to each other and to the oracle's
+    ZeRO-2 layout, every step's decisions included.  The GPU's norm is an
+    fp64 sum whose grouping follows the layout's tiles, so ZeRO-0/1 and
+    ZeRO-2/3 may differ in its last bits; the clip coefficient rounded to
+    fp32 from it must still agree (it would differ only for a norm within
+    about 1e-15 relative of an fp32 rounding boundary of the coefficient)."""
     import oracle as O
     from oracle import layouts
     import synth
+    cfg = TOY_RUNS[run]
     res = {}
     for stage in (0, 1, 2, 3):
-        res[stage] = _toy_layout(stage)
-        H.log(f"layout ZeRO-{stage}: t={res[stage][4]['t']} norm={res[stage][4]['norm']:.12g}")
+        res[stage] = _toy_layout(stage, run)
+        last = res[stage][4][-1]
+        H.log(f"{run} layout ZeRO-{stage}: t={last['t']} norm={last['norm']:.17g} "
+              f"skips={[c['skip'] for c in res[stage][4]]} clips={[c['clip'] for c in res[stage][4]]}")
     for stage in (1, 2, 3):
         for name, a, b in zip(("master", "m", "v"), res[0][:3], res[stage][:3]):
             assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), (stage, name)
         assert np.array_equal(res[0][3], res[stage][3]), (stage, "params")
-        assert res[stage][4]["sumsq"] == res[0][4]["sumsq"] or stage in (2, 3)
-    # and the oracle's ZeRO-2 layout
+        for s, (c0, c1) in enumerate(zip(res[0][4], res[stage][4]), 1):
+            for key in ("skip", "nonfinite", "t", "clip", "loss_scale", "scale_used"):
+                assert c0[key] == c1[key], (stage, s, key, c0[key], c1[key])
+            if np.isfinite(c0["norm"]):
+                assert abs(c0["norm"] - c1["norm"]) <= 1e-14 * c0["norm"], (stage, s, "norm")
+            if stage == 1:  # the same tiles: the same sum
+                assert c0["sumsq"] == c1["sumsq"] or not np.isfinite(c0["sumsq"])
+    # and the oracle's ZeRO-2 layout (exact norm)
     w = workloads.TOY
-    contrib = lambda s: synth.contrib_rows(w.seed, s, w.nranks, F16, w.contrib_sigma, 1.0, 0.0,
-                                           100.0, 0, w.psi)
-    om, omm, ov, op, _ = layouts.run(2, w.psi, w.nranks, w.steps, contrib,
-                                     synth.master_range(w.seed, w.master_sigma, 0, w.psi),
-                                     O.hparams(lr=w.lr))
+    inj = cfg["inject"]
+
+    def contrib(s):
+        C = synth.contrib_rows(w.seed, s, w.nranks, F16, w.contrib_sigma, cfg["contrib_scale"], 0.0,
+                               100.0, 0, w.psi)
+        if s in inj:
+            C[inj[s][0], inj[s][1]] = 0x7C00
+        return C
+
+    om, omm, ov, op, oreps = layouts.run(2, w.psi, w.nranks, cfg["steps"], contrib,
+                                         synth.master_range(w.seed, w.master_sigma, 0, w.psi),
+                                         O.hparams(lr=w.lr, **cfg["hp"]),
+                                         loss_scale=cfg["loss_scale"])
+    for s, (c, r) in enumerate(zip(res[2][4], oreps), 1):
+        assert (c["skip"], c["nonfinite"]) == (r["skip"], r["nonfinite"]), (s, c, r)
+        assert np.float32(c["clip"]) == np.float32(r["clip"]) or r["skip"], (s, c["clip"], r["clip"])
+        if np.isfinite(r["norm"]):
+            assert abs(c["norm"] - r["norm"]) <= H.NORM_RTOL * r["norm"], (s, c["norm"], r["norm"])
+    if run == "clip_skip":
+        skips = [r["skip"] for r in oreps]
+        assert skips == [0, 1, 0, 0]
+        assert all(r["clip"] < 1.0 for r in oreps if not r["skip"])
     H.assert_f32_close("master", res[0][0], om)
     H.assert_f32_close("m", res[0][1], omm)
     H.assert_f32_close("v", res[0][2], ov)

@@ -8,6 +8,14 @@ Parameter Models" summary, 3.4 "Model-State Memory Analysis").  Decoupled
 weight decay ("ZeRO Stage 1/2/3" guide, section 5, AdamW with weight_decay)
 adds a geometric factor.  torch.optim.AdamW in fp32 on the CPU is an
 independent library cross-check.
+
+The pages give no clip rule and no loss-scale schedule; the readings taken
+are PyTorch's, and these tests pin the oracle's decisions to PyTorch's own
+CPU routines: torch.nn.utils.clip_grads_with_norm_ (coefficient
+min(1, max / (norm + 1e-6)), here given the oracle's binary64 norm) and
+torch._amp_update_scale_ (halve on overflow, double after growth_interval
+clean steps unless the doubled scale is not finite).  The one departure,
+the min_scale floor, has its own test.
 """
 import numpy as np
 import pytest
@@ -137,7 +145,116 @@ def test_clip_rescales_to_max_norm(O, target_norm):
     assert abs(post - rep.norm / (rep.norm + 1e-6)) <= 1e-7
 
 
+def _torch_clipped(g: np.ndarray, norm: float, max_norm: float) -> np.ndarray:
+    """g (fp32) after torch.nn.utils.clip_grads_with_norm_ with total norm `norm`."""
+    t = torch.nn.Parameter(torch.zeros(g.size, dtype=torch.float32))
+    t.grad = torch.from_numpy(g.copy())
+    torch.nn.utils.clip_grads_with_norm_([t], max_norm, torch.tensor(norm, dtype=torch.float64),
+                                         foreach=False)
+    return t.grad.numpy()
+
+
+def _clip_case_grads():
+    """Gradients whose norms fall far below, just below, inside the window
+    (max - 1e-6, max], exactly on, just above and far above max = 1, and
+    around other thresholds."""
+    cases = []
+    for x in (0.5, 0.999998, 0.9999990, 0.9999995, np.nextafter(np.float32(1), np.float32(0)),
+              1.0, np.nextafter(np.float32(1), np.float32(2)), 1.0000010, 1.5, 34.7, 1e6):
+        cases.append((np.array([x], np.float32), 1.0))   # norm = |x| exactly
+    for max_norm in (1.0, 0.25, 3.0, 1e-3):
+        for target in (0.3, 0.9999999, 1.0, 1.0000003, 2.0, 316.0):
+            g = rng.normal(0, 1.0, 4096)
+            g = (g * (target * max_norm / np.linalg.norm(g))).astype(np.float32)
+            cases.append((g, max_norm))
+    for _ in range(200):
+        g = rng.normal(0, 1.0, int(rng.integers(1, 64))).astype(np.float32)
+        cases.append((g * np.float32(10.0 ** rng.uniform(-3, 3)), float(np.float32(rng.uniform(0.1, 5)))))
+    return cases
+
+
+def test_clip_rule_matches_torch():
+    """For every norm, the oracle's clipped gradient equals, bit for bit,
+    torch's clip_grads_with_norm_ given the same binary64 norm: the same
+    coefficient (rounded once to fp32, 1 where torch clamps it) applied by the
+    same fp32 multiplication.  Includes norms in (max - 1e-6, max], which
+    torch scales and a rule 'clip only when norm > max' would not."""
+    import oracle as O
+    in_window = 0
+    for g, max_norm in _clip_case_grads():
+        max_norm = float(np.float32(max_norm))  # the threshold is an fp32 setting
+        hp = O.hparams(max_grad_norm=max_norm)
+        rep = O.finalize(hp, O.new_scalars(1.0), 0, O.SumSq().add(g))
+        ref = _torch_clipped(g, rep.norm, max_norm)
+        ours = g * np.float32(rep.clip)
+        assert np.array_equal(ours.view(np.uint32), ref.view(np.uint32)), (max_norm, rep.norm, rep.clip)
+        coef = max_norm / (rep.norm + 1e-6)
+        assert (rep.clip == 1.0) == (coef >= 1.0), (max_norm, rep.norm, rep.clip)
+        if max_norm - 1e-6 < rep.norm <= max_norm:
+            in_window += 1
+            assert rep.clip < 1.0
+    assert in_window >= 3
+
+
 # ------------------------------------------------------------------------- loss scale
+def _torch_scaler(scale0: float, flags, growth_interval: int):
+    """(scale, growth tracker) after each step of torch._amp_update_scale_
+    with growth factor 2 and backoff 0.5 (GradScaler's defaults)."""
+    s = torch.tensor([scale0], dtype=torch.float32)
+    tracker = torch.zeros(1, dtype=torch.int32)
+    out = []
+    for bad in flags:
+        torch._amp_update_scale_(s, tracker, torch.tensor([1.0 if bad else 0.0]), 2.0, 0.5,
+                                 growth_interval)
+        out.append((float(s[0]), int(tracker[0])))
+    return out
+
+
+@pytest.mark.parametrize("scale0,growth_interval,p_bad", [
+    (2.0 ** 15, 1000, 0.2), (2.0 ** 15, 1, 0.3), (2.0 ** 16, 2, 0.25), (1.0, 3, 0.1),
+    (0.75, 1, 0.0), (2.0 ** 126, 1, 0.0), (2.0 ** 127, 1, 0.05), (3.0e38, 2, 0.05),
+    (2.0 ** 120, 5, 0.02), (1.5 * 2.0 ** 100, 1, 0.5)])
+def test_scaler_matches_torch(O, scale0, growth_interval, p_bad):
+    """The dynamic scaler's trace equals torch._amp_update_scale_'s (scale and
+    run count after every step), including growth that would overflow fp32:
+    torch keeps the scale there and so does the oracle."""
+    flags = [int(b) for b in np.random.default_rng(int(scale0 % 977) + growth_interval).random(300)
+             < p_bad]
+    flags[:3] = [0, 0, 0]
+    hp = O.hparams(scaler=2, min_scale=2.0 ** -126, growth_interval=growth_interval)
+    st = O.new_scalars(scale0)
+    ref = _torch_scaler(scale0, flags, growth_interval)
+    for i, (bad, (s_ref, tr_ref)) in enumerate(zip(flags, ref)):
+        assert s_ref >= 2.0 ** -126  # the floor never binds in these traces
+        _flags_step(O, hp, st, bad)
+        assert (st.scale, st.good) == (s_ref, tr_ref), (i, st.scale, st.good, s_ref, tr_ref)
+        assert np.isfinite(st.scale)
+
+
+def test_scaler_growth_never_reaches_infinity(O):
+    """From 2^127 with growth_interval 1 every applied step asks to double: the
+    scale stays 2^127 (as torch's does) instead of becoming inf."""
+    hp = O.hparams(scaler=2, min_scale=1.0, growth_interval=1)
+    st = O.new_scalars(2.0 ** 127)
+    for _ in range(5):
+        rep = _flags_step(O, hp, st, 0)
+        assert rep.skip == 0 and st.scale == 2.0 ** 127 and st.good == 0
+    assert _torch_scaler(2.0 ** 127, [0] * 5, 1)[-1] == (2.0 ** 127, 0)
+
+
+def test_scaler_floor_departs_from_torch(O):
+    """The one departure: torch halves below any floor (down to 0); the
+    oracle's scale stops at min_scale."""
+    hp = O.hparams(scaler=2, min_scale=0.25, growth_interval=1000)
+    st = O.new_scalars(1.0)
+    flags = [1, 1, 1, 1]
+    ref = _torch_scaler(1.0, flags, 1000)
+    ours = []
+    for bad in flags:
+        _flags_step(O, hp, st, bad)
+        ours.append(st.scale)
+    assert [s for s, _ in ref] == [0.5, 0.25, 0.125, 0.0625]
+    assert ours == [0.5, 0.25, 0.25, 0.25]
 def _flags_step(O, hp, st, bad):
     g = np.array([np.inf if bad else 1e-3], np.float32)
     return O.finalize(hp, st, int(bad), O.SumSq().add(g))

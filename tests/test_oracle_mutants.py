@@ -35,8 +35,16 @@ MUTANTS = {
                            "float mi = b2 * m[i] + omb2 * gi;", [ADAM]),
     "step_count_not_advanced": ("st->pow1 = st->pow1 * (double)hp->beta1;",
                                 "st->pow1 = st->pow1;", [ADAM]),
-    "clip_without_epsilon": ("rep->clip = (float)((double)hp->max_grad_norm / (rep->norm + 1e-6));",
-                             "rep->clip = (float)((double)hp->max_grad_norm / rep->norm);", [ADAM]),
+    "clip_without_epsilon": ("double coef = (double)hp->max_grad_norm / (rep->norm + 1e-6);",
+                             "double coef = (double)hp->max_grad_norm / rep->norm;", [ADAM]),
+    "clip_only_above_max": ("if (coef < 1.0) rep->clip = (float)coef;",
+                            "if (coef < 1.0 && rep->norm > (double)hp->max_grad_norm) "
+                            "rep->clip = (float)coef;", [ADAM]),
+    "clip_coefficient_in_fp32": ("double coef = (double)hp->max_grad_norm / (rep->norm + 1e-6);",
+                                 "double coef = (double)(hp->max_grad_norm / "
+                                 "(float)(rep->norm + 1e-6));", [ADAM]),
+    "growth_overflows_to_inf": ("if (isfinite(twice)) st->scale = twice;", "st->scale = twice;",
+                                [ADAM]),
     "scaler_no_halving": ("float half = st->scale * 0.5f;", "float half = st->scale;", [ADAM]),
     "reduce_reverse_order": (
         "for (int32_t k = 0; k < n; ++k) acc = acc + oracle_to_f32(C[(int64_t)k * stride + i], dtype);",
@@ -63,8 +71,8 @@ MUTANTS = {
                                   "mag = (double)f * pow2i(F->emin - fb - 1);", [FMT_ALL]),
     "sumsq_bit_position": ("int p = 2 * e + 296;", "int p = 2 * e + 297;", [REDUCE]),
     "skip_ignores_overflow": ("rep->skip = rep->nonfinite;", "rep->skip = 0;", [ADAM]),
-    "growth_without_reset": ("st->scale = st->scale * 2.0f;\n                st->good = 0;",
-                             "st->scale = st->scale * 2.0f;", [ADAM]),
+    "growth_without_reset": ("if (isfinite(twice)) st->scale = twice;\n                st->good = 0;",
+                             "if (isfinite(twice)) st->scale = twice;", [ADAM]),
     "quant_no_zero_point": ("const float z = q_clamp_code(rintf(-lo / s), qmax);",
                             "const float z = 0.0f;", [QUANT]),
     "quant_truncates": ("q_clamp_code(rintf(x / s) + z, qmax)", "q_clamp_code(truncf(x / s) + z, qmax)",

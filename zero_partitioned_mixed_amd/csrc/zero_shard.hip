@@ -699,14 +699,19 @@ __global__ void __launch_bounds__(kFinBlock) finalize_kernel(CombineArgs a) {
         } else {
             c.good_steps += 1;
             if (c.good_steps == hp.growth_interval) {
-                c.loss_scale = c.loss_scale * 2.0f;
+                // a doubling that overflows keeps the scale (the run restarts either way)
+                const float twice = c.loss_scale * 2.0f;
+                if (__builtin_isfinite(twice)) c.loss_scale = twice;
                 c.good_steps = 0;
             }
         }
     }
     if (!c.skip) {
-        if (hp.max_grad_norm > 0.0f && c.norm > (double)hp.max_grad_norm)
-            c.clip = (float)((double)hp.max_grad_norm / (c.norm + 1e-6));
+        // g is multiplied by min(1, max / (norm + 1e-6)), formed in fp64
+        if (hp.max_grad_norm > 0.0f) {
+            const double coef = (double)hp.max_grad_norm / (c.norm + 1e-6);
+            if (coef < 1.0) c.clip = (float)coef;
+        }
         c.t += 1;
         c.beta1_pow = c.beta1_pow * (double)hp.beta1;
         c.beta2_pow = c.beta2_pow * (double)hp.beta2;
