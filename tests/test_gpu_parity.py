@@ -128,13 +128,44 @@ SMALL = {
     "f16_fused_dynamic_growth": (small(60_016, 4, 3, steps=6, scaler=2, growth_interval=2,
                                        contrib_scale=2.0 ** 12, loss_scale=2.0 ** 12),
                                  (Inject(4, 1, 5, np.inf),)),
+    # growth asked for at every step from the largest power of two in fp32:
+    # the scale stays 2^127 instead of overflowing to inf (bf16 contributions
+    # carry that scale; the unscaled gradient is ~1e-3)
+    "bf16_fused_growth_at_fp32_max": (small(60_016, 4, 3, dtype=BF16, steps=4, scaler=2,
+                                            growth_interval=1, contrib_scale=2.0 ** 127,
+                                            loss_scale=2.0 ** 127), ()),
+    "bf16_twopass_growth_at_fp32_max": (small(100_003, 3, 1, dtype=BF16, steps=3, scaler=2,
+                                              growth_interval=1, contrib_scale=2.0 ** 127,
+                                              loss_scale=2.0 ** 127, max_grad_norm=1.0), ()),
 }
 
 
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_cases(name):
     w, extra = SMALL[name]
-    run_case(Case(w, w.ranks[0], w.steps, extra=tuple(extra)), name)
+    g, _ = run_case(Case(w, w.ranks[0], w.steps, extra=tuple(extra)), name)
+    if "growth_at_fp32_max" in name:
+        assert all(r["loss_scale"] == 2.0 ** 127 for r in g.reports)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_clip_threshold_just_above_the_norm(dtype):
+    """max_grad_norm set to an fp32 value in (norm, norm + 1e-6] of the first
+    step's gradient: the coefficient max / (norm + 1e-6) is below 1, so the
+    step is clipped (as torch's clip_grad_norm_ clips it) although the norm
+    does not exceed the threshold."""
+    w0 = small(100_003, 3, 1, dtype=dtype, steps=1)
+    norm = H.oracle_scalars(Case(w0, 1, 1))[0]["norm"]
+    mx = np.float32(norm)
+    while float(mx) <= norm:
+        mx = np.nextafter(mx, np.float32(np.inf))
+    assert norm < float(mx) <= norm + 1e-6
+    w = replace(w0, max_grad_norm=float(mx), steps=2)
+    c = Case(w, 1, 2)
+    reps = H.oracle_scalars(c)
+    assert reps[0]["clip"] < 1.0
+    g, _ = run_case(c, f"clip window dtype={dtype} max={float(mx)!r} norm={norm!r}")
+    assert g.reports[0]["clip"] == reps[0]["clip"] < 1.0
 
 
 DYN = dict(scaler=2, contrib_scale=2.0 ** 10, loss_scale=2.0 ** 10)
