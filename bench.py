@@ -189,6 +189,44 @@ def timed_steps(b, steps, warmup, torch, Z, graph=False, qg=None):
     return step_ms, per_step, kern_ms, red_ms, ctrl
 
 
+def timed_skip_steps(b, w, torch, reps=3):
+    """Steps that the workload's injected +inf forces to skip (the 13B
+    shard's step 2): the fused pass, the decision (skip, halve the scale) and
+    the restore of the slot from the kept master, timed whole and per part
+    with HIP events on the launch stream.  The contribution element is put
+    back afterwards."""
+    (_, k, col), = w.inject_inf
+    st, contrib, gather = b["step"], b["contrib"], b["gather"]
+    cell = contrib[k][col:col + 1] if isinstance(contrib, list) else contrib[k, col:col + 1]
+    orig = cell.clone()
+    cell.fill_(float("inf"))
+    torch.cuda.synchronize()
+    rows = []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        st.run_pieces(contrib, gather)
+        e[1].record()
+        st.decide()
+        e[2].record()
+        st.complete(gather)
+        e[3].record()
+        torch.cuda.synchronize()
+        c = st.ctrl_dict()
+        if not c["skip"]:
+            raise RuntimeError("the injected +inf did not skip the step")
+        rows.append([e[0].elapsed_time(e[3]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3]),
+                     c["loss_scale"]])
+    cell.copy_(orig)
+    torch.cuda.synchronize()
+    ms, dec_ms, restore_ms, _ = sorted(rows)[len(rows) // 2]
+    valid = b["valid"]
+    return {"ms": _fmt(ms, 5), "decision_ms": _fmt(dec_ms, 4), "restore_ms": _fmt(restore_ms, 5),
+            "restore_gbps": _fmt(6 * valid / (restore_ms * 1e-3) / 1e9, 5),
+            "restore_bytes": 6 * valid, "steps": reps,
+            "loss_scales_after": [r[3] for r in rows]}
+
+
 def copy_bandwidth(torch, synth, nbytes=8 << 30, reps=10):
     """Plain device copy: a reachable-bandwidth reference line."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -261,6 +299,93 @@ def cpu_baseline(w, sample_elems):
             "elements_per_s": _fmt(S / dt, 4)}
 
 
+def measure(w, args, bucket, torch, synth, Z) -> dict:
+    """One workload's timed steps (with the flags' contribution form, payload,
+    buckets and launch) and the fields of its bench line."""
+    b = setup(w, torch, synth, Z, rows=args.rows, qbits=args.quant, bucket=bucket)
+    b_pieces = b["step"].pieces()
+    pieces = len(b_pieces)
+    row_pass_n = w.nranks if b["fused"] else 0  # the timed pass reads the N rows (fused) or not
+    valid = b["valid"]
+    qg = Z.QGather.alloc(valid, args.qgather, torch.device("cuda", 0)) if args.qgather else None
+    ms_step, per_step, kern_ms, red_ms, ctrl = timed_steps(b, args.steps, args.warmup, torch, Z,
+                                                           graph=args.graph, qg=qg)
+    skip = None
+    if b["fused"] and w.inject_inf and not args.quant and qg is None and pieces == 1:
+        skip = timed_skip_steps(b, w, torch)
+    bpe = quant_bytes_per_elem(w, args.quant) if args.quant else w.bytes_per_elem
+    if args.qgather:  # the 2-byte slot replaced by the codes and one 8-byte record per block
+        bpe = bpe - 2 + args.qgather / 8 + 8 / 2048
+    step_bytes = int(round(bpe * valid))
+    gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    if b["fused"]:
+        kern_name = ("fused_kernel_q%d" % args.quant if args.quant else
+                     "fused_kernel_rows" if args.rows else "fused_kernel")
+        if args.qgather:
+            kern_name = ("fused_qgather_kernel_q%d" % args.qgather if kern_name == "fused_kernel"
+                         else "%s_qgather%d" % (kern_name, args.qgather))
+        kern_bytes = step_bytes
+    elif args.qgather:
+        kern_name = "adam_qgather_kernel_q%d" % args.qgather
+        kern_bytes = int(round((4 + 24 + args.qgather / 8 + 8 / 2048) * valid))  # payload, no slot
+    else:
+        kern_name = "adam_kernel"
+        kern_bytes = (4 + 26) * valid  # g + master/m/v in and out + the 16-bit slot
+    kern_gbps = kern_bytes / (kern_avg * 1e-3) / 1e9
+    del b, qg
+    torch.cuda.empty_cache()
+
+    out = {
+        "value": _fmt(gbps, 5),
+        "unit": "GB/s",
+        "ms_per_step": _fmt(ms_step, 5),
+        "config": {"workload": w.name, "psi": w.psi, "nranks": w.nranks, "rank": w.ranks[-1],
+                   "shard_elems": valid, "variant": w.variant,
+                   "contrib_dtype": "fp16" if w.dtype == Z.F16 else "bf16",
+                   "bytes_per_elem": _fmt(bpe, 6), "step_bytes": step_bytes,
+                   "contrib_layout": ("int%d_blocks" % args.quant if args.quant else
+                                      "row_table" if args.rows else "strided"),
+                   "gather_payload": ("int%d_blocks" % args.qgather if args.qgather else
+                                      "16bit_slot"),
+                   "bucket_elems": bucket, "calls_per_pass": pieces,
+                   "launch": "hip_graph" if args.graph else "stream"},
+        "step_ms_median": _fmt(per_step[len(per_step) // 2], 5),
+        "step_ms_min": _fmt(per_step[0], 5),
+        "pct_hbm_peak": _fmt(100 * gbps / HBM_PEAK_GBPS, 4),
+        "elements_per_s": _fmt(valid / (ms_step * 1e-3), 5),
+        "roofline": {"bound": "hbm", "kernel": kern_name, "achieved": _fmt(kern_gbps, 5),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": _fmt(kern_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None,
+                     "kernel_ms": _fmt(kern_avg, 5), "bytes_per_pass": kern_bytes,
+                     "launches_per_pass": sum(Z.launches(n, row_pass_n, payload=bool(
+                         args.qgather) and row_pass_n > 0) for _, n in b_pieces)},
+        "reduce_kernel": None,
+        "last_step": {"norm": ctrl["norm"], "skip": ctrl["skip"], "t": ctrl["t"],
+                      "loss_scale": ctrl["loss_scale"]},
+    }
+    # the committed counters cover the pass issued as one call
+    measured = measured_traffic(kern_name, w.name) if pieces == 1 else None
+    if measured is not None:
+        traffic, profiled_kernel, digest = measured
+        out["roofline"].update(traffic=traffic, traffic_ratio=_fmt(traffic / kern_bytes, 5),
+                               traffic_kernel=profiled_kernel, traffic_isa_sha256=digest[:16])
+    if red_ms:
+        red_avg = sum(red_ms) / len(red_ms)
+        red_bpe = 4 + (w.nranks * (args.quant / 8 + 8 / 2048) if args.quant else 2 * w.nranks)
+        red_bytes = int(round(red_bpe * valid))
+        out["reduce_kernel"] = {"ms": _fmt(red_avg, 5),
+                                "gbps": _fmt(red_bytes / (red_avg * 1e-3) / 1e9, 5),
+                                "bytes_per_pass": red_bytes}
+        red = measured_traffic("reduce_kernel", w.name) if pieces == 1 and not args.quant else None
+        if red is not None:
+            out["reduce_kernel"].update(traffic=red[0], traffic_ratio=_fmt(red[0] / red_bytes, 5))
+    if skip is not None:
+        out["skip_step"] = skip
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,6 +411,8 @@ def main():
                     help="elements of the shard the CPU oracle baseline steps over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true")
+    ap.add_argument("--no-7b", action="store_true",
+                    help="leave out the 7B two-pass line that the default run appends as 'c4'")
     ap.add_argument("--copy-only", action="store_true",
                     help="run only the plain copy kernel (counter calibration)")
     args = ap.parse_args()
@@ -316,85 +443,30 @@ def main():
     if args.bucket and not bucket:
         print("--bucket must be at least 2048 elements", file=sys.stderr)
         sys.exit(2)
-    b = setup(w, torch, synth, Z, rows=args.rows, qbits=args.quant, bucket=bucket)
-    b_pieces = b["step"].pieces()
-    pieces = len(b_pieces)
-    row_pass_n = w.nranks if b["fused"] else 0  # the timed pass reads the N rows (fused) or not
-    valid = b["valid"]
-    qg = Z.QGather.alloc(valid, args.qgather, torch.device("cuda", 0)) if args.qgather else None
-    ms_step, per_step, kern_ms, red_ms, ctrl = timed_steps(b, args.steps, args.warmup, torch, Z,
-                                                           graph=args.graph, qg=qg)
-    bpe = quant_bytes_per_elem(w, args.quant) if args.quant else w.bytes_per_elem
-    if args.qgather:  # the 2-byte slot replaced by the codes and one 8-byte record per block
-        bpe = bpe - 2 + args.qgather / 8 + 8 / 2048
-    step_bytes = int(round(bpe * valid))
-    gbps = step_bytes / (ms_step * 1e-3) / 1e9
-    kern_avg = sum(kern_ms) / len(kern_ms)
-    if b["fused"]:
-        kern_name = ("fused_kernel_q%d" % args.quant if args.quant else
-                     "fused_kernel_rows" if args.rows else "fused_kernel")
-        if args.qgather:
-            kern_name = ("fused_qgather_kernel_q%d" % args.qgather if kern_name == "fused_kernel"
-                         else "%s_qgather%d" % (kern_name, args.qgather))
-        kern_bytes = step_bytes
-    elif args.qgather:
-        kern_name = "adam_qgather_kernel_q%d" % args.qgather
-        kern_bytes = int(round((4 + 24 + args.qgather / 8 + 8 / 2048) * valid))  # payload, no slot
-    else:
-        kern_name = "adam_kernel"
-        kern_bytes = (4 + 26) * valid  # g + master/m/v in and out + the 16-bit slot
-    kern_gbps = kern_bytes / (kern_avg * 1e-3) / 1e9
-    del b, qg
-    torch.cuda.empty_cache()
-
+    head = measure(w, args, bucket, torch, synth, Z)
     out = {
         "metric": METRIC,
-        "value": _fmt(gbps, 5),
-        "unit": "GB/s",
+        "value": head.pop("value"),
+        "unit": head.pop("unit"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": _fmt(ms_step, 5),
+        "ms_per_step": head.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "psi": w.psi, "nranks": w.nranks, "rank": w.ranks[-1],
-                   "shard_elems": valid, "variant": w.variant,
-                   "contrib_dtype": "fp16" if w.dtype == Z.F16 else "bf16",
-                   "bytes_per_elem": _fmt(bpe, 6), "step_bytes": step_bytes,
-                   "contrib_layout": ("int%d_blocks" % args.quant if args.quant else
-                                      "row_table" if args.rows else "strided"),
-                   "gather_payload": ("int%d_blocks" % args.qgather if args.qgather else
-                                      "16bit_slot"),
-                   "bucket_elems": bucket, "calls_per_pass": pieces,
-                   "launch": "hip_graph" if args.graph else "stream"},
-        "step_ms_median": _fmt(per_step[len(per_step) // 2], 5),
-        "step_ms_min": _fmt(per_step[0], 5),
-        "pct_hbm_peak": _fmt(100 * gbps / HBM_PEAK_GBPS, 4),
-        "elements_per_s": _fmt(valid / (ms_step * 1e-3), 5),
-        "roofline": {"bound": "hbm", "kernel": kern_name, "achieved": _fmt(kern_gbps, 5),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": _fmt(kern_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None,
-                     "kernel_ms": _fmt(kern_avg, 5), "bytes_per_pass": kern_bytes,
-                     "launches_per_pass": sum(Z.launches(n, row_pass_n, payload=bool(
-                         args.qgather) and row_pass_n > 0) for _, n in b_pieces)},
-        "last_step": {"norm": ctrl["norm"], "skip": ctrl["skip"], "t": ctrl["t"],
-                      "loss_scale": ctrl["loss_scale"]},
     }
-    # the committed counters cover the pass issued as one call
-    measured = measured_traffic(kern_name, w.name) if pieces == 1 else None
-    if measured is not None:
-        traffic, profiled_kernel, digest = measured
-        out["roofline"].update(traffic=traffic, traffic_ratio=_fmt(traffic / kern_bytes, 5),
-                               traffic_kernel=profiled_kernel, traffic_isa_sha256=digest[:16])
-    if red_ms:
-        red_avg = sum(red_ms) / len(red_ms)
-        red_bpe = 4 + (w.nranks * (args.quant / 8 + 8 / 2048) if args.quant else 2 * w.nranks)
-        out["reduce_kernel"] = {"ms": _fmt(red_avg, 5),
-                                "gbps": _fmt(red_bpe * valid / (red_avg * 1e-3) / 1e9, 5)}
+    out.update(head)
+    plain = not (args.quant or args.qgather or bucket or args.graph or args.rows)
+    if args.workload == DEFAULT_WORKLOAD and plain and not args.no_7b:
+        # the 7B shard (clipping on, so the two-pass path), measured in the
+        # same run after the 13B buffers are freed
+        c4 = measure(workloads.P7B, args, 0, torch, synth, Z)
+        out["c4"] = {key: c4[key] for key in ("value", "unit", "ms_per_step", "pct_hbm_peak",
+                                             "step_ms_median", "step_ms_min", "elements_per_s",
+                                             "config", "roofline", "reduce_kernel", "last_step")}
     try:
         out["device"] = synth.gpu_device_info(0)
     except (RuntimeError, OSError, AttributeError) as e:  # informational only
@@ -402,7 +474,7 @@ def main():
     if not args.no_copy:
         cg, _ = copy_bandwidth(torch, synth)
         out["copy_gbps"] = _fmt(cg, 5)
-        out["pct_of_copy"] = _fmt(100 * gbps / cg, 4)
+        out["pct_of_copy"] = _fmt(100 * out["value"] / cg, 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
     print(json.dumps(out), flush=True)

@@ -148,6 +148,21 @@ def test_small_cases(name):
         assert all(r["loss_scale"] == 2.0 ** 127 for r in g.reports)
 
 
+# Shards long enough for the restore's unrolled loop (eight whole tiles per
+# workgroup of its 256-workgroup grid, so at least 2,048 tiles) plus its
+# one-tile remainder and a partial last tile; a skip at step 2 makes the
+# restore rewrite the slot.  Offsets: 8-byte, 4-byte and 2-byte aligned slots.
+@pytest.mark.parametrize("psi,n,rank", [(2 * 4_200_001, 2, 1), (3 * 4_200_002, 3, 1),
+                                        (2 * 4_200_004, 2, 1)])
+def test_restore_after_skip_long_shard(psi, n, rank):
+    w = small(psi, n, rank, steps=3, **DYN)
+    _, off, valid = H.O.partition(psi, n, rank)
+    assert valid // 2048 >= 2048
+    c = Case(w, rank, 3, extra=(Inject(2, n - 1, valid - 7, np.inf),))
+    g, _ = run_case(c, f"restore long shard psi={psi} n={n} offset%4={off % 4}")
+    assert [r["skip"] for r in g.reports] == [0, 1, 0]
+
+
 @pytest.mark.parametrize("dtype", [F16, BF16])
 def test_clip_threshold_just_above_the_norm(dtype):
     """max_grad_norm set to an fp32 value in (norm, norm + 1e-6] of the first
