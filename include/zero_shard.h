@@ -492,6 +492,28 @@ int zero_fused_restore_q(const zero_state *pair, int64_t valid_len, void *gather
                          int32_t dtype, int64_t offset, int32_t bits, void *codes_dev,
                          zero_qblock *blocks_dev, const zero_ctrl *ctrl_dev, void *stream);
 
+/* ---- Allocation-free step ---------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): one rank's
+ * whole fused step without a workspace argument.  It is zero_fused_step
+ * followed by zero_grad_norm_overflow (this rank alone, pingpong = 1) and
+ * zero_fused_restore, with the per-tile norm and overflow partials kept in
+ * a static device array inside the library (ZERO_NOALLOC_MAX_LEN /
+ * ZERO_TILE + 256 partials of ZERO_PARTIAL_BYTES, about 16 MiB, held by every
+ * GPU the library runs on until the process ends); the results equal those
+ * three calls' bit for bit.  The caller passes inputs, state, slot and ctrl
+ * as for zero_fused_step; the call allocates nothing.  All calls on one GPU
+ * share that array: calls that overlap on one GPU (on different streams, or
+ * from different threads without ordering) race, so they must be ordered.
+ * Errors: those of zero_fused_step, ERANGE for valid_len above
+ * ZERO_NOALLOC_MAX_LEN (nothing enqueued), EHIP if the array's device
+ * address cannot be obtained (first call on each device). */
+#define ZERO_NOALLOC_MAX_LEN 2147483648LL
+int zero_fused_step_noalloc(const void *contrib_dev, int32_t contrib_dtype, int32_t nranks,
+                            int64_t stride, const zero_state *pair, int64_t valid_len,
+                            void *gather_dev, int32_t gather_dtype, int64_t offset,
+                            const zero_hparams *hp, zero_ctrl *ctrl_dev, void *stream);
+
 /* Message for the last nonzero return on the calling thread ("" if none). */
 const char *zero_last_error(void);
 

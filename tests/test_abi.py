@@ -119,6 +119,26 @@ def test_fused_rejects_clipping_and_a_bad_paired_state(Z):
     assert rc == -4  # workspace too small
 
 
+def test_fused_noalloc_validation(Z):
+    """The allocation-free step rejects its arguments before it looks up its
+    scratch array or enqueues anything: sizes beyond the array, clipping, a
+    bad paired state, null ctrl and gather."""
+    pair, hp = _pair(Z), Z.hparams()
+
+    def call(valid=64, stride=64, hp=hp, pair=pair, ctrl=FAKE, gather=FAKE):
+        return Z._lib.zero_fused_step_noalloc(FAKE, 1, 8, stride, ctypes.byref(pair), valid, gather,
+                                              1, 0, ctypes.byref(hp), ctrl, None)
+
+    big = Z.NOALLOC_MAX_LEN + 8
+    assert call(valid=big, stride=big) == -3
+    assert "ZERO_NOALLOC_MAX_LEN" in Z.zero_last_error()
+    assert call(hp=Z.hparams(max_grad_norm=1.0)) == -1 and "two-pass" in Z.zero_last_error()
+    assert call(pair=Z.State(FAKE, FAKE, FAKE + 16384)) == -1
+    assert call(ctrl=0) == -1
+    assert call(gather=0) == -1
+    assert call(stride=60) == -1
+
+
 def test_hparam_validation(Z):
     s0 = Z.State(FAKE, FAKE + 256, FAKE + 512)
     for hp in (Z.hparams(beta1=1.0), Z.hparams(eps=-1.0), Z.hparams(scaler=7),

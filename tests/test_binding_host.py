@@ -36,6 +36,7 @@ def test_constants_match_header(Z):
     assert Z.LAUNCH_MIN_TILES == _header_define("ZERO_LAUNCH_MIN_TILES")
     assert Z.LAUNCH_PAYLOAD_TILES == _header_define("ZERO_LAUNCH_PAYLOAD_TILES")
     assert Z.MAX_RANKS == _header_define("ZERO_MAX_RANKS")
+    assert Z.NOALLOC_MAX_LEN == _header_define("ZERO_NOALLOC_MAX_LEN")
     # one workspace partial per tile: the workspace grows by PARTIAL_BYTES per tile
     assert Z.zero_workspace_bytes(3 * Z.TILE) - Z.zero_workspace_bytes(Z.TILE) == 2 * Z.PARTIAL_BYTES
 

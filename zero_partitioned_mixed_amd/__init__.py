@@ -66,6 +66,7 @@ LAUNCH_TILES = 32768  # ZERO_LAUNCH_TILES
 LAUNCH_ROW_TILES = 131072  # ZERO_LAUNCH_ROW_TILES
 LAUNCH_MIN_TILES = 2048  # ZERO_LAUNCH_MIN_TILES
 LAUNCH_PAYLOAD_TILES = 16384  # ZERO_LAUNCH_PAYLOAD_TILES
+NOALLOC_MAX_LEN = 1 << 31  # ZERO_NOALLOC_MAX_LEN
 
 
 def launch_tiles(nranks: int = 0, payload: bool = False) -> int:
@@ -143,6 +144,8 @@ _sig = {
     "zero_adam_step_qgather": (ctypes.c_int, [ctypes.POINTER(State), _vp, _i64,
                                               ctypes.POINTER(Hparams), _vp, _vp, _i32, _i64, _i32,
                                               _vp, _vp, _vp]),
+    "zero_fused_step_noalloc": (ctypes.c_int, [_vp, _i32, _i32, _i64, ctypes.POINTER(State), _i64,
+                                               _vp, _i32, _i64, ctypes.POINTER(Hparams), _vp, _vp]),
     "zero_launch_tiles": (ctypes.c_int64, [_i32]),
     "zero_last_error": (ctypes.c_char_p, []),
 }
@@ -287,6 +290,17 @@ def zero_fused_step(contrib, contrib_dtype: int, nranks: int, stride: int, pair,
         _ptr(contrib), contrib_dtype, nranks, stride, ctypes.byref(st), valid_len, _ptr(gather),
         gather_dtype, offset, ctypes.byref(hp), _ptr(ctrl), _ptr(ws),
         ws.numel() * ws.element_size(), _stream()))
+
+
+def zero_fused_step_noalloc(contrib, contrib_dtype: int, nranks: int, stride: int, pair,
+                            valid_len: int, gather, gather_dtype: int, offset: int, hp: Hparams,
+                            ctrl) -> None:
+    """One rank's whole fused step (pass, decision, restore) with no workspace:
+    the library keeps the partials in its own device array."""
+    st = _state(pair)
+    _check("zero_fused_step_noalloc", _lib.zero_fused_step_noalloc(
+        _ptr(contrib), contrib_dtype, nranks, stride, ctypes.byref(st), valid_len, _ptr(gather),
+        gather_dtype, offset, ctypes.byref(hp), _ptr(ctrl), _stream()))
 
 
 def zero_fused_step_rows(rows, contrib_dtype: int, pair, valid_len: int, gather,

@@ -41,6 +41,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "zero_shard.h"
 
@@ -1750,6 +1751,53 @@ int fused_qgather_launch(const SRC& src, int32_t nranks, const zero_state* pair,
 
 }  // namespace
 
+// ---------------------------------------------------------------- allocation-free step
+// For callers that cannot allocate device memory, zero_fused_step_noalloc
+// keeps the norm and overflow partials of one fused step in this array: one
+// per tile of a shard of at most ZERO_NOALLOC_MAX_LEN elements, plus the
+// second-level slots.  Every GPU the library runs on holds its own copy
+// until the process ends.  Nothing in it must start at zero: the fused pass
+// writes every partial the decision then reads, and the decision's arrival
+// counter lives in the ctrl block.
+constexpr int64_t kScratchPartials = ZERO_NOALLOC_MAX_LEN / ZERO_TILE + kFinGroups;
+static __device__ __align__(256) Partial scratch[kScratchPartials];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// The device address of `scratch` on the device that `stream` belongs to,
+// looked up once per device with that device current.  In host code the
+// array's name is only a stand-in for the symbol, never a device address.
+int scratch_on(hipStream_t stream, void** out, const char* what) {
+    int dev = -1;
+    hipError_t e = stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ZERO_EHIP, "%s: no device for the stream: %s", what, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(ZERO_ERANGE, "%s: device %d out of range", what, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        int cur = -1;
+        if ((e = hipGetDevice(&cur)) != hipSuccess)
+            return fail(ZERO_EHIP, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(ZERO_EHIP, "%s: hipSetDevice(%d): %s", what, dev, hipGetErrorString(e));
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess || p == nullptr)
+            return fail(ZERO_EHIP, "%s: hipGetSymbolAddress(scratch): %s", what, hipGetErrorString(e));
+        if (e2 != hipSuccess)
+            return fail(ZERO_EHIP, "%s: hipSetDevice(%d): %s", what, cur, hipGetErrorString(e2));
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return ZERO_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int zero_partition(int64_t psi, int32_t nranks, int32_t rank, int64_t* shard_len, int64_t* offset,
@@ -2148,6 +2196,36 @@ int zero_pair_store(const zero_state* flat, const zero_state* pair, int64_t vali
 int zero_pair_load(const zero_state* pair, const zero_state* flat, int64_t valid_len,
                    const zero_ctrl* ctrl, void* stream) {
     return pair_copy(flat, pair, valid_len, ctrl, stream, false, "zero_pair_load");
+}
+
+int zero_fused_step_noalloc(const void* contrib, int32_t contrib_dtype, int32_t nranks,
+                            int64_t stride, const zero_state* pair, int64_t valid_len, void* gather,
+                            int32_t gather_dtype, int64_t offset, const zero_hparams* hp,
+                            zero_ctrl* ctrl, void* stream) {
+    int rc;
+    const char* what = "zero_fused_step_noalloc";
+    // every argument checked before the scratch is looked up or anything enqueued
+    if ((rc = check_contrib(contrib, contrib_dtype, nranks, stride, valid_len)) != ZERO_OK) return rc;
+    if (valid_len > ZERO_NOALLOC_MAX_LEN)
+        return fail(ZERO_ERANGE, "%s: valid_len %lld exceeds the scratch's %lld elements "
+                    "(ZERO_NOALLOC_MAX_LEN); use zero_fused_step with a workspace", what,
+                    (long long)valid_len, (long long)ZERO_NOALLOC_MAX_LEN);
+    if ((rc = check_pair(pair, what)) != ZERO_OK) return rc;
+    if ((rc = check_hp(hp)) != ZERO_OK) return rc;
+    if (hp->max_grad_norm > 0.0f) return fail(ZERO_EINVAL, "%s: clipping needs the two-pass path", what);
+    if ((rc = check_ctrl(ctrl, what)) != ZERO_OK) return rc;
+    if ((rc = check_slot(gather, gather_dtype, offset)) != ZERO_OK) return rc;
+    void* ws = nullptr;
+    if ((rc = scratch_on((hipStream_t)stream, &ws, what)) != ZERO_OK) return rc;
+    const size_t ws_bytes = (size_t)kScratchPartials * sizeof(Partial);
+    // the three calls of a fused step, the partials in the scratch
+    if ((rc = zero_fused_step(contrib, contrib_dtype, nranks, stride, pair, valid_len, gather,
+                              gather_dtype, offset, hp, ctrl, ws, ws_bytes, stream)) != ZERO_OK)
+        return rc;
+    zero_ctrl* ctrls[1] = {ctrl};
+    void* wss[1] = {ws};
+    if ((rc = zero_grad_norm_overflow(1, wss, &valid_len, ctrls, hp, 1, stream)) != ZERO_OK) return rc;
+    return zero_fused_restore(pair, valid_len, gather, gather_dtype, offset, ctrl, stream);
 }
 
 const char* zero_last_error(void) { return g_err; }
