@@ -41,7 +41,10 @@ def kernel_name(demangled: str) -> str:
 def isa_digests(asm: str) -> dict:
     """{mangled symbol: sha256 of its normalised instruction stream}."""
     out = {}
+    functions = set(re.findall(r"^\s*\.type\s+(_Z\S+),@function", asm, re.M))
     for m in re.finditer(r"^(_Z\S+):", asm, re.M):
+        if m.group(1) not in functions:  # device data (the no-alloc scratch array)
+            continue
         end = asm.find(".Lfunc_end", m.end())
         lines = []
         for line in asm[m.end():end].splitlines():
