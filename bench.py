@@ -409,6 +409,9 @@ def main():
                          "calls (one pointer per row) instead of one [N, stride] buffer")
     ap.add_argument("--cpu-sample", type=int, default=160 << 20,
                     help="elements of the shard the CPU oracle baseline steps over")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="the CPU oracle baseline steps over the whole shard (13B: about two "
+                         "minutes single-threaded and 46 GB of host memory)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true")
     ap.add_argument("--no-7b", action="store_true",
@@ -476,7 +479,7 @@ def main():
         out["copy_gbps"] = _fmt(cg, 5)
         out["pct_of_copy"] = _fmt(100 * out["value"] / cg, 4)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+        out["cpu_baseline"] = cpu_baseline(w, (1 << 62) if args.cpu_full else args.cpu_sample)
     print(json.dumps(out), flush=True)
 
 

@@ -347,7 +347,11 @@ int zero_fused_step(const void *contrib_dev, int32_t contrib_dtype, int32_t nran
  * pointers, as in zero_reduce_grads_rows (same requirements on rows_dev and
  * nranks <= ZERO_MAX_RANKS): the one-pass reduce-scatter + Adam + cast of a
  * rank that reads the N ranks' slices where they lie.  Bit-identical to
- * zero_fused_step on the same rows. */
+ * zero_fused_step on the same rows.  Speed depends on where the rows lie:
+ * on the 13B shard, rows that start at the same offset in their pages (N
+ * separate, equally aligned allocations) ran about 4% slower than rows in
+ * one [N, stride] buffer, and row k started k * 4 KiB into its allocation
+ * recovered about half of that; the table itself costs 0.3%. */
 int zero_fused_step_rows(const void *const *rows_dev, int32_t contrib_dtype, int32_t nranks,
                          const zero_state *pair, int64_t valid_len, void *gather_dev,
                          int32_t gather_dtype, int64_t offset, const zero_hparams *hp,

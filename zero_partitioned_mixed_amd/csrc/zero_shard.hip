@@ -54,6 +54,7 @@ static_assert(kTile == (int64_t)kBlock * kVec, "tile = threads x elements per th
 constexpr int kFinBlock = 1024;             // threads per finalize workgroup
 constexpr int kFinGroups = 256;             // most first-level groups of the finalize
 constexpr int64_t kFinPer = 16384;          // partials per first-level finalize group
+constexpr int kFinLoads = 4;                // partial loads in flight per finalize thread
 // The restore pass: a fixed grid that, on a skipped step, walks the tiles
 // kRestoreUnroll at a time with all their loads in flight.  Measured on a
 // skipped 13B step (6 bytes per element): 256 x 1 moved 4.2-4.5 TB/s, 256 x 4
@@ -674,15 +675,15 @@ __global__ void __launch_bounds__(kFinBlock) finalize_kernel(CombineArgs a) {
     double ss = 0.0;
     uint32_t bad = 0;
     if (a.nranks == 1) {
-        // one rank: four independent loads in flight per thread, added in index order
+        // one rank: kFinLoads independent loads in flight per thread, added in index order
         const Partial* __restrict__ w = a.ws[0];
         int64_t i = lo + threadIdx.x;
-        for (; i + 3 * kFinBlock < hi; i += 4 * kFinBlock) {
-            Partial p[4];
+        for (; i + (kFinLoads - 1) * kFinBlock < hi; i += kFinLoads * kFinBlock) {
+            Partial p[kFinLoads];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) p[q] = w[i + q * kFinBlock];
+            for (int q = 0; q < kFinLoads; ++q) p[q] = w[i + q * kFinBlock];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < kFinLoads; ++q) {
                 ss += p[q].sumsq;
                 bad |= p[q].nonfinite;
             }
