@@ -257,6 +257,8 @@ def cpu_baseline(w, sample_elems):
     import synth
     rank = w.ranks[-1]
     _, off, valid = O.partition(w.psi, w.nranks, rank)
+    if len(w.ranks) > 1:  # every rank's shard: the whole buffer, element by element the same work
+        off, valid = 0, w.psi
     S = min(sample_elems, valid)
     C = np.empty((w.nranks, S), np.uint16)
     chunk = 1 << 22
@@ -293,7 +295,8 @@ def cpu_baseline(w, sample_elems):
     except OSError:
         pass
     return {"value": _fmt(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"one step over {S} contiguous elements of the measured shard "
+            "sample": f"one step over {S} contiguous elements of the measured "
+                      f"{'buffer' if len(w.ranks) > 1 else 'shard'} "
                       f"({S / valid:.2%} of it), single-threaded C oracle, {dt:.2f} s; "
                       f"host: {cpu_model}, 1 of {os.cpu_count()} cores",
             "elements_per_s": _fmt(S / dt, 4)}
@@ -386,6 +389,94 @@ def measure(w, args, bucket, torch, synth, Z) -> dict:
     return out
 
 
+def measure_all_shards(w, args, torch, synth, Z) -> dict:
+    """A workload whose every rank runs on this GPU (the toy: 32 shards of
+    637,824 elements): each step is every rank's fused pass, one decision
+    over all ranks' partials (standing in for the scalar all-reduce), and
+    every rank's restore check.  Tiny shards: the step is launch-bound."""
+    dev = torch.device("cuda", 0)
+    hp = Z.hparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                   max_grad_norm=w.max_grad_norm, scaler=w.scaler, min_scale=w.min_scale,
+                   growth_interval=w.growth_interval)
+    if w.max_grad_norm > 0:
+        raise SystemExit("the all-shards bench times the fused path")
+    tdt = torch.float16 if w.dtype == Z.F16 else torch.bfloat16
+    steps, contribs, total = [], [], 0
+    for r in w.ranks:
+        _, off, valid = Z.zero_partition(w.psi, w.nranks, r)
+        p0 = torch.empty(valid, dtype=torch.float32, device=dev)
+        synth.gpu_master_range(p0, w.seed, w.master_sigma, off)
+        stride = (valid + 63) // 64 * 64
+        steps.append(Z.ShardStep(w.nranks, stride, valid, off, w.dtype, w.dtype, hp,
+                                 (p0, torch.zeros_like(p0), torch.zeros_like(p0)), None,
+                                 w.loss_scale))
+        c = torch.empty((w.nranks, stride), dtype=tdt, device=dev)
+        synth.gpu_contrib_rows(c, w.seed, 1, w.dtype, w.contrib_sigma, w.contrib_scale,
+                               w.outlier_p, w.outlier_mult, off, valid)
+        contribs.append(c)
+        total += valid
+    gather = torch.empty(w.psi, dtype=tdt, device=dev)
+    synth.gpu_param_range(gather, w.seed, w.master_sigma, w.dtype, 0)
+    multi = Z.MultiShardStep(steps)
+    run = lambda: multi.step(contribs, gather)  # noqa: E731
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    if args.graph:
+        run = multi.capture(contribs, gather).replay
+        torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    a, c = ev(), ev()
+    a.record()
+    for _ in range(args.steps):
+        run()
+    c.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(c) / args.steps
+    # the ranks' fused passes alone (one event pair around all of them)
+    kern = []
+    for _ in range(args.steps):
+        e0, e1 = ev(), ev()
+        e0.record()
+        for s, cb in zip(steps, contribs):
+            s.run_pieces(cb, gather)
+        e1.record()
+        Z.zero_grad_norm_overflow([s.ws for s in steps], [s.valid_len for s in steps],
+                                  [s.ctrl for s in steps], hp, True)
+        for s in steps:
+            s.complete(gather)
+        kern.append((e0, e1))
+    torch.cuda.synchronize()
+    kern_ms = sum(x.elapsed_time(y) for x, y in kern) / len(kern)
+    ctrl = steps[0].ctrl_dict()
+    step_bytes = w.bytes_per_elem * total
+    gbps = step_bytes / (ms * 1e-3) / 1e9
+    kgbps = step_bytes / (kern_ms * 1e-3) / 1e9
+    launches = 2 * len(steps) + 1
+    return {
+        "value": _fmt(gbps, 5),
+        "unit": "GB/s",
+        "ms_per_step": _fmt(ms, 5),
+        "config": {"workload": w.name, "psi": w.psi, "nranks": w.nranks, "ranks": len(w.ranks),
+                   "shard_elems": total // len(w.ranks), "variant": w.variant,
+                   "contrib_dtype": "fp16" if w.dtype == Z.F16 else "bf16",
+                   "bytes_per_elem": w.bytes_per_elem, "step_bytes": step_bytes,
+                   "contrib_layout": "strided", "gather_payload": "16bit_slot",
+                   "launches_per_step": launches,
+                   "launch": "hip_graph" if args.graph else "stream"},
+        "pct_hbm_peak": _fmt(100 * gbps / HBM_PEAK_GBPS, 4),
+        "elements_per_s": _fmt(total / (ms * 1e-3), 5),
+        "roofline": {"bound": "hbm", "kernel": "fused_kernel", "achieved": _fmt(kgbps, 5),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": _fmt(kgbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "kernel_ms": _fmt(kern_ms, 5), "bytes_per_pass": step_bytes,
+                     "launches_per_pass": len(steps),
+                     "note": "the ranks' fused launches together; each shard is about ten tiles, "
+                             "so the step is bound by launches, not by HBM"},
+        "last_step": {"norm": ctrl["norm"], "skip": ctrl["skip"], "t": ctrl["t"],
+                      "loss_scale": ctrl["loss_scale"]},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -446,7 +537,13 @@ def main():
     if args.bucket and not bucket:
         print("--bucket must be at least 2048 elements", file=sys.stderr)
         sys.exit(2)
-    head = measure(w, args, bucket, torch, synth, Z)
+    if len(w.ranks) > 1:  # every rank of the workload on this GPU (the toy)
+        if args.quant or args.qgather or bucket or args.rows:
+            print("the all-shards workload is timed with the plain fused step only", file=sys.stderr)
+            sys.exit(2)
+        head = measure_all_shards(w, args, torch, synth, Z)
+    else:
+        head = measure(w, args, bucket, torch, synth, Z)
     out = {
         "metric": METRIC,
         "value": head.pop("value"),

@@ -117,3 +117,70 @@ def test_graph_replay_with_quantised_gather_payload(write_slot, clip, qbits):
     H.assert_qpayload(g.qpayload(), O.quantize(rslot, c.w.dtype, 8))
     H.log(f"graph qgather write_slot={write_slot} clip={clip} qbits={qbits}: {c.steps} replays "
           f"equal; skips {[r['skip'] for r in g.reports]}")
+
+
+def _toy_ranks(scale=2.0 ** 10):
+    """The toy workload's 32 ranks on this GPU, with a dynamic loss scale."""
+    import torch
+    import synth
+    import zero_partitioned_mixed_amd as Z
+    w = workloads.TOY
+    dev = torch.device("cuda", 0)
+    hp = Z.hparams(lr=w.lr, scaler=Z.SCALER_DYNAMIC)
+    steps, contribs, parts = [], [], []
+    for r in w.ranks:
+        _, off, valid = Z.zero_partition(w.psi, w.nranks, r)
+        p0 = torch.empty(valid, dtype=torch.float32, device=dev)
+        synth.gpu_master_range(p0, w.seed, w.master_sigma, off)
+        stride = (valid + 63) // 64 * 64
+        steps.append(Z.ShardStep(w.nranks, stride, valid, off, F16, F16, hp,
+                                 (p0, torch.zeros_like(p0), torch.zeros_like(p0)), None, scale))
+        contribs.append(torch.empty((w.nranks, stride), dtype=torch.float16, device=dev))
+        parts.append((off, valid))
+    gather = torch.empty(w.psi, dtype=torch.float16, device=dev)
+    synth.gpu_param_range(gather, w.seed, w.master_sigma, F16, 0)
+    return w, Z.MultiShardStep(steps), contribs, parts, gather
+
+
+def test_all_ranks_graph_replay_equals_eager():
+    """The toy's 32 ranks (65 launches a step: 32 fused passes, one shared
+    decision, 32 restore checks) captured once with MultiShardStep.capture and
+    replayed: every replay's decisions and the final state and parameters
+    equal the eager steps bit for bit, including a step that one rank's +inf
+    makes all 32 ranks skip."""
+    import torch
+    import synth
+    runs = []
+    for mode in ("eager", "graph"):
+        w, multi, contribs, parts, gather = _toy_ranks()
+
+        def fill(s):
+            for c, (off, valid) in zip(contribs, parts):
+                synth.gpu_contrib_rows(c, w.seed, s, F16, w.contrib_sigma, 2.0 ** 10, 0.0, 100.0,
+                                       off, valid)
+            if s == 2:
+                contribs[9][4, 1_000] = float("inf")
+
+        graph = multi.capture(contribs, gather) if mode == "graph" else None
+        torch.cuda.synchronize()
+        reports = []
+        for s in range(1, 5):
+            fill(s)
+            if graph is None:
+                multi.step(contribs, gather)
+            else:
+                graph.replay()
+            torch.cuda.synchronize()
+            reports.append([st.ctrl_dict() for st in multi.steps])
+        state = [np.concatenate([t.cpu().numpy() for t in st]) for st in
+                 (s.current() for s in multi.steps)]
+        runs.append((reports, state, gather.view(torch.int16).cpu().numpy()))
+    (ra, sa, ga), (rb, sb, gb) = runs
+    assert repr(ra) == repr(rb)
+    assert [r[0]["skip"] for r in ra] == [0, 1, 0, 0]
+    assert all(repr(r[0]) == repr(x) for r in ra for x in r)   # one decision for all ranks
+    for x, y in zip(sa, sb):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    assert np.array_equal(ga, gb)
+    H.log(f"all-ranks graph: 4 replays equal the eager steps; scales "
+          f"{[r[0]['loss_scale'] for r in ra]}")

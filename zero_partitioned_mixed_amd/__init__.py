@@ -644,3 +644,17 @@ class MultiShardStep:
                                 [s.ctrl for s in ss], ss[0].hp, self.fused)
         for s, q in zip(ss, qgathers):
             s.complete(gather, q)
+
+    def capture(self, contribs, gather, qgathers=None):
+        """Records one step of all the ranks (every rank's launches, the
+        shared decision, every rank's completion) into a HIP graph, as
+        ShardStep.capture does for one rank; ``graph.replay()`` runs a step."""
+        import torch
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                self.step(contribs, gather, qgathers)
+        torch.cuda.current_stream().wait_stream(side)
+        return graph
