@@ -382,9 +382,12 @@ int zero_pair_load(const zero_state *pair, const zero_state *flat, int64_t valid
  *     lo = min(0, min x), hi = max(0, max x),
  *     scale = (hi - lo) / Q (1 when that is 0),
  *     zero  = clamp(rint(-lo / scale), 0, Q),
- *     code  = clamp(rint(x / scale) + zero, 0, Q),
- *   each operation one fp32 rounding, rint half to even.  Real 0 is exact;
- *   |x - value| <= scale / 2 up to the roundings.  A block holding inf or
+ *     code  = clamp(rint(x * (1 / scale)) + zero, 0, Q),
+ *   each operation one fp32 rounding, rint half to even: per block, the
+ *   affine quantisation of PyTorch (MinMaxObserver's scale and zero point,
+ *   quantize_per_tensor's codes, quint4x2's nibble order), which floors the
+ *   scale at fp32 epsilon instead.  Real 0 is exact; |x - value| <= scale / 2
+ *   up to the roundings.  A block holding inf or
  *   NaN, or whose scale overflows, gets scale NaN, zero 0 and codes 0, so it
  *   dequantises to NaN and a downstream overflow check still fires.
  *   Codes: bits = 8, one byte per element; bits = 4, two per byte, the

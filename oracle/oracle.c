@@ -23,14 +23,18 @@
  * every operation rounded once in the order written (compiled with
  * -ffp-contract=off, SSE scalar arithmetic).  The squared-norm is exact.
  *
- * Parity unpinned: Adam trajectories beyond the closed forms and the library
- * cross-check in the tests (the pages print none), and the quantisation's
- * block size, zero-point form and rounding (the page fixes none of them; the
- * tests pin the oracle to the definition stated here and to arithmetic).
- * The clip rule and the loss scaler's schedule are readings too (the pages
- * give neither); the tests pin them to PyTorch's own routines on the CPU
- * (clip_grads_with_norm_, _amp_update_scale_), with the one departure
- * stated above oracle_finalize: the scale never drops below min_scale.
+ * Readings the pages leave open, and their pins: the clip rule and the loss
+ * scaler's schedule (the pages give neither) are pinned to PyTorch's own
+ * routines on the CPU (clip_grads_with_norm_, _amp_update_scale_), with the
+ * one departure stated above oracle_finalize (the scale never drops below
+ * min_scale); the block quantisation's zero-point form and rounding (the
+ * page names the form, not the arithmetic) are pinned to PyTorch's affine
+ * quantiser, block by block.  Adam is pinned by closed forms and by
+ * torch.optim.AdamW (within 1e-5 of each array's RMS; its operations are
+ * ordered differently).  Parity unpinned: the quantisation block length of
+ * 2048 elements (no page gives one; the tests only check that it is what
+ * the reading says) and the S = 1 / NaN conventions for empty and
+ * non-finite blocks.
  */
 #include <math.h>
 #include <stdint.h>
@@ -375,12 +379,17 @@ void oracle_cast(const float *p, int64_t len, int32_t dtype, uint16_t *out) {
 /*     lo = min(0, min x), hi = max(0, max x)           (exact)               */
 /*     S  = (hi - lo) / Q, replaced by 1 when it is 0   (fp32, rounded)       */
 /*     Z  = clamp(rint(-lo / S), 0, Q)                  (integer)             */
-/*     q  = clamp(rint(x / S) + Z, 0, Q)                (integer)             */
+/*     q  = clamp(rint(x * fl32(1 / S)) + Z, 0, Q)      (integer)             */
 /*     x' = S * (q - Z)                                 (fp32, rounded once)  */
 /*   a block whose S overflows counts as non-finite;                           */
 /*   rint rounds half to even; INT4 codes are packed two to a byte, the       */
 /*   element with the even index in the low nibble.                            */
-/* Real zero maps to Z and back to exactly 0; |x - x'| <= S/2 up to the two   */
+/* For finite blocks whose S is at least fp32's epsilon this is PyTorch's    */
+/* per-tensor affine quantisation of the block (MinMaxObserver's scale and   */
+/* zero point, quantize_per_tensor's codes, quint4x2's packing, dequantize); */
+/* torch floors S at epsilon where this reading takes S = 1 for an empty     */
+/* range, and has no NaN convention.                                          */
+/* Real zero maps to Z and back to exactly 0; |x - x'| <= S/2 up to the       */
 /* fp32 roundings.                                                            */
 /* ------------------------------------------------------------------------ */
 #define ORACLE_QBLOCK 2048
@@ -417,11 +426,12 @@ void oracle_quantize(const uint16_t *src, int32_t dtype, int64_t len, int32_t bi
         }
         if (s == 0.0f) s = 1.0f;
         const float z = q_clamp_code(rintf(-lo / s), qmax);
+        const float inv = 1.0f / s;  /* codes use the reciprocal, as torch's quantizer does */
         scale[b] = s;
         zero[b] = (int32_t)z;
         for (int64_t i = i0; i < i1; ++i) {
             const float x = oracle_to_f32(src[i], dtype);
-            const uint8_t q = (uint8_t)q_clamp_code(rintf(x / s) + z, qmax);
+            const uint8_t q = (uint8_t)q_clamp_code(rintf(x * inv) + z, qmax);
             if (bits == 8) codes[i] = q;
             else codes[i / 2] = (uint8_t)(codes[i / 2] | (q << (4 * (i % 2))));
         }

@@ -75,10 +75,12 @@ MUTANTS = {
                              "if (isfinite(twice)) st->scale = twice;", [ADAM]),
     "quant_no_zero_point": ("const float z = q_clamp_code(rintf(-lo / s), qmax);",
                             "const float z = 0.0f;", [QUANT]),
-    "quant_truncates": ("q_clamp_code(rintf(x / s) + z, qmax)", "q_clamp_code(truncf(x / s) + z, qmax)",
+    "quant_truncates": ("q_clamp_code(rintf(x * inv) + z, qmax)", "q_clamp_code(truncf(x * inv) + z, qmax)",
                         [QUANT]),
-    "quant_round_half_away": ("q_clamp_code(rintf(x / s) + z, qmax)",
-                              "q_clamp_code(roundf(x / s) + z, qmax)", [QUANT]),
+    "quant_divides": ("q_clamp_code(rintf(x * inv) + z, qmax)", "q_clamp_code(rintf(x / s) + z, qmax)",
+                      [QUANT]),
+    "quant_round_half_away": ("q_clamp_code(rintf(x * inv) + z, qmax)",
+                              "q_clamp_code(roundf(x * inv) + z, qmax)", [QUANT]),
     "quant_levels_off_by_one": ("const float qmax = (float)((1 << bits) - 1);",
                                 "const float qmax = (float)(1 << bits);", [QUANT]),
     "quant_range_without_zero": ("float lo = 0.0f, hi = 0.0f;",

@@ -1124,7 +1124,7 @@ __global__ void __launch_bounds__(kBlock) fused_qgather_kernel(FusedQArgs<SRC> a
 // range [lo, hi] always contains 0: lo starts at +0 and is replaced only by
 // a strictly smaller finite value, hi likewise, so the result does not depend
 // on the order in which the lanes are combined.  Then
-//   S = (hi - lo) / Q (1 if 0), Z = clamp(rint(-lo / S)), q = clamp(rint(x / S) + Z),
+//   S = (hi - lo) / Q (1 if 0), Z = clamp(rint(-lo / S)), q = clamp(rint(x * fl32(1 / S)) + Z),
 // every operation one fp32 rounding, rint half to even; a block with a
 // non-finite value, or whose S overflows, gets scale NaN, zero 0, codes 0.
 struct QuantArgs {
@@ -1196,10 +1196,11 @@ __device__ __forceinline__ void quant_tile(const float x[kVec], const Runs& r, b
     const bool ok = bad == 0u && __builtin_isfinite(sc);
     if (sc == 0.0f) sc = 1.0f;
     const float z = ok ? clamp_code(__builtin_rintf(-lo / sc), qmax) : 0.0f;
+    const float inv = 1.0f / sc;  // codes by the reciprocal, as torch's quantizer forms them
     uint32_t c[kVec];
 #pragma unroll
     for (int j = 0; j < kVec; ++j)
-        c[j] = ok ? (uint32_t)clamp_code(__builtin_rintf(x[j] / sc) + z, qmax) : 0u;
+        c[j] = ok ? (uint32_t)clamp_code(__builtin_rintf(x[j] * inv) + z, qmax) : 0u;
     if (threadIdx.x == 0) {
         zero_qblock q;
         q.scale = ok ? sc : __builtin_nanf("");
