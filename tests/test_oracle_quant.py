@@ -4,8 +4,9 @@ from 16 bits to INT8 with a zero point, gradients to INT8 or INT4).
 
 The page gives neither block size nor rounding; the oracle's reading is the
 affine zero-point map over 2048-element blocks whose range contains 0, with
-round-half-even.  What is pinned here is fixed by that definition and by
-arithmetic, not by retyping it: hand-worked examples, the error bound of
+round-half-even: PyTorch's per-tensor affine quantisation applied block by
+block.  The pins: PyTorch's own quantiser on the CPU, bit for bit, and what
+the definition and arithmetic fix: hand-worked examples, the error bound of
 rounding to a grid, exact zero, the end points of the range, monotonicity,
 exactness on grid values, block independence and size, non-finite blocks,
 and the quantised reduce against the plain reduce on exactly representable
