@@ -41,3 +41,28 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "ONE GPU" in r.stderr
+
+
+@pytest.mark.gpu
+def test_bench_skip_step_timing_restores_its_input():
+    """bench.timed_skip_steps on a small fused workload with an injected +inf:
+    every timed step is skipped (the decision halves the scale each time),
+    the parts are timed, and the contribution element is put back after."""
+    import torch
+    import bench
+    import synth
+    import zero_partitioned_mixed_amd as Z
+    from synth.workloads import F16, Workload
+    synth.gpu()
+    w = Workload(name="skipbench", psi=8 * 300_001, nranks=8, ranks=(7,), dtype=F16, steps=5,
+                 contrib_scale=2.0 ** 10, scaler=2, loss_scale=2.0 ** 10,
+                 inject_inf=((2, 3, 150_000),))
+    b = bench.setup(w, torch, synth, Z)
+    before = b["contrib"].clone()
+    bench.timed_steps(b, 3, 1, torch, Z)
+    scale0 = b["step"].ctrl_dict()["loss_scale"]
+    out = bench.timed_skip_steps(b, w, torch, reps=3)
+    assert torch.equal(b["contrib"].view(torch.int16), before.view(torch.int16))
+    assert out["steps"] == 3 and out["ms"] > 0 and out["restore_ms"] > 0
+    assert out["loss_scales_after"] == [scale0 / 2, scale0 / 4, scale0 / 8]
+    assert out["restore_bytes"] == 6 * b["valid"]
