@@ -189,14 +189,16 @@ def timed_steps(b, steps, warmup, torch, Z, graph=False, qg=None):
     return step_ms, per_step, kern_ms, red_ms, ctrl
 
 
-def timed_skip_steps(b, w, torch, reps=3):
+def timed_skip_steps(b, w, torch, reps=3, qg=None):
     """Steps that the workload's injected +inf forces to skip (the 13B
     shard's step 2): the fused pass, the decision (skip, halve the scale) and
-    the restore of the slot from the kept master, timed whole and per part
-    with HIP events on the launch stream.  The contribution element is put
-    back afterwards."""
+    the restore of the slot (or, with `qg`, of the quantised payload, with no
+    16-bit slot) from the kept master, timed whole and per part with HIP
+    events on the launch stream.  The contribution element is put back
+    afterwards."""
     (_, k, col), = w.inject_inf
-    st, contrib, gather = b["step"], b["contrib"], b["gather"]
+    st, contrib = b["step"], b["contrib"]
+    gather = None if qg is not None else b["gather"]
     cell = contrib[k][col:col + 1] if isinstance(contrib, list) else contrib[k, col:col + 1]
     orig = cell.clone()
     cell.fill_(float("inf"))
@@ -205,11 +207,11 @@ def timed_skip_steps(b, w, torch, reps=3):
     for _ in range(reps):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         e[0].record()
-        st.run_pieces(contrib, gather)
+        st.run_pieces(contrib, gather, qg)
         e[1].record()
         st.decide()
         e[2].record()
-        st.complete(gather)
+        st.complete(gather, qg)
         e[3].record()
         torch.cuda.synchronize()
         c = st.ctrl_dict()
@@ -221,9 +223,11 @@ def timed_skip_steps(b, w, torch, reps=3):
     torch.cuda.synchronize()
     ms, dec_ms, restore_ms, _ = sorted(rows)[len(rows) // 2]
     valid = b["valid"]
+    # the kept master read, the slot or the payload (codes and one record per block) written
+    rbytes = int(round(valid * (4 + (2 if qg is None else qg.bits / 8 + 8 / 2048))))
     return {"ms": _fmt(ms, 5), "decision_ms": _fmt(dec_ms, 4), "restore_ms": _fmt(restore_ms, 5),
-            "restore_gbps": _fmt(6 * valid / (restore_ms * 1e-3) / 1e9, 5),
-            "restore_bytes": 6 * valid, "steps": reps,
+            "restore_gbps": _fmt(rbytes / (restore_ms * 1e-3) / 1e9, 5),
+            "restore_bytes": rbytes, "steps": reps,
             "loss_scales_after": [r[3] for r in rows]}
 
 
@@ -314,8 +318,8 @@ def measure(w, args, bucket, torch, synth, Z) -> dict:
     ms_step, per_step, kern_ms, red_ms, ctrl = timed_steps(b, args.steps, args.warmup, torch, Z,
                                                            graph=args.graph, qg=qg)
     skip = None
-    if b["fused"] and w.inject_inf and not args.quant and qg is None and pieces == 1:
-        skip = timed_skip_steps(b, w, torch)
+    if b["fused"] and w.inject_inf and not args.quant and pieces == 1:
+        skip = timed_skip_steps(b, w, torch, qg=qg)
     bpe = quant_bytes_per_elem(w, args.quant) if args.quant else w.bytes_per_elem
     if args.qgather:  # the 2-byte slot replaced by the codes and one 8-byte record per block
         bpe = bpe - 2 + args.qgather / 8 + 8 / 2048

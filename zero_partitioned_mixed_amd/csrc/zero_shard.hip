@@ -62,6 +62,12 @@ constexpr int kFinLoads = 4;                // partial loads in flight per final
 // what a one-wave kernel does (1.6 us back to back in a graph).
 constexpr int kRestoreGrid = 256;           // workgroups of the (usually idle) restore pass
 constexpr int kRestoreUnroll = 8;           // whole tiles per restore iteration
+// The restore that also rebuilds a quantised payload meets a workgroup
+// barrier per tile (the block's range), so it needs more workgroups: on a
+// skipped 13B step with the INT8 payload, 256 workgroups took 5.8 ms without
+// the 16-bit slot and 6.2 ms with it; 1024 took 1.9 and 2.3 ms, 2048 took
+// 1.7 and 2.5 ms, 4096 took 1.8 and 2.5 ms.
+constexpr int kRestoreQGrid = 2048;         // workgroups of the restore that rebuilds a payload
 // Workgroups resident per CU, set by the LDS each streaming workgroup reserves
 // (and leaves unused) out of a CU's 160 KB.  Each wave already has every
 // load of its group in flight, so few workgroups per CU still cover HBM
@@ -2211,7 +2217,7 @@ int zero_fused_restore_q(const zero_state* pair, int64_t valid_len, void* gather
     else
         k = bits == 8 ? restore_q_kernel<ZERO_BF16, 8> : restore_q_kernel<ZERO_BF16, 4>;
     const int64_t nt = tiles_for(valid_len);
-    return launch(k, nt < kRestoreGrid ? nt : kRestoreGrid, kBlock, (hipStream_t)stream, a, what);
+    return launch(k, nt < kRestoreQGrid ? nt : kRestoreQGrid, kBlock, (hipStream_t)stream, a, what);
 }
 
 static int pair_copy(const zero_state* flat, const zero_state* pair, int64_t valid_len,
