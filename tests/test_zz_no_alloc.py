@@ -80,3 +80,43 @@ def test_noalloc_step_equals_the_calls_it_stands_for_twice_in_a_row():
         stats["slot"] = H.assert_16bit_within_ulp("slot", slot, rslot, c.w.slot_dtype, exact)
         H.log(f"noalloc call {i + 1}: ok, skips {[r['skip'] for r in g.reports]} {stats}")
     assert [r["skip"] for r in H.oracle_scalars(CASES[0])] == [0, 1, 0, 0]
+
+
+def test_noalloc_step_at_the_13b_shard():
+    """The 13B shard (1,625,000,000 elements, 793,458 partials in the
+    library's array) in the launch configuration the benchmark times: two
+    steps, the second skipped by the workload's +inf, through the allocation-
+    free call and through the three calls it stands for, on the same
+    contributions.  Every step's ctrl is equal bit for bit, and so are master,
+    m, v and the slot on 200K sampled positions (both ends, the launch
+    boundaries, the injected element and random ones).  Each path writes its
+    own slot-sized parameter buffer; together they hold about 150 GB."""
+    import torch
+    import zero_partitioned_mixed_amd as Z
+    from synth import workloads
+    torch.cuda.empty_cache()
+    w = workloads.P13B
+    c = Case(w, 7, 2)
+    _, _, valid = c.part
+    ref = H.DeviceRun(c, full_gather=False)
+    new = H.DeviceRun(c, full_gather=False)
+    new.contrib = ref.contrib  # one set of contributions for both paths
+    torch.cuda.empty_cache()
+    st = new.step_obj
+    for s in (1, 2):
+        ref.fill(s)
+        ref.step_obj.step(ref.contrib, ref.gather)
+        Z.zero_fused_step_noalloc(ref.contrib, w.dtype, w.nranks, c.stride, st.pair, valid,
+                                  new.gather, w.slot_dtype, st.offset, st.hp, st.ctrl)
+        a, b = ref.step_obj.ctrl_dict(), st.ctrl_dict()
+        assert repr(a) == repr(b), (s, a, b)
+        H.log(f"noalloc 13B step {s}: skip {b['skip']} scale {b['loss_scale']} norm {b['norm']:.12g}")
+    assert ref.step_obj.ctrl_dict()["skip"] == 1
+    chunk = Z.launch_tiles(w.nranks) * Z.TILE
+    extra = [i.col + d for i in c.injections for d in (-1, 0, 1)]
+    extra += [b0 + d for b0 in range(chunk, valid, chunk) for d in (-1, 0, 2048)]
+    cols = H.sample_cols(valid, 200_000, seed=3, extra=extra)
+    for x, y, name in zip(ref.fetch(cols), new.fetch(cols), ("master", "m", "v", "slot")):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), name
+    del ref, new, st
+    torch.cuda.empty_cache()
