@@ -250,6 +250,34 @@ def copy_bandwidth(torch, synth, nbytes=8 << 30, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9, ms
 
 
+def stream_rates(torch, synth, nbytes=8 << 30, reps=5):
+    """Plain streams of 8 GiB per array on the same GPU, in the launch form
+    that measured fastest for them (launches of 65,536 workgroups of 8 KiB,
+    three resident per CU): reads alone, writes alone, a copy, and two bytes
+    read per byte written (the fused step's mix).  Reference lines for the
+    kernels' fraction of what the HBM delivers to a simple stream."""
+    n = nbytes // 4
+    a = torch.full((n,), 0.5, dtype=torch.float32, device="cuda")
+    b = torch.full((n,), 0.25, dtype=torch.float32, device="cuda")
+    d = torch.empty(n, dtype=torch.float32, device="cuda")
+    moved = {"read": nbytes, "write": nbytes, "copy": 2 * nbytes, "mix_2r1w": 3 * nbytes}
+    out = {}
+    for kind, total in moved.items():
+        run = lambda: synth.gpu_stream(kind, a, b, d, nbytes, 65536, 48 * 1024)  # noqa: E731
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        out[kind] = _fmt(total / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 5)
+    del a, b, d
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, sample_elems):
     """The CPU oracle, single-threaded, timed on one step of a contiguous sample
     of the same shard (inputs generated beforehand, not timed)."""
@@ -579,6 +607,7 @@ def main():
         cg, _ = copy_bandwidth(torch, synth)
         out["copy_gbps"] = _fmt(cg, 5)
         out["pct_of_copy"] = _fmt(100 * out["value"] / cg, 4)
+        out["stream_gbps"] = stream_rates(torch, synth)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, (1 << 62) if args.cpu_full else args.cpu_sample)
     print(json.dumps(out), flush=True)

@@ -153,10 +153,11 @@ def gpu():
         L.synth_gpu_master_range.argtypes = [u64, f64, i64, i64, vp, vp]
         L.synth_gpu_param_range.argtypes = [u64, f64, i32, i64, i64, vp, vp]
         L.synth_gpu_copy.argtypes = [vp, vp, i64, i32, vp]
+        L.synth_gpu_stream.argtypes = [i32, vp, vp, vp, i64, i64, u32, vp]
         pi = ctypes.POINTER(i32)
         L.synth_gpu_device_info.argtypes = [i32, pi, pi, pi, pi]
         for f in (L.synth_gpu_contrib_rows, L.synth_gpu_master_range, L.synth_gpu_param_range,
-                  L.synth_gpu_copy, L.synth_gpu_device_info):
+                  L.synth_gpu_copy, L.synth_gpu_stream, L.synth_gpu_device_info):
             f.restype = ctypes.c_int
         _gpu = L
     return _gpu
@@ -200,6 +201,19 @@ def gpu_param_range(out, seed, sigma, dtype, idx0) -> None:
 def gpu_copy(src, dst, nbytes: int, grid: int = 0) -> None:
     _check(gpu().synth_gpu_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
                                 nbytes, grid, _stream()), "synth_gpu_copy")
+
+
+STREAM_KINDS = {"read": 0, "write": 1, "copy": 2, "mix_2r1w": 3}
+
+
+def gpu_stream(kind: str, a, b, d, nbytes: int, chunk: int, lds: int) -> None:
+    """A plain memory stream over nbytes of each array (reference lines for the
+    benchmark): read a, write d, copy a to d, or d = a + b (two bytes read per
+    byte written); launches of at most `chunk` workgroups of 8 KiB, each
+    reserving `lds` bytes of LDS."""
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)  # noqa: E731
+    _check(gpu().synth_gpu_stream(STREAM_KINDS[kind], ptr(a), ptr(b), ptr(d), nbytes, chunk, lds,
+                                  _stream()), "synth_gpu_stream")
 
 
 def gpu_device_info(device: int = 0) -> dict:

@@ -66,3 +66,24 @@ def test_bench_skip_step_timing_restores_its_input():
     assert out["steps"] == 3 and out["ms"] > 0 and out["restore_ms"] > 0
     assert out["loss_scales_after"] == [scale0 / 2, scale0 / 4, scale0 / 8]
     assert out["restore_bytes"] == 6 * b["valid"]
+
+
+@pytest.mark.gpu
+def test_stream_reference_lines():
+    """The plain streams the bench reports beside the kernels: each kind runs
+    over the buffers and gives a positive rate; the copy leaves the copied
+    values and the mixed stream their sums."""
+    import torch
+    import bench
+    import synth
+    synth.gpu()
+    rates = bench.stream_rates(torch, synth, nbytes=64 << 20, reps=2)
+    assert set(rates) == {"read", "write", "copy", "mix_2r1w"} and min(rates.values()) > 0
+    n = (8 << 20) // 4
+    a = torch.arange(n, dtype=torch.float32, device="cuda")
+    b = torch.full((n,), 0.5, device="cuda")
+    d = torch.zeros(n, device="cuda")
+    synth.gpu_stream("copy", a, None, d, 8 << 20, 65536, 48 * 1024)
+    assert torch.equal(d, a)
+    synth.gpu_stream("mix_2r1w", a, b, d, 8 << 20, 100, 0)  # several launches of 100 workgroups
+    assert torch.equal(d, a + b)
