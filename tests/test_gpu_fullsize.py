@@ -13,6 +13,7 @@ import pytest
 import harness as H
 from harness import Case
 from synth import workloads
+from synth.workloads import BF16, F16, Workload
 
 pytestmark = pytest.mark.gpu
 
@@ -137,3 +138,31 @@ def test_psi13e9_int8_gather_payload_fullsize():
     rebuilds the payload from the kept master), decisions over the whole
     shard, state on a sample, payload on whole sampled blocks."""
     run_fullsize(workloads.P13B, qgather=8)
+
+
+# Psi = 2^32 + 12,441 over two ranks: rank 1's shard of 2^31 + 6,220 elements
+# starts at 2^31 + 6,221, so its element indices, its slot's offset in the
+# parameter buffer and the global indices of its inputs all pass 2^31 (the
+# last ones 2^32), and it has a ragged last tile.
+PSI_PAST_2_31 = (1 << 32) + 12_441
+PAST_2_31 = {
+    "fused": Workload(name="psi2e32_n2_dynscale", psi=PSI_PAST_2_31, nranks=2, ranks=(1,),
+                      dtype=F16, steps=3, contrib_scale=2.0 ** 15, scaler=2,
+                      loss_scale=2.0 ** 15, inject_inf=((2, 1, (1 << 31) + 17),)),
+    "two_pass": Workload(name="psi2e32_n2_clip", psi=PSI_PAST_2_31, nranks=2, ranks=(1,),
+                         dtype=BF16, steps=2, outlier_p=1e-3, max_grad_norm=1.0),
+}
+
+
+@pytest.mark.parametrize("variant", list(PAST_2_31))
+def test_shard_past_2_31_elements(variant):
+    """A shard longer than 2^31 elements at an offset past 2^31: the fused
+    step with a dynamic scale and a +inf past element 2^31 at step 2 (skip and
+    halve, then the restore), and the two-pass step with clipping, each in the
+    benchmark's launch configuration (33 launches of 32,768 tiles per pass),
+    against the oracle's whole-shard decisions and on 65K sampled elements;
+    the parameter buffer outside the slot unchanged."""
+    w = PAST_2_31[variant]
+    _, off, valid = Case(w, 1, 1).part
+    assert valid == (1 << 31) + 6_220 and off == (1 << 31) + 6_221
+    run_fullsize(w)

@@ -82,41 +82,79 @@ def test_noalloc_step_equals_the_calls_it_stands_for_twice_in_a_row():
     assert [r["skip"] for r in H.oracle_scalars(CASES[0])] == [0, 1, 0, 0]
 
 
-def test_noalloc_step_at_the_13b_shard():
-    """The 13B shard (1,625,000,000 elements, 793,458 partials in the
-    library's array) in the launch configuration the benchmark times: two
-    steps, the second skipped by the workload's +inf, through the allocation-
-    free call and through the three calls it stands for, on the same
-    contributions.  Every step's ctrl is equal bit for bit, and so are master,
-    m, v and the slot on 200K sampled positions (both ends, the launch
-    boundaries, the injected element and random ones).  Each path writes its
-    own slot-sized parameter buffer; together they hold about 150 GB."""
+def _noalloc_against_calls(c: Case, samples: int, seed: int):
+    """Steps c's shard through the allocation-free call and through the three
+    calls it stands for, on one set of contributions, each path with its own
+    state and slot-sized parameter buffer: every step's ctrl equal bit for
+    bit, and master, m, v and the slot on sampled positions (both ends, the
+    launch boundaries, the injected elements and random ones).  Returns the
+    reports and the sampled results of the allocation-free path."""
     import torch
     import zero_partitioned_mixed_amd as Z
-    from synth import workloads
     torch.cuda.empty_cache()
-    w = workloads.P13B
-    c = Case(w, 7, 2)
+    w = c.w
     _, _, valid = c.part
     ref = H.DeviceRun(c, full_gather=False)
     new = H.DeviceRun(c, full_gather=False)
     new.contrib = ref.contrib  # one set of contributions for both paths
     torch.cuda.empty_cache()
     st = new.step_obj
-    for s in (1, 2):
+    for s in range(1, c.steps + 1):
         ref.fill(s)
         ref.step_obj.step(ref.contrib, ref.gather)
         Z.zero_fused_step_noalloc(ref.contrib, w.dtype, w.nranks, c.stride, st.pair, valid,
                                   new.gather, w.slot_dtype, st.offset, st.hp, st.ctrl)
         a, b = ref.step_obj.ctrl_dict(), st.ctrl_dict()
         assert repr(a) == repr(b), (s, a, b)
-        H.log(f"noalloc 13B step {s}: skip {b['skip']} scale {b['loss_scale']} norm {b['norm']:.12g}")
-    assert ref.step_obj.ctrl_dict()["skip"] == 1
+        new.reports.append(b)
+        H.log(f"noalloc {w.name} step {s}: skip {b['skip']} scale {b['loss_scale']} "
+              f"norm {b['norm']:.12g}")
     chunk = Z.launch_tiles(w.nranks) * Z.TILE
     extra = [i.col + d for i in c.injections for d in (-1, 0, 1)]
     extra += [b0 + d for b0 in range(chunk, valid, chunk) for d in (-1, 0, 2048)]
-    cols = H.sample_cols(valid, 200_000, seed=3, extra=extra)
-    for x, y, name in zip(ref.fetch(cols), new.fetch(cols), ("master", "m", "v", "slot")):
+    cols = H.sample_cols(valid, samples, seed=seed, extra=extra)
+    got = new.fetch(cols)
+    for x, y, name in zip(ref.fetch(cols), got, ("master", "m", "v", "slot")):
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), name
+    reports = new.reports
     del ref, new, st
     torch.cuda.empty_cache()
+    return reports, cols, got
+
+
+def test_noalloc_step_at_the_13b_shard():
+    """The 13B shard (1,625,000,000 elements, 793,458 partials in the
+    library's array) in the launch configuration the benchmark times: two
+    steps, the second skipped by the workload's +inf, through the allocation-
+    free call and through the three calls it stands for, on the same
+    contributions, equal bit for bit on 200K sampled positions.  Together the
+    two paths hold about 150 GB."""
+    from synth import workloads
+    reports, _, _ = _noalloc_against_calls(Case(workloads.P13B, 7, 2), 200_000, seed=3)
+    assert [r["skip"] for r in reports] == [0, 1]
+
+
+def test_noalloc_step_at_its_size_limit():
+    """A shard of exactly ZERO_NOALLOC_MAX_LEN = 2^31 elements (one row, fp16,
+    dynamic loss scale): 2^20 tiles, so the fused pass fills the library's
+    array up to its last tile partial, and the decision its 64 group slots.
+    Three steps, the second skipped by a +inf in the shard's last element;
+    equal to the three calls bit for bit, and to the oracle: decisions over
+    the whole shard, elements on 50K sampled positions."""
+    import zero_partitioned_mixed_amd as Z
+    n = Z.NOALLOC_MAX_LEN
+    w = Workload(name="noalloc_limit", psi=n, nranks=1, ranks=(0,), dtype=F16, steps=3,
+                 inject_inf=((2, 0, n - 1),), **DYN)
+    c = Case(w, 0, 3)
+    assert c.part[2] == n
+    reports, cols, (p, m, v, slot) = _noalloc_against_calls(c, 50_000, seed=5)
+    reps = H.oracle_scalars(c)
+    stats = H.assert_reports(reports, reps)
+    assert [r["skip"] for r in reps] == [0, 1, 0]
+    exact = H.same_clips(reports, reps)
+    rp, rm, rv, rslot = H.oracle_elements(c, reps, cols)
+    stats["master"] = H.assert_f32_close("master", p, rp, exact)
+    stats["m"] = H.assert_f32_close("m", m, rm, exact)
+    stats["v"] = H.assert_f32_close("v", v, rv, exact)
+    stats["slot"] = H.assert_16bit_within_ulp("slot", slot, rslot, w.slot_dtype, exact)
+    H.log(f"noalloc at 2^31 elements: ok {stats}")
