@@ -154,15 +154,21 @@ PAST_2_31 = {
 }
 
 
-@pytest.mark.parametrize("variant", list(PAST_2_31))
+@pytest.mark.parametrize("variant", [*PAST_2_31, "int4_rows_int8_payload"])
 def test_shard_past_2_31_elements(variant):
     """A shard longer than 2^31 elements at an offset past 2^31: the fused
     step with a dynamic scale and a +inf past element 2^31 at step 2 (skip and
     halve, then the restore), and the two-pass step with clipping, each in the
     benchmark's launch configuration (33 launches of 32,768 tiles per pass),
     against the oracle's whole-shard decisions and on 65K sampled elements;
-    the parameter buffer outside the slot unchanged."""
-    w = PAST_2_31[variant]
+    the parameter buffer outside the slot unchanged.  The third case takes
+    the fused step's contributions as INT4 blocks and writes the INT8
+    all-gather payload instead of the slot (byte and nibble offsets past
+    2^30), checked on 2,000 sampled elements and whole sampled blocks."""
+    w = PAST_2_31["fused" if variant == "int4_rows_int8_payload" else variant]
     _, off, valid = Case(w, 1, 1).part
     assert valid == (1 << 31) + 6_220 and off == (1 << 31) + 6_221
-    run_fullsize(w)
+    if variant == "int4_rows_int8_payload":
+        run_fullsize(w, qbits=4, qgather=8, samples=2_000)
+    else:
+        run_fullsize(w)
