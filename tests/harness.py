@@ -438,17 +438,33 @@ def _ordinal16(b: np.ndarray) -> np.ndarray:
     return np.where(b & 0x8000, -(b & 0x7FFF), b)
 
 
+def _isnan16(b: np.ndarray, dtype: int) -> np.ndarray:
+    b = b.astype(np.uint32)
+    exp, man = (0x7C00, 0x03FF) if dtype == F16 else (0x7F80, 0x007F)
+    return ((b & exp) == exp) & ((b & man) != 0)
+
+
 def assert_16bit_within_ulp(name: str, got: np.ndarray, ref: np.ndarray, dtype: int,
                             exact: bool = True) -> dict:
-    """Within 1 ulp (the graded bar) and, with `exact`, equal bits."""
+    """Within 1 ulp (the graded bar) and, with `exact`, equal bits.  NaN must
+    stand where and only where the oracle has NaN, with any sign and payload:
+    IEEE 754 fixes neither for the NaN an invalid operation makes (0/0 gives
+    the negative default NaN on the host's SSE units and the positive one on
+    the GPU), as in the fp32 comparisons."""
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
-    d = np.abs(_ordinal16(got) - _ordinal16(ref))
+    gnan, rnan = _isnan16(got, dtype), _isnan16(ref, dtype)
+    if (gnan != rnan).any():
+        i = int(np.flatnonzero(gnan != rnan)[0])
+        raise AssertionError(f"{name}: NaN at {i} on one side only: gpu {got[i]:#06x} "
+                             f"oracle {ref[i]:#06x}")
+    both_nan = gnan & rnan
+    d = np.where(both_nan, 0, np.abs(_ordinal16(got) - _ordinal16(ref)))
     bad = d > 1
     if bad.any():
         i = int(np.flatnonzero(bad)[0])
         raise AssertionError(f"{name}: {int(bad.sum())} of {got.size} more than 1 ulp apart; "
                              f"first at {i}: gpu {got[i]:#06x} oracle {ref[i]:#06x}")
-    same = got.astype(np.uint16) == ref.astype(np.uint16)
+    same = (got.astype(np.uint16) == ref.astype(np.uint16)) | both_nan
     if exact and not same.all():
         i = int(np.flatnonzero(~same)[0])
         raise AssertionError(f"{name}: {int((~same).sum())} of {got.size} differ in their bits; "

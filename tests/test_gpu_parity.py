@@ -20,6 +20,8 @@ from synth.workloads import BF16, F16, Workload
 
 pytestmark = pytest.mark.gpu
 
+_BELOW_ONE = float(np.nextafter(np.float32(1.0), np.float32(0.0)))  # 1 - 2^-24
+
 
 @pytest.fixture(scope="module", autouse=True)
 def gpu():
@@ -137,6 +139,19 @@ SMALL = {
     "bf16_twopass_growth_at_fp32_max": (small(100_003, 3, 1, dtype=BF16, steps=3, scaler=2,
                                               growth_interval=1, contrib_scale=2.0 ** 127,
                                               loss_scale=2.0 ** 127, max_grad_norm=1.0), ()),
+    # degenerate hyperparameters: no moments (each step uses g and g*g alone);
+    # moments that barely decay (1 - beta is one fp32 ulp below 1, so the bias
+    # corrections are near 6e-8 t); lr = 0 with weight decay (the master must
+    # not move); eps = 0, where an element whose gradient sums to exactly 0
+    # divides 0 by 0 and its master and parameter turn NaN on both sides
+    "f16_fused_betas_zero": (small(100_003, 3, 2, beta1=0.0, beta2=0.0), ()),
+    "bf16_twopass_betas_near_one": (small(100_003, 3, 1, dtype=BF16, beta1=_BELOW_ONE,
+                                          beta2=_BELOW_ONE, max_grad_norm=0.05), ()),
+    "f16_fused_lr_zero_wd": (small(100_003, 3, 2, lr=0.0, weight_decay=0.1), ()),
+    "f16_fused_eps_zero": (small(100_003, 3, 2, eps=0.0, contrib_scale=2.0 ** 10, scaler=1,
+                                 loss_scale=2.0 ** 10), ()),
+    "bf16_twopass_eps_zero_clip": (small(200_000, 8, 5, dtype=BF16, eps=0.0, max_grad_norm=0.05),
+                                   ()),
 }
 
 
@@ -146,6 +161,12 @@ def test_small_cases(name):
     g, _ = run_case(Case(w, w.ranks[0], w.steps, extra=tuple(extra)), name)
     if "growth_at_fp32_max" in name:
         assert all(r["loss_scale"] == 2.0 ** 127 for r in g.reports)
+    if "eps_zero" in name:   # the case is only degenerate if some element met 0/0
+        assert np.isnan(g.fetch()[0]).any()
+    if name == "f16_fused_lr_zero_wd":
+        _, off, valid = g.c.part
+        p0 = H.synth.master_range(w.seed, w.master_sigma, off, valid)
+        assert np.array_equal(g.fetch()[0].view(np.uint32), p0.view(np.uint32))
 
 
 # Shards long enough for the restore's unrolled loop (eight whole tiles per
