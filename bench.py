@@ -253,17 +253,20 @@ def copy_bandwidth(torch, synth, nbytes=8 << 30, reps=10):
 def stream_rates(torch, synth, nbytes=8 << 30, reps=5):
     """Plain streams of 8 GiB per array on the same GPU, in the launch form
     that measured fastest for them (launches of 65,536 workgroups of 8 KiB,
-    three resident per CU): reads alone, writes alone, a copy, and two bytes
-    read per byte written (the fused step's mix).  Reference lines for the
-    kernels' fraction of what the HBM delivers to a simple stream."""
+    three resident per CU): reads alone, writes alone, a copy, two bytes read
+    per byte written (the fused step's mix) and four (the reduce pass's mix,
+    over 4 GiB written).  Reference lines for the kernels' fraction of what
+    the HBM delivers to a simple stream."""
     n = nbytes // 4
     a = torch.full((n,), 0.5, dtype=torch.float32, device="cuda")
     b = torch.full((n,), 0.25, dtype=torch.float32, device="cuda")
     d = torch.empty(n, dtype=torch.float32, device="cuda")
-    moved = {"read": nbytes, "write": nbytes, "copy": 2 * nbytes, "mix_2r1w": 3 * nbytes}
+    # bytes written per stream and bytes moved in all
+    moved = {"read": (nbytes, nbytes), "write": (nbytes, nbytes), "copy": (nbytes, 2 * nbytes),
+             "mix_2r1w": (nbytes, 3 * nbytes), "mix_4r1w": (nbytes // 2, 5 * nbytes // 2)}
     out = {}
-    for kind, total in moved.items():
-        run = lambda: synth.gpu_stream(kind, a, b, d, nbytes, 65536, 48 * 1024)  # noqa: E731
+    for kind, (span, total) in moved.items():
+        run = lambda: synth.gpu_stream(kind, a, b, d, span, 65536, 48 * 1024)  # noqa: E731
         run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

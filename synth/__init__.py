@@ -203,14 +203,19 @@ def gpu_copy(src, dst, nbytes: int, grid: int = 0) -> None:
                                 nbytes, grid, _stream()), "synth_gpu_copy")
 
 
-STREAM_KINDS = {"read": 0, "write": 1, "copy": 2, "mix_2r1w": 3}
+STREAM_KINDS = {"read": 0, "write": 1, "copy": 2, "mix_2r1w": 3, "mix_4r1w": 4}
 
 
 def gpu_stream(kind: str, a, b, d, nbytes: int, chunk: int, lds: int) -> None:
     """A plain memory stream over nbytes of each array (reference lines for the
-    benchmark): read a, write d, copy a to d, or d = a + b (two bytes read per
-    byte written); launches of at most `chunk` workgroups of 8 KiB, each
-    reserving `lds` bytes of LDS."""
+    benchmark): read a, write d, copy a to d, d = a + b (two bytes read per
+    byte written), or d = a + a' + b + b' with a' and b' nbytes further on in
+    a and b (four bytes read per byte written; a and b hold 2 * nbytes);
+    launches of at most `chunk` workgroups of 8 KiB, each reserving `lds`
+    bytes of LDS."""
+    if kind == "mix_4r1w":
+        for t in (a, b):
+            assert t.numel() * t.element_size() >= 2 * nbytes, "mix_4r1w reads 2 * nbytes of a and b"
     ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)  # noqa: E731
     _check(gpu().synth_gpu_stream(STREAM_KINDS[kind], ptr(a), ptr(b), ptr(d), nbytes, chunk, lds,
                                   _stream()), "synth_gpu_stream")

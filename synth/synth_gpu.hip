@@ -71,7 +71,9 @@ copy16_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t nv
 // 8 KiB of every array it touches (256 threads, two 16-byte vectors each,
 // every wave instruction one contiguous 4 KiB span); kind 0 reads a, 1 writes
 // d, 2 copies a to d, 3 writes d = a + b (two bytes read per byte written,
-// the read:write mix of the fused shard step).
+// the read:write mix of the fused shard step), 4 writes d = a + a' + b + b'
+// where a' and b' are a and b one stream length further on (four bytes read
+// per byte written, the mix of the reduce pass).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int64_t stream_base() {
@@ -113,6 +115,24 @@ __global__ void __launch_bounds__(kBlock) stream_mix_kernel(const float* __restr
     const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(b + i + 1024));
     __builtin_nontemporal_store(x + u, reinterpret_cast<f32x4*>(d + i));
     __builtin_nontemporal_store(y + w, reinterpret_cast<f32x4*>(d + i + 1024));
+}
+
+__global__ void __launch_bounds__(kBlock) stream_mix4_kernel(const float* __restrict__ a,
+                                                             const float* __restrict__ b,
+                                                             float* __restrict__ d, int64_t far) {
+    const int64_t i = stream_base();
+    f32x4 s[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t j = i + h * 1024;
+        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a + j));
+        const f32x4 y = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a + far + j));
+        const f32x4 u = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(b + j));
+        const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(b + far + j));
+        s[h] = (x + y) + (u + w);
+    }
+    __builtin_nontemporal_store(s[0], reinterpret_cast<f32x4*>(d + i));
+    __builtin_nontemporal_store(s[1], reinterpret_cast<f32x4*>(d + i + 1024));
 }
 
 unsigned grid_for(int64_t work, int64_t per_block) {
@@ -181,30 +201,32 @@ int synth_gpu_copy(const void* src, void* dst, int64_t bytes, int32_t grid, void
 }
 
 // One plain stream (kind as above) over `bytes` of each array (a multiple of
-// 8 KiB; pointers 16-byte aligned; d at least 1 KiB for kind 0), issued as
-// launches of at most `chunk` workgroups, each reserving `lds` bytes of LDS
-// (which sets how many are resident per CU).
+// 8 KiB; pointers 16-byte aligned; d at least 1 KiB for kind 0; for kind 4, a
+// and b hold 2 * bytes each), issued as launches of at most `chunk`
+// workgroups, each reserving `lds` bytes of LDS (which sets how many are
+// resident per CU).
 int synth_gpu_stream(int32_t kind, const void* a, const void* b, void* d, int64_t bytes,
                      int64_t chunk, uint32_t lds, void* stream) {
-    if (kind < 0 || kind > 3 || bytes < 0 || bytes % 8192 != 0 || chunk < 1 || lds > 65536)
+    if (kind < 0 || kind > 4 || bytes < 0 || bytes % 8192 != 0 || chunk < 1 || lds > 65536)
         return -1;
     if (((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
           reinterpret_cast<uintptr_t>(d)) & 15u) != 0)
         return -1;
-    if ((kind != 1 && a == nullptr) || (kind == 3 && b == nullptr) || d == nullptr) return -1;
+    if ((kind != 1 && a == nullptr) || (kind >= 3 && b == nullptr) || d == nullptr) return -1;
     const int64_t wgs = bytes / 8192;
     hipStream_t s = (hipStream_t)stream;
     for (int64_t w0 = 0; w0 < wgs; w0 += chunk) {
         const int64_t g = wgs - w0 < chunk ? wgs - w0 : chunk;
         const int64_t off = w0 * 2048;  // floats
         const float* pa = (const float*)a + (kind != 1 ? off : 0);
-        const float* pb = (const float*)b + (kind == 3 ? off : 0);
+        const float* pb = (const float*)b + (kind >= 3 ? off : 0);
         float* pd = (float*)d + (kind != 0 ? off : 0);
         switch (kind) {
             case 0: hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)g), dim3(kBlock), lds, s, pa, pd); break;
             case 1: hipLaunchKernelGGL(stream_write_kernel, dim3((unsigned)g), dim3(kBlock), lds, s, pd); break;
             case 2: hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)g), dim3(kBlock), lds, s, pa, pd); break;
-            default: hipLaunchKernelGGL(stream_mix_kernel, dim3((unsigned)g), dim3(kBlock), lds, s, pa, pb, pd); break;
+            case 3: hipLaunchKernelGGL(stream_mix_kernel, dim3((unsigned)g), dim3(kBlock), lds, s, pa, pb, pd); break;
+            default: hipLaunchKernelGGL(stream_mix4_kernel, dim3((unsigned)g), dim3(kBlock), lds, s, pa, pb, pd, bytes / 4); break;
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return status(e);

@@ -72,13 +72,14 @@ def test_bench_skip_step_timing_restores_its_input():
 def test_stream_reference_lines():
     """The plain streams the bench reports beside the kernels: each kind runs
     over the buffers and gives a positive rate; the copy leaves the copied
-    values and the mixed stream their sums."""
+    values and the mixed streams their sums."""
     import torch
     import bench
     import synth
     synth.gpu()
     rates = bench.stream_rates(torch, synth, nbytes=64 << 20, reps=2)
-    assert set(rates) == {"read", "write", "copy", "mix_2r1w"} and min(rates.values()) > 0
+    assert set(rates) == {"read", "write", "copy", "mix_2r1w", "mix_4r1w"}
+    assert min(rates.values()) > 0
     n = (8 << 20) // 4
     a = torch.arange(n, dtype=torch.float32, device="cuda")
     b = torch.full((n,), 0.5, device="cuda")
@@ -87,3 +88,8 @@ def test_stream_reference_lines():
     assert torch.equal(d, a)
     synth.gpu_stream("mix_2r1w", a, b, d, 8 << 20, 100, 0)  # several launches of 100 workgroups
     assert torch.equal(d, a + b)
+    d.zero_()
+    m = n // 2  # four reads per write: each half of a and of b, into the first half of d
+    synth.gpu_stream("mix_4r1w", a, b, d, 4 << 20, 100, 0)
+    assert torch.equal(d[:m], (a[:m] + a[m:]) + (b[:m] + b[m:]))
+    assert not d[m:].any()
