@@ -86,7 +86,7 @@ def setup(w, torch, synth, Z, rows=False, qbits=0, bucket=0):
     tdt = torch.float16 if w.dtype == Z.F16 else torch.bfloat16
     # Optimizer state first, as a training job allocates it at start-up, then
     # the gradient contributions and the parameter buffer.  The order decides
-    # which physical memory each buffer gets: over fresh processes on one box,
+    # which physical memory each buffer gets: over fresh processes on one machine,
     # the 13B step's median went from 6.04 to 6.14 TB/s (14 runs each), and
     # runs below 5.7 TB/s from 6 of 20 to none of 20 in a second sample.
     p0 = torch.empty(valid, dtype=torch.float32, device=dev)

@@ -1576,7 +1576,7 @@ struct Residency<SrcQ<BITS>> {
 // with the rows each tile reads, so the best launch size falls as N grows: in
 // one process per shape, 2,048 tiles at N = 64 (+7% against 16,384), 4,096 at
 // N = 32 (+1.5%), flat from 8,192 up at N = 16; at N <= 8 and in the Adam
-// passes 32,768 (0.5-0.9% ahead of 16,384 on two boxes), except the fused
+// passes 32,768 (0.5-0.9% ahead of 16,384 on two machines), except the fused
 // step that also writes the payload, which waits at one more workgroup
 // barrier per tile: 16,384 (INT4 payload 1.4% ahead, INT8 equal).  Below
 // 2,048 tiles the launches' fill and drain cost more than the compact window
