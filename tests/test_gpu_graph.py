@@ -142,9 +142,11 @@ def _toy_ranks(scale=2.0 ** 10):
     return w, Z.MultiShardStep(steps), contribs, parts, gather
 
 
-def test_all_ranks_graph_replay_equals_eager():
+@pytest.mark.parametrize("branches", [1, 4])
+def test_all_ranks_graph_replay_equals_eager(branches):
     """The toy's 32 ranks (65 launches a step: 32 fused passes, one shared
-    decision, 32 restore checks) captured once with MultiShardStep.capture and
+    decision, 32 restore checks) captured once with MultiShardStep.capture,
+    as one chain or with the ranks' launches on four parallel branches, and
     replayed: every replay's decisions and the final state and parameters
     equal the eager steps bit for bit, including a step that one rank's +inf
     makes all 32 ranks skip."""
@@ -161,7 +163,7 @@ def test_all_ranks_graph_replay_equals_eager():
             if s == 2:
                 contribs[9][4, 1_000] = float("inf")
 
-        graph = multi.capture(contribs, gather) if mode == "graph" else None
+        graph = multi.capture(contribs, gather, branches=branches) if mode == "graph" else None
         torch.cuda.synchronize()
         reports = []
         for s in range(1, 5):
@@ -182,5 +184,5 @@ def test_all_ranks_graph_replay_equals_eager():
     for x, y in zip(sa, sb):
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
     assert np.array_equal(ga, gb)
-    H.log(f"all-ranks graph: 4 replays equal the eager steps; scales "
+    H.log(f"all-ranks graph ({branches} branches): 4 replays equal the eager steps; scales "
           f"{[r[0]['loss_scale'] for r in ra]}")

@@ -633,28 +633,50 @@ class MultiShardStep:
         self.steps = steps
         self.fused = steps[0].fused
 
-    def step(self, contribs, gather, qgathers=None) -> None:
+    def step(self, contribs, gather, qgathers=None, branches: list | None = None) -> None:
+        """One step of every rank.  With ``branches`` (streams), rank i's
+        launches go to branches[i % len(branches)], forked from and joined
+        back into the current stream around each phase; the ranks touch
+        disjoint buffers, so only the shared decision orders them."""
+        import torch
         ss = self.steps
         qgathers = [None] * len(ss) if qgathers is None else list(qgathers)
         if len(contribs) != len(ss) or len(qgathers) != len(ss):
             raise ValueError(f"one contribution set and payload per rank ({len(ss)})")
-        for s, c, q in zip(ss, contribs, qgathers):
-            s.run_pieces(c, gather, q)
+
+        def per_rank(fn):
+            if not branches:
+                for i in range(len(ss)):
+                    fn(i)
+                return
+            main = torch.cuda.current_stream()
+            for b in branches:
+                b.wait_stream(main)
+            for i in range(len(ss)):
+                with torch.cuda.stream(branches[i % len(branches)]):
+                    fn(i)
+            for b in branches:
+                main.wait_stream(b)
+
+        per_rank(lambda i: ss[i].run_pieces(contribs[i], gather, qgathers[i]))
         zero_grad_norm_overflow([s.ws for s in ss], [s.valid_len for s in ss],
                                 [s.ctrl for s in ss], ss[0].hp, self.fused)
-        for s, q in zip(ss, qgathers):
-            s.complete(gather, q)
+        per_rank(lambda i: ss[i].complete(gather, qgathers[i]))
 
-    def capture(self, contribs, gather, qgathers=None):
+    def capture(self, contribs, gather, qgathers=None, branches: int = 4):
         """Records one step of all the ranks (every rank's launches, the
         shared decision, every rank's completion) into a HIP graph, as
-        ShardStep.capture does for one rank; ``graph.replay()`` runs a step."""
+        ShardStep.capture does for one rank; ``graph.replay()`` runs a step.
+        The ranks' launches are recorded on ``branches`` parallel branches
+        of the graph (0 or 1: one chain), so that the small launches of
+        different ranks can run at the same time."""
         import torch
         graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
+        pool = [torch.cuda.Stream() for _ in range(branches)] if branches > 1 else None
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             with torch.cuda.graph(graph, stream=side):
-                self.step(contribs, gather, qgathers)
+                self.step(contribs, gather, qgathers, pool)
         torch.cuda.current_stream().wait_stream(side)
         return graph
