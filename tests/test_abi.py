@@ -43,6 +43,7 @@ def test_struct_sizes_match_header(Z):
     assert Z.zero_ctrl_bytes() == 128 == ctypes.sizeof(Z.Ctrl)
     assert ctypes.sizeof(Z.Hparams) == 36
     assert ctypes.sizeof(Z.State) == 24
+    assert ctypes.sizeof(Z.Shard) == 64
 
 
 def test_partition_matches_oracle(Z, O):
@@ -137,6 +138,55 @@ def test_fused_noalloc_validation(Z):
     assert call(ctrl=0) == -1
     assert call(gather=0) == -1
     assert call(stride=60) == -1
+
+
+def _shard(Z, **kw):
+    """A well-formed zero_shard of 64 elements at fake addresses, with changes."""
+    d = dict(contrib=FAKE, stride=64, pair=FAKE, valid_len=64, offset=0, ctrl=FAKE, ws=FAKE,
+             ws_bytes=Z.zero_workspace_bytes(64))
+    d.update(kw)
+    return Z.Shard(d["contrib"], d["stride"], d["pair"], d["valid_len"], d["offset"], d["ctrl"],
+                   d["ws"], d["ws_bytes"])
+
+
+def test_batched_shards_validation(Z):
+    """The batched fused step and restore check every shard before anything
+    is enqueued: the shard count, each shard's rows, state, workspace, ctrl
+    and slot, and that each shard fits one launch."""
+    hp = Z.hparams()
+
+    def fused(shards, n=8, hp=hp, gather=FAKE, table=True):
+        arr = (Z.Shard * max(len(shards), 1))(*shards)
+        return Z._lib.zero_fused_step_shards(arr if table else None, len(shards), 1, n, gather, 1,
+                                             ctypes.byref(hp), None)
+
+    def restore(shards, gather=FAKE):
+        arr = (Z.Shard * max(len(shards), 1))(*shards)
+        return Z._lib.zero_fused_restore_shards(arr, len(shards), gather, 1, None)
+
+    good = _shard(Z)
+    assert fused([good], table=False) == -1
+    assert fused([]) == -1 and fused([good] * 65) == -1
+    assert fused([good], hp=Z.hparams(max_grad_norm=1.0)) == -1
+    assert "two-pass" in Z.zero_last_error()
+    assert fused([good], gather=0) == -1
+    # each shard at most one launch of tiles: 32,768 at N = 8, 2,048 at N = 64
+    for n in (8, 64):
+        top = Z.launch_tiles(n) * Z.TILE
+        big = _shard(Z, valid_len=top + 1, stride=top + 8,
+                     ws_bytes=Z.zero_workspace_bytes(top + 1))
+        assert fused([good, big], n=n) == -3 and "shard 1" in Z.zero_last_error()
+    bad = [_shard(Z, contrib=0), _shard(Z, contrib=FAKE + 8), _shard(Z, stride=68),
+           _shard(Z, stride=32), _shard(Z, pair=0), _shard(Z, pair=FAKE + 4), _shard(Z, ctrl=0),
+           _shard(Z, ctrl=FAKE + 4), _shard(Z, ws=0), _shard(Z, ws_bytes=16),
+           _shard(Z, offset=-1), _shard(Z, valid_len=-1)]
+    codes = [fused([good, b, good]) for b in bad]
+    assert codes == [-1, -2, -2, -1, -1, -1, -1, -2, -1, -4, -3, -3], codes
+    # the restore: at most ZERO_LAUNCH_TILES tiles a shard, and its state, slot and ctrl
+    top = Z.LAUNCH_TILES * Z.TILE
+    assert restore([good, _shard(Z, valid_len=top + 1)]) == -3
+    assert restore([_shard(Z, pair=0)]) == -1 and restore([_shard(Z, ctrl=0)]) == -1
+    assert restore([good], gather=0) == -1 and restore([good] * 65) == -1
 
 
 def test_hparam_validation(Z):

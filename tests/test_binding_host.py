@@ -37,6 +37,7 @@ def test_constants_match_header(Z):
     assert Z.LAUNCH_PAYLOAD_TILES == _header_define("ZERO_LAUNCH_PAYLOAD_TILES")
     assert Z.MAX_RANKS == _header_define("ZERO_MAX_RANKS")
     assert Z.NOALLOC_MAX_LEN == _header_define("ZERO_NOALLOC_MAX_LEN")
+    assert Z.BATCH_SHARDS == _header_define("ZERO_BATCH_SHARDS")
     # one workspace partial per tile: the workspace grows by PARTIAL_BYTES per tile
     assert Z.zero_workspace_bytes(3 * Z.TILE) - Z.zero_workspace_bytes(Z.TILE) == 2 * Z.PARTIAL_BYTES
 
@@ -127,7 +128,8 @@ ENTRY_POINTS = ["zero_fused_step", "zero_fused_step_rows", "zero_fused_step_q",
                 "zero_fused_step_qgather", "zero_fused_step_rows_qgather",
                 "zero_fused_step_q_qgather", "zero_reduce_grads", "zero_reduce_grads_rows",
                 "zero_reduce_grads_q", "zero_grad_norm_overflow", "zero_fused_restore",
-                "zero_fused_restore_q", "zero_adam_step", "zero_adam_step_qgather"]
+                "zero_fused_restore_q", "zero_adam_step", "zero_adam_step_qgather",
+                "zero_fused_step_shards", "zero_fused_restore_shards"]
 
 
 @pytest.mark.parametrize("fused", [True, False])
@@ -186,6 +188,53 @@ def test_multi_shard_step_runs_every_rank_then_one_decision(Z, monkeypatch):
     multi.step([object(), qrows], "gather", [None, Z.QGather(1 << 24, 1 << 25, 8, 4096)])
     assert calls == ["zero_fused_step", "zero_fused_step_q_qgather", "zero_grad_norm_overflow",
                      "zero_fused_restore", "zero_fused_restore_q"]
+
+
+class _FakeRows:
+    """Stands in for a [N, stride] contribution tensor (only its address is read)."""
+
+    def data_ptr(self):
+        return id(self)
+
+
+def test_multi_shard_step_batches_small_fused_shards(Z, monkeypatch):
+    """Ranks on the fused path with one [N, stride] tensor each, a 16-bit
+    slot, no payload, no buckets and shards of at most one launch go through
+    the batched calls: three launches a step whatever the rank count; any
+    other step, or batched=False, through every rank's own calls."""
+    calls = []
+    for name in ENTRY_POINTS:
+        monkeypatch.setattr(Z, name, lambda *a, _n=name, **k: calls.append(_n))
+    monkeypatch.setattr(Z, "shard_table", lambda shards: list(shards))
+    ranks = [_fake_step(Z, True) for _ in range(5)]
+    rows = [_FakeRows() for _ in ranks]
+    multi = Z.MultiShardStep(ranks)
+    assert multi.takes_batched(rows, "gather")
+    multi.step(rows, "gather")
+    assert calls == ["zero_fused_step_shards", "zero_grad_norm_overflow",
+                     "zero_fused_restore_shards"]
+    per_rank = ["zero_fused_step"] * 5 + ["zero_grad_norm_overflow"] + ["zero_fused_restore"] * 5
+    calls.clear()
+    Z.MultiShardStep(ranks, batched=False).step(rows, "gather")
+    assert calls == per_rank
+    for change in ("table", "bucket", "long", "payload", "two_pass"):
+        calls.clear()
+        rs = [_fake_step(Z, change != "two_pass") for _ in range(5)]
+        contribs, qgs = list(rows), None
+        if change == "table":
+            contribs[2] = [1 << 20, 1 << 21]
+        elif change == "bucket":
+            rs[3].bucket = Z.TILE
+        elif change == "long":
+            rs[4].valid_len = Z.launch_tiles(2) * Z.TILE + 1
+        elif change == "payload":
+            qgs = [None] * 4 + [Z.QGather(1 << 24, 1 << 25, 8, 4096)]
+        multi = Z.MultiShardStep(rs)
+        assert not multi.takes_batched(contribs, "gather", qgs), change
+        if change in ("bucket", "long"):
+            continue  # the fake ranks would issue pieces; the routing is what is checked
+        multi.step(contribs, "gather", qgs)
+        assert "zero_fused_step_shards" not in calls and "zero_grad_norm_overflow" in calls, change
 
 
 def test_multi_shard_step_validation(Z):

@@ -1,0 +1,137 @@
+"""Several ranks' shards on one GPU through the batched calls
+(zero_fused_step_shards, zero_fused_restore_shards) against every rank's own
+calls (zero_fused_step, zero_fused_restore), bit for bit: every step's ctrl
+of every rank, every rank's state, and the whole parameter buffer.  The
+oracle checks of MultiShardStep (the toy's 32 shards, 64 ranks of a ragged
+buffer, an overflow on one rank) take the batched calls by default."""
+import itertools
+
+import numpy as np
+import pytest
+
+import harness as H
+from synth import workloads
+from synth.workloads import BF16, F16, Workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import synth
+    synth.gpu()
+    import zero_partitioned_mixed_amd  # noqa: F401
+    yield
+    torch.cuda.empty_cache()
+
+
+def _ws(psi, n, ranks, dtype=F16, steps=3, **kw):
+    return Workload(name="shards", psi=psi, nranks=n, ranks=tuple(ranks), dtype=dtype, steps=steps,
+                    **kw)
+
+
+DYN = dict(scaler=2, contrib_scale=2.0 ** 10, loss_scale=2.0 ** 10)
+
+# (workload, injected +inf as (step, rank index, row, column) or None)
+CASES = {
+    # 32 ranks of 10 tiles, N = 32 (the any-N kernel), a skip on every rank at step 2
+    "toy_skip": (_ws(workloads.TOY.psi, 32, range(32), **DYN), (2, 9, 4, 1_000)),
+    # 64 ranks (two launches of 32 shards), bf16 rows into an fp16 parameter buffer, shard
+    # length 3,001 (slots at 8-, 4- and 2-byte alignment), the last shard short
+    "ranks64_mixed_ragged": (_ws(64 * 3_001 - 40, 64, range(64), dtype=BF16, gather_dtype=F16,
+                                 weight_decay=0.01), None),
+    # N = 8 (the eight-row kernel), fp16 rows into a bf16 buffer, a skip at step 3
+    "n8_skip": (_ws(8 * 40_001, 8, range(8), gather_dtype=BF16, steps=4, **DYN), (3, 7, 0, 40_000)),
+    # three ranks of 1,500 tiles of a 64-rank buffer: one launch each (2,048 tiles a launch at N = 64)
+    "launch_split": (_ws(64 * 1_500 * 2048, 64, (0, 1, 63), dtype=BF16, steps=2), None),
+    # 16-element shards, the last rank's empty
+    "tiny_empty_rank": (_ws(1_000, 64, range(64), steps=2), None),
+}
+
+
+def _run(w, inject, batched: bool, graph: bool = False):
+    import torch
+    import synth
+    import zero_partitioned_mixed_amd as Z
+    dev = torch.device("cuda", 0)
+    hp = Z.hparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                   scaler=w.scaler, min_scale=w.min_scale, growth_interval=w.growth_interval)
+    tdt = torch.float16 if w.dtype == F16 else torch.bfloat16
+    gdt = torch.float16 if w.slot_dtype == F16 else torch.bfloat16
+    steps, contribs, parts = [], [], []
+    for r in w.ranks:
+        _, off, valid = Z.zero_partition(w.psi, w.nranks, r)
+        p0 = torch.empty(max(valid, 1), dtype=torch.float32, device=dev)
+        synth.gpu_master_range(p0, w.seed, w.master_sigma, off)
+        stride = max((valid + 63) // 64 * 64, 64)
+        steps.append(Z.ShardStep(w.nranks, stride, valid, off, w.dtype, w.slot_dtype, hp,
+                                 (p0, torch.zeros_like(p0), torch.zeros_like(p0)), None,
+                                 w.loss_scale))
+        contribs.append(torch.empty((w.nranks, stride), dtype=tdt, device=dev))
+        parts.append((off, valid))
+    gather = torch.empty(w.psi, dtype=gdt, device=dev)
+    synth.gpu_param_range(gather, w.seed, w.master_sigma, w.slot_dtype, 0)
+    multi = Z.MultiShardStep(steps, batched=batched)
+    assert (multi._batch_table(contribs, gather, [None] * len(steps)) is not None) == batched
+    g = multi.capture(contribs, gather) if graph else None
+    torch.cuda.synchronize()
+    reports = []
+    for s in range(1, w.steps + 1):
+        for c, (off, valid) in zip(contribs, parts):
+            if valid:
+                synth.gpu_contrib_rows(c, w.seed, s, w.dtype, w.contrib_sigma, w.contrib_scale,
+                                       w.outlier_p, w.outlier_mult, off, valid)
+        if inject and inject[0] == s:
+            contribs[inject[1]][inject[2], inject[3]] = float("inf")
+        if g is None:
+            multi.step(contribs, gather)
+        else:
+            g.replay()
+        torch.cuda.synchronize()
+        reports.append([st.ctrl_dict() for st in steps])
+    state = [np.concatenate([t[:valid].cpu().numpy() for t in st.current()])
+             for st, (_, valid) in zip(steps, parts)]
+    return reports, state, gather.view(torch.int16).cpu().numpy()
+
+
+# every compiled form of the batched step: contribution format, slot format,
+# the eight-row kernel or any N; all n ranks of a buffer of n shards of 5,001
+# elements (three whole tiles and a ragged one each, slots at every
+# alignment), the second step skipped so that the restore runs in each slot
+# format
+FORMS = {f"{a}_to_{b}_n{n}": (_ws(n * 5_001, n, range(n), dtype=da, gather_dtype=db, steps=3,
+                                  **DYN), (2, 0, n - 1, 4_321))
+         for (a, da), (b, db), n in itertools.product((("f16", F16), ("bf16", BF16)),
+                                                      (("f16", F16), ("bf16", BF16)), (8, 3))}
+
+
+@pytest.mark.parametrize("name", list(CASES) + list(FORMS))
+def test_batched_shards_equal_their_own_calls(name):
+    w, inject = CASES[name] if name in CASES else FORMS[name]
+    H.log(f"shards {name}: psi={w.psi} N={w.nranks} ranks={len(w.ranks)} inject={inject}")
+    ra, sa, ga = _run(w, inject, batched=False)
+    rb, sb, gb = _run(w, inject, batched=True)
+    assert repr(ra) == repr(rb)
+    for x, y in zip(sa, sb):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    assert np.array_equal(ga, gb)
+    skips = [r[0]["skip"] for r in rb]
+    assert all(repr(r[0]) == repr(x) for r in rb for x in r)  # one decision for all ranks
+    if inject:
+        assert skips[inject[0] - 1] == 1 and sum(skips) == 1
+    H.log(f"shards {name}: batched equals per-rank calls; skips {skips}")
+
+
+def test_batched_shards_in_a_graph():
+    """The batched step (three launches) captured once and replayed equals
+    the per-rank calls run eagerly, with a skip at step 2."""
+    w, inject = CASES["toy_skip"]
+    ra, sa, ga = _run(w, inject, batched=False)
+    rb, sb, gb = _run(w, inject, batched=True, graph=True)
+    assert repr(ra) == repr(rb)
+    for x, y in zip(sa, sb):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    assert np.array_equal(ga, gb)

@@ -67,6 +67,7 @@ LAUNCH_ROW_TILES = 131072  # ZERO_LAUNCH_ROW_TILES
 LAUNCH_MIN_TILES = 2048  # ZERO_LAUNCH_MIN_TILES
 LAUNCH_PAYLOAD_TILES = 16384  # ZERO_LAUNCH_PAYLOAD_TILES
 NOALLOC_MAX_LEN = 1 << 31  # ZERO_NOALLOC_MAX_LEN
+BATCH_SHARDS = 32  # ZERO_BATCH_SHARDS
 
 
 def launch_tiles(nranks: int = 0, payload: bool = False) -> int:
@@ -86,6 +87,12 @@ def launches(valid_len: int, nranks: int = 0, payload: bool = False) -> int:
 
 class State(ctypes.Structure):
     _fields_ = [("master", _vp), ("m", _vp), ("v", _vp)]
+
+
+class Shard(ctypes.Structure):
+    """zero_shard: one shard of the batched calls."""
+    _fields_ = [("contrib", _vp), ("stride", _i64), ("pair", _vp), ("valid_len", _i64),
+                ("offset", _i64), ("ctrl", _vp), ("ws", _vp), ("ws_bytes", ctypes.c_size_t)]
 
 
 _sig = {
@@ -146,6 +153,9 @@ _sig = {
                                               _vp, _vp, _vp]),
     "zero_fused_step_noalloc": (ctypes.c_int, [_vp, _i32, _i32, _i64, ctypes.POINTER(State), _i64,
                                                _vp, _i32, _i64, ctypes.POINTER(Hparams), _vp, _vp]),
+    "zero_fused_step_shards": (ctypes.c_int, [ctypes.POINTER(Shard), _i32, _i32, _i32, _vp, _i32,
+                                              ctypes.POINTER(Hparams), _vp]),
+    "zero_fused_restore_shards": (ctypes.c_int, [ctypes.POINTER(Shard), _i32, _vp, _i32, _vp]),
     "zero_launch_tiles": (ctypes.c_int64, [_i32]),
     "zero_last_error": (ctypes.c_char_p, []),
 }
@@ -316,6 +326,31 @@ def zero_fused_restore(pair, valid_len: int, gather, dtype: int, offset: int, ct
     st = _state(pair)
     _check("zero_fused_restore", _lib.zero_fused_restore(
         ctypes.byref(st), valid_len, _ptr(gather), dtype, offset, _ptr(ctrl), _stream()))
+
+
+def shard_table(shards) -> ctypes.Array:
+    """The host array of zero_shard descriptors the batched calls take, from
+    (contrib, stride, pair, valid_len, offset, ctrl, ws) per shard: contrib
+    the [N, stride] rows, pair the paired state's (master, m, v) views, ws
+    the shard's workspace tensor."""
+    table = (Shard * len(shards))()
+    for d, (contrib, stride, pair, valid_len, offset, ctrl, ws) in zip(table, shards):
+        d.contrib, d.stride, d.pair = _ptr(contrib), stride, _ptr(pair[0])
+        d.valid_len, d.offset, d.ctrl = valid_len, offset, _ptr(ctrl)
+        d.ws, d.ws_bytes = _ptr(ws), ws.numel() * ws.element_size()
+    return table
+
+
+def zero_fused_step_shards(table, contrib_dtype: int, nranks: int, gather, gather_dtype: int,
+                           hp: Hparams) -> None:
+    _check("zero_fused_step_shards", _lib.zero_fused_step_shards(
+        table, len(table), contrib_dtype, nranks, _ptr(gather), gather_dtype, ctypes.byref(hp),
+        _stream()))
+
+
+def zero_fused_restore_shards(table, gather, gather_dtype: int) -> None:
+    _check("zero_fused_restore_shards", _lib.zero_fused_restore_shards(
+        table, len(table), _ptr(gather), gather_dtype, _stream()))
 
 
 def zero_pair_store(flat, pair, valid_len: int, ctrl) -> None:
@@ -622,9 +657,15 @@ class MultiShardStep:
     """Several ranks' shard steps on one GPU whose norm and overflow decisions
     are combined across the ranks (the scalar all-reduce between ranks).  The
     ranks share one path and one set of hyperparameters; each takes its own
-    contributions (any form ShardStep takes) and optional payload."""
+    contributions (any form ShardStep takes) and optional payload.
 
-    def __init__(self, steps: list):
+    With ``batched`` (the default), a fused step whose ranks all take one
+    [N, stride] contribution tensor, write the 16-bit slot and no payload,
+    come in one piece and fit one launch goes through the batched calls:
+    one zero_fused_step_shards, the decision, one zero_fused_restore_shards
+    (per 32 ranks), bit-identical to every rank's own calls."""
+
+    def __init__(self, steps: list, batched: bool = True):
         if not 1 <= len(steps) <= MAX_RANKS:
             raise ValueError("between 1 and 64 ranks")
         first = bytes(steps[0].hp)
@@ -632,36 +673,91 @@ class MultiShardStep:
             raise ValueError("the ranks of one decision share their hyperparameters")
         self.steps = steps
         self.fused = steps[0].fused
+        self.batched = batched
+        self._table = None  # (contribution addresses, shard_table)
+
+    def _batch_table(self, contribs, gather, qgathers):
+        """The shard table of a step the batched calls can take, or None."""
+        ss, s0 = self.steps, self.steps[0]
+        if not (self.batched and self.fused) or gather is None or any(q is not None for q in qgathers):
+            return None
+        cap = launch_tiles(s0.nranks) * TILE
+        if any(s.bucket or s.valid_len > cap or s.nranks != s0.nranks or s.dtype != s0.dtype
+               or s.gather_dtype != s0.gather_dtype for s in ss):
+            return None
+        if any(isinstance(c, (list, tuple, QuantRows)) for c in contribs):
+            return None
+        key = tuple(c.data_ptr() for c in contribs)
+        if self._table is None or self._table[0] != key:
+            self._table = (key, shard_table([(c, s.stride, s.pair, s.valid_len, s.offset, s.ctrl,
+                                              s.ws) for s, c in zip(ss, contribs)]))
+        return self._table[1]
 
     def step(self, contribs, gather, qgathers=None, branches: list | None = None) -> None:
-        """One step of every rank.  With ``branches`` (streams), rank i's
-        launches go to branches[i % len(branches)], forked from and joined
-        back into the current stream around each phase; the ranks touch
-        disjoint buffers, so only the shared decision orders them."""
+        """One step of every rank.  With ``branches`` (streams) and a step
+        the batched calls do not take, rank i's launches go to
+        branches[i % len(branches)], forked from and joined back into the
+        current stream around each phase; the ranks touch disjoint buffers,
+        so only the shared decision orders them."""
+        qgathers = self._payloads(contribs, qgathers)
+        self.run_passes(contribs, gather, qgathers, branches)
+        self.decide()
+        self.complete(contribs, gather, qgathers, branches)
+
+    def takes_batched(self, contribs, gather, qgathers=None) -> bool:
+        """Whether a step on these buffers goes through the batched calls."""
+        return self._batch_table(contribs, gather, self._payloads(contribs, qgathers)) is not None
+
+    def _payloads(self, contribs, qgathers):
+        n = len(self.steps)
+        qgathers = [None] * n if qgathers is None else list(qgathers)
+        if len(contribs) != n or len(qgathers) != n:
+            raise ValueError(f"one contribution set and payload per rank ({n})")
+        return qgathers
+
+    def _per_rank(self, fn, branches) -> None:
         import torch
+        if not branches:
+            for i in range(len(self.steps)):
+                fn(i)
+            return
+        main = torch.cuda.current_stream()
+        for b in branches:
+            b.wait_stream(main)
+        for i in range(len(self.steps)):
+            with torch.cuda.stream(branches[i % len(branches)]):
+                fn(i)
+        for b in branches:
+            main.wait_stream(b)
+
+    def run_passes(self, contribs, gather, qgathers=None, branches=None) -> None:
+        """The per-element launches of a step: every rank's fused pass (one
+        batched launch per 32 ranks when the step allows) or reduce pass."""
         ss = self.steps
-        qgathers = [None] * len(ss) if qgathers is None else list(qgathers)
-        if len(contribs) != len(ss) or len(qgathers) != len(ss):
-            raise ValueError(f"one contribution set and payload per rank ({len(ss)})")
+        qgathers = self._payloads(contribs, qgathers)
+        table = self._batch_table(contribs, gather, qgathers)
+        if table is not None:
+            s0 = ss[0]
+            zero_fused_step_shards(table, s0.dtype, s0.nranks, gather, s0.gather_dtype, s0.hp)
+        else:
+            self._per_rank(lambda i: ss[i].run_pieces(contribs[i], gather, qgathers[i]), branches)
 
-        def per_rank(fn):
-            if not branches:
-                for i in range(len(ss)):
-                    fn(i)
-                return
-            main = torch.cuda.current_stream()
-            for b in branches:
-                b.wait_stream(main)
-            for i in range(len(ss)):
-                with torch.cuda.stream(branches[i % len(branches)]):
-                    fn(i)
-            for b in branches:
-                main.wait_stream(b)
-
-        per_rank(lambda i: ss[i].run_pieces(contribs[i], gather, qgathers[i]))
+    def decide(self) -> None:
+        """One decision over every rank's partials, written to every rank's ctrl."""
+        ss = self.steps
         zero_grad_norm_overflow([s.ws for s in ss], [s.valid_len for s in ss],
                                 [s.ctrl for s in ss], ss[0].hp, self.fused)
-        per_rank(lambda i: ss[i].complete(gather, qgathers[i]))
+
+    def complete(self, contribs, gather, qgathers=None, branches=None) -> None:
+        """The rest of the step: every rank's restore check (batched when the
+        passes were) or Adam pass."""
+        ss = self.steps
+        qgathers = self._payloads(contribs, qgathers)
+        table = self._batch_table(contribs, gather, qgathers)
+        if table is not None:
+            zero_fused_restore_shards(table, gather, ss[0].gather_dtype)
+        else:
+            self._per_rank(lambda i: ss[i].complete(gather, qgathers[i]), branches)
 
     def capture(self, contribs, gather, qgathers=None, branches: int = 4):
         """Records one step of all the ranks (every rank's launches, the

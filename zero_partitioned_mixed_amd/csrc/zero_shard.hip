@@ -1016,17 +1016,19 @@ struct FusedArgs {
 };
 
 // Single pass over one tile: reduce + partial + Adam (read set cur, write set
-// 1-cur of the tile) + cast.  QB = 8 or 4 also quantises the tile's new
+// 1-cur of the tile) + cast.  The tile is the workgroup's (tile_index), or
+// tile_at when AT (a launch over several shards).  QB = 8 or 4 also quantises the tile's new
 // 16-bit parameters as one block (the payload of a quantised all-gather),
 // after the per-thread work so that every thread reaches the block's barrier.
-template <int DTO, int GW, int NR, class SRC, int QB>
-__device__ __forceinline__ void fused_tile(const FusedArgs<SRC>& a, const QGatherOut& qo) {
+template <int DTO, int GW, int NR, class SRC, int QB, bool AT = false>
+__device__ __forceinline__ void fused_tile(const FusedArgs<SRC>& a, const QGatherOut& qo,
+                                           int64_t tile_at = 0) {
     const zero_ctrl* __restrict__ c = a.ctrl;
     const int cur = c->cur;
     const float inv = (float)(1.0 / ((double)a.n * (double)c->loss_scale));
     const AdamK k = make_adam(a.hp, c->beta1_pow * (double)a.hp.beta1,
                               c->beta2_pow * (double)a.hp.beta2);
-    const int64_t tile = tile_index<SRC::kGrouped>();
+    const int64_t tile = AT ? tile_at : tile_index<SRC::kGrouped>();
     const Runs r = runs_of(tile);
     double ss = 0.0;
     uint32_t bad = 0;
@@ -1123,6 +1125,75 @@ struct FusedQArgs {
 template <int DTO, int NR, class SRC, int BITS>
 __global__ void __launch_bounds__(kBlock) fused_qgather_kernel(FusedQArgs<SRC> a) {
     fused_tile<DTO, kGwRuntime, NR, SRC, BITS>(a.f, a.q);
+}
+
+// ---------------------------------------------------------------- several shards per launch
+// Small shards of several ranks on one GPU: one launch covers the tiles of up
+// to ZERO_BATCH_SHARDS shards, shard k taking workgroups [tile0_k, tile0_k +
+// its tiles).  Each tile runs exactly the code of its shard's own launch.
+struct ShardArg {
+    const uint16_t* rows;  // [n, stride] 16-bit rows
+    int64_t stride;
+    float* pair;           // paired state; m and v one and two ZERO_TILE further
+    uint16_t* slot;        // gather buffer + offset
+    int64_t len;
+    Partial* ws;
+    const zero_ctrl* ctrl;
+    int32_t tile0;         // the shard's first workgroup in the launch
+    int32_t gw;            // slot store width: 4, 2 or 1 values
+};
+
+struct ShardsArgs {
+    ShardArg s[ZERO_BATCH_SHARDS];
+    zero_hparams hp;
+    int32_t nshards;
+    int32_t n;
+};
+
+// The workgroup's shard: the last one whose first workgroup is at or below
+// blockIdx.x (tile0 increases with k; a workgroup-uniform scan).
+__device__ __forceinline__ int shard_of(const ShardsArgs& a) {
+    const int64_t w = blockIdx.x;
+    int k = 0;
+    for (int q = 1; q < a.nshards; ++q)
+        if (a.s[q].tile0 <= w) k = q;
+    return k;
+}
+
+template <int DT, int DTO, int NR>
+__global__ void __launch_bounds__(kBlock) fused_shards_kernel(ShardsArgs a) {
+    using SRC = Src16<DT, StridedRows>;
+    const ShardArg& s = a.s[shard_of(a)];
+    const FusedArgs<SRC> f{SRC{StridedRows{s.rows, s.stride}},
+                           {s.pair, s.pair + kTile, s.pair + 2 * kTile},
+                           s.slot, s.len, s.ctrl, s.ws, a.hp, a.n};
+    fused_tile<DTO, kGwRuntime, NR, SRC, 0, true>(f, QGatherOut{nullptr, nullptr, s.gw},
+                                                   (int64_t)blockIdx.x - s.tile0);
+}
+
+// The restore check of several shards: each workgroup rewrites one tile of
+// its shard's slot from the current set of the paired master when that
+// shard's step was skipped, and returns at once otherwise.
+template <int DT>
+__global__ void __launch_bounds__(kBlock) restore_shards_kernel(ShardsArgs a) {
+    const ShardArg& s = a.s[shard_of(a)];
+    if (!s.ctrl->skip) return;
+    const int cur = s.ctrl->cur;
+    const Runs r = runs_of((int64_t)blockIdx.x - s.tile0);
+    if (r.b + kRun <= s.len) {
+        const int64_t sa = pair_index(r.a, cur);
+        float p[kVec];
+        uint32_t h[kVec];
+        load8(s.pair + sa, s.pair + sa + 256, p);
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) h[j] = narrow<DT>(p[j]);
+        store_slot_rt(s.gw, s.slot, r, h);
+    } else {
+        for (int j = 0; j < kVec; ++j) {
+            const int64_t i = elem(r, j);
+            if (i < s.len) s.slot[i] = (uint16_t)narrow<DT>(s.pair[pair_index(i, cur)]);
+        }
+    }
 }
 
 // ---------------------------------------------------------------- block quantisation
@@ -1794,6 +1865,76 @@ int fused_qgather_launch(const SRC& src, int32_t nranks, const zero_state* pair,
                           Residency<SRC>::fused_q);
 }
 
+// Checks every shard of a batched call before anything is enqueued.  The
+// fused step (restore = false) needs the contribution rows, the workspace and
+// at most launch_tiles(n) tiles per shard; the restore only the state, slot
+// and ctrl, and at most ZERO_LAUNCH_TILES tiles per shard.
+int check_shards(const zero_shard* shards, int32_t nshards, int32_t contrib_dtype, int32_t n,
+                 const void* gather, int32_t gather_dtype, bool restore, const char* what) {
+    int rc;
+    if (shards == nullptr) return fail(ZERO_EINVAL, "%s: null shard array", what);
+    if (nshards < 1 || nshards > ZERO_MAX_RANKS)
+        return fail(ZERO_EINVAL, "%s: nshards %d outside [1, %d]", what, nshards, ZERO_MAX_RANKS);
+    const int64_t cap = restore ? ZERO_LAUNCH_TILES : launch_tiles(n);
+    for (int i = 0; i < nshards; ++i) {
+        const zero_shard& z = shards[i];
+        if ((rc = check_len(z.valid_len, what)) != ZERO_OK) return rc;
+        if (tiles_for(z.valid_len) > cap)
+            return fail(ZERO_ERANGE, "%s: shard %d has %lld tiles, more than the %lld of one "
+                        "launch; step it with its own calls", what, i,
+                        (long long)tiles_for(z.valid_len), (long long)cap);
+        if (!restore) {
+            if ((rc = check_contrib(z.contrib_dev, contrib_dtype, n, z.stride, z.valid_len)) != ZERO_OK)
+                return rc;
+            if ((rc = check_ws(z.ws_dev, z.ws_bytes, z.valid_len)) != ZERO_OK) return rc;
+        }
+        if (z.pair_dev == nullptr || !aligned16(z.pair_dev))
+            return fail(ZERO_EINVAL, "%s: shard %d: paired state null or not 16-byte aligned", what, i);
+        if ((rc = check_ctrl(z.ctrl_dev, what)) != ZERO_OK) return rc;
+        if ((rc = check_slot(gather, gather_dtype, z.offset)) != ZERO_OK) return rc;
+    }
+    return ZERO_OK;
+}
+
+// Packs the non-empty shards into launches of at most ZERO_BATCH_SHARDS shards
+// and `cap` tiles and calls launch_one(args, tiles) for each, in shard order.
+template <class LaunchOne>
+int for_each_shard_launch(const zero_shard* shards, int32_t nshards, uint16_t* gather,
+                          int64_t cap, LaunchOne&& launch_one) {
+    ShardsArgs a{};
+    int64_t tiles = 0;
+    for (int i = 0; i < nshards; ++i) {
+        const zero_shard& z = shards[i];
+        const int64_t t = tiles_for(z.valid_len);
+        if (t == 0) continue;
+        if (a.nshards == ZERO_BATCH_SHARDS || tiles + t > cap) {
+            const int rc = launch_one(a, tiles);
+            if (rc != ZERO_OK) return rc;
+            a = ShardsArgs{};
+            tiles = 0;
+        }
+        ShardArg& s = a.s[a.nshards++];
+        s.rows = (const uint16_t*)z.contrib_dev;
+        s.stride = z.stride;
+        s.pair = z.pair_dev;
+        s.slot = gather + z.offset;
+        s.len = z.valid_len;
+        s.ws = (Partial*)z.ws_dev;
+        s.ctrl = z.ctrl_dev;
+        s.tile0 = (int32_t)tiles;
+        s.gw = store_width(s.slot);
+        tiles += t;
+    }
+    return a.nshards > 0 ? launch_one(a, tiles) : ok();
+}
+
+template <int DT>
+Kernel<ShardsArgs> fused_shards_for(int dto, int n) {
+    if (n == 8)
+        return dto == ZERO_F16 ? fused_shards_kernel<DT, ZERO_F16, 8> : fused_shards_kernel<DT, ZERO_BF16, 8>;
+    return dto == ZERO_F16 ? fused_shards_kernel<DT, ZERO_F16, 0> : fused_shards_kernel<DT, ZERO_BF16, 0>;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- allocation-free step
@@ -2142,6 +2283,42 @@ int zero_fused_restore(const zero_state* pair, int64_t valid_len, void* gather, 
     }
     return launch(k, nt < kRestoreGrid ? nt : kRestoreGrid, kBlock, (hipStream_t)stream, a,
                   "zero_fused_restore");
+}
+
+int zero_fused_step_shards(const zero_shard* shards, int32_t nshards, int32_t contrib_dtype,
+                           int32_t nranks, void* gather, int32_t gather_dtype,
+                           const zero_hparams* hp, void* stream) {
+    int rc;
+    const char* what = "zero_fused_step_shards";
+    if ((rc = check_hp(hp)) != ZERO_OK) return rc;
+    if (hp->max_grad_norm > 0.0f) return fail(ZERO_EINVAL, "%s: clipping needs the two-pass path", what);
+    if ((rc = check_shards(shards, nshards, contrib_dtype, nranks, gather, gather_dtype, false,
+                           what)) != ZERO_OK)
+        return rc;
+    const Kernel<ShardsArgs> k = contrib_dtype == ZERO_F16
+                                     ? fused_shards_for<ZERO_F16>(gather_dtype, nranks)
+                                     : fused_shards_for<ZERO_BF16>(gather_dtype, nranks);
+    return for_each_shard_launch(shards, nshards, (uint16_t*)gather, launch_tiles(nranks),
+                                 [&](ShardsArgs& a, int64_t tiles) {
+                                     a.hp = *hp;
+                                     a.n = nranks;
+                                     return launch(k, tiles, kBlock, (hipStream_t)stream, a, what,
+                                                   kResidencyLds);
+                                 });
+}
+
+int zero_fused_restore_shards(const zero_shard* shards, int32_t nshards, void* gather,
+                              int32_t gather_dtype, void* stream) {
+    int rc;
+    const char* what = "zero_fused_restore_shards";
+    if ((rc = check_shards(shards, nshards, ZERO_F16, 1, gather, gather_dtype, true, what)) != ZERO_OK)
+        return rc;
+    const Kernel<ShardsArgs> k = gather_dtype == ZERO_F16 ? restore_shards_kernel<ZERO_F16>
+                                                          : restore_shards_kernel<ZERO_BF16>;
+    return for_each_shard_launch(shards, nshards, (uint16_t*)gather, ZERO_LAUNCH_TILES,
+                                 [&](ShardsArgs& a, int64_t tiles) {
+                                     return launch(k, tiles, kBlock, (hipStream_t)stream, a, what);
+                                 });
 }
 
 int zero_fused_step_qgather(const void* contrib, int32_t contrib_dtype, int32_t nranks,
