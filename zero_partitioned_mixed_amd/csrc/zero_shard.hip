@@ -1130,7 +1130,9 @@ __global__ void __launch_bounds__(kBlock) fused_qgather_kernel(FusedQArgs<SRC> a
 // ---------------------------------------------------------------- several shards per launch
 // Small shards of several ranks on one GPU: one launch covers the tiles of up
 // to ZERO_BATCH_SHARDS shards, shard k taking workgroups [tile0_k, tile0_k +
-// its tiles).  Each tile runs exactly the code of its shard's own launch.
+// its tiles).  Each tile does the arithmetic of its shard's own launch, in the
+// same order (the slot's store width is chosen per shard at run time), so the
+// results are bit-identical to one launch per shard.
 struct ShardArg {
     const uint16_t* rows;  // [n, stride] 16-bit rows
     int64_t stride;
