@@ -377,34 +377,41 @@ int zero_pair_load(const zero_state *pair, const zero_state *flat, int64_t valid
  * table: its toy runs every rank of the data-parallel group in one process,
  * each rank owning one shard.  When several ranks' shards share a GPU and
  * each is small (the toy's 32 shards have ten tiles each), one launch per
- * shard leaves the chip idle between launches.  These two calls are
- * zero_fused_step and zero_fused_restore for up to ZERO_MAX_RANKS shards at
+ * shard leaves the chip idle between launches.  The calls below are
+ * zero_fused_step and zero_fused_restore (fused path), and zero_reduce_grads
+ * and zero_adam_step (two-pass path), for up to ZERO_MAX_RANKS shards at
  * once, as one launch per ZERO_BATCH_SHARDS shards: every shard's results are
- * bit-identical to its own calls'.  Between them, zero_grad_norm_overflow over
- * the shards' workspaces and ctrl blocks takes the shared decision. */
+ * bit-identical to its own calls'.  Between the two launches of a step,
+ * zero_grad_norm_overflow over the shards' workspaces and ctrl blocks takes
+ * the shared decision. */
 
-/* One shard of a batched call: what zero_fused_step takes for it (its paired
- * state as the one buffer that zero_state's master points to). */
+/* One shard of a batched call: what the single-shard calls take for it.  Each
+ * call reads only the fields it needs (see below). */
 typedef struct zero_shard {
     const void *contrib_dev; /* [nranks, stride] 16-bit rows, 16-byte aligned */
     int64_t stride;          /* elements between rows: >= valid_len, a multiple of 8 */
-    float *pair_dev;         /* paired state, zero_pair_elems(valid_len) floats, 16-byte aligned */
-    int64_t valid_len;       /* at most zero_launch_tiles(nranks) tiles (see below) */
+    float *pair_dev;         /* fused path: paired state, zero_pair_elems(valid_len) floats,
+                                16-byte aligned (the buffer zero_state's master points to) */
+    int64_t valid_len;       /* at most one launch of tiles (see the calls) */
     int64_t offset;          /* the shard's slot in the gather buffer, in elements */
     zero_ctrl *ctrl_dev;     /* the shard's (rank's) ctrl block */
     void *ws_dev;            /* zero_workspace_bytes(valid_len) bytes, 16-byte aligned */
     size_t ws_bytes;
+    zero_state state;        /* two-pass path: flat master, m, v of valid_len floats */
+    float *g_dev;            /* two-pass path: the reduced gradient, valid_len floats,
+                                16-byte aligned */
 } zero_shard;
 
 #define ZERO_BATCH_SHARDS 32 /* most shards in one launch of a batched call */
 
 /* zero_fused_step for each of the nshards (1..ZERO_MAX_RANKS) shards in the
- * host array `shards`, which share contrib_dtype, nranks, the gather buffer
- * and its dtype, and hp (no clipping).  The shards' states, slots, ctrl
- * blocks and workspaces must not overlap.  Every shard is checked before
- * anything is enqueued, with the errors of zero_fused_step; a shard of more
- * than zero_launch_tiles(nranks) tiles returns ERANGE (step it with its own
- * calls).  Shards with valid_len 0 launch nothing. */
+ * host array `shards` (contrib_dev, stride, pair_dev, valid_len, offset,
+ * ctrl_dev, ws_dev and ws_bytes are read), which share contrib_dtype, nranks,
+ * the gather buffer and its dtype, and hp (no clipping).  The shards' states,
+ * slots, ctrl blocks and workspaces must not overlap.  Every shard is checked
+ * before anything is enqueued, with the errors of zero_fused_step; a shard of
+ * more than zero_launch_tiles(nranks) tiles returns ERANGE (step it with its
+ * own calls).  Shards with valid_len 0 launch nothing; so in the calls below. */
 int zero_fused_step_shards(const zero_shard *shards, int32_t nshards, int32_t contrib_dtype,
                            int32_t nranks, void *gather_dev, int32_t gather_dtype,
                            const zero_hparams *hp, void *stream);
@@ -414,6 +421,18 @@ int zero_fused_step_shards(const zero_shard *shards, int32_t nshards, int32_t co
  * per shard). */
 int zero_fused_restore_shards(const zero_shard *shards, int32_t nshards, void *gather_dev,
                               int32_t gather_dtype, void *stream);
+
+/* zero_reduce_grads for each shard (contrib_dev, stride, valid_len, ctrl_dev,
+ * ws_dev, ws_bytes and g_dev are read; at most zero_launch_tiles(nranks)
+ * tiles per shard, ERANGE otherwise). */
+int zero_reduce_grads_shards(const zero_shard *shards, int32_t nshards, int32_t contrib_dtype,
+                             int32_t nranks, void *stream);
+
+/* zero_adam_step for each shard after the decision (state, g_dev, valid_len,
+ * offset and ctrl_dev are read; at most ZERO_LAUNCH_TILES tiles per shard);
+ * gather_dev NULL writes no slot.  Clipping as in zero_adam_step. */
+int zero_adam_step_shards(const zero_shard *shards, int32_t nshards, const zero_hparams *hp,
+                          void *gather_dev, int32_t gather_dtype, void *stream);
 
 /* ---- Block-quantised payloads (ZeRO++) --------------------------------------
  * "CMU 11-868 L18", Other memory optimizations: ZeRO++ quantises the

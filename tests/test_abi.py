@@ -43,7 +43,7 @@ def test_struct_sizes_match_header(Z):
     assert Z.zero_ctrl_bytes() == 128 == ctypes.sizeof(Z.Ctrl)
     assert ctypes.sizeof(Z.Hparams) == 36
     assert ctypes.sizeof(Z.State) == 24
-    assert ctypes.sizeof(Z.Shard) == 64
+    assert ctypes.sizeof(Z.Shard) == 96
 
 
 def test_partition_matches_oracle(Z, O):
@@ -143,10 +143,11 @@ def test_fused_noalloc_validation(Z):
 def _shard(Z, **kw):
     """A well-formed zero_shard of 64 elements at fake addresses, with changes."""
     d = dict(contrib=FAKE, stride=64, pair=FAKE, valid_len=64, offset=0, ctrl=FAKE, ws=FAKE,
-             ws_bytes=Z.zero_workspace_bytes(64))
+             ws_bytes=Z.zero_workspace_bytes(64), state=(FAKE, FAKE + 256, FAKE + 512),
+             g=FAKE + 768)
     d.update(kw)
     return Z.Shard(d["contrib"], d["stride"], d["pair"], d["valid_len"], d["offset"], d["ctrl"],
-                   d["ws"], d["ws_bytes"])
+                   d["ws"], d["ws_bytes"], Z.State(*d["state"]), d["g"])
 
 
 def test_batched_shards_validation(Z):
@@ -187,6 +188,43 @@ def test_batched_shards_validation(Z):
     assert restore([good, _shard(Z, valid_len=top + 1)]) == -3
     assert restore([_shard(Z, pair=0)]) == -1 and restore([_shard(Z, ctrl=0)]) == -1
     assert restore([good], gather=0) == -1 and restore([good] * 65) == -1
+
+
+def test_batched_two_pass_validation(Z):
+    """The batched reduce and Adam passes check every shard before anything is
+    enqueued: rows, workspace and g for the reduce, flat state and g for the
+    Adam pass, ctrl and the slot (the Adam pass may write none), and that
+    each shard fits one launch."""
+    hp = Z.hparams(max_grad_norm=1.0)
+
+    def reduce(shards, n=8):
+        arr = (Z.Shard * max(len(shards), 1))(*shards)
+        return Z._lib.zero_reduce_grads_shards(arr, len(shards), 1, n, None)
+
+    def adam(shards, gather=FAKE, hp=hp, gdt=1):
+        arr = (Z.Shard * max(len(shards), 1))(*shards)
+        return Z._lib.zero_adam_step_shards(arr, len(shards), ctypes.byref(hp), gather, gdt, None)
+
+    good = _shard(Z)
+    assert reduce([]) == -1 and reduce([good] * 65) == -1
+    top = Z.launch_tiles(64) * Z.TILE
+    big = _shard(Z, valid_len=top + 1, stride=top + 8, ws_bytes=Z.zero_workspace_bytes(top + 1))
+    assert reduce([good, big], n=64) == -3
+    codes = [reduce([good, b]) for b in (_shard(Z, contrib=0), _shard(Z, contrib=FAKE + 8),
+                                         _shard(Z, stride=68), _shard(Z, ws=0),
+                                         _shard(Z, ws_bytes=16), _shard(Z, g=0),
+                                         _shard(Z, g=FAKE + 4), _shard(Z, ctrl=0))]
+    assert codes == [-1, -2, -2, -1, -4, -1, -1, -1], codes
+    assert adam([good] * 65) == -1
+    assert adam([good], hp=Z.hparams(beta1=1.0)) == -1
+    assert adam([good, _shard(Z, valid_len=Z.LAUNCH_TILES * Z.TILE + 1)]) == -3
+    codes = [adam([good, b]) for b in (_shard(Z, g=0), _shard(Z, state=(0, FAKE, FAKE + 256)),
+                                       _shard(Z, state=(FAKE, FAKE, FAKE + 256)),
+                                       _shard(Z, state=(FAKE + 4, FAKE + 256, FAKE + 512)),
+                                       _shard(Z, ctrl=0), _shard(Z, offset=-1))]
+    assert codes == [-1, -1, -1, -2, -1, -3], codes
+    assert adam([_shard(Z, g=0)], gather=None) == -1   # no slot: the rest still checked
+    assert adam([good], gather=None, gdt=7) == -1
 
 
 def test_hparam_validation(Z):

@@ -129,7 +129,8 @@ ENTRY_POINTS = ["zero_fused_step", "zero_fused_step_rows", "zero_fused_step_q",
                 "zero_fused_step_q_qgather", "zero_reduce_grads", "zero_reduce_grads_rows",
                 "zero_reduce_grads_q", "zero_grad_norm_overflow", "zero_fused_restore",
                 "zero_fused_restore_q", "zero_adam_step", "zero_adam_step_qgather",
-                "zero_fused_step_shards", "zero_fused_restore_shards"]
+                "zero_fused_step_shards", "zero_fused_restore_shards", "zero_reduce_grads_shards",
+                "zero_adam_step_shards"]
 
 
 @pytest.mark.parametrize("fused", [True, False])
@@ -198,10 +199,11 @@ class _FakeRows:
 
 
 def test_multi_shard_step_batches_small_fused_shards(Z, monkeypatch):
-    """Ranks on the fused path with one [N, stride] tensor each, a 16-bit
-    slot, no payload, no buckets and shards of at most one launch go through
-    the batched calls: three launches a step whatever the rank count; any
-    other step, or batched=False, through every rank's own calls."""
+    """Ranks with one [N, stride] tensor each, no payload, no buckets and
+    shards of at most one launch go through the batched calls, on the fused
+    path (with a 16-bit slot) and on the two-pass path: three launches a step
+    whatever the rank count; any other step, or batched=False, through every
+    rank's own calls."""
     calls = []
     for name in ENTRY_POINTS:
         monkeypatch.setattr(Z, name, lambda *a, _n=name, **k: calls.append(_n))
@@ -217,9 +219,13 @@ def test_multi_shard_step_batches_small_fused_shards(Z, monkeypatch):
     calls.clear()
     Z.MultiShardStep(ranks, batched=False).step(rows, "gather")
     assert calls == per_rank
-    for change in ("table", "bucket", "long", "payload", "two_pass"):
+    calls.clear()
+    Z.MultiShardStep([_fake_step(Z, False) for _ in range(5)]).step(rows, "gather")
+    assert calls == ["zero_reduce_grads_shards", "zero_grad_norm_overflow",
+                     "zero_adam_step_shards"]
+    for change in ("table", "bucket", "long", "payload"):
         calls.clear()
-        rs = [_fake_step(Z, change != "two_pass") for _ in range(5)]
+        rs = [_fake_step(Z, True) for _ in range(5)]
         contribs, qgs = list(rows), None
         if change == "table":
             contribs[2] = [1 << 20, 1 << 21]

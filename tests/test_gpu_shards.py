@@ -1,9 +1,11 @@
 """Several ranks' shards on one GPU through the batched calls
-(zero_fused_step_shards, zero_fused_restore_shards) against every rank's own
-calls (zero_fused_step, zero_fused_restore), bit for bit: every step's ctrl
-of every rank, every rank's state, and the whole parameter buffer.  The
-oracle checks of MultiShardStep (the toy's 32 shards, 64 ranks of a ragged
-buffer, an overflow on one rank) take the batched calls by default."""
+(zero_fused_step_shards and zero_fused_restore_shards; zero_reduce_grads_shards
+and zero_adam_step_shards) against every rank's own calls (zero_fused_step and
+zero_fused_restore; zero_reduce_grads and zero_adam_step), bit for bit: every
+step's ctrl of every rank, every rank's state, and the whole parameter
+buffer.  The oracle checks of MultiShardStep (the toy's 32 shards, 64 ranks
+of a ragged buffer, an overflow on one rank, the ZeRO layouts) take the
+batched calls by default."""
 import itertools
 
 import numpy as np
@@ -49,6 +51,16 @@ CASES = {
     "launch_split": (_ws(64 * 1_500 * 2048, 64, (0, 1, 63), dtype=BF16, steps=2), None),
     # 16-element shards, the last rank's empty
     "tiny_empty_rank": (_ws(1_000, 64, range(64), steps=2), None),
+    # the two-pass path (clipping): the toy's 32 shards with a skip at step 2 (every applied
+    # step clips at 1e-3), 64 ranks of mixed formats with decay, N = 8 with a threshold that
+    # binds on some steps only, 16-element shards with an empty rank
+    "two_pass_toy_skip": (_ws(workloads.TOY.psi, 32, range(32), max_grad_norm=1e-3, **DYN),
+                          (2, 9, 4, 1_000)),
+    "two_pass_ranks64_mixed": (_ws(64 * 3_001 - 40, 64, range(64), dtype=BF16, gather_dtype=F16,
+                                   weight_decay=0.01, max_grad_norm=0.05), None),
+    "two_pass_n8": (_ws(8 * 40_001, 8, range(8), gather_dtype=BF16, steps=4, max_grad_norm=0.06,
+                        outlier_p=1e-4), None),
+    "two_pass_tiny_empty_rank": (_ws(1_000, 64, range(64), steps=2, max_grad_norm=0.01), None),
 }
 
 
@@ -58,7 +70,8 @@ def _run(w, inject, batched: bool, graph: bool = False):
     import zero_partitioned_mixed_amd as Z
     dev = torch.device("cuda", 0)
     hp = Z.hparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
-                   scaler=w.scaler, min_scale=w.min_scale, growth_interval=w.growth_interval)
+                   max_grad_norm=w.max_grad_norm, scaler=w.scaler, min_scale=w.min_scale,
+                   growth_interval=w.growth_interval)
     tdt = torch.float16 if w.dtype == F16 else torch.bfloat16
     gdt = torch.float16 if w.slot_dtype == F16 else torch.bfloat16
     steps, contribs, parts = [], [], []
@@ -67,8 +80,9 @@ def _run(w, inject, batched: bool, graph: bool = False):
         p0 = torch.empty(max(valid, 1), dtype=torch.float32, device=dev)
         synth.gpu_master_range(p0, w.seed, w.master_sigma, off)
         stride = max((valid + 63) // 64 * 64, 64)
+        g = torch.empty_like(p0) if w.max_grad_norm > 0 else None
         steps.append(Z.ShardStep(w.nranks, stride, valid, off, w.dtype, w.slot_dtype, hp,
-                                 (p0, torch.zeros_like(p0), torch.zeros_like(p0)), None,
+                                 (p0, torch.zeros_like(p0), torch.zeros_like(p0)), g,
                                  w.loss_scale))
         contribs.append(torch.empty((w.nranks, stride), dtype=tdt, device=dev))
         parts.append((off, valid))
@@ -102,10 +116,11 @@ def _run(w, inject, batched: bool, graph: bool = False):
 # elements (three whole tiles and a ragged one each, slots at every
 # alignment), the second step skipped so that the restore runs in each slot
 # format
-FORMS = {f"{a}_to_{b}_n{n}": (_ws(n * 5_001, n, range(n), dtype=da, gather_dtype=db, steps=3,
-                                  **DYN), (2, 0, n - 1, 4_321))
-         for (a, da), (b, db), n in itertools.product((("f16", F16), ("bf16", BF16)),
-                                                      (("f16", F16), ("bf16", BF16)), (8, 3))}
+FORMS = {f"{path}_{a}_to_{b}_n{n}": (_ws(n * 5_001, n, range(n), dtype=da, gather_dtype=db,
+                                          steps=3, max_grad_norm=clip, **DYN), (2, 0, n - 1, 4_321))
+         for (path, clip), (a, da), (b, db), n in itertools.product(
+             (("fused", 0.0), ("two_pass", 0.02)), (("f16", F16), ("bf16", BF16)),
+             (("f16", F16), ("bf16", BF16)), (8, 3))}
 
 
 @pytest.mark.parametrize("name", list(CASES) + list(FORMS))
@@ -125,10 +140,11 @@ def test_batched_shards_equal_their_own_calls(name):
     H.log(f"shards {name}: batched equals per-rank calls; skips {skips}")
 
 
-def test_batched_shards_in_a_graph():
+@pytest.mark.parametrize("name", ["toy_skip", "two_pass_toy_skip"])
+def test_batched_shards_in_a_graph(name):
     """The batched step (three launches) captured once and replayed equals
     the per-rank calls run eagerly, with a skip at step 2."""
-    w, inject = CASES["toy_skip"]
+    w, inject = CASES[name]
     ra, sa, ga = _run(w, inject, batched=False)
     rb, sb, gb = _run(w, inject, batched=True, graph=True)
     assert repr(ra) == repr(rb)

@@ -92,7 +92,8 @@ class State(ctypes.Structure):
 class Shard(ctypes.Structure):
     """zero_shard: one shard of the batched calls."""
     _fields_ = [("contrib", _vp), ("stride", _i64), ("pair", _vp), ("valid_len", _i64),
-                ("offset", _i64), ("ctrl", _vp), ("ws", _vp), ("ws_bytes", ctypes.c_size_t)]
+                ("offset", _i64), ("ctrl", _vp), ("ws", _vp), ("ws_bytes", ctypes.c_size_t),
+                ("state", State), ("g", _vp)]
 
 
 _sig = {
@@ -156,6 +157,9 @@ _sig = {
     "zero_fused_step_shards": (ctypes.c_int, [ctypes.POINTER(Shard), _i32, _i32, _i32, _vp, _i32,
                                               ctypes.POINTER(Hparams), _vp]),
     "zero_fused_restore_shards": (ctypes.c_int, [ctypes.POINTER(Shard), _i32, _vp, _i32, _vp]),
+    "zero_reduce_grads_shards": (ctypes.c_int, [ctypes.POINTER(Shard), _i32, _i32, _i32, _vp]),
+    "zero_adam_step_shards": (ctypes.c_int, [ctypes.POINTER(Shard), _i32, ctypes.POINTER(Hparams),
+                                             _vp, _i32, _vp]),
     "zero_launch_tiles": (ctypes.c_int64, [_i32]),
     "zero_last_error": (ctypes.c_char_p, []),
 }
@@ -330,14 +334,19 @@ def zero_fused_restore(pair, valid_len: int, gather, dtype: int, offset: int, ct
 
 def shard_table(shards) -> ctypes.Array:
     """The host array of zero_shard descriptors the batched calls take, from
-    (contrib, stride, pair, valid_len, offset, ctrl, ws) per shard: contrib
-    the [N, stride] rows, pair the paired state's (master, m, v) views, ws
-    the shard's workspace tensor."""
+    (contrib, stride, pair, valid_len, offset, ctrl, ws, state, g) per shard:
+    contrib the [N, stride] rows, pair the paired state's (master, m, v) views
+    (fused path, else None), ws the shard's workspace tensor, state the flat
+    (master, m, v) and g the gradient buffer (two-pass path, else None)."""
     table = (Shard * len(shards))()
-    for d, (contrib, stride, pair, valid_len, offset, ctrl, ws) in zip(table, shards):
-        d.contrib, d.stride, d.pair = _ptr(contrib), stride, _ptr(pair[0])
+    for d, (contrib, stride, pair, valid_len, offset, ctrl, ws, state, g) in zip(table, shards):
+        d.contrib, d.stride = _ptr(contrib), stride
+        d.pair = _ptr(pair[0]) if pair is not None else None
         d.valid_len, d.offset, d.ctrl = valid_len, offset, _ptr(ctrl)
         d.ws, d.ws_bytes = _ptr(ws), ws.numel() * ws.element_size()
+        if state is not None:
+            d.state = _state(state)
+        d.g = _ptr(g) if g is not None else None
     return table
 
 
@@ -351,6 +360,16 @@ def zero_fused_step_shards(table, contrib_dtype: int, nranks: int, gather, gathe
 def zero_fused_restore_shards(table, gather, gather_dtype: int) -> None:
     _check("zero_fused_restore_shards", _lib.zero_fused_restore_shards(
         table, len(table), _ptr(gather), gather_dtype, _stream()))
+
+
+def zero_reduce_grads_shards(table, contrib_dtype: int, nranks: int) -> None:
+    _check("zero_reduce_grads_shards", _lib.zero_reduce_grads_shards(
+        table, len(table), contrib_dtype, nranks, _stream()))
+
+
+def zero_adam_step_shards(table, hp: Hparams, gather, gather_dtype: int) -> None:
+    _check("zero_adam_step_shards", _lib.zero_adam_step_shards(
+        table, len(table), ctypes.byref(hp), _ptr(gather), gather_dtype, _stream()))
 
 
 def zero_pair_store(flat, pair, valid_len: int, ctrl) -> None:
@@ -659,11 +678,13 @@ class MultiShardStep:
     ranks share one path and one set of hyperparameters; each takes its own
     contributions (any form ShardStep takes) and optional payload.
 
-    With ``batched`` (the default), a fused step whose ranks all take one
-    [N, stride] contribution tensor, write the 16-bit slot and no payload,
-    come in one piece and fit one launch goes through the batched calls:
-    one zero_fused_step_shards, the decision, one zero_fused_restore_shards
-    (per 32 ranks), bit-identical to every rank's own calls."""
+    With ``batched`` (the default), a step whose ranks all take one [N, stride]
+    contribution tensor, write no quantised payload, come in one piece and fit
+    one launch goes through the batched calls, one launch per 32 ranks and
+    pass: zero_fused_step_shards, the decision, zero_fused_restore_shards on
+    the fused path (which also needs the 16-bit slot); zero_reduce_grads_shards,
+    the decision, zero_adam_step_shards on the two-pass path.  Bit-identical to
+    every rank's own calls."""
 
     def __init__(self, steps: list, batched: bool = True):
         if not 1 <= len(steps) <= MAX_RANKS:
@@ -679,7 +700,9 @@ class MultiShardStep:
     def _batch_table(self, contribs, gather, qgathers):
         """The shard table of a step the batched calls can take, or None."""
         ss, s0 = self.steps, self.steps[0]
-        if not (self.batched and self.fused) or gather is None or any(q is not None for q in qgathers):
+        if not self.batched or any(q is not None for q in qgathers):
+            return None
+        if self.fused and gather is None:
             return None
         cap = launch_tiles(s0.nranks) * TILE
         if any(s.bucket or s.valid_len > cap or s.nranks != s0.nranks or s.dtype != s0.dtype
@@ -689,8 +712,9 @@ class MultiShardStep:
             return None
         key = tuple(c.data_ptr() for c in contribs)
         if self._table is None or self._table[0] != key:
-            self._table = (key, shard_table([(c, s.stride, s.pair, s.valid_len, s.offset, s.ctrl,
-                                              s.ws) for s, c in zip(ss, contribs)]))
+            self._table = (key, shard_table([
+                (c, s.stride, s.pair, s.valid_len, s.offset, s.ctrl, s.ws,
+                 None if self.fused else s.state, s.g) for s, c in zip(ss, contribs)]))
         return self._table[1]
 
     def step(self, contribs, gather, qgathers=None, branches: list | None = None) -> None:
@@ -731,14 +755,16 @@ class MultiShardStep:
             main.wait_stream(b)
 
     def run_passes(self, contribs, gather, qgathers=None, branches=None) -> None:
-        """The per-element launches of a step: every rank's fused pass (one
-        batched launch per 32 ranks when the step allows) or reduce pass."""
+        """The per-element launches of a step: every rank's fused pass or
+        reduce pass (one batched launch per 32 ranks when the step allows)."""
         ss = self.steps
         qgathers = self._payloads(contribs, qgathers)
         table = self._batch_table(contribs, gather, qgathers)
-        if table is not None:
-            s0 = ss[0]
+        s0 = ss[0]
+        if table is not None and self.fused:
             zero_fused_step_shards(table, s0.dtype, s0.nranks, gather, s0.gather_dtype, s0.hp)
+        elif table is not None:
+            zero_reduce_grads_shards(table, s0.dtype, s0.nranks)
         else:
             self._per_rank(lambda i: ss[i].run_pieces(contribs[i], gather, qgathers[i]), branches)
 
@@ -749,13 +775,15 @@ class MultiShardStep:
                                 [s.ctrl for s in ss], ss[0].hp, self.fused)
 
     def complete(self, contribs, gather, qgathers=None, branches=None) -> None:
-        """The rest of the step: every rank's restore check (batched when the
-        passes were) or Adam pass."""
+        """The rest of the step: every rank's restore check or Adam pass
+        (batched when the passes were)."""
         ss = self.steps
         qgathers = self._payloads(contribs, qgathers)
         table = self._batch_table(contribs, gather, qgathers)
-        if table is not None:
+        if table is not None and self.fused:
             zero_fused_restore_shards(table, gather, ss[0].gather_dtype)
+        elif table is not None:
+            zero_adam_step_shards(table, ss[0].hp, gather, ss[0].gather_dtype)
         else:
             self._per_rank(lambda i: ss[i].complete(gather, qgathers[i]), branches)
 

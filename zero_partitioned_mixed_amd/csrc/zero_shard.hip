@@ -618,14 +618,14 @@ struct ReduceArgs {
     int32_t n;
 };
 
-// Pass 1 of the two-pass step: g = fl32(sum_k C[k]) * inv, plus one partial
-// per tile.
-template <int NR, class SRC>
-__global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs<SRC> a) {
+// Pass 1 of the two-pass step over one tile (the workgroup's, or tile_at when
+// AT): g = fl32(sum_k C[k]) * inv, plus the tile's partial.
+template <int NR, class SRC, bool AT = false>
+__device__ __forceinline__ void reduce_tile(const ReduceArgs<SRC>& a, int64_t tile_at = 0) {
     const float inv = (float)(1.0 / ((double)a.n * (double)a.ctrl->loss_scale));
     double ss = 0.0;
     uint32_t bad = 0;
-    const int64_t tile = tile_index<SRC::kGrouped>();
+    const int64_t tile = AT ? tile_at : tile_index<SRC::kGrouped>();
     const Runs r = runs_of(tile);
     if (r.b + kRun <= a.len) {
         float acc[kVec], out[kVec];
@@ -653,6 +653,11 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs<SRC> a) {
         }
     }
     write_partial(a.ws, tile, ss, bad);
+}
+
+template <int NR, class SRC>
+__global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs<SRC> a) {
+    reduce_tile<NR, SRC>(a);
 }
 
 struct CombineArgs {
@@ -813,13 +818,14 @@ struct AdamArgs {
 // as one block of the all-gather payload.  A skipped step returns from every
 // workgroup (the flag is the same for all its threads) before writing
 // anything, so slot and payload keep the previous step's values.
-template <int DT, int GW, int QB>
-__device__ __forceinline__ void adam_tile(const AdamArgs& a, const QGatherOut& qo) {
+template <int DT, int GW, int QB, bool AT = false>
+__device__ __forceinline__ void adam_tile(const AdamArgs& a, const QGatherOut& qo,
+                                          int64_t tile_at = 0) {
     const zero_ctrl* __restrict__ c = a.ctrl;
     if (c->skip) return;
     const float clip = c->clip;
     const AdamK k = make_adam(a.hp, c->beta1_pow, c->beta2_pow);
-    const Runs r = runs_of(blockIdx.x);
+    const Runs r = runs_of(AT ? tile_at : (int64_t)blockIdx.x);
     float xq[kVec];  // QB: the new 16-bit parameters widened to fp32, 0 past the end
     if (r.b + kRun <= a.len) {
         float g[kVec], p[kVec], m[kVec], v[kVec];
@@ -854,7 +860,9 @@ __device__ __forceinline__ void adam_tile(const AdamArgs& a, const QGatherOut& q
             a.master[i] = p;
             a.m[i] = m;
             a.v[i] = v;
-            if constexpr (QB == 0) {
+            if constexpr (QB == 0 && GW == kGwRuntime) {
+                if (qo.gw != 0) a.slot[i] = (uint16_t)narrow<DT>(p);
+            } else if constexpr (QB == 0) {
                 if constexpr (GW > 0) a.slot[i] = (uint16_t)narrow<DT>(p);
             } else {
                 const uint32_t hj = narrow<DT>(p);
@@ -1154,7 +1162,8 @@ struct ShardsArgs {
 
 // The workgroup's shard: the last one whose first workgroup is at or below
 // blockIdx.x (tile0 increases with k; a workgroup-uniform scan).
-__device__ __forceinline__ int shard_of(const ShardsArgs& a) {
+template <class Args>
+__device__ __forceinline__ int shard_of(const Args& a) {
     const int64_t w = blockIdx.x;
     int k = 0;
     for (int q = 1; q < a.nshards; ++q)
@@ -1196,6 +1205,47 @@ __global__ void __launch_bounds__(kBlock) restore_shards_kernel(ShardsArgs a) {
             if (i < s.len) s.slot[i] = (uint16_t)narrow<DT>(s.pair[pair_index(i, cur)]);
         }
     }
+}
+
+// The two passes of the two-pass step for several shards: the reduce (rows
+// to g and partials) and, after the decision, the Adam pass (in place on the
+// flat state, cast into the slot), each one launch over the shards' tiles.
+struct PassArg {
+    const uint16_t* rows;  // [n, stride] 16-bit rows (reduce)
+    int64_t stride;
+    float* master;         // flat state (Adam)
+    float* m;
+    float* v;
+    float* g;
+    uint16_t* slot;        // gather buffer + offset, or null (Adam)
+    int64_t len;
+    Partial* ws;           // (reduce)
+    const zero_ctrl* ctrl;
+    int32_t tile0;
+    int32_t gw;            // slot store width: 4, 2, 1, or 0 for no slot
+};
+
+struct PassesArgs {
+    PassArg s[ZERO_BATCH_SHARDS];
+    zero_hparams hp;
+    int32_t nshards;
+    int32_t n;
+};
+
+template <int DT, int NR>
+__global__ void __launch_bounds__(kBlock) reduce_shards_kernel(PassesArgs a) {
+    using SRC = Src16<DT, StridedRows>;
+    const PassArg& s = a.s[shard_of(a)];
+    const ReduceArgs<SRC> r{SRC{StridedRows{s.rows, s.stride}}, s.len, s.ctrl, s.g, s.ws, a.n};
+    reduce_tile<NR, SRC, true>(r, (int64_t)blockIdx.x - s.tile0);
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kBlock) adam_shards_kernel(PassesArgs a) {
+    const PassArg& s = a.s[shard_of(a)];
+    const AdamArgs aa{s.master, s.m, s.v, s.g, s.slot, s.len, s.ctrl, a.hp};
+    adam_tile<DT, kGwRuntime, 0, true>(aa, QGatherOut{nullptr, nullptr, s.gw},
+                                       (int64_t)blockIdx.x - s.tile0);
 }
 
 // ---------------------------------------------------------------- block quantisation
@@ -1867,17 +1917,23 @@ int fused_qgather_launch(const SRC& src, int32_t nranks, const zero_state* pair,
                           Residency<SRC>::fused_q);
 }
 
-// Checks every shard of a batched call before anything is enqueued.  The
-// fused step (restore = false) needs the contribution rows, the workspace and
-// at most launch_tiles(n) tiles per shard; the restore only the state, slot
-// and ctrl, and at most ZERO_LAUNCH_TILES tiles per shard.
+// What a batched call does with its shards, for the checks below.
+enum class ShardCall { kFused, kRestore, kReduce, kAdam };
+
+// Checks every shard of a batched call before anything is enqueued: the
+// shard count, each shard's length (at most one launch of tiles: launch_tiles(n)
+// for a pass over rows, ZERO_LAUNCH_TILES otherwise), and the buffers the call
+// reads or writes: rows and workspace (fused, reduce), paired state (fused,
+// restore), flat state and g (reduce: g; Adam: both), ctrl, and the slot
+// (fused, restore; Adam when gather is not null).
 int check_shards(const zero_shard* shards, int32_t nshards, int32_t contrib_dtype, int32_t n,
-                 const void* gather, int32_t gather_dtype, bool restore, const char* what) {
+                 const void* gather, int32_t gather_dtype, ShardCall call, const char* what) {
     int rc;
     if (shards == nullptr) return fail(ZERO_EINVAL, "%s: null shard array", what);
     if (nshards < 1 || nshards > ZERO_MAX_RANKS)
         return fail(ZERO_EINVAL, "%s: nshards %d outside [1, %d]", what, nshards, ZERO_MAX_RANKS);
-    const int64_t cap = restore ? ZERO_LAUNCH_TILES : launch_tiles(n);
+    const bool rows = call == ShardCall::kFused || call == ShardCall::kReduce;
+    const int64_t cap = rows ? launch_tiles(n) : ZERO_LAUNCH_TILES;
     for (int i = 0; i < nshards; ++i) {
         const zero_shard& z = shards[i];
         if ((rc = check_len(z.valid_len, what)) != ZERO_OK) return rc;
@@ -1885,25 +1941,32 @@ int check_shards(const zero_shard* shards, int32_t nshards, int32_t contrib_dtyp
             return fail(ZERO_ERANGE, "%s: shard %d has %lld tiles, more than the %lld of one "
                         "launch; step it with its own calls", what, i,
                         (long long)tiles_for(z.valid_len), (long long)cap);
-        if (!restore) {
+        if (rows) {
             if ((rc = check_contrib(z.contrib_dev, contrib_dtype, n, z.stride, z.valid_len)) != ZERO_OK)
                 return rc;
             if ((rc = check_ws(z.ws_dev, z.ws_bytes, z.valid_len)) != ZERO_OK) return rc;
         }
-        if (z.pair_dev == nullptr || !aligned16(z.pair_dev))
+        if ((call == ShardCall::kFused || call == ShardCall::kRestore) &&
+            (z.pair_dev == nullptr || !aligned16(z.pair_dev)))
             return fail(ZERO_EINVAL, "%s: shard %d: paired state null or not 16-byte aligned", what, i);
+        if ((call == ShardCall::kReduce || call == ShardCall::kAdam) &&
+            (z.g_dev == nullptr || !aligned16(z.g_dev)))
+            return fail(ZERO_EINVAL, "%s: shard %d: g null or not 16-byte aligned", what, i);
+        if (call == ShardCall::kAdam && (rc = check_state(&z.state, what)) != ZERO_OK) return rc;
         if ((rc = check_ctrl(z.ctrl_dev, what)) != ZERO_OK) return rc;
+        if (call == ShardCall::kReduce || (call == ShardCall::kAdam && gather == nullptr)) continue;
         if ((rc = check_slot(gather, gather_dtype, z.offset)) != ZERO_OK) return rc;
     }
     return ZERO_OK;
 }
 
 // Packs the non-empty shards into launches of at most ZERO_BATCH_SHARDS shards
-// and `cap` tiles and calls launch_one(args, tiles) for each, in shard order.
-template <class LaunchOne>
-int for_each_shard_launch(const zero_shard* shards, int32_t nshards, uint16_t* gather,
-                          int64_t cap, LaunchOne&& launch_one) {
-    ShardsArgs a{};
+// and `cap` tiles; fill(entry, shard) fills an entry of the kernel arguments
+// and launch_one(args, tiles) launches, in shard order.
+template <class Args, class Fill, class LaunchOne>
+int for_each_shard_launch(const zero_shard* shards, int32_t nshards, int64_t cap, Fill&& fill,
+                          LaunchOne&& launch_one) {
+    Args a{};
     int64_t tiles = 0;
     for (int i = 0; i < nshards; ++i) {
         const zero_shard& z = shards[i];
@@ -1912,22 +1975,42 @@ int for_each_shard_launch(const zero_shard* shards, int32_t nshards, uint16_t* g
         if (a.nshards == ZERO_BATCH_SHARDS || tiles + t > cap) {
             const int rc = launch_one(a, tiles);
             if (rc != ZERO_OK) return rc;
-            a = ShardsArgs{};
+            a = Args{};
             tiles = 0;
         }
-        ShardArg& s = a.s[a.nshards++];
-        s.rows = (const uint16_t*)z.contrib_dev;
-        s.stride = z.stride;
-        s.pair = z.pair_dev;
-        s.slot = gather + z.offset;
-        s.len = z.valid_len;
-        s.ws = (Partial*)z.ws_dev;
-        s.ctrl = z.ctrl_dev;
-        s.tile0 = (int32_t)tiles;
-        s.gw = store_width(s.slot);
+        auto& e = a.s[a.nshards++];
+        fill(e, z);
+        e.tile0 = (int32_t)tiles;
         tiles += t;
     }
     return a.nshards > 0 ? launch_one(a, tiles) : ok();
+}
+
+// A shard's entry for the fused step and the restore.
+void fill_shard(ShardArg& e, const zero_shard& z, uint16_t* gather) {
+    e.rows = (const uint16_t*)z.contrib_dev;
+    e.stride = z.stride;
+    e.pair = z.pair_dev;
+    e.slot = gather + z.offset;
+    e.len = z.valid_len;
+    e.ws = (Partial*)z.ws_dev;
+    e.ctrl = z.ctrl_dev;
+    e.gw = store_width(e.slot);
+}
+
+// A shard's entry for the two passes of the two-pass step.
+void fill_pass(PassArg& e, const zero_shard& z, uint16_t* gather) {
+    e.rows = (const uint16_t*)z.contrib_dev;
+    e.stride = z.stride;
+    e.master = z.state.master;
+    e.m = z.state.m;
+    e.v = z.state.v;
+    e.g = z.g_dev;
+    e.slot = gather == nullptr ? nullptr : gather + z.offset;
+    e.len = z.valid_len;
+    e.ws = (Partial*)z.ws_dev;
+    e.ctrl = z.ctrl_dev;
+    e.gw = e.slot == nullptr ? 0 : store_width(e.slot);
 }
 
 template <int DT>
@@ -2294,33 +2377,80 @@ int zero_fused_step_shards(const zero_shard* shards, int32_t nshards, int32_t co
     const char* what = "zero_fused_step_shards";
     if ((rc = check_hp(hp)) != ZERO_OK) return rc;
     if (hp->max_grad_norm > 0.0f) return fail(ZERO_EINVAL, "%s: clipping needs the two-pass path", what);
-    if ((rc = check_shards(shards, nshards, contrib_dtype, nranks, gather, gather_dtype, false,
-                           what)) != ZERO_OK)
+    if ((rc = check_shards(shards, nshards, contrib_dtype, nranks, gather, gather_dtype,
+                           ShardCall::kFused, what)) != ZERO_OK)
         return rc;
     const Kernel<ShardsArgs> k = contrib_dtype == ZERO_F16
                                      ? fused_shards_for<ZERO_F16>(gather_dtype, nranks)
                                      : fused_shards_for<ZERO_BF16>(gather_dtype, nranks);
-    return for_each_shard_launch(shards, nshards, (uint16_t*)gather, launch_tiles(nranks),
-                                 [&](ShardsArgs& a, int64_t tiles) {
-                                     a.hp = *hp;
-                                     a.n = nranks;
-                                     return launch(k, tiles, kBlock, (hipStream_t)stream, a, what,
-                                                   kResidencyLds);
-                                 });
+    return for_each_shard_launch<ShardsArgs>(
+        shards, nshards, launch_tiles(nranks),
+        [&](ShardArg& e, const zero_shard& z) { fill_shard(e, z, (uint16_t*)gather); },
+        [&](ShardsArgs& a, int64_t tiles) {
+            a.hp = *hp;
+            a.n = nranks;
+            return launch(k, tiles, kBlock, (hipStream_t)stream, a, what, kResidencyLds);
+        });
 }
 
 int zero_fused_restore_shards(const zero_shard* shards, int32_t nshards, void* gather,
                               int32_t gather_dtype, void* stream) {
     int rc;
     const char* what = "zero_fused_restore_shards";
-    if ((rc = check_shards(shards, nshards, ZERO_F16, 1, gather, gather_dtype, true, what)) != ZERO_OK)
+    if ((rc = check_shards(shards, nshards, ZERO_F16, 1, gather, gather_dtype, ShardCall::kRestore,
+                           what)) != ZERO_OK)
         return rc;
     const Kernel<ShardsArgs> k = gather_dtype == ZERO_F16 ? restore_shards_kernel<ZERO_F16>
                                                           : restore_shards_kernel<ZERO_BF16>;
-    return for_each_shard_launch(shards, nshards, (uint16_t*)gather, ZERO_LAUNCH_TILES,
-                                 [&](ShardsArgs& a, int64_t tiles) {
-                                     return launch(k, tiles, kBlock, (hipStream_t)stream, a, what);
-                                 });
+    return for_each_shard_launch<ShardsArgs>(
+        shards, nshards, ZERO_LAUNCH_TILES,
+        [&](ShardArg& e, const zero_shard& z) { fill_shard(e, z, (uint16_t*)gather); },
+        [&](ShardsArgs& a, int64_t tiles) {
+            return launch(k, tiles, kBlock, (hipStream_t)stream, a, what);
+        });
+}
+
+int zero_reduce_grads_shards(const zero_shard* shards, int32_t nshards, int32_t contrib_dtype,
+                             int32_t nranks, void* stream) {
+    int rc;
+    const char* what = "zero_reduce_grads_shards";
+    if ((rc = check_shards(shards, nshards, contrib_dtype, nranks, nullptr, ZERO_F16,
+                           ShardCall::kReduce, what)) != ZERO_OK)
+        return rc;
+    Kernel<PassesArgs> k;
+    if (nranks == 8)
+        k = contrib_dtype == ZERO_F16 ? reduce_shards_kernel<ZERO_F16, 8> : reduce_shards_kernel<ZERO_BF16, 8>;
+    else
+        k = contrib_dtype == ZERO_F16 ? reduce_shards_kernel<ZERO_F16, 0> : reduce_shards_kernel<ZERO_BF16, 0>;
+    return for_each_shard_launch<PassesArgs>(
+        shards, nshards, launch_tiles(nranks),
+        [&](PassArg& e, const zero_shard& z) { fill_pass(e, z, nullptr); },
+        [&](PassesArgs& a, int64_t tiles) {
+            a.n = nranks;
+            return launch(k, tiles, kBlock, (hipStream_t)stream, a, what,
+                          Residency<Src16<ZERO_F16, StridedRows>>::reduce);
+        });
+}
+
+int zero_adam_step_shards(const zero_shard* shards, int32_t nshards, const zero_hparams* hp,
+                          void* gather, int32_t gather_dtype, void* stream) {
+    int rc;
+    const char* what = "zero_adam_step_shards";
+    if ((rc = check_hp(hp)) != ZERO_OK) return rc;
+    if (gather == nullptr && !valid_dtype(gather_dtype))
+        return fail(ZERO_EINVAL, "%s: unknown gather dtype %d", what, gather_dtype);
+    if ((rc = check_shards(shards, nshards, ZERO_F16, 1, gather, gather_dtype, ShardCall::kAdam,
+                           what)) != ZERO_OK)
+        return rc;
+    const Kernel<PassesArgs> k = gather_dtype == ZERO_F16 ? adam_shards_kernel<ZERO_F16>
+                                                          : adam_shards_kernel<ZERO_BF16>;
+    return for_each_shard_launch<PassesArgs>(
+        shards, nshards, ZERO_LAUNCH_TILES,
+        [&](PassArg& e, const zero_shard& z) { fill_pass(e, z, (uint16_t*)gather); },
+        [&](PassesArgs& a, int64_t tiles) {
+            a.hp = *hp;
+            return launch(k, tiles, kBlock, (hipStream_t)stream, a, what, kResidencyLds);
+        });
 }
 
 int zero_fused_step_qgather(const void* contrib, int32_t contrib_dtype, int32_t nranks,
