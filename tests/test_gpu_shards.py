@@ -151,3 +151,48 @@ def test_batched_shards_in_a_graph(name):
     for x, y in zip(sa, sb):
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
     assert np.array_equal(ga, gb)
+
+
+def _draw(seed: int):
+    """A random multi-rank step: N, Psi (ragged, sometimes with empty tail
+    ranks), a random subset of the ranks (at most 64) in random order, the
+    formats in and out, the path, the scaler, the step count, decay, and
+    sometimes a +inf in one rank's rows."""
+    rng = np.random.default_rng(5000 + seed)
+    n = int(rng.choice([1, 2, 3, 5, 8, 8, 13, 32, 64]))
+    psi = int(rng.integers(1, 200_000))
+    nr = int(rng.integers(1, n + 1))
+    ranks = tuple(int(r) for r in rng.permutation(n)[:nr])
+    dtype = int(rng.choice([F16, BF16]))
+    gdt = int(rng.choice([F16, BF16]))
+    steps = int(rng.integers(1, 4))
+    scaler = int(rng.choice([0, 1, 2]))
+    scale = float(2.0 ** int(rng.integers(4, 12))) if scaler else 1.0
+    kw = dict(contrib_scale=scale, loss_scale=scale, scaler=scaler, growth_interval=2,
+              weight_decay=float(rng.choice([0.0, 0.01])), gather_dtype=gdt)
+    if rng.random() < 0.5:
+        kw["max_grad_norm"] = float(rng.choice([1e-3, 0.05, 10.0]))
+    w = _ws(psi, n, ranks, dtype=dtype, steps=steps, **kw)
+    inject = None
+    if rng.random() < 0.3 and steps > 1:
+        i = int(rng.integers(0, nr))
+        _, _, valid = H.O.partition(psi, n, ranks[i])
+        if valid:
+            inject = (int(rng.integers(1, steps + 1)), i, int(rng.integers(0, n)),
+                      int(rng.integers(0, valid)))
+    return w, inject
+
+
+@pytest.mark.parametrize("seed", range(1, 49))
+def test_random_batched_shards_equal_their_own_calls(seed):
+    """48 random multi-rank steps through the batched calls and through every
+    rank's own calls: bit for bit, as in the fixed cases."""
+    w, inject = _draw(seed)
+    ra, sa, ga = _run(w, inject, batched=False)
+    rb, sb, gb = _run(w, inject, batched=True)
+    assert repr(ra) == repr(rb)
+    for x, y in zip(sa, sb):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    assert np.array_equal(ga, gb)
+    H.log(f"random shards {seed}: psi={w.psi} N={w.nranks} ranks={len(w.ranks)} "
+          f"{w.variant} inject={inject}: batched equals per-rank calls")
