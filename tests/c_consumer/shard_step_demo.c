@@ -14,6 +14,8 @@
  *     rank 2, two-pass path as rank 1, writing the slot and an INT4 payload
  *     rank 1, fused path as rank 2 over INT8-quantised contributions, writing
  *       only the INT8 payload (ZeRO++ end to end)
+ *     all three ranks at once through the batched calls, fused path as rank 2
+ *       (the +inf in rank 1's contribution 2), then two-pass path as rank 1
  *   all of Psi = 120,007 (fp16) over N = 3 ranks, 3 steps.
  */
 #include <hip/hip_runtime_api.h>
@@ -210,6 +212,112 @@ static void run_rank(FILE *f, int32_t rank, float max_grad_norm, int inject, int
     free(out);
 }
 
+/* All NR ranks' STEPS steps through the batched calls (one launch per pass
+ * for all of them) with one shared decision per step; appends every rank's
+ * ctrl after each step, then each rank's master, m, v (its valid floats
+ * each), then the whole parameter buffer (PSI 16-bit words). */
+static void run_batched(FILE *f, float max_grad_norm) {
+    const int fused = !(max_grad_norm > 0.0f);
+    zero_hparams hp = {1e-3f, 0.9f, 0.999f, 1e-8f, 0.0f, max_grad_norm,
+                       fused ? ZERO_SCALER_DYNAMIC : ZERO_SCALER_STATIC, 1.0f, 1000};
+    zero_shard sh[NR];
+    void *ws_arr[NR];
+    int64_t len_arr[NR], off_arr[NR];
+    zero_ctrl *ctrl_arr[NR];
+    uint16_t *C[NR];
+    float *bufs[NR][5]; /* flat master, m, v; g; paired buffer */
+    uint16_t *gather = malloc(sizeof(uint16_t) * PSI);
+    void *dG;
+    synth_param_range(0, 0.02, ZERO_F16, 0, PSI, gather);
+    HIP(hipMalloc(&dG, sizeof(uint16_t) * PSI));
+    HIP(hipMemcpy(dG, gather, sizeof(uint16_t) * PSI, hipMemcpyHostToDevice));
+    memset(sh, 0, sizeof sh);
+    for (int r = 0; r < NR; ++r) {
+        int64_t shard, off, valid;
+        ZERO(zero_partition(PSI, NR, r, &shard, &off, &valid));
+        const int64_t stride = (shard + 63) / 64 * 64;
+        float *p0 = malloc(sizeof(float) * valid);
+        synth_master_range(0, 0.02, off, valid, p0);
+        C[r] = malloc(sizeof(uint16_t) * NR * stride);
+        void *dC, *dWs;
+        zero_ctrl *dCtrl;
+        HIP(hipMalloc(&dC, sizeof(uint16_t) * NR * stride));
+        HIP(hipMalloc((void **)&dCtrl, zero_ctrl_bytes()));
+        HIP(hipMalloc(&dWs, zero_workspace_bytes(valid)));
+        for (int q = 0; q < 4; ++q) {
+            HIP(hipMalloc((void **)&bufs[r][q], sizeof(float) * valid));
+            HIP(hipMemset(bufs[r][q], 0, sizeof(float) * valid));
+        }
+        HIP(hipMalloc((void **)&bufs[r][4], sizeof(float) * zero_pair_elems(valid)));
+        HIP(hipMemcpy(bufs[r][0], p0, sizeof(float) * valid, hipMemcpyHostToDevice));
+        ZERO(zero_ctrl_init(dCtrl, (float)SCALE, NULL));
+        zero_state flat = {bufs[r][0], bufs[r][1], bufs[r][2]};
+        zero_state pair = {bufs[r][4], bufs[r][4] + ZERO_TILE, bufs[r][4] + 2 * ZERO_TILE};
+        if (fused) ZERO(zero_pair_store(&flat, &pair, valid, dCtrl, NULL));
+        sh[r].contrib_dev = dC;
+        sh[r].stride = stride;
+        sh[r].pair_dev = bufs[r][4];
+        sh[r].valid_len = valid;
+        sh[r].offset = off;
+        sh[r].ctrl_dev = dCtrl;
+        sh[r].ws_dev = dWs;
+        sh[r].ws_bytes = zero_workspace_bytes(valid);
+        sh[r].state = flat;
+        sh[r].g_dev = bufs[r][3];
+        ws_arr[r] = dWs;
+        len_arr[r] = valid;
+        off_arr[r] = off;
+        ctrl_arr[r] = dCtrl;
+        free(p0);
+    }
+    for (uint32_t s = 1; s <= STEPS; ++s) {
+        for (int r = 0; r < NR; ++r) {
+            synth_contrib_rows(0, s, NR, ZERO_F16, 1e-3, SCALE, 0, 100.0, off_arr[r], len_arr[r],
+                               sh[r].stride, C[r]);
+            if (fused && r == 1 && s == 2) C[r][2 * sh[r].stride + 77] = 0x7C00; /* +inf */
+            HIP(hipMemcpy((void *)sh[r].contrib_dev, C[r], sizeof(uint16_t) * NR * sh[r].stride,
+                          hipMemcpyHostToDevice));
+        }
+        if (fused) {
+            ZERO(zero_fused_step_shards(sh, NR, ZERO_F16, NR, dG, ZERO_F16, &hp, NULL));
+            ZERO(zero_grad_norm_overflow(NR, ws_arr, len_arr, ctrl_arr, &hp, 1, NULL));
+            ZERO(zero_fused_restore_shards(sh, NR, dG, ZERO_F16, NULL));
+        } else {
+            ZERO(zero_reduce_grads_shards(sh, NR, ZERO_F16, NR, NULL));
+            ZERO(zero_grad_norm_overflow(NR, ws_arr, len_arr, ctrl_arr, &hp, 0, NULL));
+            ZERO(zero_adam_step_shards(sh, NR, &hp, dG, ZERO_F16, NULL));
+        }
+        for (int r = 0; r < NR; ++r) {
+            zero_ctrl c;
+            HIP(hipMemcpy(&c, ctrl_arr[r], sizeof c, hipMemcpyDeviceToHost));
+            fwrite(&c, sizeof c, 1, f);
+        }
+    }
+    for (int r = 0; r < NR; ++r) {
+        const int64_t valid = len_arr[r];
+        zero_state pair = {bufs[r][4], bufs[r][4] + ZERO_TILE, bufs[r][4] + 2 * ZERO_TILE};
+        if (fused) ZERO(zero_pair_load(&pair, &sh[r].state, valid, ctrl_arr[r], NULL));
+        HIP(hipDeviceSynchronize());
+        float *out = malloc(sizeof(float) * (valid ? valid : 1));
+        for (int q = 0; q < 3; ++q) {
+            HIP(hipMemcpy(out, bufs[r][q], sizeof(float) * valid, hipMemcpyDeviceToHost));
+            fwrite(out, sizeof(float), (size_t)valid, f);
+        }
+        free(out);
+    }
+    HIP(hipMemcpy(gather, dG, sizeof(uint16_t) * PSI, hipMemcpyDeviceToHost));
+    fwrite(gather, sizeof(uint16_t), PSI, f);
+    for (int r = 0; r < NR; ++r) {
+        for (int q = 0; q < 5; ++q) HIP(hipFree(bufs[r][q]));
+        HIP(hipFree((void *)sh[r].contrib_dev));
+        HIP(hipFree(sh[r].ws_dev));
+        HIP(hipFree(ctrl_arr[r]));
+        free(C[r]);
+    }
+    HIP(hipFree(dG));
+    free(gather);
+}
+
 int main(int argc, char **argv) {
     if (argc >= 2 && strcmp(argv[1], "host") == 0) return host_mode();
     if (argc >= 3 && strcmp(argv[1], "gpu") == 0) {
@@ -220,6 +328,8 @@ int main(int argc, char **argv) {
         run_rank(f, 0, 0.0f, 1, 0, 8, 0);
         run_rank(f, 2, 0.01f, 0, 1, 4, 0);
         run_rank(f, 1, 0.0f, 1, 0, 8, 8);
+        run_batched(f, 0.0f);
+        run_batched(f, 0.01f);
         fclose(f);
         printf("gpu ok\n");
         return 0;
